@@ -1,0 +1,201 @@
+"""CPU oracle for the FP16-input, FP32-accumulate GEMM  C = alpha*A@B + beta*C.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU library
+(``dense_mixed_precision_amd``) never imports it, and the two share no code:
+the arithmetic lives in ``oracle.c`` (plain C, FP64), built by :func:`build`
+with gcc into ``liboracle.so`` and called here through ctypes.
+
+What it computes is the plain definition of the product ("Capstone 4: a
+tensor-core GEMM", Minimal model and Compare like with like): FP16 inputs
+widened exactly to FP64, products exact, the sum carried in FP64 in ascending
+k, then ``alpha*s + beta*c`` with C not read when ``beta == 0``.
+
+The acceptance rule for a GPU result ``c`` against this oracle is
+``|c - ref| <= 1e-3 * sum_k|a_ik*b_kj| + 1e-5`` elementwise (see
+:func:`tolerance_ok`); the oracle returns that sum alongside the result.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+#: gcc flags: no fast-math, no contraction, so the FP64 sum is evaluated
+#: exactly as written (ascending k, separate multiply and add).
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+          "-fPIC", "-shared"]
+
+# Relative and absolute terms of the acceptance rule.
+TOL_REL = 1e-3
+TOL_ABS = 1e-5
+
+_lib = None
+
+
+def build() -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` (always recompiles)."""
+    global _lib
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, _LIB_PATH)
+    _lib = None
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = ctypes.c_double
+    lib.oracle_f16_to_f64_array.argtypes = [vp, i64, vp]
+    lib.oracle_f16_to_f64_array.restype = None
+    lib.oracle_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64,
+                                ctypes.c_double, ctypes.c_double, vp, vp]
+    lib.oracle_gemm.restype = ctypes.c_int
+    lib.oracle_gemm_entries.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64,
+                                        ctypes.c_double, ctypes.c_double,
+                                        i64, vp, vp, vp, vp]
+    lib.oracle_gemm_entries.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS or all host cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _as_bits_2d(x, name):
+    """Return (array, leading dimension) for a 2-D uint16 row-major view."""
+    x = np.asarray(x)
+    if x.dtype == np.float16:
+        x = x.view(np.uint16)
+    if x.dtype != np.uint16 or x.ndim != 2:
+        raise TypeError(f"{name} must be a 2-D float16 or uint16 (FP16 bits) array")
+    if x.size == 0:
+        return np.zeros(x.shape, dtype=np.uint16), max(x.shape[1], 1)
+    if x.strides[1] != 2 or x.strides[0] % 2:
+        raise ValueError(f"{name} must be row-major with unit inner stride")
+    ld = max(x.strides[0] // 2, max(x.shape[1], 1))
+    return x, ld
+
+
+def _as_c(C, M, N, beta):
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        return None, max(N, 1)
+    C = np.asarray(C)
+    if C.dtype != np.float32 or C.ndim != 2 or C.shape != (M, N):
+        raise TypeError("C must be a float32 array of shape (M, N)")
+    if C.strides[1] != 4 or C.strides[0] % 4:
+        raise ValueError("C must be row-major with unit inner stride")
+    return C, max(C.strides[0] // 4, max(N, 1))
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    """Decode FP16 bit patterns to FP64 with the oracle's own decoder."""
+    bits = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().oracle_f16_to_f64_array(_ptr(bits), bits.size, _ptr(out))
+    return out
+
+
+def _check(rc):
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+
+
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0):
+    """Full product.  Returns ``(ref, absdot)``, both float64 (M, N).
+
+    A: (M, K) FP16 bits, B: (K, N) FP16 bits, C: (M, N) float32 or None.
+    alpha and beta are rounded to float32 first, as the GPU entry point
+    receives them.
+    """
+    A, lda = _as_bits_2d(A, "A")
+    B, ldb = _as_bits_2d(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    alpha = float(np.float32(alpha))
+    beta = float(np.float32(beta))
+    C, ldc = _as_c(C, M, N, beta)
+    ref = np.empty((M, N), dtype=np.float64)
+    absdot = np.empty((M, N), dtype=np.float64)
+    _check(_load().oracle_gemm(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                               alpha, beta, _ptr(ref), _ptr(absdot)))
+    return ref, absdot
+
+
+def gemm_entries(A, B, C, alpha: float, beta: float, rows, cols):
+    """Selected entries (rows[t], cols[t]).  Returns ``(ref, absdot)`` 1-D."""
+    A, lda = _as_bits_2d(A, "A")
+    B, ldb = _as_bits_2d(B, "B")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    alpha = float(np.float32(alpha))
+    beta = float(np.float32(beta))
+    C, ldc = _as_c(C, M, N, beta)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape or rows.ndim != 1:
+        raise ValueError("rows and cols must be 1-D and equal length")
+    ref = np.empty(rows.shape, dtype=np.float64)
+    absdot = np.empty(rows.shape, dtype=np.float64)
+    _check(_load().oracle_gemm_entries(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                       alpha, beta, rows.size, _ptr(rows), _ptr(cols),
+                                       _ptr(ref), _ptr(absdot)))
+    return ref, absdot
+
+
+def tolerance_ok(got, ref, absdot):
+    """Elementwise acceptance: ``|got - ref| <= 1e-3*absdot + 1e-5``.
+
+    The comparison is ``err <= tol``, which is False for NaN, so NaN or Inf in
+    ``got`` fails.  Returns a boolean array of the broadcast shape.
+    """
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    tol = TOL_REL * absdot + TOL_ABS
+    return err <= tol
+
+
+def worst(got, ref, absdot):
+    """Diagnostics for a failure message: index of the worst element (by
+    err/tol), its err and tol, and the count of failing elements."""
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    tol = TOL_REL * absdot + TOL_ABS
+    ratio = np.where(np.isfinite(err), err / tol, np.inf)
+    idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape) if ratio.size else ()
+    bad = int(np.count_nonzero(~(err <= tol)))
+    return {"index": tuple(int(i) for i in idx),
+            "got": float(got[idx]) if ratio.size else None,
+            "want": float(ref[idx]) if ratio.size else None,
+            "err": float(err[idx]) if ratio.size else None,
+            "tol": float(tol[idx]) if ratio.size else None,
+            "failing": bad}

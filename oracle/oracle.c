@@ -1,0 +1,182 @@
+/*
+ * oracle.c -- CPU oracle for the FP16-input, FP32-accumulate matrix product
+ *
+ *     C[i][j] <- alpha * sum_k A[i][k] * B[k][j] + beta * C[i][j]
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links it, and it shares no code, header, table or helper with the GPU path.
+ *
+ * What it follows (the method is the plain matrix product, so the oracle is
+ * that definition written out):
+ *   - "Capstone 4: a tensor-core GEMM", Minimal model: A and B are stored as
+ *     FP16, the sum and C are wider (FP32 on the GPU).  Here every input is
+ *     widened exactly to FP64 and the sum is carried in FP64, which is the
+ *     "double-precision CPU result" the same page checks every element against
+ *     (section "Compare like with like").
+ *   - Row-major A (M x K, leading dimension lda), row-major B (K x N, ldb),
+ *     row-major C (M x N, ldc), all leading dimensions counted in elements.
+ *   - beta == 0 means C is not read at all (the output may hold NaN poison,
+ *     "02_mixed_precision_gemm", Verification).
+ *
+ * Arithmetic: an FP16 value is an integer times 2^-24 with at most 11
+ * significant bits, so its FP64 widening is exact and every product of two
+ * widened values is exact in FP64 (22 significant bits).  Only the running
+ * sum rounds, in ascending k order, with error at most K * 2^-53 * sum|a*b|.
+ * Build with -O2 -fno-fast-math -ffp-contract=off so the compiler neither
+ * reassociates the sum nor fuses alpha*s + beta*c.
+ *
+ * Parallelism: rows are split across OpenMP threads; each output element is
+ * computed by one thread in the same order, so results do not depend on the
+ * thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/*
+ * IEEE 754 binary16 -> binary64, from the format's definition:
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ *   exponent 0      : zero or subnormal, value = fraction * 2^-24
+ *   exponent 1..30  : normal, value = (1024 + fraction) * 2^(exponent - 25)
+ *   exponent 31     : infinity (fraction 0) or NaN (fraction != 0)
+ */
+double oracle_f16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int exponent = (h >> 10) & 0x1f;
+    const int fraction = h & 0x3ff;
+    double v;
+    if (exponent == 0) {
+        v = ldexp((double)fraction, -24);
+    } else if (exponent == 31) {
+        v = (fraction == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(1024 + fraction), exponent - 25);
+    }
+    return sign ? -v : v;
+}
+
+void oracle_f16_to_f64_array(const uint16_t *h, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f16_to_f64(h[i]);
+}
+
+/*
+ * One output element: the dot product of row i of A with column j of B in
+ * ascending k, then alpha*s + beta*c.  Also returns sum_k |a_ik * b_kj|, the
+ * scale the acceptance rule is written against.
+ */
+static void entry(int64_t i, int64_t j, int64_t K,
+                  const uint16_t *A, int64_t lda,
+                  const uint16_t *B, int64_t ldb,
+                  const float *C, int64_t ldc,
+                  double alpha, double beta,
+                  double *ref, double *absdot)
+{
+    double s = 0.0;
+    double s_abs = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        const double a = oracle_f16_to_f64(A[i * lda + k]);
+        const double b = oracle_f16_to_f64(B[k * ldb + j]);
+        const double p = a * b; /* exact */
+        s += p;
+        s_abs += fabs(p);
+    }
+    double r = alpha * s;
+    if (beta != 0.0)
+        r += beta * (double)C[i * ldc + j];
+    *ref = r;
+    if (absdot)
+        *absdot = s_abs;
+}
+
+/* Error codes shared by both entry points. */
+#define ORACLE_OK 0
+#define ORACLE_EBADDIM (-1)
+#define ORACLE_EBADLD (-2)
+#define ORACLE_ENULL (-3)
+
+static int check_args(int64_t M, int64_t N, int64_t K,
+                      const uint16_t *A, int64_t lda,
+                      const uint16_t *B, int64_t ldb,
+                      const float *C, int64_t ldc, double beta)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return ORACLE_EBADDIM;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+        return ORACLE_EBADLD;
+    if (M > 0 && N > 0 && K > 0 && (A == NULL || B == NULL))
+        return ORACLE_ENULL;
+    if (M > 0 && N > 0 && beta != 0.0 && C == NULL)
+        return ORACLE_ENULL;
+    return ORACLE_OK;
+}
+
+/*
+ * Full product.  ref and absdot (absdot may be NULL) are M x N, row-major,
+ * packed (leading dimension N), owned by the caller.
+ */
+int oracle_gemm(int64_t M, int64_t N, int64_t K,
+                const uint16_t *A, int64_t lda,
+                const uint16_t *B, int64_t ldb,
+                const float *C, int64_t ldc,
+                double alpha, double beta,
+                double *ref, double *absdot)
+{
+    const int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc, beta);
+    if (rc != ORACLE_OK)
+        return rc;
+    if (M > 0 && N > 0 && ref == NULL)
+        return ORACLE_ENULL;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            entry(i, j, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                  &ref[i * N + j], absdot ? &absdot[i * N + j] : NULL);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Selected entries only: element t of the output is (rows[t], cols[t]).
+ * Used where the full product would take too long on the CPU.
+ */
+int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
+                        const uint16_t *A, int64_t lda,
+                        const uint16_t *B, int64_t ldb,
+                        const float *C, int64_t ldc,
+                        double alpha, double beta,
+                        int64_t count, const int64_t *rows, const int64_t *cols,
+                        double *ref, double *absdot)
+{
+    const int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc, beta);
+    if (rc != ORACLE_OK)
+        return rc;
+    if (count < 0)
+        return ORACLE_EBADDIM;
+    for (int64_t t = 0; t < count; ++t) {
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)
+            return ORACLE_EBADDIM;
+    }
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < count; ++t) {
+        entry(rows[t], cols[t], K, A, lda, B, ldb, C, ldc, alpha, beta,
+              &ref[t], absdot ? &absdot[t] : NULL);
+    }
+    return ORACLE_OK;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,316 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is trusted only after it is checked against things other than
+itself: a library decoder over every FP16 code, exact rational arithmetic on
+tiny shapes, closed forms, values the source pages print, a library FP64
+matmul, exact integer products, and symmetry/linearity identities.  The last
+tests plant plausible mistakes (on the CPU, in copies of the oracle's output)
+and confirm that a pin catches each one.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_mixed_precision_amd.workloads import WORKLOADS, bits, make_inputs, workload_inputs
+from tests.exact import exact_gemm, fp64_sum_bound
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_values.json")))
+
+ALL_CODES = np.arange(65536, dtype=np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# FP16 decoder
+# ----------------------------------------------------------------------------
+
+def test_decoder_exhaustive_matches_numpy():
+    """All 65,536 bit patterns against numpy's float16 -> float64 conversion."""
+    mine = oracle.f16_to_f64(ALL_CODES)
+    lib = ALL_CODES.view(np.float16).astype(np.float64)
+    nan_mine = np.isnan(mine)
+    assert np.array_equal(nan_mine, np.isnan(lib))
+    assert nan_mine.sum() == 2 * 1023  # exponent 31 with non-zero fraction, both signs
+    fin = ~nan_mine
+    assert np.array_equal(mine[fin], lib[fin])
+    assert np.array_equal(np.signbit(mine[fin]), np.signbit(lib[fin]))  # -0.0 stays -0.0
+
+
+def test_decoder_page_values():
+    """Largest finite value and the integer grid the pages state."""
+    vals = oracle.f16_to_f64(ALL_CODES)
+    finite = vals[np.isfinite(vals)]
+    assert finite.max() == GOLDEN["fp16_max_finite"]["value"]
+    assert oracle.f16_to_f64(np.array([0x7BFF], dtype=np.uint16))[0] == 65504.0
+    grid = GOLDEN["fp16_integer_grid"]
+    s = set(finite.tolist())
+    a, b, c = grid["every_integer_up_to"], grid["every_second_up_to"], grid["every_fourth_up_to"]
+    assert all(float(n) in s for n in range(0, a + 1))
+    assert all((float(n) in s) == (n % 2 == 0) for n in range(a, b + 1))
+    assert all((float(n) in s) == (n % 4 == 0) for n in range(b, c + 1))
+    # smallest subnormal and smallest normal
+    assert oracle.f16_to_f64(np.array([0x0001], dtype=np.uint16))[0] == 2.0 ** -24
+    assert oracle.f16_to_f64(np.array([0x0400], dtype=np.uint16))[0] == 2.0 ** -14
+
+
+# ----------------------------------------------------------------------------
+# Exact brute force on tiny shapes
+# ----------------------------------------------------------------------------
+
+def _special_mix(M, K, seed):
+    """FP16 bits mixing uniform values with subnormals, tiny normals, signed
+    zeros and large magnitudes, so every decoder branch feeds the product."""
+    rng = np.random.default_rng(seed)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x0400, 0x3C00, 0xBC00,
+                         0x7BFF, 0xFBFF, 0x5800, 0x1400], dtype=np.uint16)
+    base = bits(make_inputs(M, K, 1, "uniform", seed)[0])
+    mask = rng.random((M, K)) < 0.3
+    pick = specials[rng.integers(0, specials.size, (M, K))]
+    return np.where(mask, pick, base).astype(np.uint16)
+
+
+TINY = [(1, 1, 1), (1, 1, 17), (3, 5, 7), (16, 16, 16), (17, 15, 33), (33, 31, 65)]
+
+
+@pytest.mark.parametrize("M,N,K", TINY)
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (1.5, 0.5), (-0.75, 2.0)])
+def test_brute_force_exact(M, N, K, alpha, beta):
+    A, B, C = make_inputs(M, N, K, "uniform", seed=7 * M + N + K, c_init="uniform")
+    A_bits, B_bits, C_np = bits(A), bits(B), C.numpy()
+    ref, absdot = oracle.gemm(A_bits, B_bits, C_np, alpha, beta)
+    eref, eabs, _ = exact_gemm(A_bits, B_bits, C_np, alpha, beta)
+    assert np.array_equal(absdot, eabs) or np.allclose(absdot, eabs, rtol=K * 2.0 ** -52, atol=0)
+    bound = fp64_sum_bound(K, alpha, beta, eabs, C_np)
+    assert np.all(np.abs(ref - eref) <= bound)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 16), (17, 15, 33), (9, 11, 40)])
+def test_brute_force_special_values(M, N, K):
+    A_bits = _special_mix(M, K, seed=M * 100 + K)
+    B_bits = _special_mix(K, N, seed=N * 100 + K + 1)
+    ref, absdot = oracle.gemm(A_bits, B_bits)
+    eref, eabs, _ = exact_gemm(A_bits, B_bits)
+    bound = fp64_sum_bound(K, 1.0, 0.0, eabs)
+    assert np.all(np.abs(ref - eref) <= bound)
+
+
+# ----------------------------------------------------------------------------
+# Closed forms
+# ----------------------------------------------------------------------------
+
+def test_all_ones_gives_K():
+    M, N, K = 5, 7, 617
+    A, B, C = make_inputs(M, N, K, "ones", seed=1, c_init="uniform")
+    ref, absdot = oracle.gemm(bits(A), bits(B))
+    assert np.all(ref == K) and np.all(absdot == K)
+    ref2, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 1.5, 0.5)
+    assert np.array_equal(ref2, 1.5 * K + 0.5 * C.numpy().astype(np.float64))
+
+
+def test_identity_gives_copy():
+    K, N = 64, 37
+    A = np.eye(K, dtype=np.float16).view(np.uint16)
+    _, B, _ = make_inputs(K, N, K, "uniform", seed=3)
+    ref, _ = oracle.gemm(A, bits(B))
+    assert np.array_equal(ref, B.numpy().astype(np.float64))
+
+
+def test_zero_A_and_zero_alpha_give_beta_C():
+    M, N, K = 6, 9, 31
+    A, B, C = make_inputs(M, N, K, "zeros", seed=2, c_init="uniform", dist_b="uniform")
+    c64 = C.numpy().astype(np.float64)
+    ref, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 1.0, 0.5)
+    assert np.array_equal(ref, 0.5 * c64)
+    A2, _, _ = make_inputs(M, N, K, "uniform", seed=4)
+    ref2, _ = oracle.gemm(bits(A2), bits(B), C.numpy(), 0.0, 0.5)
+    assert np.array_equal(ref2, 0.5 * c64)
+
+
+def test_beta_zero_does_not_read_C():
+    """NaN-poisoned C with beta == 0 must not leak into the result."""
+    M, N, K = 8, 8, 8
+    A, B, _ = make_inputs(M, N, K, "uniform", seed=5)
+    poison = np.full((M, N), np.nan, dtype=np.float32)
+    ref, _ = oracle.gemm(bits(A), bits(B), poison, 1.0, 0.0)
+    assert np.all(np.isfinite(ref))
+    clean, _ = oracle.gemm(bits(A), bits(B))
+    assert np.array_equal(ref, clean)
+
+
+def test_empty_dimensions():
+    A, B, C = make_inputs(4, 3, 0, "uniform", seed=6, c_init="uniform")
+    ref, absdot = oracle.gemm(bits(A), bits(B), C.numpy(), 2.0, 0.5)
+    assert np.array_equal(ref, 0.5 * C.numpy().astype(np.float64)) and np.all(absdot == 0)
+    A, B, _ = make_inputs(0, 3, 5, "uniform", seed=6)
+    ref, _ = oracle.gemm(bits(A), bits(B))
+    assert ref.shape == (0, 3)
+
+
+# ----------------------------------------------------------------------------
+# Values printed on the pages
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("K", [256, 2048])
+def test_largest_small_integer_dot(K):
+    g = GOLDEN["small_integer_fill"]
+    amax, bmax = g["A_range"][1], g["B_range"][1]
+    A = np.full((2, K), amax, dtype=np.float16).view(np.uint16)
+    B = np.full((K, 3), bmax, dtype=np.float16).view(np.uint16)
+    ref, _ = oracle.gemm(A, B)
+    assert amax * bmax == g["largest_product"]
+    assert np.all(ref == g["largest_dot"][str(K)])
+    A[1] = np.float16(g["A_range"][0]).view(np.uint16)
+    ref, _ = oracle.gemm(A, B)
+    assert np.all(ref[1] == -g["largest_dot"][str(K)])
+
+
+def test_k_tail_617_splits_as_608_plus_9():
+    g = GOLDEN["k_tail_617"]
+    K, head = g["K"], g["full_steps_reach"]
+    assert head == (K // g["step"]) * g["step"] and K - head == g["valid_in_last_step"]
+    assert g["step"] - g["valid_in_last_step"] == g["past_edge_in_last_step"]
+    A, B, _ = make_inputs(23, 19, K, "uniform", seed=617)
+    Ab, Bb = bits(A), bits(B)
+    full, absdot = oracle.gemm(Ab, Bb)
+    p1, a1 = oracle.gemm(np.ascontiguousarray(Ab[:, :head]), np.ascontiguousarray(Bb[:head]))
+    p2, a2 = oracle.gemm(np.ascontiguousarray(Ab[:, head:]), np.ascontiguousarray(Bb[head:]))
+    assert np.all(np.abs(full - (p1 + p2)) <= fp64_sum_bound(K, 1.0, 0.0, absdot) * 2)
+    assert np.allclose(absdot, a1 + a2, rtol=1e-13, atol=0)
+
+
+# ----------------------------------------------------------------------------
+# Library cross-checks and identities
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["square256", "ragged1000x800x617"])
+def test_against_numpy_float64_matmul(name):
+    w = WORKLOADS[name]
+    A, B, C = workload_inputs(w)
+    C_np = None if C is None else C.numpy()
+    ref, absdot = oracle.gemm(bits(A), bits(B), C_np, w.alpha, w.beta)
+    lib = w.alpha * (A.numpy().astype(np.float64) @ B.numpy().astype(np.float64))
+    if C is not None and w.beta != 0:
+        lib = lib + w.beta * C_np.astype(np.float64)
+    bound = 2 * fp64_sum_bound(w.K, w.alpha, w.beta, absdot, C_np)
+    assert np.all(np.abs(ref - lib) <= bound)
+
+
+def test_exact_integers_match_integer_matmul():
+    """The pages' exact small-integer fill on a ragged shape: every partial
+    sum is an integer below 2^24, so the oracle must equal int64 matmul."""
+    M, N, K = 123, 77, 617
+    A, B, _ = make_inputs(M, N, K, "smallint", seed=11)
+    ref, _ = oracle.gemm(bits(A), bits(B))
+    ints = A.numpy().astype(np.int64) @ B.numpy().astype(np.int64)
+    assert np.array_equal(ref, ints.astype(np.float64))
+
+
+def test_transpose_identity_is_bitwise():
+    """(B^T A^T)^T = A B with the same products in the same order."""
+    A, B, _ = make_inputs(13, 29, 47, "uniform", seed=12)
+    Ab, Bb = bits(A), bits(B)
+    r1, s1 = oracle.gemm(Ab, Bb)
+    r2, s2 = oracle.gemm(np.ascontiguousarray(Bb.T), np.ascontiguousarray(Ab.T))
+    assert np.array_equal(r1, r2.T) and np.array_equal(s1, s2.T)
+
+
+def test_power_of_two_scaling_is_exact():
+    A, B, _ = make_inputs(21, 18, 99, "uniform", seed=13)
+    r1, _ = oracle.gemm(bits(A), bits(B))
+    r2, _ = oracle.gemm(bits(A * 2), bits(B))
+    assert np.array_equal(r2, 2 * r1)
+
+
+def test_strided_leading_dimensions():
+    """Views with lda > K, ldb > N and ldc > N give the packed answer."""
+    A, B, C = make_inputs(20, 24, 30, "uniform", seed=14, c_init="uniform")
+    Ab, Bb, Cn = bits(A), bits(B), C.numpy()
+    big_a = np.zeros((20, 37), dtype=np.uint16); big_a[:, :30] = Ab
+    big_b = np.zeros((30, 29), dtype=np.uint16); big_b[:, :24] = Bb
+    big_c = np.full((20, 31), np.nan, dtype=np.float32); big_c[:, :24] = Cn
+    r1, _ = oracle.gemm(Ab, Bb, Cn, 1.25, -0.5)
+    r2, _ = oracle.gemm(big_a[:, :30], big_b[:, :24], big_c[:, :24], 1.25, -0.5)
+    assert np.array_equal(r1, r2)
+
+
+def test_entries_match_full_product():
+    w = WORKLOADS["ragged1000x800x617"]
+    A, B, C = make_inputs(200, 160, 617, "uniform", seed=15, c_init="uniform")
+    full, fabs_ = oracle.gemm(bits(A), bits(B), C.numpy(), w.alpha, w.beta)
+    rows = np.array([0, 199, 0, 199, 57, 123])
+    cols = np.array([0, 159, 159, 0, 81, 2])
+    ent, eabs = oracle.gemm_entries(bits(A), bits(B), C.numpy(), w.alpha, w.beta, rows, cols)
+    assert np.array_equal(ent, full[rows, cols]) and np.array_equal(eabs, fabs_[rows, cols])
+
+
+def test_argument_errors():
+    A, B, _ = make_inputs(4, 4, 4, "uniform", seed=16)
+    with pytest.raises(ValueError):
+        oracle.gemm(bits(A), bits(B)[:3])
+    with pytest.raises(ValueError):
+        oracle.gemm_entries(bits(A), bits(B), None, 1.0, 0.0, [4], [0])
+    with pytest.raises(ValueError):
+        oracle.gemm(bits(A), bits(B), None, 1.0, 0.5)
+
+
+# ----------------------------------------------------------------------------
+# The acceptance rule
+# ----------------------------------------------------------------------------
+
+def test_tolerance_rule():
+    ref = np.zeros(5)
+    absdot = np.array([10.0, 10.0, 10.0, 10.0, 0.0])
+    tol0 = 1e-3 * 10.0 + 1e-5
+    got = np.array([-tol0, 1.01 * tol0, np.nan, np.inf, 1e-5])
+    ok = oracle.tolerance_ok(got, ref, absdot)
+    assert ok.tolist() == [True, False, False, False, True]
+
+
+# ----------------------------------------------------------------------------
+# Planted mistakes: each must fail at least one pin
+# ----------------------------------------------------------------------------
+
+def _pins_pass(M, N, K, compute):
+    """Run a candidate oracle through the exact brute-force pin and the
+    transpose pin; True only if both hold."""
+    A, B, C = make_inputs(M, N, K, "uniform", seed=99, c_init="uniform")
+    Ab, Bb, Cn = bits(A), bits(B), C.numpy()
+    ref, _ = compute(Ab, Bb, Cn, 1.5, 0.5)
+    eref, eabs, _ = exact_gemm(Ab, Bb, Cn, 1.5, 0.5)
+    exact_ok = np.all(np.abs(ref - eref) <= fp64_sum_bound(K, 1.5, 0.5, eabs, Cn))
+    r1, _ = compute(Ab, Bb, None, 1.0, 0.0)
+    r2, _ = compute(np.ascontiguousarray(Bb.T), np.ascontiguousarray(Ab.T), None, 1.0, 0.0)
+    return bool(exact_ok and np.array_equal(r1, r2.T))
+
+
+def test_real_oracle_passes_the_mutation_harness():
+    assert _pins_pass(7, 5, 17, oracle.gemm)
+
+
+@pytest.mark.parametrize("mistake", ["drop_last_k", "drop_first_k", "sign", "transposed_A",
+                                     "beta_ignored", "alpha_ignored", "swapped_alpha_beta"])
+def test_planted_mistakes_are_caught(mistake):
+    def compute(Ab, Bb, Cn, alpha, beta):
+        if mistake == "drop_last_k":
+            return oracle.gemm(np.ascontiguousarray(Ab[:, :-1]), np.ascontiguousarray(Bb[:-1]), Cn, alpha, beta)
+        if mistake == "drop_first_k":
+            return oracle.gemm(np.ascontiguousarray(Ab[:, 1:]), np.ascontiguousarray(Bb[1:]), Cn, alpha, beta)
+        if mistake == "sign":
+            r, s = oracle.gemm(Ab, Bb, Cn, alpha, beta)
+            return -r, s
+        if mistake == "transposed_A":
+            # reads A[k][i] instead of A[i][k] on a square block
+            n = min(Ab.shape)
+            At = np.ascontiguousarray(Ab[:n, :n].T)
+            Af = Ab.copy(); Af[:n, :n] = At
+            return oracle.gemm(Af, Bb, Cn, alpha, beta)
+        if mistake == "beta_ignored":
+            return oracle.gemm(Ab, Bb, None, alpha, 0.0)
+        if mistake == "alpha_ignored":
+            return oracle.gemm(Ab, Bb, Cn, 1.0, beta)
+        if mistake == "swapped_alpha_beta":
+            return oracle.gemm(Ab, Bb, Cn, beta if Cn is not None else alpha, alpha if Cn is not None else beta)
+        raise AssertionError(mistake)
+    assert not _pins_pass(7, 7, 17, compute)
