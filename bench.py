@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark: FP16-input / FP32-accumulate GEMM on one MI355X (gfx950).
+
+One "step" is one call of the whole hot path, C = alpha*A@B + beta*C, on one
+synthetic workload already resident in HBM.  The headline workload is the
+2048^3 product (uniform[-1,1] inputs, alpha=1, beta=0); the 8192^3 roofline
+shape and the other workloads are timed too and reported under "workloads"
+in the same JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Timing: W untimed warm-up steps, then exactly K steps bracketed by
+torch.cuda.synchronize() on both sides (wall clock -> ms_per_step), with HIP
+events recorded on the launch stream around the same region (-> the average
+kernel duration used for the roofline).  FLOP = 2*M*N*K.
+
+The CPU baseline is the oracle (oracle/, plain C, FP64) timed on a bounded
+sample of the headline workload: a block of whole rows of C, sized to about
+--cpu-seconds of work on the host cores.  The same rows of the GPU result are
+checked against it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (no sparsity): FP16 matrix cores and HBM3E.
+PEAK_F16_TFLOPS = 2516.6   # 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = ("FP16->FP32 GEMM TFLOP/s at 2048^3 (headline) and 8192^3; "
+          "% of MI355X dense FP16 MFMA peak")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="square2048")
+    p.add_argument("--no-others", action="store_true", help="time only the headline workload")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    return p.parse_args()
+
+
+def time_workload(w, steps, warmup, torch, mp):
+    from dense_mixed_precision_amd.workloads import workload_inputs
+
+    dev = torch.device("cuda:0")
+    A, B, C = workload_inputs(w)
+    Ad, Bd = A.to(dev), B.to(dev)
+    Cd = C.to(dev) if C is not None else torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    cfg = mp.query_for(Ad, Bd, Cd, w.alpha, w.beta)
+
+    def step():
+        mp.gemm(Ad, Bd, Cd, w.alpha, w.beta, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / steps
+    kern_ms = ev0.elapsed_time(ev1) / steps
+    return {"A": A, "B": B, "C": C, "Cd": Cd, "cfg": cfg, "wall_ms": wall_ms, "kernel_ms": kern_ms}
+
+
+def roofline_entry(w, kernel_ms):
+    """MFMA bound for the compute-heavy shapes, HBM bound where the
+    arithmetic intensity (FLOP per algorithmic byte) is below the ridge."""
+    ai = w.flop / w.algorithmic_bytes
+    ridge = PEAK_F16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge:
+        achieved = w.flop / (kernel_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None}
+    achieved = w.algorithmic_bytes / (kernel_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+
+
+def cpu_baseline(w, res, seconds):
+    """The oracle, as it stands, on whole rows of C of the headline workload."""
+    import numpy as np
+
+    import oracle
+    from dense_mixed_precision_amd.workloads import bits
+
+    Ab, Bb = bits(res["A"]), bits(res["B"])
+    Cn = None if res["C"] is None else res["C"].numpy()
+    got = res["Cd"].cpu().numpy() if w.beta == 0 else None
+
+    def run_rows(r0, r1):
+        a = np.ascontiguousarray(Ab[r0:r1])
+        c = None if Cn is None else np.ascontiguousarray(Cn[r0:r1])
+        t = time.perf_counter()
+        ref, absdot = oracle.gemm(a, Bb, c, w.alpha, w.beta)
+        return time.perf_counter() - t, ref, absdot
+
+    probe_rows = max(1, min(w.M, 4))
+    dt, _, _ = run_rows(0, probe_rows)
+    per_row = max(dt / probe_rows, 1e-6)
+    rows = int(max(1, min(w.M, seconds / per_row)))
+    r0 = (w.M - rows) // 2
+    dt, ref, absdot = run_rows(r0, r0 + rows)
+    flop = 2.0 * rows * w.N * w.K
+    out = {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": f"rows {r0}..{r0 + rows - 1} of {w.M} ({rows} rows x {w.N} cols x K={w.K}) "
+                     f"of {w.name}; {dt:.1f} s wall",
+           "seconds": round(dt, 2)}
+    if got is not None:
+        ok = oracle.tolerance_ok(got[r0:r0 + rows], ref, absdot)
+        err = np.abs(got[r0:r0 + rows] - ref) / (oracle.TOL_REL * absdot + oracle.TOL_ABS)
+        out["gpu_rows_match"] = bool(ok.all())
+        out["gpu_rows_worst_err_over_tol"] = float(err.max())
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this GEMM path has "
+              "no multi-GPU mode. Run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import dense_mixed_precision_amd as mp
+    from dense_mixed_precision_amd.workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mp.load()
+    head = WORKLOADS[args.workload]
+    print(f"# timing {head.name} ({args.warmup} warm-up + {args.steps} steps)", file=sys.stderr, flush=True)
+    res = time_workload(head, args.steps, args.warmup, torch, mp)
+    value = head.flop / (res["wall_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["wall_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": head.name, "M": head.M, "N": head.N, "K": head.K,
+                   "alpha": head.alpha, "beta": head.beta, "inputs": head.dist,
+                   "accumulate": "f32", "output": "f32", "layout": "row-major A, B, C",
+                   "kernel": {k: res["cfg"][k] for k in ("id", "kind_name", "bm", "bn", "bk", "wave_m",
+                                                        "wave_n", "vec_a", "vec_b", "grid")},
+                   "pct_of_peak": round(100 * value / PEAK_F16_TFLOPS, 2),
+                   "peak_tflops": PEAK_F16_TFLOPS},
+        "roofline": roofline_entry(head, res["kernel_ms"]),
+    }
+    line["roofline"]["kernel_ms"] = round(res["kernel_ms"], 5)
+    others = {}
+    if not args.no_others:
+        for name, w in WORKLOADS.items():
+            if name == head.name:
+                continue
+            steps = max(5, min(args.steps, 20 if w.flop > 1e12 else args.steps))
+            print(f"# timing {name} ({steps} steps)", file=sys.stderr, flush=True)
+            r = time_workload(w, steps, max(3, args.warmup // 2), torch, mp)
+            others[name] = {"tflops": round(w.flop / (r["kernel_ms"] * 1e-3) / 1e12, 2),
+                            "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
+                            "pct_of_peak": round(100 * w.flop / (r["kernel_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
+                            "roofline": roofline_entry(w, r["kernel_ms"]),
+                            "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "vec_a", "vec_b", "grid")}}
+            del r
+            torch.cuda.empty_cache()
+        line["workloads"] = others
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(head, res, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,45 @@
-"""Placeholder; replaced by the binding."""
+"""dense_mixed_precision_amd -- FP16-input, FP32-accumulate GEMM for gfx950.
+
+Thin Python binding over the C ABI in ``include/mpgemm.h`` (library
+``libmpgemm.so``, built in-tree by ``build.build()``).  Every step of the
+product runs in the HIP kernels; Python only marshals arguments.  There is no
+CPU or library fallback: if the shared library is missing, every call raises.
+
+Raw entry points (same names and argument order as the C ABI; pointers are
+integers holding device addresses, ``stream`` a hipStream_t as an integer,
+0 for the default stream):
+    mpgemm_f16f32(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream) -> int
+    mpgemm_f16f32_query(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta) -> dict
+    mpgemm_f16f32_with_config(cfg, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream) -> int
+    mpgemm_num_configs(), mpgemm_config_info(id), mpgemm_probe_mfma_layout(shape, out, stream)
+    mpgemm_strerror(code), mpgemm_version()
+
+Tensor convenience: ``gemm(A, B, C, alpha, beta)`` for torch tensors on the
+GPU (A, B float16, C float32, row-major with unit inner stride), launched on
+torch's current stream.
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    MPGEMM_EALIGN,
+    MPGEMM_ECONFIG,
+    MPGEMM_EDIM,
+    MPGEMM_ELAUNCH,
+    MPGEMM_ELD,
+    MPGEMM_ENULL,
+    MPGEMM_OK,
+    MpgemmError,
+    config_fields,
+    gemm,
+    lib_path,
+    load,
+    mpgemm_config_info,
+    mpgemm_f16f32,
+    mpgemm_f16f32_query,
+    mpgemm_f16f32_with_config,
+    mpgemm_num_configs,
+    mpgemm_probe_mfma_layout,
+    mpgemm_strerror,
+    mpgemm_version,
+    query_for,
+)

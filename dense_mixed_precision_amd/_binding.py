@@ -1,0 +1,180 @@
+"""ctypes binding for libmpgemm.so (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmpgemm.so")
+
+MPGEMM_OK = 0
+MPGEMM_EDIM = -1
+MPGEMM_ELD = -2
+MPGEMM_ENULL = -3
+MPGEMM_ELAUNCH = -4
+MPGEMM_ECONFIG = -5
+MPGEMM_EALIGN = -6
+
+
+class MpgemmConfig(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "id", "kind", "bm", "bn", "bk", "waves_m", "waves_n", "wave_m", "wave_n",
+        "mfma_m", "mfma_n", "mfma_k", "vec_a", "vec_b", "stages", "threads", "lds_bytes")] + [
+        ("grid", ctypes.c_int64)]
+
+
+config_fields = [f[0] for f in MpgemmConfig._fields_]
+KIND_NAMES = {0: "tiled", 1: "direct", 2: "scale", 3: "none"}
+
+
+class MpgemmError(RuntimeError):
+    def __init__(self, code: int, where: str = "mpgemm"):
+        self.code = code
+        super().__init__(f"{where}: error {code}: {mpgemm_strerror(code)}")
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load the in-tree libmpgemm.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python -m dense_mixed_precision_amd.build` (no fallback path exists)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, f32, vp, i32 = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
+    gemm_args = [i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, f32]
+    lib.mpgemm_f16f32.argtypes = gemm_args + [vp]
+    lib.mpgemm_f16f32.restype = i32
+    lib.mpgemm_f16f32_query.argtypes = gemm_args + [ctypes.POINTER(MpgemmConfig)]
+    lib.mpgemm_f16f32_query.restype = i32
+    lib.mpgemm_f16f32_with_config.argtypes = [i32] + gemm_args + [vp]
+    lib.mpgemm_f16f32_with_config.restype = i32
+    lib.mpgemm_num_configs.argtypes = []
+    lib.mpgemm_num_configs.restype = i32
+    lib.mpgemm_config_info.argtypes = [i32, ctypes.POINTER(MpgemmConfig)]
+    lib.mpgemm_config_info.restype = i32
+    lib.mpgemm_probe_mfma_layout.argtypes = [i32, vp, vp]
+    lib.mpgemm_probe_mfma_layout.restype = i32
+    lib.mpgemm_strerror.argtypes = [i32]
+    lib.mpgemm_strerror.restype = ctypes.c_char_p
+    lib.mpgemm_version.argtypes = []
+    lib.mpgemm_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _cfg_dict(c: MpgemmConfig) -> dict:
+    d = {name: int(getattr(c, name)) for name in config_fields}
+    d["kind_name"] = KIND_NAMES.get(d["kind"], "?")
+    return d
+
+
+# ---- raw entry points (same names as the C ABI) ----------------------------
+
+def mpgemm_f16f32(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream=0) -> int:
+    return int(load().mpgemm_f16f32(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream))
+
+
+def mpgemm_f16f32_query(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta) -> dict:
+    out = MpgemmConfig()
+    rc = load().mpgemm_f16f32_query(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                                    ctypes.byref(out))
+    if rc != MPGEMM_OK:
+        raise MpgemmError(rc, "mpgemm_f16f32_query")
+    return _cfg_dict(out)
+
+
+def mpgemm_f16f32_with_config(config_id, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                              stream=0) -> int:
+    return int(load().mpgemm_f16f32_with_config(config_id, M, N, K, A, lda, B, ldb, C, ldc,
+                                                 alpha, beta, stream))
+
+
+def mpgemm_num_configs() -> int:
+    return int(load().mpgemm_num_configs())
+
+
+def mpgemm_config_info(config_id: int) -> dict:
+    out = MpgemmConfig()
+    rc = load().mpgemm_config_info(config_id, ctypes.byref(out))
+    if rc != MPGEMM_OK:
+        raise MpgemmError(rc, "mpgemm_config_info")
+    return _cfg_dict(out)
+
+
+def mpgemm_probe_mfma_layout(shape: int, out: int, stream=0) -> int:
+    return int(load().mpgemm_probe_mfma_layout(shape, out, stream))
+
+
+def mpgemm_strerror(code: int) -> str:
+    return load().mpgemm_strerror(code).decode()
+
+
+def mpgemm_version() -> str:
+    return load().mpgemm_version().decode()
+
+
+# ---- torch tensor convenience ----------------------------------------------
+
+def _check_tensor(t, name, dtype):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major with unit inner stride")
+    return max(t.stride(0), max(t.shape[1], 1)) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _args(A, B, C):
+    import torch
+    lda = _check_tensor(A, "A", torch.float16)
+    ldb = _check_tensor(B, "B", torch.float16)
+    ldc = _check_tensor(C, "C", torch.float32)
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    return M, N, K, lda, ldb, ldc
+
+
+def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, config: int | None = None, stream=None):
+    """C <- alpha*A@B + beta*C in place on the GPU; returns C.
+
+    ``stream``: a torch.cuda.Stream or raw handle (default: current stream).
+    ``config``: force a table entry (tests and sweeps)."""
+    import torch
+    M, N, K, lda, ldb, ldc = _args(A, B, C)
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if config is None:
+        rc = mpgemm_f16f32(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                           float(alpha), float(beta), handle)
+    else:
+        rc = mpgemm_f16f32_with_config(int(config), M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                       C.data_ptr(), ldc, float(alpha), float(beta), handle)
+    if rc != MPGEMM_OK:
+        raise MpgemmError(rc, "mpgemm_f16f32" if config is None else f"config {config}")
+    return C
+
+
+def query_for(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> dict:
+    """The factory's choice for these tensors (no launch)."""
+    M, N, K, lda, ldb, ldc = _args(A, B, C)
+    return mpgemm_f16f32_query(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                               float(alpha), float(beta))

@@ -1,0 +1,442 @@
+// kernels.hpp -- gfx950 device code for C = alpha*A*B + beta*C with FP16 A, B
+// and FP32 accumulation and output (the mixed-precision contract of
+// "Capstone 4: a tensor-core GEMM", sections "Capability" and "Minimal model").
+//
+// Kernels:
+//   gemm_tiled<Cfg>   block tile staged through a two-deep LDS ring, wave tiles
+//                     on v_mfma_f32_32x32x16_f16, bounds-checked alpha/beta
+//                     epilogue.  The pages' staged-tile design ("Worked path",
+//                     and the double-buffered copy of "02_mixed_precision_gemm",
+//                     Summary) is the prior art; the layout below is gfx950's.
+//   gemm_direct       one 32x32 MFMA tile per wave with operands loaded
+//                     straight from memory, 64-bit addressing, any size and
+//                     stride: the universal fallback.
+//   scale_c           C <- beta*C when alpha == 0 or K == 0.
+//   probe_mfma        writes the accumulator lane layout of one instruction.
+//
+// Matrix-core lane layouts used here (CDNA3/CDNA4 matrix instruction docs,
+// checked on the device by probe_mfma):
+//   v_mfma_f32_32x32x16_f16: lane l supplies A[l%32][8*(l/32) + 0..7] and
+//     B[8*(l/32) + 0..7][l%32]; accumulator v (0..15) of lane l holds
+//     D[8*(v/4) + 4*(l/32) + v%4][l%32].
+//   v_mfma_f32_16x16x32_f16: lane l supplies A[l%16][8*(l/16) + 0..7] and
+//     B[8*(l/16) + 0..7][l%16]; accumulator v (0..3) holds D[4*(l/16) + v][l%16].
+// Any permutation of k that A and B share gives the same sum, so only the
+// row/column placement matters for correctness.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mpg {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource: raw (stride 0) byte-addressed buffer.  Word 3 is the
+// gfx9-family data-format word.  A load whose byte offset is >= num_records
+// returns zero; the kernels send every out-of-range element to kOOB, which
+// is how ragged M, N and K edges read zeros without host padding.
+constexpr int32_t kNumRecords = 0x7FFFFFFF;
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int32_t kRsrcWord3 = 0x00020000;
+
+// MI355X dispatches consecutive workgroup ids round-robin over its 8 XCDs,
+// each with a private L2.
+constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             kNumRecords, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi)
+{
+    return (lo & 0xFFFFu) | (hi << 16);
+}
+
+// Eight consecutive FP16 values starting at byte offset `off` (or kOOB).
+// VEC = 8: one 16-byte load (offset 16-byte aligned).  VEC = 1: eight
+// 2-byte loads (any 2-byte alignment).
+template <int VEC>
+__device__ __forceinline__ u32x4 load8_full(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    if constexpr (VEC == 8) {
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    } else {
+        static_assert(VEC == 1, "vector width must be 8 or 1");
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            h[e] = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2u * e, 0, 0);
+        return u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+    }
+}
+
+// Same, but only the first `nvalid` (1..7) elements are in range; the rest
+// read as zero.  Used where a vector straddles the end of a row.
+__device__ __forceinline__ u32x4 load8_partial(__amdgpu_buffer_rsrc_t r, uint32_t off, int nvalid)
+{
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        h[e] = __builtin_amdgcn_raw_buffer_load_b16(r, e < nvalid ? off + 2u * e : kOOB, 0, 0);
+    return u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+}
+
+// nvalid >= 8: whole vector; <= 0: zeros; otherwise partial.
+template <int VEC>
+__device__ __forceinline__ u32x4 load8(__amdgpu_buffer_rsrc_t r, uint32_t off, int nvalid)
+{
+    u32x4 v = load8_full<VEC>(r, nvalid >= 8 ? off : kOOB);
+    if (nvalid > 0 && nvalid < 8)
+        v = load8_partial(r, off, nvalid);
+    return v;
+}
+
+struct GemmArgs {
+    const uint16_t *A;
+    const uint16_t *B;
+    float *C;
+    int64_t M, N, K;
+    int64_t lda, ldb, ldc;
+    float alpha, beta;
+    int32_t tiles_m, tiles_n;
+    int32_t group_m;
+};
+
+// Workgroup id -> (tile row, tile column).  First undo the round-robin XCD
+// dispatch so each XCD owns one contiguous run of tile ids, then walk that
+// run in groups of `group_m` tile rows so the workgroups resident on one XCD
+// at the same time share A row-panels and B column-panels in its L2.
+__device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_n, int tiles_m, int group_m,
+                                            int &tm, int &tn)
+{
+    const int xcd = bid % kNumXcd;
+    const int local = bid / kNumXcd;
+    const int per = nb / kNumXcd;
+    const int rem = nb % kNumXcd;
+    const int t = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+    const int group = group_m * tiles_n;
+    const int first_m = (t / group) * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const int in_group = t % group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+// Bounds-checked epilogue for one 32x32 accumulator tile whose top-left
+// element is C[row0][col0]: C = alpha*acc + beta*C, C not read when beta == 0.
+__device__ __forceinline__ void store_tile32(const floatx16 &acc, float *C, int64_t ldc,
+                                             int64_t M, int64_t N, int64_t row0, int64_t col0,
+                                             float alpha, float beta, int lane)
+{
+    const int64_t col = col0 + (lane & 31);
+    if (col >= N)
+        return;
+    const int64_t rbase = row0 + 4 * (lane >> 5);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int64_t row = rbase + 8 * (v >> 2) + (v & 3);
+        if (row < M) {
+            float *p = C + row * ldc + col;
+            const float s = acc[v];
+            *p = (beta == 0.0f) ? alpha * s : __builtin_fmaf(alpha, s, beta * *p);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int VEC_A_, int VEC_B_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int VEC_A = VEC_A_, VEC_B = VEC_B_;
+    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int WTM = BM / WAVES_M;       // rows of C per wave
+    static constexpr int WTN = BN / WAVES_N;       // columns of C per wave
+    static constexpr int FM = WTM / 32;            // 32x32 MFMA tiles per wave, along M
+    static constexpr int FN = WTN / 32;            // ... along N
+    static constexpr int KS = BK / 16;             // MFMA k-steps per stage
+    static constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
+    static constexpr int ROWB = BK * 2;            // bytes per LDS row
+    static constexpr int A_CHUNKS = BM * CH / NT;  // 16-byte A chunks each thread copies per stage
+    static constexpr int KB = BK * BN / (8 * NT);  // B rows per thread per stage (8-column block)
+    static constexpr int A_BYTES = BM * ROWB;
+    static constexpr int B_BYTES = BN * ROWB;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+
+    static_assert(BK == 64 || BK == 128, "LDS swizzle is laid out for 64 or 128 K per stage");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+    static_assert((BM * CH) % NT == 0, "A stage must split evenly over the threads");
+    static_assert(KB == 2 || KB == 4 || KB == 8, "B stage must split into 8-column blocks of 2, 4 or 8 rows");
+    static_assert((BN / 8) * (BK / KB) == NT, "B blocks must cover the stage exactly");
+    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
+};
+
+// XOR swizzle of the 16-byte chunk index inside an LDS row.  Reads take 8
+// consecutive rows at one logical chunk; the transposed B writes take rows
+// 8 apart.  (r ^ r>>3) & 7 sends both patterns to 8 distinct 16-byte bank
+// slots, so neither the ds_read_b128 nor the ds_write_b128 conflicts.
+__device__ __forceinline__ int swz(int row)
+{
+    return (row ^ (row >> 3)) & 7;
+}
+
+template <class Cfg>
+__global__ void __launch_bounds__(Cfg::NT)
+gemm_tiled(GemmArgs args)
+{
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, KS = Cfg::KS, CH = Cfg::CH, ROWB = Cfg::ROWB;
+    constexpr int NT = Cfg::NT, KB = Cfg::KB, A_CHUNKS = Cfg::A_CHUNKS;
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / Cfg::WAVES_N;
+    const int wn = wave % Cfg::WAVES_N;
+
+    int tm, tn;
+    tile_coords(blockIdx.x, gridDim.x, args.tiles_n, args.tiles_m, args.group_m, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t M = args.M, N = args.N, K = args.K;
+    const int64_t lda = args.lda, ldb = args.ldb;
+
+    // ---- per-thread copy assignment -------------------------------------
+    // A: chunk q = tid + NT*i covers row q/CH, elements 8*(q%CH) .. +7.
+    uint32_t a_off[A_CHUNKS];
+    int a_row_ok[A_CHUNKS];
+    int a_col[A_CHUNKS];
+    uint32_t a_lds[A_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+        const int q = tid + NT * i;
+        const int r = q / CH, c = q % CH;
+        a_off[i] = (uint32_t)((r * lda + 8 * c) * 2);
+        a_row_ok[i] = (m0 + r) < M;
+        a_col[i] = 8 * c;
+        a_lds[i] = r * ROWB + ((c ^ swz(r)) * 16);
+    }
+    // B: thread owns the 8-column block nc and rows KB*kq .. KB*kq+KB-1.
+    const int nc = tid % (BN / 8);
+    const int kq = tid / (BN / 8);
+    const int64_t b_cols_left = N - (n0 + 8 * nc);
+    const int b_nvalid = b_cols_left >= 8 ? 8 : (b_cols_left <= 0 ? 0 : (int)b_cols_left);
+    uint32_t b_off[KB];
+#pragma unroll
+    for (int rr = 0; rr < KB; ++rr)
+        b_off[rr] = (uint32_t)(((KB * kq + rr) * ldb + 8 * nc) * 2);
+    // LDS destination of transposed column j of the block: row 8*nc + j,
+    // k offset KB*kq inside that row.
+    uint32_t b_lds[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int n = 8 * nc + j;
+        const int kk = KB * kq;
+        b_lds[j] = Cfg::A_BYTES + n * ROWB + (((kk >> 3) ^ swz(n)) * 16) + (kk & 7) * 2;
+    }
+
+    u32x4 ra[A_CHUNKS];
+    u32x4 rb[KB];
+
+    auto load_stage = [&](int64_t k0) {
+        const __amdgpu_buffer_rsrc_t rsA = make_rsrc(args.A + m0 * lda + k0);
+        const __amdgpu_buffer_rsrc_t rsB = make_rsrc(args.B + k0 * ldb + n0);
+        const int64_t k_left = K - k0;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) {
+            const int64_t left = k_left - a_col[i];
+            const int nv = !a_row_ok[i] ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : (int)left));
+            ra[i] = load8<Cfg::VEC_A>(rsA, a_off[i], nv);
+        }
+#pragma unroll
+        for (int rr = 0; rr < KB; ++rr) {
+            const int nv = (KB * kq + rr) < k_left ? b_nvalid : 0;
+            rb[rr] = load8<Cfg::VEC_B>(rsB, b_off[rr], nv);
+        }
+    };
+
+    auto store_stage = [&](int stage) {
+        uint8_t *base = smem + stage * Cfg::STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i)
+            *reinterpret_cast<u32x4 *>(base + a_lds[i]) = ra[i];
+        // 8 x KB block -> KB x 8: column j gathers element j of each row.
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t col[KB / 2];
+#pragma unroll
+            for (int p = 0; p < KB / 2; ++p) {
+                const uint32_t lo = rb[2 * p][j >> 1];
+                const uint32_t hi = rb[2 * p + 1][j >> 1];
+                col[p] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+            }
+            if constexpr (KB == 8)
+                *reinterpret_cast<u32x4 *>(base + b_lds[j]) = u32x4{col[0], col[1], col[2], col[3]};
+            else if constexpr (KB == 4)
+                *reinterpret_cast<u32x2 *>(base + b_lds[j]) = u32x2{col[0], col[1]};
+            else
+                *reinterpret_cast<uint32_t *>(base + b_lds[j]) = col[0];
+        }
+    };
+
+    // ---- operand read offsets (bytes inside a stage) ---------------------
+    uint32_t a_rd[FM], b_rd[FN];
+    int a_sw[FM], b_sw[FN];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+        const int r = wm * Cfg::WTM + f * 32 + (lane & 31);
+        a_rd[f] = r * ROWB;
+        a_sw[f] = swz(r);
+    }
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+        const int n = wn * Cfg::WTN + f * 32 + (lane & 31);
+        b_rd[f] = Cfg::A_BYTES + n * ROWB;
+        b_sw[f] = swz(n);
+    }
+    const int khalf = lane >> 5;
+
+    floatx16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = floatx16{0};
+
+    const int64_t num_k = (K + BK - 1) / BK;
+    if (num_k > 0) {
+        load_stage(0);
+        store_stage(0);
+        __syncthreads();
+    }
+    for (int64_t kt = 0; kt < num_k; ++kt) {
+        const int stage = (int)(kt & 1);
+        const bool has_next = kt + 1 < num_k;
+        if (has_next)
+            load_stage((kt + 1) * BK);
+        const uint8_t *base = smem + stage * Cfg::STAGE_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c = 2 * ks + khalf;
+            half8 a[FM], b[FN];
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+                a[f] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(
+                                                     base + a_rd[f] + ((c ^ a_sw[f]) * 16)));
+#pragma unroll
+            for (int f = 0; f < FN; ++f)
+                b[f] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(
+                                                     base + b_rd[f] + ((c ^ b_sw[f]) * 16)));
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        if (has_next)
+            store_stage(stage ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            store_tile32(acc[i][j], args.C, args.ldc, M, N,
+                         m0 + wm * Cfg::WTM + i * 32, n0 + wn * Cfg::WTN + j * 32,
+                         args.alpha, args.beta, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Direct kernel: 4 waves, 64x64 of C per workgroup, operands from memory.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+gemm_direct(GemmArgs args)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t tm = blockIdx.x / args.tiles_n;
+    const int64_t tn = blockIdx.x % args.tiles_n;
+    const int64_t row0 = tm * 64 + (wave >> 1) * 32;
+    const int64_t col0 = tn * 64 + (wave & 1) * 32;
+    const int64_t ra = row0 + (lane & 31);
+    const int64_t cb = col0 + (lane & 31);
+    const bool ra_ok = ra < args.M;
+    const bool cb_ok = cb < args.N;
+    const int kbase = 8 * (lane >> 5);
+    floatx16 acc = floatx16{0};
+    for (int64_t k0 = 0; k0 < args.K; k0 += 16) {
+        half8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t k = k0 + kbase + e;
+            const bool k_ok = k < args.K;
+            const uint16_t av = (ra_ok && k_ok) ? args.A[ra * args.lda + k] : (uint16_t)0;
+            const uint16_t bv = (cb_ok && k_ok) ? args.B[k * args.ldb + cb] : (uint16_t)0;
+            a[e] = __builtin_bit_cast(_Float16, av);
+            b[e] = __builtin_bit_cast(_Float16, bv);
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+    }
+    store_tile32(acc, args.C, args.ldc, args.M, args.N, row0, col0, args.alpha, args.beta, lane);
+}
+
+// C <- beta*C (beta == 0 writes zeros without reading C).  Grid-stride over
+// rows in y and columns in x.
+__global__ void __launch_bounds__(256)
+scale_c(float *C, int64_t M, int64_t N, int64_t ldc, float beta)
+{
+    for (int64_t i = blockIdx.y; i < M; i += gridDim.y) {
+        for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < N;
+             j += (int64_t)gridDim.x * blockDim.x) {
+            float *p = C + i * ldc + j;
+            *p = (beta == 0.0f) ? 0.0f : beta * *p;
+        }
+    }
+}
+
+// One wave.  A[i][0] = i, A[i][1] = 1, B[0][j] = 1, B[1][j] = S*j, the rest
+// zero, so D[i][j] = i + S*j; each lane writes its accumulators in order.
+__global__ void __launch_bounds__(64)
+probe_mfma(float *out, int shape)
+{
+    const int l = threadIdx.x;
+    half8 a = half8{0}, b = half8{0};
+    if (shape == 32) {
+        if (l < 32) {  // k = 0..7 held by lanes 0..31
+            a[0] = (_Float16)(float)(l & 31);
+            a[1] = (_Float16)1.0f;
+            b[0] = (_Float16)1.0f;
+            b[1] = (_Float16)(float)(32 * (l & 31));
+        }
+        floatx16 d = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, floatx16{0}, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            out[l * 16 + v] = d[v];
+    } else {
+        if (l < 16) {  // k = 0..7 held by lanes 0..15
+            a[0] = (_Float16)(float)(l & 15);
+            a[1] = (_Float16)1.0f;
+            b[0] = (_Float16)1.0f;
+            b[1] = (_Float16)(float)(16 * (l & 15));
+        }
+        floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, floatx4{0}, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            out[l * 4 + v] = d[v];
+    }
+}
+
+}  // namespace mpg

@@ -1,0 +1,401 @@
+// mpgemm.hip -- host side of the gfx950 FP16-input / FP32-accumulate GEMM:
+// argument validation, the tile-config factory, launches and the C ABI
+// declared in include/mpgemm.h.
+//
+// The factory is the gfx950 form of the "kernel factory" of the
+// "GEMM kernels 1-7 + Tensor Cores" visualizer (kernel 7: the host picks the
+// tile shape per configuration): a small table of compiled block/wave tiles,
+// chosen per shape so that the grid fills the 256 compute units, and per
+// pointer/leading-dimension alignment so that 16-byte loads are used only
+// where every vector is 16-byte aligned.
+#include "mpgemm.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+using mpg::GemmArgs;
+using mpg::TileCfg;
+
+constexpr int kNumCu = 256;
+
+// ---------------------------------------------------------------------------
+// Config table
+// ---------------------------------------------------------------------------
+using launch_fn = hipError_t (*)(const GemmArgs &, dim3, hipStream_t);
+
+struct Entry {
+    mpgemm_config cfg;
+    launch_fn launch;
+};
+
+template <class Cfg>
+hipError_t launch_tiled(const GemmArgs &a, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(mpg::gemm_tiled<Cfg>, grid, dim3(Cfg::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_direct(const GemmArgs &a, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(mpg::gemm_direct, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <class Cfg>
+constexpr Entry tiled_entry(int id)
+{
+    mpgemm_config c{};
+    c.id = id;
+    c.kind = MPGEMM_KIND_TILED;
+    c.bm = Cfg::BM;
+    c.bn = Cfg::BN;
+    c.bk = Cfg::BK;
+    c.waves_m = Cfg::WAVES_M;
+    c.waves_n = Cfg::WAVES_N;
+    c.wave_m = Cfg::WTM;
+    c.wave_n = Cfg::WTN;
+    c.mfma_m = 32;
+    c.mfma_n = 32;
+    c.mfma_k = 16;
+    c.vec_a = Cfg::VEC_A;
+    c.vec_b = Cfg::VEC_B;
+    c.stages = 2;
+    c.threads = Cfg::NT;
+    c.lds_bytes = Cfg::LDS_BYTES;
+    c.grid = 0;
+    return Entry{c, &launch_tiled<Cfg>};
+}
+
+constexpr Entry direct_entry(int id)
+{
+    mpgemm_config c{};
+    c.id = id;
+    c.kind = MPGEMM_KIND_DIRECT;
+    c.bm = 64;
+    c.bn = 64;
+    c.bk = 16;
+    c.waves_m = 2;
+    c.waves_n = 2;
+    c.wave_m = 32;
+    c.wave_n = 32;
+    c.mfma_m = 32;
+    c.mfma_n = 32;
+    c.mfma_k = 16;
+    c.vec_a = 1;
+    c.vec_b = 1;
+    c.stages = 0;
+    c.threads = 256;
+    c.lds_bytes = 0;
+    return Entry{c, &launch_direct};
+}
+
+constexpr Entry scale_entry(int id)
+{
+    mpgemm_config c{};
+    c.id = id;
+    c.kind = MPGEMM_KIND_SCALE;
+    c.threads = 256;
+    return Entry{c, nullptr};
+}
+
+// Tile shapes.  Each is compiled for the four (vec_a, vec_b) combinations.
+#define MPG_TILE_ENTRIES(base, BM, BN, BK, WM, WN)                     \
+    tiled_entry<TileCfg<BM, BN, BK, WM, WN, 8, 8>>(base + 0),          \
+        tiled_entry<TileCfg<BM, BN, BK, WM, WN, 1, 8>>(base + 1),      \
+        tiled_entry<TileCfg<BM, BN, BK, WM, WN, 8, 1>>(base + 2),      \
+        tiled_entry<TileCfg<BM, BN, BK, WM, WN, 1, 1>>(base + 3)
+
+const Entry kTable[] = {
+    MPG_TILE_ENTRIES(0, 256, 256, 64, 2, 2),  // 0..3   large products
+    MPG_TILE_ENTRIES(4, 128, 128, 64, 2, 2),  // 4..7   2048-class and tall-skinny
+    MPG_TILE_ENTRIES(8, 64, 64, 64, 2, 2),    // 8..11  small or ragged products
+    direct_entry(12),                         // 12     any stride / size
+    scale_entry(13),                          // 13     alpha == 0 or K == 0
+};
+constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
+constexpr int kDirectId = 12;
+constexpr int kScaleId = 13;
+
+// Tile groups in the table, largest first: (first id, BM, BN).
+struct TileGroup {
+    int first;
+    int bm, bn;
+};
+constexpr TileGroup kGroups[] = {{0, 256, 256}, {4, 128, 128}, {8, 64, 64}};
+
+// ---------------------------------------------------------------------------
+// Validation and selection (pure host code, no HIP calls)
+// ---------------------------------------------------------------------------
+struct Problem {
+    int64_t M, N, K, lda, ldb, ldc;
+    const uint16_t *A;
+    const uint16_t *B;
+    const float *C;
+    float alpha, beta;
+};
+
+int validate(const Problem &p)
+{
+    if (p.M < 0 || p.N < 0 || p.K < 0)
+        return MPGEMM_EDIM;
+    const int64_t kmin = p.K > 1 ? p.K : 1;
+    const int64_t nmin = p.N > 1 ? p.N : 1;
+    if (p.lda < kmin || p.ldb < nmin || p.ldc < nmin)
+        return MPGEMM_ELD;
+    if (p.M == 0 || p.N == 0)
+        return MPGEMM_OK;
+    if (p.C == nullptr)
+        return MPGEMM_ENULL;
+    const bool reads_ab = p.K > 0 && p.alpha != 0.0f;
+    if (reads_ab && (p.A == nullptr || p.B == nullptr))
+        return MPGEMM_ENULL;
+    if ((reinterpret_cast<uintptr_t>(p.C) & 3u) != 0)
+        return MPGEMM_EALIGN;
+    if (reads_ab && (((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 1u) != 0))
+        return MPGEMM_EALIGN;
+    return MPGEMM_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// 16-byte loads need a 16-byte aligned base and a leading dimension that
+// keeps every row 16-byte aligned.
+int vec_for(const void *ptr, int64_t ld)
+{
+    return ((reinterpret_cast<uintptr_t>(ptr) & 15u) == 0 && (ld % 8) == 0) ? 8 : 1;
+}
+
+// Can table entry `e` run problem `p`?
+bool entry_fits(const Entry &e, const Problem &p)
+{
+    const mpgemm_config &c = e.cfg;
+    const bool trivial = p.M == 0 || p.N == 0;
+    const bool scale_only = p.K == 0 || p.alpha == 0.0f;
+    if (c.kind == MPGEMM_KIND_SCALE)
+        return scale_only || trivial;
+    if (c.kind == MPGEMM_KIND_DIRECT)
+        return true;
+    if (trivial || scale_only)
+        return true;  // the tiled kernel also handles these; the factory never picks it for them
+    if (c.vec_a == 8 && vec_for(p.A, p.lda) != 8)
+        return false;
+    if (c.vec_b == 8 && vec_for(p.B, p.ldb) != 8)
+        return false;
+    // Per-stage buffer offsets are 32-bit: the A stage spans bm rows of lda,
+    // the B stage bk rows of ldb.
+    const int64_t a_span = ((int64_t)c.bm * p.lda + c.bk) * 2;
+    const int64_t b_span = ((int64_t)c.bk * p.ldb + c.bn) * 2;
+    if (a_span >= (int64_t)0x7FFFFFF0 || b_span >= (int64_t)0x7FFFFFF0)
+        return false;
+    const int64_t tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    if (tiles > 0x7FFFFFFF)
+        return false;
+    return true;
+}
+
+int64_t grid_for(const mpgemm_config &c, const Problem &p)
+{
+    switch (c.kind) {
+    case MPGEMM_KIND_TILED:
+        return cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    case MPGEMM_KIND_DIRECT:
+        return cdiv(p.M, 64) * cdiv(p.N, 64);
+    case MPGEMM_KIND_SCALE:
+        return 0;
+    default:
+        return 0;
+    }
+}
+
+// The factory.  Largest tile whose grid still fills the chip; smaller tiles
+// when the product is small.  Returns a table id, or -1 for "nothing to do".
+int select(const Problem &p)
+{
+    if (p.M == 0 || p.N == 0)
+        return -1;
+    if (p.K == 0 || p.alpha == 0.0f)
+        return kScaleId;
+    const int va = vec_for(p.A, p.lda) == 8 ? 0 : 1;
+    const int vb = vec_for(p.B, p.ldb) == 8 ? 0 : 2;
+    // Enough 256x256 tiles for every CU: large products.
+    // Else 128x128 if that makes at least half a wave of workgroups.
+    // Else 64x64.
+    int group;
+    if (cdiv(p.M, 256) * cdiv(p.N, 256) >= kNumCu)
+        group = 0;
+    else if (cdiv(p.M, 128) * cdiv(p.N, 128) >= kNumCu / 2)
+        group = 1;
+    else
+        group = 2;
+    for (int g = group; g < 3; ++g) {
+        const int id = kGroups[g].first + va + vb;
+        if (entry_fits(kTable[id], p))
+            return id;
+    }
+    return kDirectId;
+}
+
+int fill_config(int id, const Problem &p, mpgemm_config *out)
+{
+    if (id < 0) {
+        mpgemm_config c{};
+        c.id = -1;
+        c.kind = MPGEMM_KIND_NONE;
+        *out = c;
+        return MPGEMM_OK;
+    }
+    *out = kTable[id].cfg;
+    out->grid = grid_for(out[0], p);
+    return MPGEMM_OK;
+}
+
+int run(int id, const Problem &p, void *stream)
+{
+    if (id < 0)
+        return MPGEMM_OK;
+    const Entry &e = kTable[id];
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (e.cfg.kind == MPGEMM_KIND_SCALE || p.K == 0 || p.alpha == 0.0f) {
+        if (p.M == 0 || p.N == 0)
+            return MPGEMM_OK;
+        const int64_t gx = cdiv(p.N, 256) < 64 ? cdiv(p.N, 256) : 64;
+        const int64_t gy = p.M < 65535 ? p.M : 65535;
+        hipLaunchKernelGGL(mpg::scale_c, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s,
+                           const_cast<float *>(p.C), p.M, p.N, p.ldc, p.beta);
+        return hipGetLastError() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
+    }
+    GemmArgs a;
+    a.A = p.A;
+    a.B = p.B;
+    a.C = const_cast<float *>(p.C);
+    a.M = p.M;
+    a.N = p.N;
+    a.K = p.K;
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.alpha = p.alpha;
+    a.beta = p.beta;
+    const int64_t grid = grid_for(e.cfg, p);
+    if (e.cfg.kind == MPGEMM_KIND_DIRECT) {
+        a.tiles_m = (int32_t)cdiv(p.M, 64);
+        a.tiles_n = (int32_t)cdiv(p.N, 64);
+    } else {
+        a.tiles_m = (int32_t)cdiv(p.M, e.cfg.bm);
+        a.tiles_n = (int32_t)cdiv(p.N, e.cfg.bn);
+    }
+    a.group_m = 8;
+    if (grid <= 0 || grid > 0x7FFFFFFF)
+        return MPGEMM_ECONFIG;
+    // A launch error from an earlier, unrelated call must not be reported
+    // as this call's failure.
+    (void)hipGetLastError();
+    const hipError_t err = e.launch(a, dim3((unsigned)grid), s);
+    return err == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
+}
+
+Problem make_problem(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                     const uint16_t *B, int64_t ldb, const float *C, int64_t ldc,
+                     float alpha, float beta)
+{
+    return Problem{M, N, K, lda, ldb, ldc, A, B, C, alpha, beta};
+}
+
+}  // namespace
+
+extern "C" {
+
+int mpgemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                  const uint16_t *B, int64_t ldb, float *C, int64_t ldc, float alpha,
+                  float beta, void *stream)
+{
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta);
+    const int rc = validate(p);
+    if (rc != MPGEMM_OK)
+        return rc;
+    return run(select(p), p, stream);
+}
+
+int mpgemm_f16f32_query(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                        const uint16_t *B, int64_t ldb, const float *C, int64_t ldc,
+                        float alpha, float beta, mpgemm_config *out)
+{
+    if (out == nullptr)
+        return MPGEMM_ENULL;
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta);
+    const int rc = validate(p);
+    if (rc != MPGEMM_OK)
+        return rc;
+    return fill_config(select(p), p, out);
+}
+
+int mpgemm_f16f32_with_config(int config_id, int64_t M, int64_t N, int64_t K,
+                              const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                              float *C, int64_t ldc, float alpha, float beta, void *stream)
+{
+    if (config_id < 0 || config_id >= kNumEntries)
+        return MPGEMM_ECONFIG;
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta);
+    const int rc = validate(p);
+    if (rc != MPGEMM_OK)
+        return rc;
+    if (!entry_fits(kTable[config_id], p))
+        return MPGEMM_ECONFIG;
+    if (p.M == 0 || p.N == 0)
+        return MPGEMM_OK;
+    return run(config_id, p, stream);
+}
+
+int mpgemm_num_configs(void) { return kNumEntries; }
+
+int mpgemm_config_info(int config_id, mpgemm_config *out)
+{
+    if (config_id < 0 || config_id >= kNumEntries)
+        return MPGEMM_ECONFIG;
+    if (out == nullptr)
+        return MPGEMM_ENULL;
+    *out = kTable[config_id].cfg;
+    return MPGEMM_OK;
+}
+
+int mpgemm_probe_mfma_layout(int shape, float *out, void *stream)
+{
+    if (shape != 32 && shape != 16)
+        return MPGEMM_ECONFIG;
+    if (out == nullptr)
+        return MPGEMM_ENULL;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(mpg::probe_mfma, dim3(1), dim3(64), 0,
+                       reinterpret_cast<hipStream_t>(stream), out, shape);
+    return hipGetLastError() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
+}
+
+const char *mpgemm_strerror(int code)
+{
+    switch (code) {
+    case MPGEMM_OK:
+        return "success";
+    case MPGEMM_EDIM:
+        return "a dimension is negative";
+    case MPGEMM_ELD:
+        return "a leading dimension is smaller than its row length";
+    case MPGEMM_ENULL:
+        return "a required pointer is NULL";
+    case MPGEMM_ELAUNCH:
+        return "the HIP kernel launch failed";
+    case MPGEMM_ECONFIG:
+        return "unknown config, or the config cannot run these arguments";
+    case MPGEMM_EALIGN:
+        return "A/B are not 2-byte aligned or C is not 4-byte aligned";
+    default:
+        return "unknown error code";
+    }
+}
+
+const char *mpgemm_version(void) { return "mpgemm 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+/*
+ * mpgemm.h -- C ABI of the FP16-input, FP32-accumulate GEMM for gfx950
+ * (AMD Instinct MI355X).
+ *
+ * The operation (the mixed-precision contract of "Capstone 4: a tensor-core
+ * GEMM", sections "Capability" and "Minimal model": FP16 inputs, an FP32
+ * running sum and an FP32 result, correct when no tile divides the matrix):
+ *
+ *     C[i][j] <- alpha * sum_{k<K} A[i][k] * B[k][j] + beta * C[i][j]
+ *                for 0 <= i < M, 0 <= j < N
+ *
+ * Layouts.  All three matrices are row-major and live in device memory:
+ *     A[i][k] at A[i*lda + k]   (M x K, FP16 bit patterns, lda >= max(1,K))
+ *     B[k][j] at B[k*ldb + j]   (K x N, FP16 bit patterns, ldb >= max(1,N))
+ *     C[i][j] at C[i*ldc + j]   (M x N, IEEE binary32,     ldc >= max(1,N))
+ * Leading dimensions count elements, not bytes.  Any M, N, K >= 0 is
+ * accepted; no padding is needed and none is done.  A and B must be 2-byte
+ * aligned and C 4-byte aligned; wider alignment of the pointers and leading
+ * dimensions only selects faster load paths.
+ *
+ * Arithmetic.  Products of FP16 values are exact in FP32 and are summed in
+ * FP32 by the matrix cores; alpha and beta are applied in FP32 at the end.
+ * When beta == 0, C is written without being read (it may hold NaN).  When
+ * alpha == 0 or K == 0, A and B are not read and C <- beta*C.  Elements of C
+ * outside the M x N window (columns N..ldc-1) are never touched.
+ *
+ * Ownership and concurrency.  The caller owns every buffer.  The library
+ * allocates nothing, frees nothing, keeps no per-call state and never
+ * synchronizes: work is enqueued on `stream` (a hipStream_t passed as
+ * void*; NULL is the default stream) and is complete when the stream is.
+ * Entry points may be called from several host threads at once.  Calls
+ * whose output regions overlap race like any two kernels writing the same
+ * memory.
+ *
+ * Errors.  Every entry point returns 0 on success or a negative
+ * MPGEMM_E* code.  Argument errors are detected on the host before any HIP
+ * call, so nothing is enqueued.  MPGEMM_ELAUNCH reports the HIP error that
+ * the launch itself returned.
+ */
+#ifndef MPGEMM_H
+#define MPGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MPGEMM_OK 0
+#define MPGEMM_EDIM (-1)       /* M, N or K negative                              */
+#define MPGEMM_ELD (-2)        /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+#define MPGEMM_ENULL (-3)      /* NULL pointer for an operand that must be read   */
+#define MPGEMM_ELAUNCH (-4)    /* the HIP launch failed                           */
+#define MPGEMM_ECONFIG (-5)    /* unknown config id, or it cannot run these args  */
+#define MPGEMM_EALIGN (-6)     /* A/B not 2-byte aligned or C not 4-byte aligned  */
+
+/* Kinds of kernel a config can name. */
+#define MPGEMM_KIND_TILED 0    /* LDS-staged, double-buffered MFMA block tile     */
+#define MPGEMM_KIND_DIRECT 1   /* operands straight from memory; any size/stride  */
+#define MPGEMM_KIND_SCALE 2    /* C <- beta*C only (alpha == 0 or K == 0)         */
+#define MPGEMM_KIND_NONE 3     /* nothing to do (M == 0 or N == 0)                */
+
+/* One entry of the kernel-config table, as reported by the factory. */
+typedef struct mpgemm_config {
+    int32_t id;          /* index in the table (see mpgemm_num_configs)          */
+    int32_t kind;        /* MPGEMM_KIND_*                                         */
+    int32_t bm, bn, bk;  /* block tile: rows of C, columns of C, K per LDS stage  */
+    int32_t waves_m;     /* waves along M in a workgroup                          */
+    int32_t waves_n;     /* waves along N                                         */
+    int32_t wave_m;      /* rows of C per wave                                    */
+    int32_t wave_n;      /* columns of C per wave                                 */
+    int32_t mfma_m, mfma_n, mfma_k; /* matrix-core instruction shape              */
+    int32_t vec_a;       /* FP16 elements per global load of A (8 or 1)           */
+    int32_t vec_b;       /* FP16 elements per global load of B (8 or 1)           */
+    int32_t stages;      /* LDS buffers in flight                                 */
+    int32_t threads;     /* threads per workgroup                                 */
+    int32_t lds_bytes;   /* LDS per workgroup                                     */
+    int64_t grid;        /* workgroups for the queried shape (0 in the table)     */
+} mpgemm_config;
+
+/*
+ * The GEMM.  Picks a kernel config for the shape, alignment and scalars
+ * (the same choice mpgemm_f16f32_query reports) and enqueues it on
+ * `stream`.  Returns MPGEMM_OK or a negative code; see the file header for
+ * the arguments, layouts and semantics.
+ */
+int mpgemm_f16f32(int64_t M, int64_t N, int64_t K,
+                  const uint16_t *A, int64_t lda,
+                  const uint16_t *B, int64_t ldb,
+                  float *C, int64_t ldc,
+                  float alpha, float beta,
+                  void *stream);
+
+/*
+ * The factory's choice for these arguments, without launching anything and
+ * without any HIP call (pointers are only inspected for alignment and NULL).
+ * Fills *out and returns MPGEMM_OK, or returns the error mpgemm_f16f32
+ * would return.  `out` is caller-owned host memory.
+ */
+int mpgemm_f16f32_query(int64_t M, int64_t N, int64_t K,
+                        const uint16_t *A, int64_t lda,
+                        const uint16_t *B, int64_t ldb,
+                        const float *C, int64_t ldc,
+                        float alpha, float beta,
+                        mpgemm_config *out);
+
+/*
+ * The GEMM forced onto table entry `config_id` (for tests and tile sweeps).
+ * Same arguments and semantics as mpgemm_f16f32.  Returns MPGEMM_ECONFIG if
+ * the id is unknown or the entry cannot run these arguments (for example a
+ * vec_a = 8 entry on a misaligned A, or the scale-only entry with K > 0).
+ */
+int mpgemm_f16f32_with_config(int config_id,
+                              int64_t M, int64_t N, int64_t K,
+                              const uint16_t *A, int64_t lda,
+                              const uint16_t *B, int64_t ldb,
+                              float *C, int64_t ldc,
+                              float alpha, float beta,
+                              void *stream);
+
+/* Number of entries in the config table. */
+int mpgemm_num_configs(void);
+
+/* Table entry `config_id` into *out (grid = 0).  MPGEMM_ECONFIG if unknown. */
+int mpgemm_config_info(int config_id, mpgemm_config *out);
+
+/*
+ * Diagnostic: runs one matrix-core instruction on known operands and writes
+ * where each output element landed, so the documented lane layout can be
+ * checked on the device.  shape 32 uses the 32x32x16 FP16 instruction,
+ * shape 16 the 16x16x32 one.  Operands: A[i][0] = i, A[i][1] = 1,
+ * B[0][j] = 1, B[1][j] = S*j (S = 32 or 16), every other entry 0, so
+ * D[i][j] = i + S*j exactly.  `out` is device memory for 64*16 floats
+ * (shape 32) or 64*4 floats (shape 16): out[lane*V + v] = lane's v-th
+ * accumulator.  MPGEMM_ECONFIG for another shape.
+ */
+int mpgemm_probe_mfma_layout(int shape, float *out, void *stream);
+
+/* Static text for an error code (never NULL). */
+const char *mpgemm_strerror(int code);
+
+/* Library version string, e.g. "mpgemm 0.1.0 gfx950". */
+const char *mpgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPGEMM_H */

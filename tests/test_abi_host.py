@@ -1,0 +1,159 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+function include/mpgemm.h declares, rejects bad arguments before any HIP call,
+and the tile-config factory picks the intended entry per shape/alignment.
+Pointers here are fake integers: only validation and the factory run, both
+pure host code."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_mixed_precision_amd as mp
+from dense_mixed_precision_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpgemm.h")
+
+FAKE_A = 0x7F0000000000   # 256-byte aligned fake device addresses
+FAKE_B = 0x7F1000000000
+FAKE_C = 0x7F2000000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mpgemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("mpgemm_f16f32", "mpgemm_f16f32_query", "mpgemm_f16f32_with_config",
+                 "mpgemm_num_configs", "mpgemm_config_info", "mpgemm_strerror", "mpgemm_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mp.lib_path())
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_version_and_strerror():
+    assert "gfx950" in mp.mpgemm_version()
+    for code in range(-6, 1):
+        assert mp.mpgemm_strerror(code)
+    assert mp.mpgemm_strerror(-99) == "unknown error code"
+
+
+def q(M, N, K, A=FAKE_A, lda=None, B=FAKE_B, ldb=None, C=FAKE_C, ldc=None, alpha=1.0, beta=0.0):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return mp.mpgemm_f16f32_query(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta)
+
+
+def code(M, N, K, A=FAKE_A, lda=None, B=FAKE_B, ldb=None, C=FAKE_C, ldc=None, alpha=1.0, beta=0.0):
+    try:
+        q(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta)
+        return 0
+    except mp.MpgemmError as e:
+        return e.code
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(M=-1, N=4, K=4), mp.MPGEMM_EDIM),
+    (dict(M=4, N=-1, K=4), mp.MPGEMM_EDIM),
+    (dict(M=4, N=4, K=-3), mp.MPGEMM_EDIM),
+    (dict(M=4, N=4, K=8, lda=7), mp.MPGEMM_ELD),
+    (dict(M=4, N=8, K=4, ldb=7), mp.MPGEMM_ELD),
+    (dict(M=4, N=8, K=4, ldc=7), mp.MPGEMM_ELD),
+    (dict(M=4, N=4, K=0, lda=0), mp.MPGEMM_ELD),
+    (dict(M=4, N=4, K=4, A=0), mp.MPGEMM_ENULL),
+    (dict(M=4, N=4, K=4, B=0), mp.MPGEMM_ENULL),
+    (dict(M=4, N=4, K=4, C=0), mp.MPGEMM_ENULL),
+    (dict(M=4, N=4, K=4, C=FAKE_C + 2), mp.MPGEMM_EALIGN),
+    (dict(M=4, N=4, K=4, A=FAKE_A + 1), mp.MPGEMM_EALIGN),
+    (dict(M=4, N=4, K=4, B=FAKE_B + 1), mp.MPGEMM_EALIGN),
+    # A and B are not read when alpha == 0 or K == 0: NULL is fine there
+    (dict(M=4, N=4, K=4, A=0, B=0, alpha=0.0, beta=0.5), 0),
+    (dict(M=4, N=4, K=0, A=0, B=0), 0),
+    # nothing to do at all: C may be NULL
+    (dict(M=0, N=4, K=4, C=0), 0),
+    (dict(M=4, N=0, K=4, C=0), 0),
+])
+def test_validation_codes(args, expect):
+    assert code(**args) == expect
+
+
+def test_validation_happens_before_launch():
+    # the launching entry point returns the same codes without touching HIP
+    rc = mp.mpgemm_f16f32(-1, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0)
+    assert rc == mp.MPGEMM_EDIM
+    rc = mp.mpgemm_f16f32(4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C + 1, 4, 1.0, 0.0, 0)
+    assert rc == mp.MPGEMM_EALIGN
+    rc = mp.mpgemm_f16f32_with_config(999, 4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0)
+    assert rc == mp.MPGEMM_ECONFIG
+    rc = mp.mpgemm_f16f32_with_config(-1, 4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0)
+    assert rc == mp.MPGEMM_ECONFIG
+
+
+def test_config_table_is_consistent():
+    n = mp.mpgemm_num_configs()
+    assert n >= 4
+    kinds = set()
+    for i in range(n):
+        c = mp.mpgemm_config_info(i)
+        assert c["id"] == i
+        kinds.add(c["kind_name"])
+        if c["kind_name"] == "tiled":
+            assert c["bm"] % (32 * c["waves_m"]) == 0 and c["bn"] % (32 * c["waves_n"]) == 0
+            assert c["wave_m"] * c["waves_m"] == c["bm"] and c["wave_n"] * c["waves_n"] == c["bn"]
+            assert c["threads"] == 64 * c["waves_m"] * c["waves_n"]
+            assert c["lds_bytes"] == c["stages"] * (c["bm"] + c["bn"]) * c["bk"] * 2
+            assert c["lds_bytes"] <= 160 * 1024
+            assert c["vec_a"] in (1, 8) and c["vec_b"] in (1, 8)
+    assert {"tiled", "direct", "scale"} <= kinds
+    with pytest.raises(mp.MpgemmError):
+        mp.mpgemm_config_info(n)
+
+
+def _pick(w):
+    return q(w.M, w.N, w.K, alpha=w.alpha, beta=w.beta)
+
+
+def test_factory_choices_for_the_workloads():
+    c = _pick(WORKLOADS["square8192"])
+    assert (c["kind_name"], c["bm"], c["bn"], c["vec_a"], c["vec_b"]) == ("tiled", 256, 256, 8, 8)
+    assert c["grid"] == 32 * 32
+    c = _pick(WORKLOADS["square2048"])
+    assert (c["bm"], c["bn"]) == (128, 128) and c["grid"] == 256
+    c = _pick(WORKLOADS["tallskinny32768x128x4096"])
+    assert c["kind_name"] == "tiled" and c["grid"] >= 256
+    c = _pick(WORKLOADS["ragged1000x800x617"])
+    # lda = 617 is odd: A rows are only 2-byte aligned, so A takes the
+    # element-wise path; B (ldb = 800) keeps 16-byte loads.
+    assert c["kind_name"] == "tiled" and c["vec_a"] == 1 and c["vec_b"] == 8
+    c = _pick(WORKLOADS["square256"])
+    assert c["kind_name"] == "tiled" and c["grid"] >= 16
+
+
+def test_factory_alignment_and_degenerate_cases():
+    assert q(512, 512, 512, A=FAKE_A + 2)["vec_a"] == 1
+    assert q(512, 512, 512, B=FAKE_B + 8)["vec_b"] == 1
+    assert q(512, 512, 512, lda=516)["vec_a"] == 1
+    assert q(512, 512, 512, lda=520)["vec_a"] == 8
+    assert q(512, 512, 0)["kind_name"] == "scale"
+    assert q(512, 512, 64, alpha=0.0, beta=2.0)["kind_name"] == "scale"
+    assert q(0, 512, 64)["kind_name"] == "none"
+
+
+def test_factory_falls_back_to_direct_for_huge_strides():
+    # a 256-row A stage with lda = 2^23 spans 4 GiB: 32-bit buffer offsets
+    # cannot reach it, so only the 64-bit direct kernel fits.
+    c = q(300, 300, 64, lda=1 << 23)
+    assert c["kind_name"] in ("tiled", "direct")
+    if c["kind_name"] == "tiled":
+        assert (c["bm"] * (1 << 23) + c["bk"]) * 2 < 0x7FFFFFF0
+    c = q(300, 300, 64, lda=1 << 30)
+    assert c["kind_name"] == "direct"

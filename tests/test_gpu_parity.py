@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Acceptance (elementwise): |C_gpu - C_ref| <= 1e-3 * sum_k |a_ik b_kj| + 1e-5,
+NaN/Inf fail.  Small and ragged products are compared on every element; the
+large workloads on sampled entries (at least one in every 128x128 block, the
+last row and column, the corners) plus Freivalds' whole-output check.
+Exact-integer, all-ones and identity inputs must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_mixed_precision_amd as mp
+import oracle
+from dense_mixed_precision_amd.workloads import WORKLOADS, bits, make_inputs, workload_inputs
+from tests.gpu_util import (Guarded, assert_close, device, freivalds_ok, run, tile_samples)
+
+pytestmark = pytest.mark.gpu
+
+
+def _c_np(C):
+    return None if C is None else C.numpy()
+
+
+def full_check(label, A, B, C0, alpha, beta, **kw):
+    got, gC = run(A, B, C0, alpha, beta, **kw)
+    ref, absdot = oracle.gemm(bits(A), bits(B), _c_np(C0), alpha, beta)
+    assert_close(label, got, ref, absdot)
+    assert gC.untouched_outside_window(), f"{label}: wrote outside the M x N window"
+    return got, ref
+
+
+# ----------------------------------------------------------------------------
+# Matrix-core lane layout
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape,nv", [(32, 16), (16, 4)])
+def test_mfma_layout_probe(shape, nv):
+    out = torch.full((64 * nv,), -1.0, device=device())
+    assert mp.mpgemm_probe_mfma_layout(shape, out.data_ptr(), 0) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(64, nv)
+    for lane in range(64):
+        for v in range(nv):
+            if shape == 32:
+                row, col = 8 * (v // 4) + 4 * (lane // 32) + v % 4, lane % 32
+            else:
+                row, col = 4 * (lane // 16) + v, lane % 16
+            assert got[lane, v] == row + shape * col, (lane, v, got[lane, v])
+
+
+# ----------------------------------------------------------------------------
+# The five workloads
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["square256", "ragged1000x800x617"])
+def test_workload_every_element(name):
+    w = WORKLOADS[name]
+    A, B, C = workload_inputs(w)
+    print(f"[{name}] {mp.query_for(A.to(device()), B.to(device()), torch.empty(w.M, w.N, device=device()))}",
+          flush=True)
+    full_check(name, A, B, C, w.alpha, w.beta)
+
+
+@pytest.mark.parametrize("name", ["square2048", "tallskinny32768x128x4096", "square8192"])
+def test_workload_sampled_and_freivalds(name):
+    w = WORKLOADS[name]
+    print(f"[{name}] generating inputs", flush=True)
+    A, B, C = workload_inputs(w)
+    got, gC = run(A, B, C, w.alpha, w.beta)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    rows, cols = tile_samples(w.M, w.N, tile=128, per_tile=1, seed=w.seed)
+    ref, absdot = oracle.gemm_entries(bits(A), bits(B), _c_np(C), w.alpha, w.beta, rows, cols)
+    assert_close(name, got[rows, cols], ref, absdot, rows, cols)
+    ok, ratio = freivalds_ok(got, A, B, C, w.alpha, w.beta, seed=w.seed)
+    print(f"[{name}] {rows.size} sampled entries ok; Freivalds worst ratio {ratio:.3g}", flush=True)
+    assert ok, f"{name}: Freivalds check failed (worst err/bound {ratio:.3g})"
+    assert gC.untouched_outside_window()
+
+
+# ----------------------------------------------------------------------------
+# Ragged edges, every kernel config, strides and alignment
+# ----------------------------------------------------------------------------
+
+EDGE_SHAPES = [
+    (1, 1, 1), (1, 1, 17), (15, 17, 16), (16, 16, 16), (17, 15, 33), (31, 33, 65),
+    (33, 31, 63), (64, 64, 64), (65, 63, 129), (127, 129, 255), (129, 127, 257),
+    (611, 613, 617), (256, 256, 1), (300, 17, 40), (17, 300, 40), (1, 512, 96), (512, 1, 96),
+    (4096, 16, 256), (16, 4096, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE_SHAPES)
+def test_edge_shapes_factory(M, N, K):
+    A, B, C = make_inputs(M, N, K, "uniform", seed=M * 7 + N * 3 + K, c_init="uniform")
+    full_check(f"{M}x{N}x{K} beta=0", A, B, None, 1.0, 0.0)
+    full_check(f"{M}x{N}x{K} beta=.5", A, B, C, 1.5, 0.5)
+
+
+def _tiled_and_direct_ids():
+    ids = []
+    for i in range(mp.mpgemm_num_configs()):
+        c = mp.mpgemm_config_info(i)
+        if c["kind_name"] in ("tiled", "direct"):
+            ids.append(i)
+    return ids
+
+
+@pytest.mark.parametrize("cfg", _tiled_and_direct_ids())
+def test_every_config_on_ragged_strided_input(cfg):
+    """M, N, K fit no tile; lda/ldb are multiples of 8 (so the 16-byte load
+    variants apply) but K % 8 and N % 8 leave partial vectors at the edges;
+    ldc > N."""
+    M, N, K = 261, 147, 101
+    A, B, C = make_inputs(M, N, K, "uniform", seed=cfg + 100, c_init="uniform")
+    full_check(f"config {cfg}", A, B, C, 1.25, -0.75, config=cfg, lda=112, ldb=160, ldc=151)
+    full_check(f"config {cfg} beta=0", A, B, None, 1.0, 0.0, config=cfg, lda=112, ldb=160, ldc=149)
+
+
+@pytest.mark.parametrize("cfg", _tiled_and_direct_ids())
+def test_every_config_multi_tile(cfg):
+    """Several tiles of every size in both directions and a K loop longer
+    than the LDS ring, with exact small integers: must match bit for bit."""
+    M, N, K = 520, 600, 392
+    A, B, _ = make_inputs(M, N, K, "smallint", seed=cfg + 200)
+    got, gC = run(A, B, None, 1.0, 0.0, config=cfg)
+    ref, _ = oracle.gemm(bits(A), bits(B))
+    assert np.array_equal(got, ref.astype(np.float32)), f"config {cfg}: not bitwise"
+
+
+def test_misaligned_pointers_and_odd_leading_dimensions():
+    M, N, K = 333, 250, 617
+    A, B, C = make_inputs(M, N, K, "uniform", seed=41, c_init="uniform")
+    for a_off, b_off, lda, ldb in [(1, 0, K, N), (0, 1, K, N), (1, 1, K + 3, N + 5), (0, 0, K, N + 1)]:
+        full_check(f"a_off={a_off} b_off={b_off} lda={lda} ldb={ldb}", A, B, C, 1.5, 0.5,
+                   a_off=a_off, b_off=b_off, lda=lda, ldb=ldb)
+
+
+# ----------------------------------------------------------------------------
+# Exact cases
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1000, 800, 617), (333, 257, 129), (256, 256, 256), (64, 4096, 2048)])
+def test_small_integers_bitwise(M, N, K):
+    A, B, _ = make_inputs(M, N, K, "smallint", seed=M + N + K)
+    got, _ = run(A, B, None, 1.0, 0.0)
+    ref, _ = oracle.gemm(bits(A), bits(B))
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_all_ones_gives_K_and_identity_gives_copy():
+    M, N, K = 300, 200, 617
+    A, B, _ = make_inputs(M, N, K, "ones", seed=1)
+    got, _ = run(A, B, None, 1.0, 0.0)
+    assert np.all(got == K)
+    Kq = 300
+    I = torch.eye(Kq, dtype=torch.float16)
+    _, B2, _ = make_inputs(Kq, 211, Kq, "uniform", seed=2)
+    got, _ = run(I, B2, None, 1.0, 0.0)
+    assert np.array_equal(got, B2.numpy().astype(np.float32))
+
+
+def test_alpha_zero_and_k_zero_scale_C():
+    M, N = 130, 70
+    A, B, C = make_inputs(M, N, 33, "uniform", seed=3, c_init="uniform")
+    got, _ = run(A, B, C, 0.0, 0.5)
+    assert np.array_equal(got, (np.float32(0.5) * C.numpy()))
+    A0, B0, _ = make_inputs(M, N, 0, "uniform", seed=3)
+    got, _ = run(A0, B0, C, 1.0, -2.0)
+    assert np.array_equal(got, (np.float32(-2.0) * C.numpy()))
+    got, _ = run(A0, B0, None, 1.0, 0.0)
+    assert np.all(got == 0)
+
+
+def test_nan_poisoned_C_is_not_read_when_beta_is_zero():
+    M, N, K = 257, 255, 129
+    A, B, _ = make_inputs(M, N, K, "uniform", seed=4)
+    got, _ = run(A, B, None, 1.0, 0.0, poison=True)
+    assert np.all(np.isfinite(got))
+
+
+def test_deterministic_bitwise_across_runs():
+    w = WORKLOADS["ragged1000x800x617"]
+    A, B, C = workload_inputs(w)
+    g1, _ = run(A, B, C, w.alpha, w.beta)
+    g2, _ = run(A, B, C, w.alpha, w.beta)
+    assert np.array_equal(g1, g2)
+    A, B, _ = make_inputs(2048, 2048, 2048, "uniform", seed=5)
+    g1, _ = run(A, B, None, 1.0, 0.0)
+    g2, _ = run(A, B, None, 1.0, 0.0)
+    assert np.array_equal(g1, g2)
+
+
+def test_non_default_stream():
+    M, N, K = 640, 384, 200
+    A, B, C = make_inputs(M, N, K, "uniform", seed=6, c_init="uniform")
+    s = torch.cuda.Stream()
+    full_check("side stream", A, B, C, 1.0, 1.0, stream=s)
