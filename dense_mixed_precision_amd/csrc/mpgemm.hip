@@ -18,6 +18,7 @@
 namespace {
 
 using mpg::GemmArgs;
+using mpg::PipeCfg;
 using mpg::TileCfg;
 
 constexpr int kNumCu = 256;
@@ -36,6 +37,13 @@ template <class Cfg>
 hipError_t launch_tiled(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
     hipLaunchKernelGGL(mpg::gemm_tiled<Cfg>, grid, dim3(Cfg::NT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <class Cfg>
+hipError_t launch_pipe(const GemmArgs &a, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(mpg::gemm_pipe<Cfg>, grid, dim3(Cfg::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -68,6 +76,31 @@ constexpr Entry tiled_entry(int id)
     c.lds_bytes = Cfg::LDS_BYTES;
     c.grid = 0;
     return Entry{c, &launch_tiled<Cfg>};
+}
+
+template <class Cfg>
+constexpr Entry pipe_entry(int id)
+{
+    mpgemm_config c{};
+    c.id = id;
+    c.kind = MPGEMM_KIND_PIPE;
+    c.bm = Cfg::BM;
+    c.bn = Cfg::BN;
+    c.bk = Cfg::BK;
+    c.waves_m = Cfg::WAVES_M;
+    c.waves_n = Cfg::WAVES_N;
+    c.wave_m = Cfg::WTM;
+    c.wave_n = Cfg::WTN;
+    c.mfma_m = 32;
+    c.mfma_n = 32;
+    c.mfma_k = 16;
+    c.vec_a = Cfg::VEC_A;
+    c.vec_b = Cfg::VEC_B;
+    c.stages = Cfg::STAGES;
+    c.threads = Cfg::NT;
+    c.lds_bytes = Cfg::LDS_BYTES;
+    c.grid = 0;
+    return Entry{c, &launch_pipe<Cfg>};
 }
 
 constexpr Entry direct_entry(int id)
@@ -109,23 +142,33 @@ constexpr Entry scale_entry(int id)
         tiled_entry<TileCfg<BM, BN, BK, WM, WN, 8, 1>>(base + 2),      \
         tiled_entry<TileCfg<BM, BN, BK, WM, WN, 1, 1>>(base + 3)
 
+#define MPG_PIPE_ENTRIES(base, BM, BN, WM, WN, S)                      \
+    pipe_entry<PipeCfg<BM, BN, WM, WN, S, 8, 8>>(base + 0),            \
+        pipe_entry<PipeCfg<BM, BN, WM, WN, S, 1, 8>>(base + 1),        \
+        pipe_entry<PipeCfg<BM, BN, WM, WN, S, 8, 1>>(base + 2),        \
+        pipe_entry<PipeCfg<BM, BN, WM, WN, S, 1, 1>>(base + 3)
+
 const Entry kTable[] = {
-    MPG_TILE_ENTRIES(0, 256, 256, 64, 2, 2),  // 0..3   large products
-    MPG_TILE_ENTRIES(4, 128, 128, 64, 2, 2),  // 4..7   2048-class and tall-skinny
-    MPG_TILE_ENTRIES(8, 64, 64, 64, 2, 2),    // 8..11  small or ragged products
+    MPG_TILE_ENTRIES(0, 256, 256, 64, 2, 2),  // 0..3   register-staged copies
+    MPG_TILE_ENTRIES(4, 128, 128, 64, 2, 2),  // 4..7
+    MPG_TILE_ENTRIES(8, 64, 64, 64, 2, 2),    // 8..11
     direct_entry(12),                         // 12     any stride / size
     scale_entry(13),                          // 13     alpha == 0 or K == 0
+    MPG_PIPE_ENTRIES(14, 256, 256, 2, 2, 2),  // 14..17 large products
+    MPG_PIPE_ENTRIES(18, 128, 128, 2, 2, 3),  // 18..21 2048-class and tall-skinny
+    MPG_PIPE_ENTRIES(22, 64, 64, 2, 2, 2),    // 22..25 small or ragged products
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
 constexpr int kDirectId = 12;
 constexpr int kScaleId = 13;
 
-// Tile groups in the table, largest first: (first id, BM, BN).
+// Tile groups the factory chooses from, largest first: (first id, BM, BN).
+// Each group holds the four (vec_a, vec_b) variants in the order 88, 18, 81, 11.
 struct TileGroup {
     int first;
     int bm, bn;
 };
-constexpr TileGroup kGroups[] = {{0, 256, 256}, {4, 128, 128}, {8, 64, 64}};
+constexpr TileGroup kGroups[] = {{14, 256, 256}, {18, 128, 128}, {22, 64, 64}};
 
 // ---------------------------------------------------------------------------
 // Validation and selection (pure host code, no HIP calls)
@@ -201,6 +244,7 @@ int64_t grid_for(const mpgemm_config &c, const Problem &p)
 {
     switch (c.kind) {
     case MPGEMM_KIND_TILED:
+    case MPGEMM_KIND_PIPE:
         return cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
     case MPGEMM_KIND_DIRECT:
         return cdiv(p.M, 64) * cdiv(p.N, 64);

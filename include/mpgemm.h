@@ -59,6 +59,8 @@ extern "C" {
 #define MPGEMM_KIND_DIRECT 1   /* operands straight from memory; any size/stride  */
 #define MPGEMM_KIND_SCALE 2    /* C <- beta*C only (alpha == 0 or K == 0)         */
 #define MPGEMM_KIND_NONE 3     /* nothing to do (M == 0 or N == 0)                */
+#define MPGEMM_KIND_PIPE 4     /* LDS ring filled by direct-to-LDS copies, B read
+                                  with the transposing LDS load; the fast path    */
 
 /* One entry of the kernel-config table, as reported by the factory. */
 typedef struct mpgemm_config {

@@ -106,14 +106,14 @@ def test_config_table_is_consistent():
         c = mp.mpgemm_config_info(i)
         assert c["id"] == i
         kinds.add(c["kind_name"])
-        if c["kind_name"] == "tiled":
+        if c["kind_name"] in ("tiled", "pipe"):
             assert c["bm"] % (32 * c["waves_m"]) == 0 and c["bn"] % (32 * c["waves_n"]) == 0
             assert c["wave_m"] * c["waves_m"] == c["bm"] and c["wave_n"] * c["waves_n"] == c["bn"]
             assert c["threads"] == 64 * c["waves_m"] * c["waves_n"]
             assert c["lds_bytes"] == c["stages"] * (c["bm"] + c["bn"]) * c["bk"] * 2
             assert c["lds_bytes"] <= 160 * 1024
             assert c["vec_a"] in (1, 8) and c["vec_b"] in (1, 8)
-    assert {"tiled", "direct", "scale"} <= kinds
+    assert {"tiled", "pipe", "direct", "scale"} <= kinds
     with pytest.raises(mp.MpgemmError):
         mp.mpgemm_config_info(n)
 
@@ -124,18 +124,18 @@ def _pick(w):
 
 def test_factory_choices_for_the_workloads():
     c = _pick(WORKLOADS["square8192"])
-    assert (c["kind_name"], c["bm"], c["bn"], c["vec_a"], c["vec_b"]) == ("tiled", 256, 256, 8, 8)
+    assert (c["kind_name"], c["bm"], c["bn"], c["vec_a"], c["vec_b"]) == ("pipe", 256, 256, 8, 8)
     assert c["grid"] == 32 * 32
     c = _pick(WORKLOADS["square2048"])
     assert (c["bm"], c["bn"]) == (128, 128) and c["grid"] == 256
     c = _pick(WORKLOADS["tallskinny32768x128x4096"])
-    assert c["kind_name"] == "tiled" and c["grid"] >= 256
+    assert c["kind_name"] == "pipe" and c["grid"] >= 256
     c = _pick(WORKLOADS["ragged1000x800x617"])
     # lda = 617 is odd: A rows are only 2-byte aligned, so A takes the
     # element-wise path; B (ldb = 800) keeps 16-byte loads.
-    assert c["kind_name"] == "tiled" and c["vec_a"] == 1 and c["vec_b"] == 8
+    assert c["kind_name"] == "pipe" and c["vec_a"] == 1 and c["vec_b"] == 8
     c = _pick(WORKLOADS["square256"])
-    assert c["kind_name"] == "tiled" and c["grid"] >= 16
+    assert c["kind_name"] == "pipe" and c["grid"] >= 16
 
 
 def test_factory_alignment_and_degenerate_cases():
@@ -152,8 +152,8 @@ def test_factory_falls_back_to_direct_for_huge_strides():
     # a 256-row A stage with lda = 2^23 spans 4 GiB: 32-bit buffer offsets
     # cannot reach it, so only the 64-bit direct kernel fits.
     c = q(300, 300, 64, lda=1 << 23)
-    assert c["kind_name"] in ("tiled", "direct")
-    if c["kind_name"] == "tiled":
+    assert c["kind_name"] in ("pipe", "direct")
+    if c["kind_name"] == "pipe":
         assert (c["bm"] * (1 << 23) + c["bk"]) * 2 < 0x7FFFFFF0
     c = q(300, 300, 64, lda=1 << 30)
     assert c["kind_name"] == "direct"

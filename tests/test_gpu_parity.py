@@ -101,7 +101,7 @@ def _tiled_and_direct_ids():
     ids = []
     for i in range(mp.mpgemm_num_configs()):
         c = mp.mpgemm_config_info(i)
-        if c["kind_name"] in ("tiled", "direct"):
+        if c["kind_name"] in ("tiled", "pipe", "direct"):
             ids.append(i)
     return ids
 
