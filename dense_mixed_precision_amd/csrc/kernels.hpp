@@ -442,57 +442,84 @@ probe_mfma(float *out, int shape)
 // ---------------------------------------------------------------------------
 // Pipelined kernel: global -> LDS with buffer_load ... lds, B read transposed
 // ---------------------------------------------------------------------------
-// LDS layout of one stage:
-//   A: BM rows x 64 K, K-contiguous, 128 B per row; the 16-byte chunk c of
-//      row r sits at physical chunk c ^ (r & 7), so the 8 consecutive rows a
-//      ds_read_b128 group touches hit 8 distinct 16-byte bank slots.
-//   B: 64 K rows x BN columns, N-contiguous (as in memory); chunk c of row k
-//      sits at c ^ 2*(k & 3), so the 4 rows x 32 bytes each 16-lane group of a
-//      ds_read_b64_tr_b16 touches are 8 distinct bank slots.
-// Copies: each wave instruction of buffer_load_dwordx4 ... lds writes 64
+// LDS layout of one stage (BK = 32 or 64).  gfx950's LDS has 64 banks of
+// 4 bytes: a ds_read_b128 serves 16 lanes per cycle and a ds_read_b64
+// (including the transposing read) 32 lanes, so each such group must touch
+// 256 distinct bytes of bank space to run at full rate.
+//   A: BM rows x BK, K-contiguous (2*BK bytes per row).  The 16-byte chunk c
+//      of row r sits at physical chunk c ^ swz_a(r).  One 16-lane group reads
+//      16 consecutive rows at one logical chunk; with 128-byte rows two rows
+//      share a 256-byte bank window, so swz_a(r) = (r >> 1) & 7 gives the 8
+//      rows of each parity 8 distinct chunks; with 64-byte rows four rows
+//      share a window and swz_a(r) = (r >> 2) & 3.
+//   B: BK rows x BN, N-contiguous as in memory.  Chunk c of row k sits at
+//      c ^ swz_b(k).  One 32-lane group of the transposing read touches 4
+//      consecutive rows x 4 consecutive chunks; swz_b(k) = 4*(k & 3) moves
+//      the rows to 4 different 64-byte quarters of the window (rows of 256
+//      bytes or more), or 4*((k >> 1) & 1) for 128-byte rows (BN = 64),
+//      where row parity already selects the window half.
+// Copies: one wave instruction of buffer_load_dwordx4 ... lds writes 64
 // lanes x 16 B to LDS at M0 + 16*lane (a contiguous KiB); the swizzle is
 // applied by choosing which global chunk each lane fetches.  Lanes whose
-// chunk lies outside the matrix get an offset past num_records and write
-// zeros.  Vectors that straddle the end of a row, and operands that are not
-// 16-byte aligned, are filled through registers instead (ds_write_b128).
+// chunk is outside the matrix get an offset past num_records and write
+// zeros.  Vectors that straddle the end of a row, and operands without
+// 16-byte alignment, are filled through registers instead.
+//
+// Schedule (per wave, per K tile of BK): each k-step first issues every
+// operand read of the next k-step (into the other register set), then runs
+// its MFMAs in groups of FN, each group followed by its share of the copies
+// for the tile STAGES-1 ahead.  The copies are all issued before the
+// end-of-tile barrier, which sits before the last k-step's MFMAs so that
+// the reads of the next tile's first k-step overlap them.
 typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int VEC_A_, int VEC_B_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int VEC_A_, int VEC_B_>
 struct PipeCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 64;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int VEC_A = VEC_A_, VEC_B = VEC_B_;
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int KS = BK / 16;
-    static constexpr int A_ROWB = BK * 2;                 // 128
+    static constexpr int KS = BK / 16;                    // MFMA k-steps per tile
+    static constexpr int A_ROWB = BK * 2;
     static constexpr int B_ROWB = BN * 2;
     static constexpr int A_BYTES = BM * A_ROWB;
     static constexpr int B_BYTES = BK * B_ROWB;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-    static constexpr int B_CH = BN / 8;                   // 16-byte chunks per B row
-    static constexpr int A_RPI = 8;                       // A rows per wave instruction
-    static constexpr int B_RPI = 64 / B_CH;               // B rows per wave instruction
-    static constexpr int A_PER_WAVE = BM / A_RPI / NW;    // A copy instructions per wave per stage
-    static constexpr int B_PER_WAVE = BK / B_RPI / NW;
+    static constexpr int A_CH = BK / 8;                   // 16-byte chunks per A row
+    static constexpr int B_CH = BN / 8;                   // ... per B row
+    static constexpr int A_RPI = 64 / A_CH;               // A rows per copy instruction
+    static constexpr int B_RPI = 64 / B_CH;               // B rows per copy instruction
+    static constexpr int APW = BM / A_RPI / NW;           // A copies per wave per tile
+    static constexpr int BPW = BK / B_RPI / NW;           // B copies per wave per tile
+    static constexpr int NL = (VEC_A == 8 ? APW : 0) + (VEC_B == 8 ? BPW : 0);  // vmcnt per tile
+    // MFMA groups (one per A row-block, FM per k-step) over which a tile's
+    // copies are spread: with two stages they must land within the same
+    // tile, so they all go out after the first group; deeper rings spread
+    // them over every group before the barrier.
+    static constexpr int COPY_GROUPS = STAGES == 2 ? 1 : (KS - 1) * FM;
+    static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
     static_assert(BN >= 64 && 64 % B_CH == 0, "B rows must hold 8..64 chunks");
     static_assert((BM / A_RPI) % NW == 0 && (BK / B_RPI) % NW == 0, "copies must split evenly over waves");
-    static_assert(STAGES >= 2 && STAGES <= 4, "2..4 LDS stages");
+    static_assert(STAGES >= 2 && STAGES <= 5, "2..5 LDS stages");
+    static_assert(NL * (STAGES - 2) < 64, "vmcnt is 6 bits");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 };
 
 // Copies and the waits for them are issued through inline asm, so the
-// compiler neither tracks them nor inserts its own conservative
-// "vmcnt(0) before any LDS read" waits (which would serialize the
-// prefetch); the kernel accounts for them with explicit vmcnt waits.  The
-// "memory" clobber keeps every compiler-visible memory access on its side.
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// compiler neither tracks them nor inserts its own conservative "vmcnt(0)
+// before any LDS read" waits (which would serialize the prefetch); the
+// kernel accounts for them with explicit vmcnt waits.  The "memory" clobber
+// keeps every compiler-visible memory access on its side of each copy, and
+// volatile asm is not moved across other volatile asm or barriers, so the
+// source order below is the issue order.
 
 // Raw buffer descriptor in four scalar registers: 48-bit base, stride 0,
 // num_records, gfx9-family data-format word.
@@ -509,9 +536,9 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// One wave instruction: lane l copies 16 bytes from rsrc at voff + soff
-// into LDS at byte address lds_addr + 16*l.  M0 carries lds_addr; one wait
-// state separates its write from the copy that reads it.
+// One wave instruction: lane l copies 16 bytes from rsrc at voff + soff into
+// LDS at byte address lds_addr + 16*l.  M0 carries lds_addr; one wait state
+// separates its write from the copy that reads it.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff)
 {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -525,11 +552,9 @@ gemm_pipe(GemmArgs args)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
     constexpr int FM = Cfg::FM, FN = Cfg::FN, KS = Cfg::KS, NW = Cfg::NW;
-    constexpr int A_ROWB = Cfg::A_ROWB, B_ROWB = Cfg::B_ROWB, B_CH = Cfg::B_CH;
+    constexpr int A_ROWB = Cfg::A_ROWB, B_ROWB = Cfg::B_ROWB, A_CH = Cfg::A_CH, B_CH = Cfg::B_CH;
     constexpr int A_RPI = Cfg::A_RPI, B_RPI = Cfg::B_RPI;
-    constexpr int APW = Cfg::A_PER_WAVE, BPW = Cfg::B_PER_WAVE;
-    // copy instructions per thread per stage that count against vmcnt
-    constexpr int NL = (Cfg::VEC_A == 8 ? APW : 0) + (Cfg::VEC_B == 8 ? BPW : 0);
+    constexpr int APW = Cfg::APW, BPW = Cfg::BPW, NL = Cfg::NL;
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES];
     lds_u8 *const lds = (lds_u8 *)smem;
@@ -537,8 +562,8 @@ gemm_pipe(GemmArgs args)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    // wave index, made explicitly wave-uniform so everything derived from
-    // it (copy offsets, M0) stays in scalar registers
+    // wave index, made explicitly wave-uniform so everything derived from it
+    // (copy offsets, M0) stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WAVES_N;
     const int wn = wave % Cfg::WAVES_N;
@@ -547,80 +572,97 @@ gemm_pipe(GemmArgs args)
     tile_coords(blockIdx.x, gridDim.x, args.tiles_n, args.tiles_m, args.group_m, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
-    const int64_t M = args.M, N = args.N, K = args.K;
+    const int64_t K = args.K;
     const int64_t lda = args.lda, ldb = args.ldb;
-    const int64_t rows_left = M - m0;   // > 0
-    const int64_t cols_left = N - n0;   // > 0
+    const int64_t rows_left = args.M - m0;  // > 0
+    const int64_t cols_left = args.N - n0;  // > 0
 
-    // ---- copy assignment (the same chunks for DMA and register fill) ------
-    // A instruction i of this wave covers rows 8*j .. 8*j+7, j = i*NW + wave;
-    // lane -> row 8*j + lane/8, physical chunk lane%8, logical chunk
-    // (lane%8) ^ (lane/8).
-    const int a_r = lane >> 3;
-    const int a_c = (lane & 7) ^ a_r;
-    const uint32_t a_voff = (uint32_t)((a_r * lda + 8 * a_c) * 2);
-    // B instruction i covers rows B_RPI*j .. +B_RPI-1; lane -> row
-    // B_RPI*j + lane/B_CH, physical chunk lane%B_CH, logical chunk
-    // physical ^ 2*(row & 3).
+    // ---- copy assignment (the same chunks for copies and register fill) ---
+    // A copy i of this wave covers rows A_RPI*j .. +A_RPI-1, j = i*NW + wave;
+    // lane -> row A_RPI*j + lane/A_CH, physical chunk lane%A_CH.
+    auto swz_a = [](int r) __attribute__((always_inline)) {
+        return A_CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+    };
+    auto swz_b = [](int k) __attribute__((always_inline)) {
+        return B_CH >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+    };
+    const int a_r = lane / A_CH;
+    const int a_p = lane % A_CH;
+    // logical chunk fetched by this lane in A copy j (its row is A_RPI*j + a_r)
+    auto a_c_of = [&](int j) __attribute__((always_inline)) { return a_p ^ swz_a(A_RPI * j + a_r); };
+    // B copy i covers rows B_RPI*j .. +B_RPI-1; lane -> row B_RPI*j + lane/B_CH,
+    // physical chunk lane%B_CH, logical chunk physical ^ swz_b(row).
     const int b_r = lane / B_CH;
     const int b_p = lane % B_CH;
-    auto b_c_of = [&](int j) __attribute__((always_inline)) { return b_p ^ (2 * ((B_RPI * j + b_r) & 3)); };
+    auto b_c_of = [&](int j) __attribute__((always_inline)) { return b_p ^ swz_b(B_RPI * j + b_r); };
 
-    auto issue = [&](int64_t kt, int buf) __attribute__((always_inline)) {
-        const int64_t k0 = kt * BK;
-        const int64_t k_left = K - k0;
-        const uint32_t sbase = lds_base + buf * Cfg::STAGE_BYTES;
-        if constexpr (Cfg::VEC_A == 8) {
-            const i32x4 rsA = make_rsrc4(args.A + m0 * lda + k0);
-            const bool col_ok = 8 * a_c + 8 <= k_left;
-#pragma unroll
-            for (int i = 0; i < APW; ++i) {
-                const int j = i * NW + wave;
-                const bool ok = col_ok && (A_RPI * j + a_r) < rows_left;
-                dma16(rsA, sbase + j * 1024, ok ? a_voff : kOOB, (uint32_t)(A_RPI * j * lda * 2));
+    int64_t copy_tile = 0;   // tile whose copies are being issued
+    int copy_buf = 0;
+    bool copy_live = false;
+    i32x4 rsA, rsB;
+    int64_t copy_kleft = 0;
+    auto begin_copies = [&](int64_t t, int buf) __attribute__((always_inline)) {
+        copy_tile = t;
+        copy_buf = buf;
+        copy_live = t < (K + BK - 1) / BK;
+        const int64_t k0 = t * BK;
+        copy_kleft = K - k0;
+        rsA = make_rsrc4(args.A + m0 * lda + k0);
+        rsB = make_rsrc4(args.B + k0 * ldb + n0);
+    };
+    // copy number q (0 .. APW+BPW-1) of the current tile
+    auto copy_one = [&](int q) __attribute__((always_inline)) {
+        if (!copy_live)
+            return;
+        const uint32_t sbase = lds_base + copy_buf * Cfg::STAGE_BYTES;
+        if (q < APW) {
+            if constexpr (Cfg::VEC_A == 8) {
+                const int j = q * NW + wave;
+                const int c = a_c_of(j);
+                const bool ok = (8 * c + 8 <= copy_kleft) && (A_RPI * j + a_r) < rows_left;
+                const uint32_t voff = (uint32_t)((a_r * lda + 8 * c) * 2);
+                dma16(rsA, sbase + j * 1024, ok ? voff : kOOB, (uint32_t)(A_RPI * j * lda * 2));
             }
-        }
-        if constexpr (Cfg::VEC_B == 8) {
-            const i32x4 rsB = make_rsrc4(args.B + k0 * ldb + n0);
-#pragma unroll
-            for (int i = 0; i < BPW; ++i) {
-                const int j = i * NW + wave;
+        } else {
+            if constexpr (Cfg::VEC_B == 8) {
+                const int j = (q - APW) * NW + wave;
                 const int c = b_c_of(j);
-                const bool ok = (B_RPI * j + b_r) < k_left && 8 * c + 8 <= cols_left;
+                const bool ok = (B_RPI * j + b_r) < copy_kleft && 8 * c + 8 <= cols_left;
                 const uint32_t voff = (uint32_t)((b_r * ldb + 8 * c) * 2);
                 dma16(rsB, sbase + Cfg::A_BYTES + j * 1024, ok ? voff : kOOB,
                       (uint32_t)(B_RPI * j * ldb * 2));
             }
         }
     };
+    constexpr int NCOPY = APW + BPW;
 
     // Register fill: operands without 16-byte alignment, and the vectors that
-    // straddle the end of a row (the DMA wrote zeros there).  Runs after all
-    // of this thread's copies for the tile have landed.
+    // straddle the end of a row (the copies wrote zeros there).  Runs after
+    // this thread's copies for the tile have landed.
     auto fill = [&](int64_t kt, int buf) __attribute__((always_inline)) {
         const int64_t k0 = kt * BK;
         const int64_t k_left = K - k0;
         lds_u8 *const sbase = lds + buf * Cfg::STAGE_BYTES;
         const bool a_all = Cfg::VEC_A != 8;
         if (a_all || (k_left < BK && (k_left & 7) != 0)) {
-            const __amdgpu_buffer_rsrc_t rsA = make_rsrc(args.A + m0 * lda + k0);
-            const int64_t left = k_left - 8 * a_c;
-            const int nv = left >= 8 ? 8 : (left <= 0 ? 0 : (int)left);
-            if (a_all || (nv > 0 && nv < 8)) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.A + m0 * lda + k0);
 #pragma unroll
-                for (int i = 0; i < APW; ++i) {
-                    const int j = i * NW + wave;
-                    const int r = A_RPI * j + a_r;
-                    const int nvr = r < rows_left ? nv : 0;
-                    const uint32_t off = (uint32_t)((r * lda + 8 * a_c) * 2);
-                    const u32x4 v = (nvr >= 8) ? load8_full<1>(rsA, off) : load8_partial(rsA, off, nvr);
+            for (int i = 0; i < APW; ++i) {
+                const int j = i * NW + wave;
+                const int c = a_c_of(j);
+                const int r = A_RPI * j + a_r;
+                const int64_t left = k_left - 8 * c;
+                const int nv = r >= rows_left ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : (int)left));
+                if (a_all || (nv > 0 && nv < 8)) {
+                    const uint32_t off = (uint32_t)((r * lda + 8 * c) * 2);
+                    const u32x4 v = (nv >= 8) ? load8_full<1>(rs, off) : load8_partial(rs, off, nv);
                     *(lds_u32x4 *)(sbase + j * 1024 + lane * 16) = v;
                 }
             }
         }
         const bool b_all = Cfg::VEC_B != 8;
         if (b_all || (cols_left < BN && (cols_left & 7) != 0)) {
-            const __amdgpu_buffer_rsrc_t rsB = make_rsrc(args.B + k0 * ldb + n0);
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.B + k0 * ldb + n0);
 #pragma unroll
             for (int i = 0; i < BPW; ++i) {
                 const int j = i * NW + wave;
@@ -630,7 +672,7 @@ gemm_pipe(GemmArgs args)
                 const int nv = k < k_left ? (left >= 8 ? 8 : (left <= 0 ? 0 : (int)left)) : 0;
                 if (b_all || (nv > 0 && nv < 8)) {
                     const uint32_t off = (uint32_t)((k * ldb + 8 * c) * 2);
-                    const u32x4 v = (nv >= 8) ? load8_full<1>(rsB, off) : load8_partial(rsB, off, nv);
+                    const u32x4 v = (nv >= 8) ? load8_full<1>(rs, off) : load8_partial(rs, off, nv);
                     *(lds_u32x4 *)(sbase + Cfg::A_BYTES + j * 1024 + lane * 16) = v;
                 }
             }
@@ -648,33 +690,38 @@ gemm_pipe(GemmArgs args)
     // logical chunk 2*ks + lane/32.
     const int a_row = wm * Cfg::WTM + (lane & 31);
     const uint32_t a_rd_base = a_row * A_ROWB;
-    const int a_sw = a_row & 7;
-    // B, operand f of k-step ks, half h: group g = lane/16 and index q = lane%16
+    const int a_sw = swz_a(a_row);
+    // B, operand f of k-step ks, half h: group g = lane/16, index q = lane%16
     // address row 16*ks + 8*(g/2) + 4*h + q/4, column wn*WTN + 32*f + 16*(g%2) + 4*(q%4).
     const int g = lane >> 4, q = lane & 15;
-    const int b_row_l = 8 * (g >> 1) + (q >> 2);          // + 16*ks + 4*h
-    const int b_sw = 2 * (b_row_l & 3);                    // (16ks + 4h) keeps row & 3
+    const int b_row_l = 8 * (g >> 1) + (q >> 2);                    // + 16*ks + 4*h
+    const int b_sw = swz_b(b_row_l);                                 // 16*ks + 4*h leave it unchanged
     const int b_col_l = wn * Cfg::WTN + 16 * (g & 1) + 4 * (q & 3);  // + 32*f
 
     half8 ra[2][FM], rb[2][FN];
-    auto read_ops = [&](int buf, int ks, int set) __attribute__((always_inline)) {
+    auto read_a = [&](int buf, int ks, int set, int f) __attribute__((always_inline)) {
         const lds_u8 *const sbase = lds + buf * Cfg::STAGE_BYTES;
+        const uint32_t off = a_rd_base + f * 32 * A_ROWB + (((2 * ks + (lane >> 5)) ^ a_sw) * 16);
+        ra[set][f] = __builtin_bit_cast(half8, *(const lds_u32x4 *)(sbase + off));
+    };
+    auto read_b = [&](int buf, int ks, int set, int f) __attribute__((always_inline)) {
+        const lds_u8 *const sbase = lds + buf * Cfg::STAGE_BYTES;
+        const int col = b_col_l + 32 * f;
+        const int cpos = (((col >> 3) ^ b_sw) * 16) + (col & 7) * 2;
+        const lds_u8 *p0 = sbase + Cfg::A_BYTES + (16 * ks + b_row_l) * B_ROWB + cpos;
+        const fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) fp16x4 *)p0);
+        const fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (__attribute__((address_space(3))) fp16x4 *)(p0 + 4 * B_ROWB));
+        rb[set][f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    // reads for one group: A operand f (if f < FM) and the B operands
+    // assigned to that group (FN spread over FM groups)
+    auto read_group = [&](int buf, int ks, int set, int grp) __attribute__((always_inline)) {
+        read_a(buf, ks, set, grp);
 #pragma unroll
-        for (int f = 0; f < FM; ++f) {
-            const uint32_t off = a_rd_base + f * 32 * A_ROWB + (((2 * ks + (lane >> 5)) ^ a_sw) * 16);
-            ra[set][f] = __builtin_bit_cast(half8, *(const lds_u32x4 *)(sbase + off));
-        }
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-            fp16x4 lo, hi;
-            const int col = b_col_l + 32 * f;
-            const int cpos = (((col >> 3) ^ b_sw) * 16) + (col & 7) * 2;
-            const lds_u8 *p0 = sbase + Cfg::A_BYTES + (16 * ks + b_row_l) * B_ROWB + cpos;
-            lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) fp16x4 *)p0);
-            hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-                (__attribute__((address_space(3))) fp16x4 *)(p0 + 4 * B_ROWB));
-            rb[set][f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+        for (int f = 0; f < FN; ++f)
+            if (f % FM == grp)
+                read_b(buf, ks, set, f);
     };
 
     floatx16 acc[FM][FN];
@@ -684,29 +731,29 @@ gemm_pipe(GemmArgs args)
         for (int j = 0; j < FN; ++j)
             acc[i][j] = floatx16{0};
 
-    auto mfmas = [&](int set) __attribute__((always_inline)) {
+    auto mfma_group = [&](int set, int i) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[set][i], rb[set][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[set][i], rb[set][j], acc[i][j], 0, 0, 0);
     };
 
     // Make tile t (in buffer buf) visible to the workgroup: this thread's
-    // copies of tile t have landed (later tiles may still be in flight),
-    // registers fill what the copies could not, then the barrier.
+    // copies of tile t have landed (`newer` later tiles may still be in
+    // flight), registers fill what the copies could not, then the barrier.
     auto publish = [&](int64_t t, int buf, int64_t num_k) __attribute__((always_inline)) {
-        const int64_t newer = num_k - 1 - t;  // tiles issued after t
-        const int pending = (int)(newer < (S - 2) ? newer : (S - 2));
+        const int64_t newer_all = num_k - 1 - t;
+        const int newer = (int)(newer_all < (S - 2) ? newer_all : (S - 2));
         if (needs_fill(t)) {
             wait_vmcnt<0>();
             fill(t, buf);
-        } else if (pending <= 0) {
+        } else if (newer <= 0) {
             wait_vmcnt<0>();
-        } else if (pending == 1) {
+        } else if (newer == 1) {
             wait_vmcnt<NL>();
+        } else if (newer == 2) {
+            wait_vmcnt<(S > 3 ? 2 : 1) * NL>();
         } else {
-            wait_vmcnt<2 * NL>();
+            wait_vmcnt<(S > 4 ? 3 : 1) * NL>();
         }
         __syncthreads();
     };
@@ -714,37 +761,89 @@ gemm_pipe(GemmArgs args)
     const int64_t num_k = (K + BK - 1) / BK;
     if (num_k > 0) {
 #pragma unroll
-        for (int t = 0; t < S - 1; ++t)
-            if (t < num_k)
-                issue(t, t);
+        for (int t = 0; t < S - 1; ++t) {
+            begin_copies(t, t);
+#pragma unroll
+            for (int c = 0; c < NCOPY; ++c)
+                copy_one(c);
+        }
         publish(0, 0, num_k);
-        read_ops(0, 0, 0);
+#pragma unroll
+        for (int grp = 0; grp < FM; ++grp)
+            read_group(0, 0, 0, grp);
     }
     int buf = 0;
     for (int64_t kt = 0; kt < num_k; ++kt) {
-        if (kt + S - 1 < num_k)
-            issue(kt + S - 1, (int)((kt + S - 1) % S));
+        const int nbuf = (buf + 1 == S) ? 0 : buf + 1;
+        begin_copies(kt + S - 1, (int)((kt + S - 1) % S));
+        int copies_done = 0;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) {
-                read_ops(buf, ks + 1, (ks + 1) & 1);
-            } else if (kt + 1 < num_k) {
-                const int nb = (buf + 1 == S) ? 0 : buf + 1;
-                publish(kt + 1, nb, num_k);
-                read_ops(nb, 0, 0);
+            const int set = ks & 1;
+            const bool last = ks + 1 == KS;
+            // All operand reads for the next k-step go out first, a whole
+            // k-step (16 MFMAs per wave) ahead of their use; the scheduling
+            // barriers keep the compiler from sinking them next to their uses.
+            if (last && kt + 1 < num_k)
+                publish(kt + 1, nbuf, num_k);
+#pragma unroll
+            for (int grp = 0; grp < FM; ++grp) {
+                if (!last)
+                    read_group(buf, ks + 1, set ^ 1, grp);
+                else if (kt + 1 < num_k)
+                    read_group(nbuf, 0, set ^ 1, grp);
             }
-            mfmas(ks & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int grp = 0; grp < FM; ++grp) {
+                mfma_group(set, grp);
+                const int gi = ks * FM + grp;
+                if (gi < Cfg::COPY_GROUPS) {
+                    const int upto = ((gi + 1) * NCOPY + Cfg::COPY_GROUPS - 1) / Cfg::COPY_GROUPS;
+#pragma unroll
+                    for (int c = 0; c < NCOPY; ++c)
+                        if (c >= copies_done && c < upto)
+                            copy_one(c);
+                    copies_done = upto;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        buf = (buf + 1 == S) ? 0 : buf + 1;
+        buf = nbuf;
     }
 
+    // ---- epilogue: C = alpha*acc + beta*C through buffer stores whose
+    // out-of-range offsets the hardware drops (and loads read as zero).
+    const int64_t wrow0 = m0 + wm * Cfg::WTM;
+    const int64_t wcol0 = n0 + wn * Cfg::WTN;
+    const int64_t wrows = args.M - wrow0;
+    const int64_t wcols = args.N - wcol0;
+    if (wrows > 0 && wcols > 0) {
+        const __amdgpu_buffer_rsrc_t rsC = make_rsrc(args.C + wrow0 * args.ldc + wcol0);
+        const int ldc = (int)args.ldc;
+        const float alpha = args.alpha, beta = args.beta;
+        const int cl = lane & 31;
+        const int rl = 4 * (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            store_tile32(acc[i][j], args.C, args.ldc, M, N,
-                         m0 + wm * Cfg::WTM + i * 32, n0 + wn * Cfg::WTN + j * 32,
-                         args.alpha, args.beta, lane);
+            for (int j = 0; j < FN; ++j) {
+                const int c = 32 * j + cl;
+                const bool c_ok = c < wcols;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = 32 * i + 8 * (v >> 2) + rl + (v & 3);
+                    const uint32_t off = (c_ok && r < wrows) ? (uint32_t)((r * ldc + c) * 4) : kOOB;
+                    float val = alpha * acc[i][j][v];
+                    if (beta != 0.0f)
+                        val = __builtin_fmaf(beta,
+                                             __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsC, off, 0, 0)),
+                                             val);
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off, 0, 0);
+                }
+            }
+        }
+    }
 }
 
 }  // namespace mpg

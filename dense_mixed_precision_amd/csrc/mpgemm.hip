@@ -142,11 +142,11 @@ constexpr Entry scale_entry(int id)
         tiled_entry<TileCfg<BM, BN, BK, WM, WN, 8, 1>>(base + 2),      \
         tiled_entry<TileCfg<BM, BN, BK, WM, WN, 1, 1>>(base + 3)
 
-#define MPG_PIPE_ENTRIES(base, BM, BN, WM, WN, S)                      \
-    pipe_entry<PipeCfg<BM, BN, WM, WN, S, 8, 8>>(base + 0),            \
-        pipe_entry<PipeCfg<BM, BN, WM, WN, S, 1, 8>>(base + 1),        \
-        pipe_entry<PipeCfg<BM, BN, WM, WN, S, 8, 1>>(base + 2),        \
-        pipe_entry<PipeCfg<BM, BN, WM, WN, S, 1, 1>>(base + 3)
+#define MPG_PIPE_ENTRIES(base, BM, BN, BK, WM, WN, S)                  \
+    pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 8, 8>>(base + 0),        \
+        pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 1, 8>>(base + 1),    \
+        pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 8, 1>>(base + 2),    \
+        pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 1, 1>>(base + 3)
 
 const Entry kTable[] = {
     MPG_TILE_ENTRIES(0, 256, 256, 64, 2, 2),  // 0..3   register-staged copies
@@ -154,21 +154,41 @@ const Entry kTable[] = {
     MPG_TILE_ENTRIES(8, 64, 64, 64, 2, 2),    // 8..11
     direct_entry(12),                         // 12     any stride / size
     scale_entry(13),                          // 13     alpha == 0 or K == 0
-    MPG_PIPE_ENTRIES(14, 256, 256, 2, 2, 2),  // 14..17 large products
-    MPG_PIPE_ENTRIES(18, 128, 128, 2, 2, 3),  // 18..21 2048-class and tall-skinny
-    MPG_PIPE_ENTRIES(22, 64, 64, 2, 2, 2),    // 22..25 small or ragged products
+    MPG_PIPE_ENTRIES(14, 256, 256, 32, 2, 2, 4),  // 14..17 large products
+    MPG_PIPE_ENTRIES(18, 128, 128, 64, 2, 2, 3),  // 18..21 2048-class and tall-skinny
+    MPG_PIPE_ENTRIES(22, 64, 64, 64, 2, 2, 2),    // 22..25 small or ragged products
+    // alternative shapes (16-byte aligned operands only), for tile sweeps
+    pipe_entry<PipeCfg<256, 256, 64, 2, 2, 2, 8, 8>>(26),
+    pipe_entry<PipeCfg<256, 256, 32, 2, 2, 5, 8, 8>>(27),
+    pipe_entry<PipeCfg<256, 128, 64, 2, 2, 3, 8, 8>>(28),
+    pipe_entry<PipeCfg<128, 128, 32, 2, 2, 4, 8, 8>>(29),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 2, 2, 8, 8>>(30),
+    pipe_entry<PipeCfg<64, 64, 32, 2, 2, 4, 8, 8>>(31),
+    // eight waves per workgroup (two per SIMD)
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8>>(32),
+    pipe_entry<PipeCfg<256, 256, 32, 2, 4, 4, 8, 8>>(33),
+    pipe_entry<PipeCfg<256, 256, 32, 2, 4, 3, 8, 8>>(34),
+    pipe_entry<PipeCfg<256, 128, 64, 4, 2, 3, 8, 8>>(35),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, 8, 8>>(36),
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
 constexpr int kDirectId = 12;
 constexpr int kScaleId = 13;
 
-// Tile groups the factory chooses from, largest first: (first id, BM, BN).
-// Each group holds the four (vec_a, vec_b) variants in the order 88, 18, 81, 11.
+// Tile groups the factory chooses from, largest first.  ids[] holds the
+// table entry for each (vec_a, vec_b) pair in the order 88, 18, 81, 11; the
+// eight-wave shapes exist for 16-byte aligned operands only, and the other
+// pairs fall back to the four-wave form of the same tile.
 struct TileGroup {
-    int first;
     int bm, bn;
+    int ids[4];
 };
-constexpr TileGroup kGroups[] = {{14, 256, 256}, {18, 128, 128}, {22, 64, 64}};
+constexpr TileGroup kGroups[] = {
+    {256, 256, {32, 15, 16, 17}},
+    {128, 128, {36, 19, 20, 21}},
+    {64, 64, {22, 23, 24, 25}},
+};
+constexpr int kNumGroups = sizeof(kGroups) / sizeof(kGroups[0]);
 
 // ---------------------------------------------------------------------------
 // Validation and selection (pure host code, no HIP calls)
@@ -234,6 +254,11 @@ bool entry_fits(const Entry &e, const Problem &p)
     const int64_t b_span = ((int64_t)c.bk * p.ldb + c.bn) * 2;
     if (a_span >= (int64_t)0x7FFFFFF0 || b_span >= (int64_t)0x7FFFFFF0)
         return false;
+    // The pipelined kernel's epilogue addresses a wave's C tile with 32-bit
+    // buffer offsets as well.
+    const int64_t c_span = ((int64_t)c.bm * p.ldc + c.bn) * 4;
+    if (c.kind == MPGEMM_KIND_PIPE && c_span >= (int64_t)0x7FFFFFF0)
+        return false;
     const int64_t tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
     if (tiles > 0x7FFFFFFF)
         return false;
@@ -265,6 +290,7 @@ int select(const Problem &p)
         return kScaleId;
     const int va = vec_for(p.A, p.lda) == 8 ? 0 : 1;
     const int vb = vec_for(p.B, p.ldb) == 8 ? 0 : 2;
+    const int v = va + vb;
     // Enough 256x256 tiles for every CU: large products.
     // Else 128x128 if that makes at least half a wave of workgroups.
     // Else 64x64.
@@ -275,8 +301,8 @@ int select(const Problem &p)
         group = 1;
     else
         group = 2;
-    for (int g = group; g < 3; ++g) {
-        const int id = kGroups[g].first + va + vb;
+    for (int g = group; g < kNumGroups; ++g) {
+        const int id = kGroups[g].ids[v];
         if (entry_fits(kTable[id], p))
             return id;
     }
