@@ -47,7 +47,45 @@ def parse():
     p.add_argument("--no-others", action="store_true", help="time only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--calibrate-copy-mb", type=int, default=0,
+                   help="after timing, run one plain device copy of this many MiB (a known-size "
+                        "kernel for scaling the HBM byte counters of a rocprofv3 --pmc run)")
     return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources; counter readings are only reused while it matches."""
+    import hashlib
+
+    h = hashlib.sha256()
+    base = os.path.join(ROOT, "dense_mixed_precision_amd", "csrc")
+    for name in sorted(os.listdir(base)):
+        with open(os.path.join(base, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel_ms: float):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary for this
+    workload (FETCH_SIZE and WRITE_SIZE, each scaled by the reading of a plain
+    copy of known size), or None if there is none or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        read_b = float(vals["hbm_read_bytes_per_launch"])
+        write_b = float(vals["hbm_write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+    return {"bytes_per_launch": read_b + write_b, "read_bytes": read_b, "write_bytes": write_b,
+            "GBps": round((read_b + write_b) / (kernel_ms * 1e-3) / 1e9, 1), "source": os.path.relpath(path, ROOT)}
 
 
 def time_workload(w, steps, warmup, torch, mp):
@@ -112,17 +150,28 @@ def cpu_baseline(w, res, seconds):
         ref, absdot = oracle.gemm(a, Bb, c, w.alpha, w.beta)
         return time.perf_counter() - t, ref, absdot
 
-    probe_rows = max(1, min(w.M, 4))
-    dt, _, _ = run_rows(0, probe_rows)
-    per_row = max(dt / probe_rows, 1e-6)
-    rows = int(max(1, min(w.M, seconds / per_row)))
-    r0 = (w.M - rows) // 2
-    dt, ref, absdot = run_rows(r0, r0 + rows)
+    # Whole rows, in blocks sized from the previous block's rate, until about
+    # `seconds` of oracle time or the whole matrix.
+    r0 = 0
+    refs, absd = [], []
+    dt = 0.0
+    block = max(1, min(w.M, 8))
+    while r0 < w.M and dt < seconds:
+        t_block, ref_b, abs_b = run_rows(r0, min(w.M, r0 + block))
+        refs.append(ref_b)
+        absd.append(abs_b)
+        dt += t_block
+        r0 = min(w.M, r0 + block)
+        per_row = t_block / ref_b.shape[0]
+        block = int(max(1, min(w.M - r0, (seconds - dt) / max(per_row, 1e-9))))
+    rows = r0
+    ref, absdot = np.concatenate(refs), np.concatenate(absd)
+    r0 = 0
     flop = 2.0 * rows * w.N * w.K
     out = {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
            "kind": "oracle",
-           "sample": f"rows {r0}..{r0 + rows - 1} of {w.M} ({rows} rows x {w.N} cols x K={w.K}) "
-                     f"of {w.name}; {dt:.1f} s wall",
+           "sample": f"rows 0..{rows - 1} of {w.M} ({rows} rows x {w.N} cols x K={w.K}) "
+                     f"of {w.name}; {dt:.1f} s of oracle time",
            "seconds": round(dt, 2)}
     if got is not None:
         ok = oracle.tolerance_ok(got[r0:r0 + rows], ref, absdot)
@@ -174,6 +223,7 @@ def main():
         "roofline": roofline_entry(head, res["kernel_ms"]),
     }
     line["roofline"]["kernel_ms"] = round(res["kernel_ms"], 5)
+    line["roofline"]["traffic"] = measured_traffic(head.name, res["kernel_ms"])
     others = {}
     if not args.no_others:
         for name, w in WORKLOADS.items():
@@ -193,6 +243,14 @@ def main():
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(head, res, args.cpu_seconds)
+    if args.calibrate_copy_mb > 0:
+        n = args.calibrate_copy_mb * 1024 * 1024 // 4
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = n * 4
     print(json.dumps(line), flush=True)
 
 

@@ -44,6 +44,9 @@ constexpr int32_t kNumRecords = 0x7FFFFFFF;
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr int32_t kRsrcWord3 = 0x00020000;
 
+// Cache-policy bits of a buffer store: non-temporal (streaming) write.
+constexpr int32_t kStoreNT = 2;
+
 // MI355X dispatches consecutive workgroup ids round-robin over its 8 XCDs,
 // each with a private L2.
 constexpr int kNumXcd = 8;
@@ -814,6 +817,9 @@ gemm_pipe(GemmArgs args)
 
     // ---- epilogue: C = alpha*acc + beta*C through buffer stores whose
     // out-of-range offsets the hardware drops (and loads read as zero).
+    // The stores are non-temporal: C is written once and should not evict
+    // the A and B panels other workgroups are still streaming through the
+    // caches (about 5% at 8192^3).
     const int64_t wrow0 = m0 + wm * Cfg::WTM;
     const int64_t wcol0 = n0 + wn * Cfg::WTN;
     const int64_t wrows = args.M - wrow0;
@@ -839,7 +845,7 @@ gemm_pipe(GemmArgs args)
                         val = __builtin_fmaf(beta,
                                              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsC, off, 0, 0)),
                                              val);
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off, 0, kStoreNT);
                 }
             }
         }
