@@ -470,10 +470,12 @@ probe_mfma(float *out, int shape)
 //
 // Schedule (per wave, per K tile of BK): each k-step first issues every
 // operand read of the next k-step (into the other register set), then runs
-// its MFMAs in groups of FN, each group followed by its share of the copies
-// for the tile STAGES-1 ahead.  The copies are all issued before the
-// end-of-tile barrier, which sits before the last k-step's MFMAs so that
-// the reads of the next tile's first k-step overlap them.
+// its MFMAs in groups of FN.  The barrier that publishes tile t+1 sits
+// before the last k-step of tile t, so the reads of tile t+1's first k-step
+// overlap that k-step's MFMAs.  Past that barrier no wave reads tile t's
+// buffer again, and the copies of tile t+STAGES into it start at once,
+// spread over the following MFMA groups: the copy engine is never left
+// without work while a buffer is free.
 typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -502,17 +504,20 @@ struct PipeCfg {
     static constexpr int APW = BM / A_RPI / NW;           // A copies per wave per tile
     static constexpr int BPW = BK / B_RPI / NW;           // B copies per wave per tile
     static constexpr int NL = (VEC_A == 8 ? APW : 0) + (VEC_B == 8 ? BPW : 0);  // vmcnt per tile
-    // MFMA groups (one per A row-block, FM per k-step) over which a tile's
-    // copies are spread: with two stages they must land within the same
-    // tile, so they all go out after the first group; deeper rings spread
-    // them over every group before the barrier.
-    static constexpr int COPY_GROUPS = STAGES == 2 ? 1 : (KS - 1) * FM;
+    static constexpr int NCOPY = APW + BPW;                // copy instructions per wave per tile
+    // MFMA groups (FM per k-step) over which a tile's copies are spread,
+    // counted from the barrier that frees their buffer.  With two stages the
+    // copies must land one tile later, so they go out one per group, at
+    // about the rate the memory system serves them, leaving the rest of the
+    // tile as slack; deeper rings spread them over a whole tile.
+    static constexpr int COPY_WINDOW =
+        STAGES == 2 ? (NCOPY < KS * FM ? (NCOPY > 0 ? NCOPY : 1) : KS * FM) : KS * FM;
     static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
     static_assert(BN >= 64 && 64 % B_CH == 0, "B rows must hold 8..64 chunks");
     static_assert((BM / A_RPI) % NW == 0 && (BK / B_RPI) % NW == 0, "copies must split evenly over waves");
     static_assert(STAGES >= 2 && STAGES <= 5, "2..5 LDS stages");
-    static_assert(NL * (STAGES - 2) < 64, "vmcnt is 6 bits");
+    static_assert(NL * (STAGES - 1) < 64, "vmcnt is 6 bits");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 };
 
@@ -637,7 +642,7 @@ gemm_pipe(GemmArgs args)
             }
         }
     };
-    constexpr int NCOPY = APW + BPW;
+    constexpr int NCOPY = Cfg::NCOPY;
 
     // Register fill: operands without 16-byte alignment, and the vectors that
     // straddle the end of a row (the copies wrote zeros there).  Runs after
@@ -741,11 +746,10 @@ gemm_pipe(GemmArgs args)
     };
 
     // Make tile t (in buffer buf) visible to the workgroup: this thread's
-    // copies of tile t have landed (`newer` later tiles may still be in
-    // flight), registers fill what the copies could not, then the barrier.
-    auto publish = [&](int64_t t, int buf, int64_t num_k) __attribute__((always_inline)) {
-        const int64_t newer_all = num_k - 1 - t;
-        const int newer = (int)(newer_all < (S - 2) ? newer_all : (S - 2));
+    // copies of tile t have landed (the `newer` whole tiles issued after it
+    // may still be in flight), registers fill what the copies could not,
+    // then the barrier.
+    auto publish = [&](int64_t t, int buf, int newer) __attribute__((always_inline)) {
         if (needs_fill(t)) {
             wait_vmcnt<0>();
             fill(t, buf);
@@ -754,23 +758,34 @@ gemm_pipe(GemmArgs args)
         } else if (newer == 1) {
             wait_vmcnt<NL>();
         } else if (newer == 2) {
-            wait_vmcnt<(S > 3 ? 2 : 1) * NL>();
+            wait_vmcnt<(S > 2 ? 2 : 1) * NL>();
+        } else if (newer == 3) {
+            wait_vmcnt<(S > 3 ? 3 : 1) * NL>();
         } else {
-            wait_vmcnt<(S > 4 ? 3 : 1) * NL>();
+            wait_vmcnt<(S > 4 ? 4 : 1) * NL>();
         }
         __syncthreads();
+    };
+    // the copies of the current copy tile that belong to window position p
+    auto copy_slice = [&](int p) __attribute__((always_inline)) {
+        constexpr int W = Cfg::COPY_WINDOW;
+#pragma unroll
+        for (int c = 0; c < NCOPY; ++c)
+            if (c >= (p * NCOPY + W - 1) / W && c < ((p + 1) * NCOPY + W - 1) / W)
+                copy_one(c);
     };
 
     const int64_t num_k = (K + BK - 1) / BK;
     if (num_k > 0) {
+        // the whole ring: tiles 0 .. S-1
 #pragma unroll
-        for (int t = 0; t < S - 1; ++t) {
+        for (int t = 0; t < S; ++t) {
             begin_copies(t, t);
 #pragma unroll
             for (int c = 0; c < NCOPY; ++c)
                 copy_one(c);
         }
-        publish(0, 0, num_k);
+        publish(0, 0, (int)(num_k - 1 < S - 1 ? num_k - 1 : S - 1));
 #pragma unroll
         for (int grp = 0; grp < FM; ++grp)
             read_group(0, 0, 0, grp);
@@ -778,17 +793,20 @@ gemm_pipe(GemmArgs args)
     int buf = 0;
     for (int64_t kt = 0; kt < num_k; ++kt) {
         const int nbuf = (buf + 1 == S) ? 0 : buf + 1;
-        begin_copies(kt + S - 1, (int)((kt + S - 1) % S));
-        int copies_done = 0;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int set = ks & 1;
             const bool last = ks + 1 == KS;
+            if (last && kt + 1 < num_k) {
+                // tiles kt+2 .. kt+S-1 may still be in flight
+                const int64_t newer = num_k - 2 - kt;
+                publish(kt + 1, nbuf, (int)(newer < S - 2 ? newer : S - 2));
+            }
+            if (last)
+                begin_copies(kt + S, buf);
             // All operand reads for the next k-step go out first, a whole
             // k-step (16 MFMAs per wave) ahead of their use; the scheduling
             // barriers keep the compiler from sinking them next to their uses.
-            if (last && kt + 1 < num_k)
-                publish(kt + 1, nbuf, num_k);
 #pragma unroll
             for (int grp = 0; grp < FM; ++grp) {
                 if (!last)
@@ -800,15 +818,13 @@ gemm_pipe(GemmArgs args)
 #pragma unroll
             for (int grp = 0; grp < FM; ++grp) {
                 mfma_group(set, grp);
-                const int gi = ks * FM + grp;
-                if (gi < Cfg::COPY_GROUPS) {
-                    const int upto = ((gi + 1) * NCOPY + Cfg::COPY_GROUPS - 1) / Cfg::COPY_GROUPS;
-#pragma unroll
-                    for (int c = 0; c < NCOPY; ++c)
-                        if (c >= copies_done && c < upto)
-                            copy_one(c);
-                    copies_done = upto;
-                }
+                // The last k-step opens the window of tile kt+S; the others
+                // continue that of tile kt+S-1, which the ring fill issued
+                // whole when kt == 0.
+                if (last)
+                    copy_slice(grp);
+                else if (kt > 0)
+                    copy_slice(FM + ks * FM + grp);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
