@@ -445,7 +445,7 @@ probe_mfma(float *out, int shape)
 // ---------------------------------------------------------------------------
 // Pipelined kernel: global -> LDS with buffer_load ... lds, B read transposed
 // ---------------------------------------------------------------------------
-// LDS layout of one stage (BK = 32 or 64).  gfx950's LDS has 64 banks of
+// LDS layout of one stage (BK = 32, 64 or 128).  gfx950's LDS has 64 banks of
 // 4 bytes: a ds_read_b128 serves 16 lanes per cycle and a ds_read_b64
 // (including the transposing read) 32 lanes, so each such group must touch
 // 256 distinct bytes of bank space to run at full rate.
@@ -454,7 +454,8 @@ probe_mfma(float *out, int shape)
 //      16 consecutive rows at one logical chunk; with 128-byte rows two rows
 //      share a 256-byte bank window, so swz_a(r) = (r >> 1) & 7 gives the 8
 //      rows of each parity 8 distinct chunks; with 64-byte rows four rows
-//      share a window and swz_a(r) = (r >> 2) & 3.
+//      share a window and swz_a(r) = (r >> 2) & 3; a 256-byte row fills the
+//      window by itself and swz_a(r) = r & 15.
 //   B: BK rows x BN, N-contiguous as in memory.  Chunk c of row k sits at
 //      c ^ swz_b(k).  One 32-lane group of the transposing read touches 4
 //      consecutive rows x 4 consecutive chunks; swz_b(k) = 4*(k & 3) moves
@@ -512,7 +513,7 @@ struct PipeCfg {
     // tile as slack; deeper rings spread them over a whole tile.
     static constexpr int COPY_WINDOW =
         STAGES == 2 ? (NCOPY < KS * FM ? (NCOPY > 0 ? NCOPY : 1) : KS * FM) : KS * FM;
-    static_assert(BK == 32 || BK == 64, "BK must be 32 or 64");
+    static_assert(BK == 32 || BK == 64 || BK == 128, "BK must be 32, 64 or 128");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
     static_assert(BN >= 64 && 64 % B_CH == 0, "B rows must hold 8..64 chunks");
     static_assert((BM / A_RPI) % NW == 0 && (BK / B_RPI) % NW == 0, "copies must split evenly over waves");
@@ -589,7 +590,7 @@ gemm_pipe(GemmArgs args)
     // A copy i of this wave covers rows A_RPI*j .. +A_RPI-1, j = i*NW + wave;
     // lane -> row A_RPI*j + lane/A_CH, physical chunk lane%A_CH.
     auto swz_a = [](int r) __attribute__((always_inline)) {
-        return A_CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+        return A_CH == 16 ? (r & 15) : A_CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
     };
     auto swz_b = [](int k) __attribute__((always_inline)) {
         return B_CH >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);

@@ -170,6 +170,10 @@ const Entry kTable[] = {
     pipe_entry<PipeCfg<256, 256, 32, 2, 4, 3, 8, 8>>(34),
     pipe_entry<PipeCfg<256, 128, 64, 4, 2, 3, 8, 8>>(35),
     pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, 8, 8>>(36),
+    // K tiles of 128: half as many barriers per K for the narrower tiles
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8>>(37),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, 8, 8>>(38),
+    pipe_entry<PipeCfg<64, 64, 128, 2, 2, 3, 8, 8>>(39),
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
 constexpr int kDirectId = 12;
@@ -179,6 +183,7 @@ constexpr int kScaleId = 13;
 // table entry for each (vec_a, vec_b) pair in the order 88, 18, 81, 11; the
 // eight-wave shapes exist for 16-byte aligned operands only, and the other
 // pairs fall back to the four-wave form of the same tile.
+constexpr int kWideKId = 37;  // 128x128, K tile 128, eight waves
 struct TileGroup {
     int bm, bn;
     int ids[4];
@@ -301,6 +306,12 @@ int select(const Problem &p)
         group = 1;
     else
         group = 2;
+    // 128x128 tiles with both panels reused across tiles (B panels by at
+    // least four column tiles) take K steps of 128: half as many barriers.
+    // A tall-skinny product streams A once and keeps the deeper 64-wide ring.
+    if (group == 1 && v == 0 && cdiv(p.N, 128) >= 4 && cdiv(p.M, 128) >= 4 &&
+        entry_fits(kTable[kWideKId], p))
+        return kWideKId;
     for (int g = group; g < kNumGroups; ++g) {
         const int id = kGroups[g].ids[v];
         if (entry_fits(kTable[id], p))

@@ -127,9 +127,9 @@ def test_factory_choices_for_the_workloads():
     assert (c["kind_name"], c["bm"], c["bn"], c["vec_a"], c["vec_b"]) == ("pipe", 256, 256, 8, 8)
     assert c["grid"] == 32 * 32
     c = _pick(WORKLOADS["square2048"])
-    assert (c["bm"], c["bn"]) == (128, 128) and c["grid"] == 256
+    assert (c["bm"], c["bn"], c["bk"]) == (128, 128, 128) and c["grid"] == 256
     c = _pick(WORKLOADS["tallskinny32768x128x4096"])
-    assert c["kind_name"] == "pipe" and c["grid"] >= 256
+    assert c["kind_name"] == "pipe" and c["grid"] >= 256 and c["bk"] == 64
     c = _pick(WORKLOADS["ragged1000x800x617"])
     # lda = 617 is odd: A rows are only 2-byte aligned, so A takes the
     # element-wise path; B (ldb = 800) keeps 16-byte loads.
