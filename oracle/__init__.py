@@ -70,6 +70,10 @@ def _load():
                                         ctypes.c_double, ctypes.c_double,
                                         i64, vp, vp, vp, vp]
     lib.oracle_gemm_entries.restype = ctypes.c_int
+    lib.oracle_gemm_layout.argtypes = [ctypes.c_int, ctypes.c_int] + lib.oracle_gemm.argtypes
+    lib.oracle_gemm_layout.restype = ctypes.c_int
+    lib.oracle_gemm_layout_entries.argtypes = [ctypes.c_int, ctypes.c_int] + lib.oracle_gemm_entries.argtypes
+    lib.oracle_gemm_layout_entries.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -94,9 +98,10 @@ def _as_bits_2d(x, name):
         raise TypeError(f"{name} must be a 2-D float16 or uint16 (FP16 bits) array")
     if x.size == 0:
         return np.zeros(x.shape, dtype=np.uint16), max(x.shape[1], 1)
-    if x.strides[1] != 2 or x.strides[0] % 2:
+    # a dimension of extent 1 has no meaningful stride (numpy may report any)
+    if (x.shape[1] > 1 and x.strides[1] != 2) or (x.shape[0] > 1 and (x.strides[0] % 2 or x.strides[0] <= 0)):
         raise ValueError(f"{name} must be row-major with unit inner stride")
-    ld = max(x.strides[0] // 2, max(x.shape[1], 1))
+    ld = max(x.strides[0] // 2 if x.shape[0] > 1 else 0, max(x.shape[1], 1))
     return x, ld
 
 
@@ -108,9 +113,9 @@ def _as_c(C, M, N, beta):
     C = np.asarray(C)
     if C.dtype != np.float32 or C.ndim != 2 or C.shape != (M, N):
         raise TypeError("C must be a float32 array of shape (M, N)")
-    if C.strides[1] != 4 or C.strides[0] % 4:
+    if (N > 1 and C.strides[1] != 4) or (M > 1 and (C.strides[0] % 4 or C.strides[0] <= 0)):
         raise ValueError("C must be row-major with unit inner stride")
-    return C, max(C.strides[0] // 4, max(N, 1))
+    return C, max(C.strides[0] // 4 if M > 1 else 0, max(N, 1))
 
 
 def f16_to_f64(bits) -> np.ndarray:
@@ -121,42 +126,57 @@ def f16_to_f64(bits) -> np.ndarray:
     return out
 
 
+#: Storage orders of A and B (C is always row-major).
+ROW_MAJOR = 0
+COL_MAJOR = 1
+
+
+def _operands(A, B, layout_a, layout_b):
+    """Stored arrays and their leading dimensions -> (A, lda, B, ldb, M, N, K).
+
+    A is stored (M, K) when row-major and (K, M) when column-major; B is
+    stored (K, N) when row-major and (N, K) when column-major."""
+    if layout_a not in (ROW_MAJOR, COL_MAJOR) or layout_b not in (ROW_MAJOR, COL_MAJOR):
+        raise ValueError("layouts must be ROW_MAJOR (0) or COL_MAJOR (1)")
+    A, lda = _as_bits_2d(A, "A")
+    B, ldb = _as_bits_2d(B, "B")
+    M, K = A.shape if layout_a == ROW_MAJOR else A.shape[::-1]
+    K2, N = B.shape if layout_b == ROW_MAJOR else B.shape[::-1]
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    return A, lda, B, ldb, M, N, K
+
+
 def _check(rc):
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
 
 
-def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0):
+def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0,
+         layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR):
     """Full product.  Returns ``(ref, absdot)``, both float64 (M, N).
 
-    A: (M, K) FP16 bits, B: (K, N) FP16 bits, C: (M, N) float32 or None.
-    alpha and beta are rounded to float32 first, as the GPU entry point
-    receives them.
+    A: FP16 bits stored (M, K) (row-major) or (K, M) (``layout_a=COL_MAJOR``);
+    B: stored (K, N) or (N, K) (``layout_b=COL_MAJOR``); C: (M, N) float32
+    or None.  alpha and beta are rounded to float32 first, as the GPU entry
+    point receives them.
     """
-    A, lda = _as_bits_2d(A, "A")
-    B, ldb = _as_bits_2d(B, "B")
-    M, K = A.shape
-    K2, N = B.shape
-    if K2 != K:
-        raise ValueError("inner dimensions differ")
+    A, lda, B, ldb, M, N, K = _operands(A, B, layout_a, layout_b)
     alpha = float(np.float32(alpha))
     beta = float(np.float32(beta))
     C, ldc = _as_c(C, M, N, beta)
     ref = np.empty((M, N), dtype=np.float64)
     absdot = np.empty((M, N), dtype=np.float64)
-    _check(_load().oracle_gemm(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
-                               alpha, beta, _ptr(ref), _ptr(absdot)))
+    _check(_load().oracle_gemm_layout(layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B), ldb,
+                                      _ptr(C), ldc, alpha, beta, _ptr(ref), _ptr(absdot)))
     return ref, absdot
 
 
-def gemm_entries(A, B, C, alpha: float, beta: float, rows, cols):
-    """Selected entries (rows[t], cols[t]).  Returns ``(ref, absdot)`` 1-D."""
-    A, lda = _as_bits_2d(A, "A")
-    B, ldb = _as_bits_2d(B, "B")
-    M, K = A.shape
-    K2, N = B.shape
-    if K2 != K:
-        raise ValueError("inner dimensions differ")
+def gemm_entries(A, B, C, alpha: float, beta: float, rows, cols,
+                 layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR):
+    """Selected entries (rows[t], cols[t]).  Returns ``(ref, absdot)`` 1-D.
+    Operands as for :func:`gemm`."""
+    A, lda, B, ldb, M, N, K = _operands(A, B, layout_a, layout_b)
     alpha = float(np.float32(alpha))
     beta = float(np.float32(beta))
     C, ldc = _as_c(C, M, N, beta)
@@ -166,9 +186,9 @@ def gemm_entries(A, B, C, alpha: float, beta: float, rows, cols):
         raise ValueError("rows and cols must be 1-D and equal length")
     ref = np.empty(rows.shape, dtype=np.float64)
     absdot = np.empty(rows.shape, dtype=np.float64)
-    _check(_load().oracle_gemm_entries(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
-                                       alpha, beta, rows.size, _ptr(rows), _ptr(cols),
-                                       _ptr(ref), _ptr(absdot)))
+    _check(_load().oracle_gemm_layout_entries(layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B), ldb,
+                                              _ptr(C), ldc, alpha, beta, rows.size, _ptr(rows),
+                                              _ptr(cols), _ptr(ref), _ptr(absdot)))
     return ref, absdot
 
 

@@ -16,6 +16,10 @@
  *     (section "Compare like with like").
  *   - Row-major A (M x K, leading dimension lda), row-major B (K x N, ldb),
  *     row-major C (M x N, ldc), all leading dimensions counted in elements.
+ *     The *_layout entry points also take A and/or B stored column-major
+ *     (A[i][k] at A[k*lda + i], B[k][j] at B[j*ldb + k]), the layout of the
+ *     same page's "Independent gate" (A row-major, B column-major); only the
+ *     element addressing changes, the arithmetic is the same.
  *   - beta == 0 means C is not read at all (the output may hold NaN poison,
  *     "02_mixed_precision_gemm", Verification).
  *
@@ -67,13 +71,33 @@ void oracle_f16_to_f64_array(const uint16_t *h, int64_t n, double *out)
 }
 
 /*
+ * Element strides of the two operands: A[i][k] is A[i*a_i + k*a_k] and
+ * B[k][j] is B[k*b_k + j*b_j].
+ */
+typedef struct {
+    int64_t a_i, a_k, b_k, b_j;
+} strides_t;
+
+#define ORACLE_ROW_MAJOR 0
+#define ORACLE_COL_MAJOR 1
+
+static strides_t strides_for(int layout_a, int layout_b, int64_t lda, int64_t ldb)
+{
+    strides_t t;
+    t.a_i = layout_a == ORACLE_COL_MAJOR ? 1 : lda;
+    t.a_k = layout_a == ORACLE_COL_MAJOR ? lda : 1;
+    t.b_k = layout_b == ORACLE_COL_MAJOR ? 1 : ldb;
+    t.b_j = layout_b == ORACLE_COL_MAJOR ? ldb : 1;
+    return t;
+}
+
+/*
  * One output element: the dot product of row i of A with column j of B in
  * ascending k, then alpha*s + beta*c.  Also returns sum_k |a_ik * b_kj|, the
  * scale the acceptance rule is written against.
  */
 static void entry(int64_t i, int64_t j, int64_t K,
-                  const uint16_t *A, int64_t lda,
-                  const uint16_t *B, int64_t ldb,
+                  const uint16_t *A, const uint16_t *B, strides_t st,
                   const float *C, int64_t ldc,
                   double alpha, double beta,
                   double *ref, double *absdot)
@@ -81,8 +105,8 @@ static void entry(int64_t i, int64_t j, int64_t K,
     double s = 0.0;
     double s_abs = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        const double a = oracle_f16_to_f64(A[i * lda + k]);
-        const double b = oracle_f16_to_f64(B[k * ldb + j]);
+        const double a = oracle_f16_to_f64(A[i * st.a_i + k * st.a_k]);
+        const double b = oracle_f16_to_f64(B[k * st.b_k + j * st.b_j]);
         const double p = a * b; /* exact */
         s += p;
         s_abs += fabs(p);
@@ -100,15 +124,23 @@ static void entry(int64_t i, int64_t j, int64_t K,
 #define ORACLE_EBADDIM (-1)
 #define ORACLE_EBADLD (-2)
 #define ORACLE_ENULL (-3)
+#define ORACLE_EBADLAYOUT (-4)
 
-static int check_args(int64_t M, int64_t N, int64_t K,
+/* A stored row-major needs lda >= K, column-major lda >= M; B row-major
+ * needs ldb >= N, column-major ldb >= K; C (always row-major) ldc >= N. */
+static int check_args(int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
                       const uint16_t *A, int64_t lda,
                       const uint16_t *B, int64_t ldb,
                       const float *C, int64_t ldc, double beta)
 {
+    if ((layout_a != ORACLE_ROW_MAJOR && layout_a != ORACLE_COL_MAJOR) ||
+        (layout_b != ORACLE_ROW_MAJOR && layout_b != ORACLE_COL_MAJOR))
+        return ORACLE_EBADLAYOUT;
     if (M < 0 || N < 0 || K < 0)
         return ORACLE_EBADDIM;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    const int64_t a_row = layout_a == ORACLE_COL_MAJOR ? M : K;
+    const int64_t b_row = layout_b == ORACLE_COL_MAJOR ? K : N;
+    if (lda < (a_row > 1 ? a_row : 1) || ldb < (b_row > 1 ? b_row : 1) || ldc < (N > 1 ? N : 1))
         return ORACLE_EBADLD;
     if (M > 0 && N > 0 && K > 0 && (A == NULL || B == NULL))
         return ORACLE_ENULL;
@@ -118,9 +150,35 @@ static int check_args(int64_t M, int64_t N, int64_t K,
 }
 
 /*
- * Full product.  ref and absdot (absdot may be NULL) are M x N, row-major,
- * packed (leading dimension N), owned by the caller.
+ * Full product with the given storage orders of A and B.  ref and absdot
+ * (absdot may be NULL) are M x N, row-major, packed (leading dimension N),
+ * owned by the caller.
  */
+int oracle_gemm_layout(int layout_a, int layout_b,
+                       int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda,
+                       const uint16_t *B, int64_t ldb,
+                       const float *C, int64_t ldc,
+                       double alpha, double beta,
+                       double *ref, double *absdot)
+{
+    const int rc = check_args(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, beta);
+    if (rc != ORACLE_OK)
+        return rc;
+    if (M > 0 && N > 0 && ref == NULL)
+        return ORACLE_ENULL;
+    const strides_t st = strides_for(layout_a, layout_b, lda, ldb);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            entry(i, j, K, A, B, st, C, ldc, alpha, beta,
+                  &ref[i * N + j], absdot ? &absdot[i * N + j] : NULL);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Full product, A and B row-major. */
 int oracle_gemm(int64_t M, int64_t N, int64_t K,
                 const uint16_t *A, int64_t lda,
                 const uint16_t *B, int64_t ldb,
@@ -128,34 +186,24 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
                 double alpha, double beta,
                 double *ref, double *absdot)
 {
-    const int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc, beta);
-    if (rc != ORACLE_OK)
-        return rc;
-    if (M > 0 && N > 0 && ref == NULL)
-        return ORACLE_ENULL;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t i = 0; i < M; ++i) {
-        for (int64_t j = 0; j < N; ++j) {
-            entry(i, j, K, A, lda, B, ldb, C, ldc, alpha, beta,
-                  &ref[i * N + j], absdot ? &absdot[i * N + j] : NULL);
-        }
-    }
-    return ORACLE_OK;
+    return oracle_gemm_layout(ORACLE_ROW_MAJOR, ORACLE_ROW_MAJOR, M, N, K, A, lda, B, ldb,
+                              C, ldc, alpha, beta, ref, absdot);
 }
 
 /*
  * Selected entries only: element t of the output is (rows[t], cols[t]).
  * Used where the full product would take too long on the CPU.
  */
-int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
-                        const uint16_t *A, int64_t lda,
-                        const uint16_t *B, int64_t ldb,
-                        const float *C, int64_t ldc,
-                        double alpha, double beta,
-                        int64_t count, const int64_t *rows, const int64_t *cols,
-                        double *ref, double *absdot)
+int oracle_gemm_layout_entries(int layout_a, int layout_b,
+                               int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda,
+                               const uint16_t *B, int64_t ldb,
+                               const float *C, int64_t ldc,
+                               double alpha, double beta,
+                               int64_t count, const int64_t *rows, const int64_t *cols,
+                               double *ref, double *absdot)
 {
-    const int rc = check_args(M, N, K, A, lda, B, ldb, C, ldc, beta);
+    const int rc = check_args(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, beta);
     if (rc != ORACLE_OK)
         return rc;
     if (count < 0)
@@ -164,12 +212,26 @@ int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
         if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)
             return ORACLE_EBADDIM;
     }
+    const strides_t st = strides_for(layout_a, layout_b, lda, ldb);
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t t = 0; t < count; ++t) {
-        entry(rows[t], cols[t], K, A, lda, B, ldb, C, ldc, alpha, beta,
+        entry(rows[t], cols[t], K, A, B, st, C, ldc, alpha, beta,
               &ref[t], absdot ? &absdot[t] : NULL);
     }
     return ORACLE_OK;
+}
+
+/* Selected entries, A and B row-major. */
+int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
+                        const uint16_t *A, int64_t lda,
+                        const uint16_t *B, int64_t ldb,
+                        const float *C, int64_t ldc,
+                        double alpha, double beta,
+                        int64_t count, const int64_t *rows, const int64_t *cols,
+                        double *ref, double *absdot)
+{
+    return oracle_gemm_layout_entries(ORACLE_ROW_MAJOR, ORACLE_ROW_MAJOR, M, N, K, A, lda, B, ldb,
+                                      C, ldc, alpha, beta, count, rows, cols, ref, absdot);
 }
 
 int oracle_num_threads(void)

@@ -256,6 +256,78 @@ def test_argument_errors():
 
 
 # ----------------------------------------------------------------------------
+# Column-major operands ("Capstone 4: a tensor-core GEMM", Independent gate:
+# A row-major, B column-major; the other combinations follow)
+# ----------------------------------------------------------------------------
+
+LAYOUTS = [(0, 1), (1, 0), (1, 1)]
+
+
+def _stored(X, col_major, pad=0):
+    """Logical FP16 bits -> stored array: X itself (row-major) or X^T
+    (column-major), optionally inside a wider row so ld exceeds the extent."""
+    S = np.ascontiguousarray(X.T) if col_major else X
+    if pad:
+        big = np.full((S.shape[0], S.shape[1] + pad), 0x7E00, dtype=np.uint16)  # NaN filler
+        big[:, :S.shape[1]] = S
+        return big[:, :S.shape[1]]
+    return S
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 17), (3, 5, 7), (17, 15, 33), (33, 31, 65)])
+def test_layout_exact_brute_force(la, lb, M, N, K):
+    A, B, C = make_inputs(M, N, K, "uniform", seed=5 * M + 3 * N + K + la + 2 * lb, c_init="uniform")
+    Ab, Bb, Cn = bits(A), bits(B), C.numpy()
+    ref, absdot = oracle.gemm(_stored(Ab, la), _stored(Bb, lb), Cn, 1.5, 0.5, layout_a=la, layout_b=lb)
+    eref, eabs, _ = exact_gemm(Ab, Bb, Cn, 1.5, 0.5)
+    assert np.all(np.abs(ref - eref) <= fp64_sum_bound(K, 1.5, 0.5, eabs, Cn))
+    assert np.allclose(absdot, eabs, rtol=K * 2.0 ** -52, atol=0)
+
+
+@pytest.mark.parametrize("la,lb", LAYOUTS)
+def test_layout_matches_row_major_bitwise(la, lb):
+    """Same products, same ascending-k order: the stored order must not
+    change a single bit, also with leading dimensions beyond the extents
+    (the padding holds NaN, so reading it would show)."""
+    M, N, K = 37, 29, 83
+    A, B, C = make_inputs(M, N, K, "uniform", seed=31 + la + 2 * lb, c_init="uniform")
+    Ab, Bb, Cn = bits(A), bits(B), C.numpy()
+    r0, s0 = oracle.gemm(Ab, Bb, Cn, -0.75, 2.0)
+    r1, s1 = oracle.gemm(_stored(Ab, la, pad=5), _stored(Bb, lb, pad=3), Cn, -0.75, 2.0,
+                         layout_a=la, layout_b=lb)
+    assert np.array_equal(r0, r1) and np.array_equal(s0, s1)
+    rows, cols = np.array([0, M - 1, 5, M - 1]), np.array([0, N - 1, 7, 0])
+    e1, _ = oracle.gemm_entries(_stored(Ab, la, pad=5), _stored(Bb, lb, pad=3), Cn, -0.75, 2.0,
+                                rows, cols, layout_a=la, layout_b=lb)
+    assert np.array_equal(e1, r0[rows, cols])
+
+
+def test_layout_argument_errors():
+    A, B, _ = make_inputs(6, 4, 5, "uniform", seed=17)
+    Ab, Bb = bits(A), bits(B)
+    with pytest.raises(ValueError):       # stored shapes that do not chain
+        oracle.gemm(Ab, Bb, layout_a=1)
+    with pytest.raises(ValueError):
+        oracle.gemm(Ab, Bb, layout_a=2)
+    # column-major A needs lda >= M (checked in the C entry point itself)
+    rc = oracle._load().oracle_gemm_layout(1, 0, 6, 4, 5, Ab.ctypes.data, 5, Bb.ctypes.data, 4,
+                                           None, 4, 1.0, 0.0, np.empty(24).ctypes.data, None)
+    assert rc == -2  # lda = 5 < M = 6 for a column-major A
+
+
+def test_layout_ignored_is_caught():
+    """A plausible slip, reading a column-major operand as if row-major (on a
+    square operand, so the shapes still chain), fails the exact pin."""
+    M = K = 9
+    A, B, _ = make_inputs(M, 7, K, "uniform", seed=18)
+    Ab, Bb = bits(A), bits(B)
+    wrong, _ = oracle.gemm(_stored(Ab, 1), Bb)        # layout flag dropped
+    eref, eabs, _ = exact_gemm(Ab, Bb)
+    assert not np.all(np.abs(wrong - eref) <= fp64_sum_bound(K, 1.0, 0.0, eabs))
+
+
+# ----------------------------------------------------------------------------
 # The acceptance rule
 # ----------------------------------------------------------------------------
 
