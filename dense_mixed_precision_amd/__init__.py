@@ -11,12 +11,15 @@ integers holding device addresses, ``stream`` a hipStream_t as an integer,
     mpgemm_f16f32(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream) -> int
     mpgemm_f16f32_query(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta) -> dict
     mpgemm_f16f32_with_config(cfg, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream) -> int
+    mpgemm_f16f32_layout(layout_a, layout_b, M, N, K, ...) -> int   (A and/or B column-major)
+    mpgemm_f16f32_layout_query(layout_a, layout_b, M, N, K, ...) -> dict
+    mpgemm_f16f32_layout_with_config(cfg, layout_a, layout_b, M, N, K, ...) -> int
     mpgemm_num_configs(), mpgemm_config_info(id), mpgemm_probe_mfma_layout(shape, out, stream)
     mpgemm_strerror(code), mpgemm_version()
 
 Tensor convenience: ``gemm(A, B, C, alpha, beta)`` for torch tensors on the
-GPU (A, B float16, C float32, row-major with unit inner stride), launched on
-torch's current stream.
+GPU (A, B float16, each row- or column-major, e.g. a transposed view; C
+float32 row-major), launched on torch's current stream.
 """
 from __future__ import annotations
 
@@ -25,9 +28,12 @@ from ._binding import (  # noqa: F401
     MPGEMM_ECONFIG,
     MPGEMM_EDIM,
     MPGEMM_ELAUNCH,
+    MPGEMM_ELAYOUT,
     MPGEMM_ELD,
     MPGEMM_ENULL,
     MPGEMM_OK,
+    MPGEMM_COL_MAJOR,
+    MPGEMM_ROW_MAJOR,
     MpgemmError,
     config_fields,
     gemm,
@@ -37,6 +43,9 @@ from ._binding import (  # noqa: F401
     mpgemm_f16f32,
     mpgemm_f16f32_query,
     mpgemm_f16f32_with_config,
+    mpgemm_f16f32_layout,
+    mpgemm_f16f32_layout_query,
+    mpgemm_f16f32_layout_with_config,
     mpgemm_num_configs,
     mpgemm_probe_mfma_layout,
     mpgemm_strerror,

@@ -14,13 +14,17 @@ MPGEMM_ENULL = -3
 MPGEMM_ELAUNCH = -4
 MPGEMM_ECONFIG = -5
 MPGEMM_EALIGN = -6
+MPGEMM_ELAYOUT = -7
+
+MPGEMM_ROW_MAJOR = 0
+MPGEMM_COL_MAJOR = 1
 
 
 class MpgemmConfig(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "id", "kind", "bm", "bn", "bk", "waves_m", "waves_n", "wave_m", "wave_n",
         "mfma_m", "mfma_n", "mfma_k", "vec_a", "vec_b", "stages", "threads", "lds_bytes")] + [
-        ("grid", ctypes.c_int64)]
+        ("grid", ctypes.c_int64), ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32)]
 
 
 config_fields = [f[0] for f in MpgemmConfig._fields_]
@@ -58,6 +62,12 @@ def load():
     lib.mpgemm_f16f32_query.restype = i32
     lib.mpgemm_f16f32_with_config.argtypes = [i32] + gemm_args + [vp]
     lib.mpgemm_f16f32_with_config.restype = i32
+    lib.mpgemm_f16f32_layout.argtypes = [i32, i32] + gemm_args + [vp]
+    lib.mpgemm_f16f32_layout.restype = i32
+    lib.mpgemm_f16f32_layout_query.argtypes = [i32, i32] + gemm_args + [ctypes.POINTER(MpgemmConfig)]
+    lib.mpgemm_f16f32_layout_query.restype = i32
+    lib.mpgemm_f16f32_layout_with_config.argtypes = [i32, i32, i32] + gemm_args + [vp]
+    lib.mpgemm_f16f32_layout_with_config.restype = i32
     lib.mpgemm_num_configs.argtypes = []
     lib.mpgemm_num_configs.restype = i32
     lib.mpgemm_config_info.argtypes = [i32, ctypes.POINTER(MpgemmConfig)]
@@ -99,6 +109,28 @@ def mpgemm_f16f32_with_config(config_id, M, N, K, A, lda, B, ldb, C, ldc, alpha,
                                                  alpha, beta, stream))
 
 
+def mpgemm_f16f32_layout(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                         stream=0) -> int:
+    return int(load().mpgemm_f16f32_layout(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc,
+                                           alpha, beta, stream))
+
+
+def mpgemm_f16f32_layout_query(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha,
+                               beta) -> dict:
+    out = MpgemmConfig()
+    rc = load().mpgemm_f16f32_layout_query(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc,
+                                           alpha, beta, ctypes.byref(out))
+    if rc != MPGEMM_OK:
+        raise MpgemmError(rc, "mpgemm_f16f32_layout_query")
+    return _cfg_dict(out)
+
+
+def mpgemm_f16f32_layout_with_config(config_id, layout_a, layout_b, M, N, K, A, lda, B, ldb, C,
+                                     ldc, alpha, beta, stream=0) -> int:
+    return int(load().mpgemm_f16f32_layout_with_config(config_id, layout_a, layout_b, M, N, K, A,
+                                                       lda, B, ldb, C, ldc, alpha, beta, stream))
+
+
 def mpgemm_num_configs() -> int:
     return int(load().mpgemm_num_configs())
 
@@ -125,7 +157,12 @@ def mpgemm_version() -> str:
 
 # ---- torch tensor convenience ----------------------------------------------
 
-def _check_tensor(t, name, dtype):
+def _check_tensor(t, name, dtype, allow_col_major=False):
+    """Validate a 2-D GPU tensor; returns (layout, leading dimension).
+
+    Row-major: unit stride along dimension 1, ld = stride(0).  Column-major
+    (A and B only): unit stride along dimension 0, ld = stride(1).  An
+    extent-1 dimension's stride is ignored."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -135,46 +172,54 @@ def _check_tensor(t, name, dtype):
         raise ValueError(f"{name} must be 2-D")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
-    if t.shape[1] > 1 and t.stride(1) != 1:
-        raise ValueError(f"{name} must be row-major with unit inner stride")
-    return max(t.stride(0), max(t.shape[1], 1)) if t.shape[0] > 1 else max(t.shape[1], 1)
+    rows, cols = t.shape
+    if cols <= 1 or t.stride(1) == 1:
+        return MPGEMM_ROW_MAJOR, (max(t.stride(0), max(cols, 1)) if rows > 1 else max(cols, 1))
+    if allow_col_major and (rows <= 1 or t.stride(0) == 1):
+        return MPGEMM_COL_MAJOR, max(t.stride(1), max(rows, 1))
+    raise ValueError(f"{name} must have unit stride along one dimension"
+                     + ("" if allow_col_major else " (row-major)"))
 
 
 def _args(A, B, C):
     import torch
-    lda = _check_tensor(A, "A", torch.float16)
-    ldb = _check_tensor(B, "B", torch.float16)
-    ldc = _check_tensor(C, "C", torch.float32)
+    la, lda = _check_tensor(A, "A", torch.float16, allow_col_major=True)
+    lb, ldb = _check_tensor(B, "B", torch.float16, allow_col_major=True)
+    _, ldc = _check_tensor(C, "C", torch.float32)
     M, K = A.shape
     K2, N = B.shape
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
-    return M, N, K, lda, ldb, ldc
+    return M, N, K, la, lda, lb, ldb, ldc
 
 
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, config: int | None = None, stream=None):
     """C <- alpha*A@B + beta*C in place on the GPU; returns C.
 
+    A (M x K) and B (K x N) may each be row-major or column-major (e.g. the
+    transpose view of a row-major tensor); the storage order is read from the
+    strides.  C must be row-major.
     ``stream``: a torch.cuda.Stream or raw handle (default: current stream).
     ``config``: force a table entry (tests and sweeps)."""
     import torch
-    M, N, K, lda, ldb, ldc = _args(A, B, C)
+    M, N, K, la, lda, lb, ldb, ldc = _args(A, B, C)
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     if config is None:
-        rc = mpgemm_f16f32(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
-                           float(alpha), float(beta), handle)
+        rc = mpgemm_f16f32_layout(la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                  C.data_ptr(), ldc, float(alpha), float(beta), handle)
     else:
-        rc = mpgemm_f16f32_with_config(int(config), M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
-                                       C.data_ptr(), ldc, float(alpha), float(beta), handle)
+        rc = mpgemm_f16f32_layout_with_config(int(config), la, lb, M, N, K, A.data_ptr(), lda,
+                                              B.data_ptr(), ldb, C.data_ptr(), ldc, float(alpha),
+                                              float(beta), handle)
     if rc != MPGEMM_OK:
-        raise MpgemmError(rc, "mpgemm_f16f32" if config is None else f"config {config}")
+        raise MpgemmError(rc, "mpgemm_f16f32_layout" if config is None else f"config {config}")
     return C
 
 
 def query_for(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> dict:
     """The factory's choice for these tensors (no launch)."""
-    M, N, K, lda, ldb, ldc = _args(A, B, C)
-    return mpgemm_f16f32_query(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
-                               float(alpha), float(beta))
+    M, N, K, la, lda, lb, ldb, ldc = _args(A, B, C)
+    return mpgemm_f16f32_layout_query(la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                      C.data_ptr(), ldc, float(alpha), float(beta))

@@ -9,8 +9,8 @@
 //                     and the double-buffered copy of "02_mixed_precision_gemm",
 //                     Summary) is the prior art; the layout below is gfx950's.
 //   gemm_direct       one 32x32 MFMA tile per wave with operands loaded
-//                     straight from memory, 64-bit addressing, any size and
-//                     stride: the universal fallback.
+//                     straight from memory, 64-bit addressing, any size,
+//                     stride and storage order: the universal fallback.
 //   scale_c           C <- beta*C when alpha == 0 or K == 0.
 //   probe_mfma        writes the accumulator lane layout of one instruction.
 //
@@ -107,6 +107,9 @@ struct GemmArgs {
     float *C;
     int64_t M, N, K;
     int64_t lda, ldb, ldc;
+    // element strides: A[i][k] at A[i*a_i + k*a_k], B[k][j] at B[k*b_k + j*b_j]
+    // (read by the direct kernel; the tiled kernels compile their layout in)
+    int64_t a_i, a_k, b_k, b_j;
     float alpha, beta;
     int32_t tiles_m, tiles_n;
     int32_t group_m;
@@ -386,8 +389,8 @@ gemm_direct(GemmArgs args)
         for (int e = 0; e < 8; ++e) {
             const int64_t k = k0 + kbase + e;
             const bool k_ok = k < args.K;
-            const uint16_t av = (ra_ok && k_ok) ? args.A[ra * args.lda + k] : (uint16_t)0;
-            const uint16_t bv = (cb_ok && k_ok) ? args.B[k * args.ldb + cb] : (uint16_t)0;
+            const uint16_t av = (ra_ok && k_ok) ? args.A[ra * args.a_i + k * args.a_k] : (uint16_t)0;
+            const uint16_t bv = (cb_ok && k_ok) ? args.B[k * args.b_k + cb * args.b_j] : (uint16_t)0;
             a[e] = __builtin_bit_cast(_Float16, av);
             b[e] = __builtin_bit_cast(_Float16, bv);
         }
@@ -443,25 +446,31 @@ probe_mfma(float *out, int shape)
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined kernel: global -> LDS with buffer_load ... lds, B read transposed
+// Pipelined kernel: global -> LDS with buffer_load ... lds
 // ---------------------------------------------------------------------------
-// LDS layout of one stage (BK = 32, 64 or 128).  gfx950's LDS has 64 banks of
-// 4 bytes: a ds_read_b128 serves 16 lanes per cycle and a ds_read_b64
-// (including the transposing read) 32 lanes, so each such group must touch
-// 256 distinct bytes of bank space to run at full rate.
-//   A: BM rows x BK, K-contiguous (2*BK bytes per row).  The 16-byte chunk c
-//      of row r sits at physical chunk c ^ swz_a(r).  One 16-lane group reads
-//      16 consecutive rows at one logical chunk; with 128-byte rows two rows
-//      share a 256-byte bank window, so swz_a(r) = (r >> 1) & 7 gives the 8
-//      rows of each parity 8 distinct chunks; with 64-byte rows four rows
-//      share a window and swz_a(r) = (r >> 2) & 3; a 256-byte row fills the
-//      window by itself and swz_a(r) = r & 15.
-//   B: BK rows x BN, N-contiguous as in memory.  Chunk c of row k sits at
-//      c ^ swz_b(k).  One 32-lane group of the transposing read touches 4
-//      consecutive rows x 4 consecutive chunks; swz_b(k) = 4*(k & 3) moves
-//      the rows to 4 different 64-byte quarters of the window (rows of 256
-//      bytes or more), or 4*((k >> 1) & 1) for 128-byte rows (BN = 64),
-//      where row parity already selects the window half.
+// Each operand tile of a stage sits in LDS in its storage order, in one of two
+// forms (BK = 32, 64 or 128; BX = BM for A, BN for B):
+//   K-contiguous: one LDS row of BK values (2*BK bytes) per M row of A
+//     (row-major A) or per N column of B (column-major B).  Operands are read
+//     with ds_read_b128: lane l takes the 8 K-consecutive values of row l%32
+//     at logical chunk 2*ks + l/32.
+//   outer-contiguous: one LDS row of BX values per k, as a row-major B or a
+//     column-major A holds them in memory.  Operands are read with the
+//     transposing ds_read_b64_tr_b16, two per operand.
+// gfx950's LDS has 64 banks of 4 bytes: a ds_read_b128 serves 16 lanes per
+// cycle and a ds_read_b64 (including the transposing read) 32 lanes, so each
+// such group must touch 256 distinct bytes of bank space to run at full rate.
+// The 16-byte chunk c of LDS row r sits at physical chunk c ^ swz(r):
+//   K-contiguous: one 16-lane group reads 16 consecutive rows at one logical
+//     chunk.  With 128-byte rows two rows share a 256-byte bank window, so
+//     swz(r) = (r >> 1) & 7 gives the 8 rows of each parity 8 distinct chunks;
+//     with 64-byte rows four rows share a window and swz(r) = (r >> 2) & 3; a
+//     256-byte row fills the window by itself and swz(r) = r & 15.
+//   outer-contiguous: one 32-lane group of the transposing read touches 4
+//     consecutive rows x 4 consecutive chunks; swz(k) = 4*(k & 3) moves the
+//     rows to 4 different 64-byte quarters of the window (rows of 256 bytes or
+//     more), or 4*((k >> 1) & 1) for 128-byte rows (BX = 64), where row
+//     parity already selects the window half.
 // Copies: one wave instruction of buffer_load_dwordx4 ... lds writes 64
 // lanes x 16 B to LDS at M0 + 16*lane (a contiguous KiB); the swizzle is
 // applied by choosing which global chunk each lane fetches.  Lanes whose
@@ -482,28 +491,56 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int VEC_A_, int VEC_B_>
+// Storage order of an operand in memory (C is always row-major).
+constexpr int kRowMajor = 0;
+constexpr int kColMajor = 1;
+
+// One operand tile in LDS.  KC = true: K-contiguous rows (BX rows of BK);
+// KC = false: outer-contiguous rows (BK rows of BX).  NW waves share the
+// copies; each copy instruction fills RPI whole LDS rows.
+template <int BX, int BK, bool KC, int NW>
+struct OpTile {
+    static constexpr bool K_CONTIG = KC;
+    static constexpr int NWAVES = NW;
+    static constexpr int ROWS = KC ? BX : BK;
+    static constexpr int ROWB = 2 * (KC ? BK : BX);   // bytes per LDS row
+    static constexpr int CH = ROWB / 16;               // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;                // rows per copy instruction
+    static constexpr int PW = ROWS / RPI / NW;         // copies per wave per tile
+    static constexpr int BYTES = ROWS * ROWB;
+    static_assert(64 % CH == 0, "a row must hold at most 64 chunks");
+    static_assert(KC ? (CH == 4 || CH == 8 || CH == 16) : CH >= 8,
+                  "no conflict-free swizzle for this row width");
+    static_assert((ROWS / RPI) % NW == 0, "copies must split evenly over waves");
+    __device__ static __forceinline__ int swz(int r)
+    {
+        if constexpr (KC)
+            return CH == 16 ? (r & 15) : CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+        else
+            return CH >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+    }
+};
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int VEC_A_, int VEC_B_,
+          int LAYOUT_A_ = kRowMajor, int LAYOUT_B_ = kRowMajor>
 struct PipeCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int VEC_A = VEC_A_, VEC_B = VEC_B_;
+    static constexpr int LAYOUT_A = LAYOUT_A_, LAYOUT_B = LAYOUT_B_;
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int KS = BK / 16;                    // MFMA k-steps per tile
-    static constexpr int A_ROWB = BK * 2;
-    static constexpr int B_ROWB = BN * 2;
-    static constexpr int A_BYTES = BM * A_ROWB;
-    static constexpr int B_BYTES = BK * B_ROWB;
+    // row-major A and column-major B are K-contiguous in memory
+    using TA = OpTile<BM, BK, LAYOUT_A == kRowMajor, NW>;
+    using TB = OpTile<BN, BK, LAYOUT_B == kColMajor, NW>;
+    static constexpr int A_BYTES = TA::BYTES;
+    static constexpr int B_BYTES = TB::BYTES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-    static constexpr int A_CH = BK / 8;                   // 16-byte chunks per A row
-    static constexpr int B_CH = BN / 8;                   // ... per B row
-    static constexpr int A_RPI = 64 / A_CH;               // A rows per copy instruction
-    static constexpr int B_RPI = 64 / B_CH;               // B rows per copy instruction
-    static constexpr int APW = BM / A_RPI / NW;           // A copies per wave per tile
-    static constexpr int BPW = BK / B_RPI / NW;           // B copies per wave per tile
+    static constexpr int APW = TA::PW, BPW = TB::PW;      // copies per wave per tile
     static constexpr int NL = (VEC_A == 8 ? APW : 0) + (VEC_B == 8 ? BPW : 0);  // vmcnt per tile
     static constexpr int NCOPY = APW + BPW;                // copy instructions per wave per tile
     // MFMA groups (FM per k-step) over which a tile's copies are spread,
@@ -515,8 +552,6 @@ struct PipeCfg {
         STAGES == 2 ? (NCOPY < KS * FM ? (NCOPY > 0 ? NCOPY : 1) : KS * FM) : KS * FM;
     static_assert(BK == 32 || BK == 64 || BK == 128, "BK must be 32, 64 or 128");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
-    static_assert(BN >= 64 && 64 % B_CH == 0, "B rows must hold 8..64 chunks");
-    static_assert((BM / A_RPI) % NW == 0 && (BK / B_RPI) % NW == 0, "copies must split evenly over waves");
     static_assert(STAGES >= 2 && STAGES <= 5, "2..5 LDS stages");
     static_assert(NL * (STAGES - 1) < 64, "vmcnt is 6 bits");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
@@ -555,15 +590,119 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, uint32_t vo
                  : "memory", "m0");
 }
 
+// The operand tile as it sits in memory: a window of `row_left` rows (capped
+// by the tile) of the stored matrix, `chunk_left` elements wide, starting at
+// `origin`, rows `ld` elements apart.  For a K-contiguous tile the rows are
+// M rows or N columns and the width runs along K; otherwise the rows are k
+// values and the width runs along M or N.
+struct TileSrc {
+    const uint16_t *origin;
+    int64_t ld;
+    int64_t row_left;
+    int64_t chunk_left;
+};
+
+// Copy number i (0 .. T::PW-1) of this wave for one operand tile: LDS row
+// r = RPI*j + lane/CH with j = i*NW + wave, physical chunk lane%CH, logical
+// chunk (lane%CH) ^ swz(r).
+template <class T>
+__device__ __forceinline__ void copy_slot(int i, int wave, int lane, i32x4 rs, const TileSrc &src,
+                                          uint32_t region)
+{
+    const int j = i * T::NWAVES + wave;
+    const int rl = lane / T::CH;
+    const int r = T::RPI * j + rl;
+    const int c = (lane % T::CH) ^ T::swz(r);
+    const bool ok = r < src.row_left && 8 * c + 8 <= src.chunk_left;
+    const uint32_t voff = (uint32_t)((rl * src.ld + 8 * c) * 2);
+    dma16(rs, region + j * 1024, ok ? voff : kOOB, (uint32_t)(T::RPI * j * src.ld * 2));
+}
+
+// Register fill of one operand tile: every slot when `all` (operands without
+// 16-byte alignment, which the copies skip), else only the vectors that
+// straddle the end of a row (the copies wrote zeros there).  Runs after this
+// thread's copies for the tile have landed.
+template <class T>
+__device__ __forceinline__ void fill_tile(int wave, int lane, const TileSrc &src, lds_u8 *region, bool all)
+{
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src.origin);
+#pragma unroll
+    for (int i = 0; i < T::PW; ++i) {
+        const int j = i * T::NWAVES + wave;
+        const int r = T::RPI * j + lane / T::CH;
+        const int c = (lane % T::CH) ^ T::swz(r);
+        const int64_t left = src.chunk_left - 8 * c;
+        const int nv = r >= src.row_left ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : (int)left));
+        if (all || (nv > 0 && nv < 8)) {
+            const uint32_t off = (uint32_t)((r * src.ld + 8 * c) * 2);
+            const u32x4 v = (nv >= 8) ? load8_full<1>(rs, off) : load8_partial(rs, off, nv);
+            *(lds_u32x4 *)(region + j * 1024 + lane * 16) = v;
+        }
+    }
+}
+
+// Does a tile with this many elements along its rows leave a partial vector?
+template <class T>
+__device__ __forceinline__ bool has_partial(int64_t chunk_left)
+{
+    return chunk_left < 8 * T::CH && (chunk_left & 7) != 0;
+}
+
+// Per-lane operand read addressing for a wave whose part of the operand
+// starts at outer index `w_off` (wm*WTM for A, wn*WTN for B).
+template <class T>
+struct OpReader {
+    int base;    // byte offset of this lane's first read within the region
+    int sw;      // swizzle of this lane's rows
+    int col;     // outer-contiguous: this lane's first column
+
+    __device__ __forceinline__ OpReader(int w_off, int lane)
+    {
+        if constexpr (T::K_CONTIG) {
+            const int row = w_off + (lane & 31);
+            sw = T::swz(row);
+            base = row * T::ROWB;
+            col = 0;
+        } else {
+            // group g = lane/16, index q = lane%16: rows 8*(g/2) + q/4 (+ 16*ks
+            // + 4*h, which leave the swizzle unchanged), columns 16*(g%2) + 4*(q%4)
+            const int g = lane >> 4, q = lane & 15;
+            const int row_l = 8 * (g >> 1) + (q >> 2);
+            sw = T::swz(row_l);
+            base = row_l * T::ROWB;
+            col = w_off + 16 * (g & 1) + 4 * (q & 3);
+        }
+    }
+
+    // The 8 K-consecutive values lane l contributes to MFMA operand f of
+    // k-step ks: outer index (w_off + 32*f + l%32), k = 16*ks + 8*(l/32) + 0..7.
+    __device__ __forceinline__ half8 read(const lds_u8 *region, int ks, int f, int lane) const
+    {
+        if constexpr (T::K_CONTIG) {
+            const int off = base + f * 32 * T::ROWB + (((2 * ks + (lane >> 5)) ^ sw) * 16);
+            return __builtin_bit_cast(half8, *(const lds_u32x4 *)(region + off));
+        } else {
+            const int c = col + 32 * f;
+            const lds_u8 *p0 = region + base + 16 * ks * T::ROWB + (((c >> 3) ^ sw) * 16) + (c & 7) * 2;
+            const fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) fp16x4 *)p0);
+            const fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                (__attribute__((address_space(3))) fp16x4 *)(p0 + 4 * T::ROWB));
+            return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    }
+};
+
 template <class Cfg>
 __global__ void __launch_bounds__(Cfg::NT)
 gemm_pipe(GemmArgs args)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
-    constexpr int FM = Cfg::FM, FN = Cfg::FN, KS = Cfg::KS, NW = Cfg::NW;
-    constexpr int A_ROWB = Cfg::A_ROWB, B_ROWB = Cfg::B_ROWB, A_CH = Cfg::A_CH, B_CH = Cfg::B_CH;
-    constexpr int A_RPI = Cfg::A_RPI, B_RPI = Cfg::B_RPI;
-    constexpr int APW = Cfg::APW, BPW = Cfg::BPW, NL = Cfg::NL;
+    constexpr int FM = Cfg::FM, FN = Cfg::FN, KS = Cfg::KS;
+    constexpr int APW = Cfg::APW, BPW = Cfg::BPW, NL = Cfg::NL, NCOPY = Cfg::NCOPY;
+    using TA = typename Cfg::TA;
+    using TB = typename Cfg::TB;
+    constexpr bool A_ROW = Cfg::LAYOUT_A == kRowMajor;
+    constexpr bool B_ROW = Cfg::LAYOUT_B == kRowMajor;
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS_BYTES];
     lds_u8 *const lds = (lds_u8 *)smem;
@@ -586,142 +725,72 @@ gemm_pipe(GemmArgs args)
     const int64_t rows_left = args.M - m0;  // > 0
     const int64_t cols_left = args.N - n0;  // > 0
 
-    // ---- copy assignment (the same chunks for copies and register fill) ---
-    // A copy i of this wave covers rows A_RPI*j .. +A_RPI-1, j = i*NW + wave;
-    // lane -> row A_RPI*j + lane/A_CH, physical chunk lane%A_CH.
-    auto swz_a = [](int r) __attribute__((always_inline)) {
-        return A_CH == 16 ? (r & 15) : A_CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+    // The A and B tiles of K tile t as windows of the stored matrices.
+    auto src_a = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t k0 = t * BK;
+        if constexpr (A_ROW)
+            return TileSrc{args.A + m0 * lda + k0, lda, rows_left, K - k0};
+        else
+            return TileSrc{args.A + k0 * lda + m0, lda, K - k0, rows_left};
     };
-    auto swz_b = [](int k) __attribute__((always_inline)) {
-        return B_CH >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+    auto src_b = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t k0 = t * BK;
+        if constexpr (B_ROW)
+            return TileSrc{args.B + k0 * ldb + n0, ldb, K - k0, cols_left};
+        else
+            return TileSrc{args.B + n0 * ldb + k0, ldb, cols_left, K - k0};
     };
-    const int a_r = lane / A_CH;
-    const int a_p = lane % A_CH;
-    // logical chunk fetched by this lane in A copy j (its row is A_RPI*j + a_r)
-    auto a_c_of = [&](int j) __attribute__((always_inline)) { return a_p ^ swz_a(A_RPI * j + a_r); };
-    // B copy i covers rows B_RPI*j .. +B_RPI-1; lane -> row B_RPI*j + lane/B_CH,
-    // physical chunk lane%B_CH, logical chunk physical ^ swz_b(row).
-    const int b_r = lane / B_CH;
-    const int b_p = lane % B_CH;
-    auto b_c_of = [&](int j) __attribute__((always_inline)) { return b_p ^ swz_b(B_RPI * j + b_r); };
 
-    int64_t copy_tile = 0;   // tile whose copies are being issued
-    int copy_buf = 0;
+    // ---- copies of one K tile into one ring buffer, issued a few at a time
+    TileSrc cpa{}, cpb{};
+    uint32_t copy_region = 0;  // LDS byte address of the buffer being filled
     bool copy_live = false;
     i32x4 rsA, rsB;
-    int64_t copy_kleft = 0;
     auto begin_copies = [&](int64_t t, int buf) __attribute__((always_inline)) {
-        copy_tile = t;
-        copy_buf = buf;
+        copy_region = lds_base + buf * Cfg::STAGE_BYTES;
         copy_live = t < (K + BK - 1) / BK;
-        const int64_t k0 = t * BK;
-        copy_kleft = K - k0;
-        rsA = make_rsrc4(args.A + m0 * lda + k0);
-        rsB = make_rsrc4(args.B + k0 * ldb + n0);
+        cpa = src_a(t);
+        cpb = src_b(t);
+        rsA = make_rsrc4(cpa.origin);
+        rsB = make_rsrc4(cpb.origin);
     };
-    // copy number q (0 .. APW+BPW-1) of the current tile
+    // copy number q (0 .. NCOPY-1) of the current tile
     auto copy_one = [&](int q) __attribute__((always_inline)) {
         if (!copy_live)
             return;
-        const uint32_t sbase = lds_base + copy_buf * Cfg::STAGE_BYTES;
         if (q < APW) {
-            if constexpr (Cfg::VEC_A == 8) {
-                const int j = q * NW + wave;
-                const int c = a_c_of(j);
-                const bool ok = (8 * c + 8 <= copy_kleft) && (A_RPI * j + a_r) < rows_left;
-                const uint32_t voff = (uint32_t)((a_r * lda + 8 * c) * 2);
-                dma16(rsA, sbase + j * 1024, ok ? voff : kOOB, (uint32_t)(A_RPI * j * lda * 2));
-            }
+            if constexpr (Cfg::VEC_A == 8)
+                copy_slot<TA>(q, wave, lane, rsA, cpa, copy_region);
         } else {
-            if constexpr (Cfg::VEC_B == 8) {
-                const int j = (q - APW) * NW + wave;
-                const int c = b_c_of(j);
-                const bool ok = (B_RPI * j + b_r) < copy_kleft && 8 * c + 8 <= cols_left;
-                const uint32_t voff = (uint32_t)((b_r * ldb + 8 * c) * 2);
-                dma16(rsB, sbase + Cfg::A_BYTES + j * 1024, ok ? voff : kOOB,
-                      (uint32_t)(B_RPI * j * ldb * 2));
-            }
+            if constexpr (Cfg::VEC_B == 8)
+                copy_slot<TB>(q - APW, wave, lane, rsB, cpb, copy_region + Cfg::A_BYTES);
         }
     };
-    constexpr int NCOPY = Cfg::NCOPY;
 
-    // Register fill: operands without 16-byte alignment, and the vectors that
-    // straddle the end of a row (the copies wrote zeros there).  Runs after
-    // this thread's copies for the tile have landed.
+    // Register fill after this thread's copies of tile kt have landed.
     auto fill = [&](int64_t kt, int buf) __attribute__((always_inline)) {
-        const int64_t k0 = kt * BK;
-        const int64_t k_left = K - k0;
         lds_u8 *const sbase = lds + buf * Cfg::STAGE_BYTES;
-        const bool a_all = Cfg::VEC_A != 8;
-        if (a_all || (k_left < BK && (k_left & 7) != 0)) {
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.A + m0 * lda + k0);
-#pragma unroll
-            for (int i = 0; i < APW; ++i) {
-                const int j = i * NW + wave;
-                const int c = a_c_of(j);
-                const int r = A_RPI * j + a_r;
-                const int64_t left = k_left - 8 * c;
-                const int nv = r >= rows_left ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : (int)left));
-                if (a_all || (nv > 0 && nv < 8)) {
-                    const uint32_t off = (uint32_t)((r * lda + 8 * c) * 2);
-                    const u32x4 v = (nv >= 8) ? load8_full<1>(rs, off) : load8_partial(rs, off, nv);
-                    *(lds_u32x4 *)(sbase + j * 1024 + lane * 16) = v;
-                }
-            }
-        }
-        const bool b_all = Cfg::VEC_B != 8;
-        if (b_all || (cols_left < BN && (cols_left & 7) != 0)) {
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.B + k0 * ldb + n0);
-#pragma unroll
-            for (int i = 0; i < BPW; ++i) {
-                const int j = i * NW + wave;
-                const int c = b_c_of(j);
-                const int k = B_RPI * j + b_r;
-                const int64_t left = cols_left - 8 * c;
-                const int nv = k < k_left ? (left >= 8 ? 8 : (left <= 0 ? 0 : (int)left)) : 0;
-                if (b_all || (nv > 0 && nv < 8)) {
-                    const uint32_t off = (uint32_t)((k * ldb + 8 * c) * 2);
-                    const u32x4 v = (nv >= 8) ? load8_full<1>(rs, off) : load8_partial(rs, off, nv);
-                    *(lds_u32x4 *)(sbase + Cfg::A_BYTES + j * 1024 + lane * 16) = v;
-                }
-            }
-        }
+        const TileSrc a = src_a(kt), b = src_b(kt);
+        if (Cfg::VEC_A != 8 || has_partial<TA>(a.chunk_left))
+            fill_tile<TA>(wave, lane, a, sbase, Cfg::VEC_A != 8);
+        if (Cfg::VEC_B != 8 || has_partial<TB>(b.chunk_left))
+            fill_tile<TB>(wave, lane, b, sbase + Cfg::A_BYTES, Cfg::VEC_B != 8);
     };
     auto needs_fill = [&](int64_t kt) __attribute__((always_inline)) {
         if (Cfg::VEC_A != 8 || Cfg::VEC_B != 8)
             return true;
-        const int64_t k_left = K - kt * BK;
-        return (k_left < BK && (k_left & 7) != 0) || (cols_left < BN && (cols_left & 7) != 0);
+        return has_partial<TA>(src_a(kt).chunk_left) || has_partial<TB>(src_b(kt).chunk_left);
     };
 
     // ---- operand reads -----------------------------------------------------
-    // A, 32x32x16 operand f of k-step ks: lane reads row wm*WTM + 32f + lane%32,
-    // logical chunk 2*ks + lane/32.
-    const int a_row = wm * Cfg::WTM + (lane & 31);
-    const uint32_t a_rd_base = a_row * A_ROWB;
-    const int a_sw = swz_a(a_row);
-    // B, operand f of k-step ks, half h: group g = lane/16, index q = lane%16
-    // address row 16*ks + 8*(g/2) + 4*h + q/4, column wn*WTN + 32*f + 16*(g%2) + 4*(q%4).
-    const int g = lane >> 4, q = lane & 15;
-    const int b_row_l = 8 * (g >> 1) + (q >> 2);                    // + 16*ks + 4*h
-    const int b_sw = swz_b(b_row_l);                                 // 16*ks + 4*h leave it unchanged
-    const int b_col_l = wn * Cfg::WTN + 16 * (g & 1) + 4 * (q & 3);  // + 32*f
-
+    const OpReader<TA> rd_a(wm * Cfg::WTM, lane);
+    const OpReader<TB> rd_b(wn * Cfg::WTN, lane);
     half8 ra[2][FM], rb[2][FN];
     auto read_a = [&](int buf, int ks, int set, int f) __attribute__((always_inline)) {
-        const lds_u8 *const sbase = lds + buf * Cfg::STAGE_BYTES;
-        const uint32_t off = a_rd_base + f * 32 * A_ROWB + (((2 * ks + (lane >> 5)) ^ a_sw) * 16);
-        ra[set][f] = __builtin_bit_cast(half8, *(const lds_u32x4 *)(sbase + off));
+        ra[set][f] = rd_a.read(lds + buf * Cfg::STAGE_BYTES, ks, f, lane);
     };
     auto read_b = [&](int buf, int ks, int set, int f) __attribute__((always_inline)) {
-        const lds_u8 *const sbase = lds + buf * Cfg::STAGE_BYTES;
-        const int col = b_col_l + 32 * f;
-        const int cpos = (((col >> 3) ^ b_sw) * 16) + (col & 7) * 2;
-        const lds_u8 *p0 = sbase + Cfg::A_BYTES + (16 * ks + b_row_l) * B_ROWB + cpos;
-        const fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) fp16x4 *)p0);
-        const fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-            (__attribute__((address_space(3))) fp16x4 *)(p0 + 4 * B_ROWB));
-        rb[set][f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        rb[set][f] = rd_b.read(lds + buf * Cfg::STAGE_BYTES + Cfg::A_BYTES, ks, f, lane);
     };
     // reads for one group: A operand f (if f < FM) and the B operands
     // assigned to that group (FN spread over FM groups)

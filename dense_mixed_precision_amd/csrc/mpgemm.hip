@@ -18,6 +18,8 @@
 namespace {
 
 using mpg::GemmArgs;
+using mpg::kColMajor;
+using mpg::kRowMajor;
 using mpg::PipeCfg;
 using mpg::TileCfg;
 
@@ -75,6 +77,8 @@ constexpr Entry tiled_entry(int id)
     c.threads = Cfg::NT;
     c.lds_bytes = Cfg::LDS_BYTES;
     c.grid = 0;
+    c.layout_a = MPGEMM_ROW_MAJOR;
+    c.layout_b = MPGEMM_ROW_MAJOR;
     return Entry{c, &launch_tiled<Cfg>};
 }
 
@@ -100,6 +104,8 @@ constexpr Entry pipe_entry(int id)
     c.threads = Cfg::NT;
     c.lds_bytes = Cfg::LDS_BYTES;
     c.grid = 0;
+    c.layout_a = Cfg::LAYOUT_A;
+    c.layout_b = Cfg::LAYOUT_B;
     return Entry{c, &launch_pipe<Cfg>};
 }
 
@@ -148,6 +154,14 @@ constexpr Entry scale_entry(int id)
         pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 8, 1>>(base + 2),    \
         pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 1, 1>>(base + 3)
 
+#define MPG_LAYOUT_ENTRIES(base, LA, LB)                                     \
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, LA, LB>>(base + 0),      \
+        pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4, 1, 1, LA, LB>>(base + 1),  \
+        pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, 8, 8, LA, LB>>(base + 2),  \
+        pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3, 1, 1, LA, LB>>(base + 3),  \
+        pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 8, 8, LA, LB>>(base + 4),    \
+        pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 1, 1, LA, LB>>(base + 5)
+
 const Entry kTable[] = {
     MPG_TILE_ENTRIES(0, 256, 256, 64, 2, 2),  // 0..3   register-staged copies
     MPG_TILE_ENTRIES(4, 128, 128, 64, 2, 2),  // 4..7
@@ -174,26 +188,39 @@ const Entry kTable[] = {
     pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8>>(37),
     pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, 8, 8>>(38),
     pipe_entry<PipeCfg<64, 64, 128, 2, 2, 3, 8, 8>>(39),
+    // A and/or B column-major: the three tile groups, each for 16-byte
+    // aligned operands and for any 2-byte alignment
+    MPG_LAYOUT_ENTRIES(40, kColMajor, kRowMajor),  // 40..45
+    MPG_LAYOUT_ENTRIES(46, kRowMajor, kColMajor),  // 46..51
+    MPG_LAYOUT_ENTRIES(52, kColMajor, kColMajor),  // 52..57
+    // 128x128 tiles with K tiles of 128 for the column-major pairs
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kColMajor, kRowMajor>>(58),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kRowMajor, kColMajor>>(59),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kColMajor, kColMajor>>(60),
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
 constexpr int kDirectId = 12;
 constexpr int kScaleId = 13;
 
-// Tile groups the factory chooses from, largest first.  ids[] holds the
-// table entry for each (vec_a, vec_b) pair in the order 88, 18, 81, 11; the
-// eight-wave shapes exist for 16-byte aligned operands only, and the other
-// pairs fall back to the four-wave form of the same tile.
-constexpr int kWideKId = 37;  // 128x128, K tile 128, eight waves
+// Tile groups the factory chooses from, largest first, per storage-order
+// pair (layout_a + 2*layout_b).  ids[] holds the table entry for each
+// (vec_a, vec_b) pair in the order 88, 18, 81, 11.  For row-major operands
+// the eight-wave shapes exist for 16-byte aligned operands only and the
+// other pairs fall back to the four-wave form of the same tile; for the
+// column-major pairs every pair but 88 takes the 2-byte (11) entry.
+// 128x128, K tile 128, eight waves, per storage-order pair
+constexpr int kWideKIds[4] = {37, 58, 59, 60};
 struct TileGroup {
     int bm, bn;
     int ids[4];
 };
-constexpr TileGroup kGroups[] = {
-    {256, 256, {32, 15, 16, 17}},
-    {128, 128, {36, 19, 20, 21}},
-    {64, 64, {22, 23, 24, 25}},
+constexpr int kNumGroups = 3;
+constexpr TileGroup kGroups[4][kNumGroups] = {
+    {{256, 256, {32, 15, 16, 17}}, {128, 128, {36, 19, 20, 21}}, {64, 64, {22, 23, 24, 25}}},
+    {{256, 256, {40, 41, 41, 41}}, {128, 128, {42, 43, 43, 43}}, {64, 64, {44, 45, 45, 45}}},
+    {{256, 256, {46, 47, 47, 47}}, {128, 128, {48, 49, 49, 49}}, {64, 64, {50, 51, 51, 51}}},
+    {{256, 256, {52, 53, 53, 53}}, {128, 128, {54, 55, 55, 55}}, {64, 64, {56, 57, 57, 57}}},
 };
-constexpr int kNumGroups = sizeof(kGroups) / sizeof(kGroups[0]);
 
 // ---------------------------------------------------------------------------
 // Validation and selection (pure host code, no HIP calls)
@@ -204,15 +231,23 @@ struct Problem {
     const uint16_t *B;
     const float *C;
     float alpha, beta;
+    int la, lb;  // storage orders of A and B
 };
+
+int64_t at_least_one(int64_t v) { return v > 1 ? v : 1; }
 
 int validate(const Problem &p)
 {
+    if ((p.la != MPGEMM_ROW_MAJOR && p.la != MPGEMM_COL_MAJOR) ||
+        (p.lb != MPGEMM_ROW_MAJOR && p.lb != MPGEMM_COL_MAJOR))
+        return MPGEMM_ELAYOUT;
     if (p.M < 0 || p.N < 0 || p.K < 0)
         return MPGEMM_EDIM;
-    const int64_t kmin = p.K > 1 ? p.K : 1;
-    const int64_t nmin = p.N > 1 ? p.N : 1;
-    if (p.lda < kmin || p.ldb < nmin || p.ldc < nmin)
+    // a stored row holds K values of A (row-major) or M (column-major), N of
+    // B (row-major) or K (column-major), N of C
+    const int64_t amin = at_least_one(p.la == MPGEMM_COL_MAJOR ? p.M : p.K);
+    const int64_t bmin = at_least_one(p.lb == MPGEMM_COL_MAJOR ? p.K : p.N);
+    if (p.lda < amin || p.ldb < bmin || p.ldc < at_least_one(p.N))
         return MPGEMM_ELD;
     if (p.M == 0 || p.N == 0)
         return MPGEMM_OK;
@@ -247,16 +282,21 @@ bool entry_fits(const Entry &e, const Problem &p)
         return scale_only || trivial;
     if (c.kind == MPGEMM_KIND_DIRECT)
         return true;
+    if (c.layout_a != p.la || c.layout_b != p.lb)
+        return false;
     if (trivial || scale_only)
         return true;  // the tiled kernel also handles these; the factory never picks it for them
     if (c.vec_a == 8 && vec_for(p.A, p.lda) != 8)
         return false;
     if (c.vec_b == 8 && vec_for(p.B, p.ldb) != 8)
         return false;
-    // Per-stage buffer offsets are 32-bit: the A stage spans bm rows of lda,
-    // the B stage bk rows of ldb.
-    const int64_t a_span = ((int64_t)c.bm * p.lda + c.bk) * 2;
-    const int64_t b_span = ((int64_t)c.bk * p.ldb + c.bn) * 2;
+    // Per-stage buffer offsets are 32-bit: a stage spans bm (A row-major) or
+    // bk (A column-major) stored rows of lda, and bk (B row-major) or bn (B
+    // column-major) stored rows of ldb.
+    const int64_t a_span = p.la == MPGEMM_ROW_MAJOR ? ((int64_t)c.bm * p.lda + c.bk) * 2
+                                                    : ((int64_t)c.bk * p.lda + c.bm) * 2;
+    const int64_t b_span = p.lb == MPGEMM_ROW_MAJOR ? ((int64_t)c.bk * p.ldb + c.bn) * 2
+                                                    : ((int64_t)c.bn * p.ldb + c.bk) * 2;
     if (a_span >= (int64_t)0x7FFFFFF0 || b_span >= (int64_t)0x7FFFFFF0)
         return false;
     // The pipelined kernel's epilogue addresses a wave's C tile with 32-bit
@@ -309,11 +349,13 @@ int select(const Problem &p)
     // 128x128 tiles with both panels reused across tiles (B panels by at
     // least four column tiles) take K steps of 128: half as many barriers.
     // A tall-skinny product streams A once and keeps the deeper 64-wide ring.
+    const int wide = kWideKIds[p.la + 2 * p.lb];
     if (group == 1 && v == 0 && cdiv(p.N, 128) >= 4 && cdiv(p.M, 128) >= 4 &&
-        entry_fits(kTable[kWideKId], p))
-        return kWideKId;
+        entry_fits(kTable[wide], p))
+        return wide;
+    const TileGroup *groups = kGroups[p.la + 2 * p.lb];
     for (int g = group; g < kNumGroups; ++g) {
-        const int id = kGroups[g].ids[v];
+        const int id = groups[g].ids[v];
         if (entry_fits(kTable[id], p))
             return id;
     }
@@ -326,11 +368,15 @@ int fill_config(int id, const Problem &p, mpgemm_config *out)
         mpgemm_config c{};
         c.id = -1;
         c.kind = MPGEMM_KIND_NONE;
+        c.layout_a = p.la;
+        c.layout_b = p.lb;
         *out = c;
         return MPGEMM_OK;
     }
     *out = kTable[id].cfg;
     out->grid = grid_for(out[0], p);
+    out->layout_a = p.la;
+    out->layout_b = p.lb;
     return MPGEMM_OK;
 }
 
@@ -359,6 +405,10 @@ int run(int id, const Problem &p, void *stream)
     a.lda = p.lda;
     a.ldb = p.ldb;
     a.ldc = p.ldc;
+    a.a_i = p.la == MPGEMM_COL_MAJOR ? 1 : p.lda;
+    a.a_k = p.la == MPGEMM_COL_MAJOR ? p.lda : 1;
+    a.b_k = p.lb == MPGEMM_COL_MAJOR ? 1 : p.ldb;
+    a.b_j = p.lb == MPGEMM_COL_MAJOR ? p.ldb : 1;
     a.alpha = p.alpha;
     a.beta = p.beta;
     const int64_t grid = grid_for(e.cfg, p);
@@ -381,9 +431,50 @@ int run(int id, const Problem &p, void *stream)
 
 Problem make_problem(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                      const uint16_t *B, int64_t ldb, const float *C, int64_t ldc,
-                     float alpha, float beta)
+                     float alpha, float beta, int la = MPGEMM_ROW_MAJOR, int lb = MPGEMM_ROW_MAJOR)
 {
-    return Problem{M, N, K, lda, ldb, ldc, A, B, C, alpha, beta};
+    return Problem{M, N, K, lda, ldb, ldc, A, B, C, alpha, beta, la, lb};
+}
+
+int gemm_layout(int la, int lb, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                const uint16_t *B, int64_t ldb, float *C, int64_t ldc, float alpha, float beta,
+                void *stream)
+{
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb);
+    const int rc = validate(p);
+    if (rc != MPGEMM_OK)
+        return rc;
+    return run(select(p), p, stream);
+}
+
+int query_layout(int la, int lb, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                 const uint16_t *B, int64_t ldb, const float *C, int64_t ldc, float alpha,
+                 float beta, mpgemm_config *out)
+{
+    if (out == nullptr)
+        return MPGEMM_ENULL;
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb);
+    const int rc = validate(p);
+    if (rc != MPGEMM_OK)
+        return rc;
+    return fill_config(select(p), p, out);
+}
+
+int with_config_layout(int config_id, int la, int lb, int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float *C,
+                       int64_t ldc, float alpha, float beta, void *stream)
+{
+    if (config_id < 0 || config_id >= kNumEntries)
+        return MPGEMM_ECONFIG;
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb);
+    const int rc = validate(p);
+    if (rc != MPGEMM_OK)
+        return rc;
+    if (!entry_fits(kTable[config_id], p))
+        return MPGEMM_ECONFIG;
+    if (p.M == 0 || p.N == 0)
+        return MPGEMM_OK;
+    return run(config_id, p, stream);
 }
 
 }  // namespace
@@ -394,41 +485,48 @@ int mpgemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t ld
                   const uint16_t *B, int64_t ldb, float *C, int64_t ldc, float alpha,
                   float beta, void *stream)
 {
-    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta);
-    const int rc = validate(p);
-    if (rc != MPGEMM_OK)
-        return rc;
-    return run(select(p), p, stream);
+    return gemm_layout(MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K, A, lda, B, ldb, C, ldc,
+                       alpha, beta, stream);
 }
 
 int mpgemm_f16f32_query(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                         const uint16_t *B, int64_t ldb, const float *C, int64_t ldc,
                         float alpha, float beta, mpgemm_config *out)
 {
-    if (out == nullptr)
-        return MPGEMM_ENULL;
-    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta);
-    const int rc = validate(p);
-    if (rc != MPGEMM_OK)
-        return rc;
-    return fill_config(select(p), p, out);
+    return query_layout(MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K, A, lda, B, ldb, C, ldc,
+                        alpha, beta, out);
 }
 
 int mpgemm_f16f32_with_config(int config_id, int64_t M, int64_t N, int64_t K,
                               const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                               float *C, int64_t ldc, float alpha, float beta, void *stream)
 {
-    if (config_id < 0 || config_id >= kNumEntries)
-        return MPGEMM_ECONFIG;
-    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta);
-    const int rc = validate(p);
-    if (rc != MPGEMM_OK)
-        return rc;
-    if (!entry_fits(kTable[config_id], p))
-        return MPGEMM_ECONFIG;
-    if (p.M == 0 || p.N == 0)
-        return MPGEMM_OK;
-    return run(config_id, p, stream);
+    return with_config_layout(config_id, MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K, A, lda,
+                              B, ldb, C, ldc, alpha, beta, stream);
+}
+
+int mpgemm_f16f32_layout(int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
+                         const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                         float *C, int64_t ldc, float alpha, float beta, void *stream)
+{
+    return gemm_layout(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream);
+}
+
+int mpgemm_f16f32_layout_query(int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                               const float *C, int64_t ldc, float alpha, float beta,
+                               mpgemm_config *out)
+{
+    return query_layout(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, out);
+}
+
+int mpgemm_f16f32_layout_with_config(int config_id, int layout_a, int layout_b, int64_t M,
+                                     int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                                     const uint16_t *B, int64_t ldb, float *C, int64_t ldc,
+                                     float alpha, float beta, void *stream)
+{
+    return with_config_layout(config_id, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc,
+                              alpha, beta, stream);
 }
 
 int mpgemm_num_configs(void) { return kNumEntries; }
@@ -472,11 +570,13 @@ const char *mpgemm_strerror(int code)
         return "unknown config, or the config cannot run these arguments";
     case MPGEMM_EALIGN:
         return "A/B are not 2-byte aligned or C is not 4-byte aligned";
+    case MPGEMM_ELAYOUT:
+        return "a layout is neither MPGEMM_ROW_MAJOR nor MPGEMM_COL_MAJOR";
     default:
         return "unknown error code";
     }
 }
 
-const char *mpgemm_version(void) { return "mpgemm 0.1.0 gfx950"; }
+const char *mpgemm_version(void) { return "mpgemm 0.2.0 gfx950"; }
 
 }  // extern "C"

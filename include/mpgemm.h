@@ -9,10 +9,13 @@
  *     C[i][j] <- alpha * sum_{k<K} A[i][k] * B[k][j] + beta * C[i][j]
  *                for 0 <= i < M, 0 <= j < N
  *
- * Layouts.  All three matrices are row-major and live in device memory:
+ * Layouts.  In mpgemm_f16f32 all three matrices are row-major and live in
+ * device memory:
  *     A[i][k] at A[i*lda + k]   (M x K, FP16 bit patterns, lda >= max(1,K))
  *     B[k][j] at B[k*ldb + j]   (K x N, FP16 bit patterns, ldb >= max(1,N))
  *     C[i][j] at C[i*ldc + j]   (M x N, IEEE binary32,     ldc >= max(1,N))
+ * The *_layout entry points also take A and/or B column-major (see
+ * mpgemm_f16f32_layout); C is always row-major.
  * Leading dimensions count elements, not bytes.  Any M, N, K >= 0 is
  * accepted; no padding is needed and none is done.  A and B must be 2-byte
  * aligned and C 4-byte aligned; wider alignment of the pointers and leading
@@ -48,19 +51,25 @@ extern "C" {
 
 #define MPGEMM_OK 0
 #define MPGEMM_EDIM (-1)       /* M, N or K negative                              */
-#define MPGEMM_ELD (-2)        /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+#define MPGEMM_ELD (-2)        /* a leading dimension below its stored row length  */
 #define MPGEMM_ENULL (-3)      /* NULL pointer for an operand that must be read   */
 #define MPGEMM_ELAUNCH (-4)    /* the HIP launch failed                           */
 #define MPGEMM_ECONFIG (-5)    /* unknown config id, or it cannot run these args  */
 #define MPGEMM_EALIGN (-6)     /* A/B not 2-byte aligned or C not 4-byte aligned  */
+#define MPGEMM_ELAYOUT (-7)    /* a layout argument is not one of MPGEMM_*_MAJOR  */
+
+/* Storage order of A or B (C is always row-major). */
+#define MPGEMM_ROW_MAJOR 0
+#define MPGEMM_COL_MAJOR 1
 
 /* Kinds of kernel a config can name. */
 #define MPGEMM_KIND_TILED 0    /* LDS-staged, double-buffered MFMA block tile     */
 #define MPGEMM_KIND_DIRECT 1   /* operands straight from memory; any size/stride  */
 #define MPGEMM_KIND_SCALE 2    /* C <- beta*C only (alpha == 0 or K == 0)         */
 #define MPGEMM_KIND_NONE 3     /* nothing to do (M == 0 or N == 0)                */
-#define MPGEMM_KIND_PIPE 4     /* LDS ring filled by direct-to-LDS copies, B read
-                                  with the transposing LDS load; the fast path    */
+#define MPGEMM_KIND_PIPE 4     /* LDS ring filled by direct-to-LDS copies; operands
+                                  stored along M or N read with the transposing
+                                  LDS load; the fast path                         */
 
 /* One entry of the kernel-config table, as reported by the factory. */
 typedef struct mpgemm_config {
@@ -78,6 +87,9 @@ typedef struct mpgemm_config {
     int32_t threads;     /* threads per workgroup                                 */
     int32_t lds_bytes;   /* LDS per workgroup                                     */
     int64_t grid;        /* workgroups for the queried shape (0 in the table)     */
+    int32_t layout_a;    /* storage order of A the entry reads (MPGEMM_*_MAJOR)   */
+    int32_t layout_b;    /* storage order of B; the direct and scale kernels take
+                            any order and report the one they were asked for     */
 } mpgemm_config;
 
 /*
@@ -120,6 +132,48 @@ int mpgemm_f16f32_with_config(int config_id,
                               float alpha, float beta,
                               void *stream);
 
+/*
+ * The GEMM with A and/or B stored column-major, as the operands of the
+ * independent gate of "Capstone 4: a tensor-core GEMM" (section
+ * "Independent gate": A row-major, B column-major, C row-major):
+ *     layout_a == MPGEMM_ROW_MAJOR: A[i][k] at A[i*lda + k], lda >= max(1,K)
+ *     layout_a == MPGEMM_COL_MAJOR: A[i][k] at A[k*lda + i], lda >= max(1,M)
+ *     layout_b == MPGEMM_ROW_MAJOR: B[k][j] at B[k*ldb + j], ldb >= max(1,N)
+ *     layout_b == MPGEMM_COL_MAJOR: B[k][j] at B[j*ldb + k], ldb >= max(1,K)
+ * Everything else (C, alpha, beta, alignment, errors, ownership) is as for
+ * mpgemm_f16f32, which is this call with (MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR).
+ * A layout value other than the two above returns MPGEMM_ELAYOUT.
+ */
+int mpgemm_f16f32_layout(int layout_a, int layout_b,
+                         int64_t M, int64_t N, int64_t K,
+                         const uint16_t *A, int64_t lda,
+                         const uint16_t *B, int64_t ldb,
+                         float *C, int64_t ldc,
+                         float alpha, float beta,
+                         void *stream);
+
+/* The factory's choice for mpgemm_f16f32_layout (no launch, no HIP call). */
+int mpgemm_f16f32_layout_query(int layout_a, int layout_b,
+                               int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda,
+                               const uint16_t *B, int64_t ldb,
+                               const float *C, int64_t ldc,
+                               float alpha, float beta,
+                               mpgemm_config *out);
+
+/*
+ * mpgemm_f16f32_layout forced onto table entry `config_id`.  MPGEMM_ECONFIG
+ * if the entry was compiled for other storage orders (its layout_a and
+ * layout_b fields) or cannot run these arguments.
+ */
+int mpgemm_f16f32_layout_with_config(int config_id, int layout_a, int layout_b,
+                                     int64_t M, int64_t N, int64_t K,
+                                     const uint16_t *A, int64_t lda,
+                                     const uint16_t *B, int64_t ldb,
+                                     float *C, int64_t ldc,
+                                     float alpha, float beta,
+                                     void *stream);
+
 /* Number of entries in the config table. */
 int mpgemm_num_configs(void);
 
@@ -141,7 +195,7 @@ int mpgemm_probe_mfma_layout(int shape, float *out, void *stream);
 /* Static text for an error code (never NULL). */
 const char *mpgemm_strerror(int code);
 
-/* Library version string, e.g. "mpgemm 0.1.0 gfx950". */
+/* Library version string, e.g. "mpgemm 0.2.0 gfx950". */
 const char *mpgemm_version(void);
 
 #ifdef __cplusplus

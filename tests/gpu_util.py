@@ -140,3 +140,32 @@ def freivalds_ok(got, A, B, C0, alpha, beta, seed=0):
     err = np.abs(lhs - rhs)
     ok = bool(np.all(err <= bound))
     return ok, float(np.max(err / bound))
+
+
+def stored(X, col_major):
+    """Logical (rows, cols) host tensor -> the tensor as stored: itself
+    (row-major) or its transpose, contiguous (column-major)."""
+    return X.t().contiguous() if col_major else X
+
+
+def run_layout(A, B, C0, alpha, beta, layout_a, layout_b, config=None, lda=None, ldb=None,
+               ldc=None, a_off=0, b_off=0, poison=True):
+    """Like run(), with A and/or B stored column-major.  A (M,K) and B (K,N)
+    are the logical host matrices; a column-major operand is stored as its
+    transpose (leading dimension lda >= M or ldb >= K) and handed to the
+    library as the transposed view, so the binding reads the storage order
+    from the strides."""
+    M, K = A.shape
+    N = B.shape[1]
+    gA = Guarded(stored(A, layout_a), ld=lda, offset=a_off)
+    gB = Guarded(stored(B, layout_b), ld=ldb, offset=b_off)
+    if C0 is None:
+        gC = Guarded(torch.zeros((M, N), dtype=torch.float32), ld=ldc,
+                     fill=float("nan") if poison else 0.0)
+    else:
+        gC = Guarded(C0, ld=ldc)
+    a_view = gA.view().t() if layout_a else gA.view()
+    b_view = gB.view().t() if layout_b else gB.view()
+    mp.gemm(a_view, b_view, gC.view(), alpha, beta, config=config)
+    torch.cuda.synchronize()
+    return gC.result(), gC

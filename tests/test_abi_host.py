@@ -157,3 +157,74 @@ def test_factory_falls_back_to_direct_for_huge_strides():
         assert (c["bm"] * (1 << 23) + c["bk"]) * 2 < 0x7FFFFFF0
     c = q(300, 300, 64, lda=1 << 30)
     assert c["kind_name"] == "direct"
+
+
+# ----------------------------------------------------------------------------
+# Column-major operands
+# ----------------------------------------------------------------------------
+
+def ql(la, lb, M, N, K, A=FAKE_A, lda=None, B=FAKE_B, ldb=None, C=FAKE_C, ldc=None,
+       alpha=1.0, beta=0.0):
+    lda = max(M if la else K, 1) if lda is None else lda
+    ldb = max(K if lb else N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return mp.mpgemm_f16f32_layout_query(la, lb, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta)
+
+
+def code_l(*args, **kw):
+    try:
+        ql(*args, **kw)
+        return 0
+    except mp.MpgemmError as e:
+        return e.code
+
+
+@pytest.mark.parametrize("args,kw,expect", [
+    ((2, 0, 4, 4, 4), {}, mp.MPGEMM_ELAYOUT),
+    ((0, -1, 4, 4, 4), {}, mp.MPGEMM_ELAYOUT),
+    # column-major A: lda counts M, not K
+    ((1, 0, 8, 4, 4), dict(lda=7), mp.MPGEMM_ELD),
+    ((1, 0, 8, 4, 16), dict(lda=8), 0),
+    # column-major B: ldb counts K, not N
+    ((0, 1, 4, 8, 16), dict(ldb=15), mp.MPGEMM_ELD),
+    ((0, 1, 4, 32, 16), dict(ldb=16), 0),
+    ((1, 1, 4, 4, 4), dict(A=FAKE_A + 1), mp.MPGEMM_EALIGN),
+    ((1, 1, 4, 4, 4), dict(C=0), mp.MPGEMM_ENULL),
+])
+def test_layout_validation_codes(args, kw, expect):
+    assert code_l(*args, **kw) == expect
+
+
+def test_layout_launch_validates_before_hip():
+    rc = mp.mpgemm_f16f32_layout(3, 0, 4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0)
+    assert rc == mp.MPGEMM_ELAYOUT
+    rc = mp.mpgemm_f16f32_layout_with_config(32, 1, 0, 4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4,
+                                             1.0, 0.0, 0)
+    assert rc == mp.MPGEMM_ECONFIG  # a row-major entry asked to read a column-major A
+
+
+def test_every_layout_pair_has_pipelined_entries():
+    pairs = {}
+    for i in range(mp.mpgemm_num_configs()):
+        c = mp.mpgemm_config_info(i)
+        assert c["layout_a"] in (0, 1) and c["layout_b"] in (0, 1)
+        if c["kind_name"] == "tiled":
+            assert (c["layout_a"], c["layout_b"]) == (0, 0)
+        if c["kind_name"] == "pipe":
+            pairs.setdefault((c["layout_a"], c["layout_b"]), set()).add((c["bm"], c["bn"]))
+    for pair in [(0, 0), (0, 1), (1, 0), (1, 1)]:
+        assert {(256, 256), (128, 128), (64, 64)} <= pairs[pair], pair
+
+
+@pytest.mark.parametrize("la,lb", [(0, 1), (1, 0), (1, 1)])
+def test_layout_factory_choices(la, lb):
+    c = ql(la, lb, 8192, 8192, 8192)
+    assert (c["kind_name"], c["bm"], c["bn"], c["vec_a"], c["vec_b"]) == ("pipe", 256, 256, 8, 8)
+    assert (c["layout_a"], c["layout_b"]) == (la, lb) and c["grid"] == 1024
+    c = ql(la, lb, 2048, 2048, 2048)
+    assert (c["bm"], c["bn"], c["bk"]) == (128, 128, 128) and c["grid"] == 256
+    c = ql(la, lb, 1000, 800, 617, lda=(1001 if la else 617), ldb=(617 if lb else 800))
+    assert c["kind_name"] == "pipe" and (c["vec_a"], c["vec_b"]) == (1, 1)
+    # a stored stage beyond 32-bit offsets leaves only the 64-bit direct kernel
+    c = ql(la, lb, 300, 300, 64, lda=(1 << 30), ldb=(1 << 30))
+    assert c["kind_name"] == "direct" and (c["layout_a"], c["layout_b"]) == (la, lb)

@@ -101,7 +101,8 @@ def _tiled_and_direct_ids():
     ids = []
     for i in range(mp.mpgemm_num_configs()):
         c = mp.mpgemm_config_info(i)
-        if c["kind_name"] in ("tiled", "pipe", "direct"):
+        # row-major entries; the column-major ones have their own tests
+        if c["kind_name"] in ("tiled", "pipe", "direct") and (c["layout_a"], c["layout_b"]) == (0, 0):
             ids.append(i)
     return ids
 
