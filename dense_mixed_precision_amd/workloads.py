@@ -69,7 +69,7 @@ WORKLOADS = {
 }
 
 
-def _draw(g: torch.Generator, shape, dist: str, which: str) -> torch.Tensor:
+def _draw(g: torch.Generator, shape, dist: str, which: str, dtype=torch.float16) -> torch.Tensor:
     if dist == "uniform":
         x = torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
     elif dist == "normal4":
@@ -83,17 +83,20 @@ def _draw(g: torch.Generator, shape, dist: str, which: str) -> torch.Tensor:
         x = torch.zeros(shape, dtype=torch.float32)
     else:
         raise ValueError(f"unknown distribution {dist!r}")
-    return x.to(torch.float16)
+    return x.to(dtype)
 
 
 def make_inputs(M: int, N: int, K: int, dist: str = "uniform", seed: int = 0,
-                c_init: Optional[str] = None, dist_b: Optional[str] = None):
-    """Draw (A, B, C) on the CPU: A (M,K) fp16, B (K,N) fp16, C (M,N) fp32 or
-    None.  ``dist_b`` overrides the distribution of B."""
+                c_init: Optional[str] = None, dist_b: Optional[str] = None,
+                dtype=torch.float16):
+    """Draw (A, B, C) on the CPU: A (M,K) and B (K,N) in ``dtype`` (float16,
+    or bfloat16: the same float32 draw rounded to nearest-even into the
+    other format), C (M,N) fp32 or None.  ``dist_b`` overrides the
+    distribution of B."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
-    A = _draw(g, (M, K), dist, "A")
-    B = _draw(g, (K, N), dist_b or dist, "B")
+    A = _draw(g, (M, K), dist, "A", dtype)
+    B = _draw(g, (K, N), dist_b or dist, "B", dtype)
     C = None
     if c_init is not None:
         if c_init == "uniform":
@@ -105,14 +108,14 @@ def make_inputs(M: int, N: int, K: int, dist: str = "uniform", seed: int = 0,
     return A, B, C
 
 
-def workload_inputs(w: Workload):
-    return make_inputs(w.M, w.N, w.K, w.dist, w.seed, w.c_init)
+def workload_inputs(w: Workload, dtype=torch.float16):
+    return make_inputs(w.M, w.N, w.K, w.dist, w.seed, w.c_init, dtype=dtype)
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """FP16 tensor (CPU) -> numpy uint16 array of its bit patterns."""
-    if t.dtype != torch.float16:
-        raise TypeError("expected a float16 tensor")
+    """FP16 or BF16 tensor (CPU) -> numpy uint16 array of its bit patterns."""
+    if t.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("expected a float16 or bfloat16 tensor")
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
 

@@ -74,6 +74,14 @@ def _load():
     lib.oracle_gemm_layout.restype = ctypes.c_int
     lib.oracle_gemm_layout_entries.argtypes = [ctypes.c_int, ctypes.c_int] + lib.oracle_gemm_entries.argtypes
     lib.oracle_gemm_layout_entries.restype = ctypes.c_int
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_bf16_to_f64_array.argtypes = [vp, i64, vp]
+    lib.oracle_bf16_to_f64_array.restype = None
+    lib.oracle_gemm_bf16_layout.argtypes = lib.oracle_gemm_layout.argtypes
+    lib.oracle_gemm_bf16_layout.restype = ctypes.c_int
+    lib.oracle_gemm_bf16_layout_entries.argtypes = lib.oracle_gemm_layout_entries.argtypes
+    lib.oracle_gemm_bf16_layout_entries.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -90,12 +98,13 @@ def _ptr(a):
 
 
 def _as_bits_2d(x, name):
-    """Return (array, leading dimension) for a 2-D uint16 row-major view."""
+    """Return (array, leading dimension) for a 2-D uint16 row-major view
+    (FP16 or BF16 bit patterns)."""
     x = np.asarray(x)
     if x.dtype == np.float16:
         x = x.view(np.uint16)
     if x.dtype != np.uint16 or x.ndim != 2:
-        raise TypeError(f"{name} must be a 2-D float16 or uint16 (FP16 bits) array")
+        raise TypeError(f"{name} must be a 2-D float16 or uint16 (16-bit patterns) array")
     if x.size == 0:
         return np.zeros(x.shape, dtype=np.uint16), max(x.shape[1], 1)
     # a dimension of extent 1 has no meaningful stride (numpy may report any)
@@ -147,35 +156,58 @@ def _operands(A, B, layout_a, layout_b):
     return A, lda, B, ldb, M, N, K
 
 
+def bf16_to_f64(bits) -> np.ndarray:
+    """Decode BF16 bit patterns to FP64 with the oracle's own decoder."""
+    bits = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().oracle_bf16_to_f64_array(_ptr(bits), bits.size, _ptr(out))
+    return out
+
+
+#: Input formats of A and B: "f16" (IEEE binary16) or "bf16" (bfloat16).
+IN_TYPES = ("f16", "bf16")
+
+
+def _entry_points(in_type):
+    lib = _load()
+    if in_type == "f16":
+        return lib.oracle_gemm_layout, lib.oracle_gemm_layout_entries
+    if in_type == "bf16":
+        return lib.oracle_gemm_bf16_layout, lib.oracle_gemm_bf16_layout_entries
+    raise ValueError(f"in_type must be one of {IN_TYPES}")
+
+
 def _check(rc):
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
 
 
 def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0,
-         layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR):
+         layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR, in_type: str = "f16"):
     """Full product.  Returns ``(ref, absdot)``, both float64 (M, N).
 
-    A: FP16 bits stored (M, K) (row-major) or (K, M) (``layout_a=COL_MAJOR``);
-    B: stored (K, N) or (N, K) (``layout_b=COL_MAJOR``); C: (M, N) float32
-    or None.  alpha and beta are rounded to float32 first, as the GPU entry
-    point receives them.
+    A: 16-bit patterns (FP16, or BF16 with ``in_type="bf16"``) stored (M, K)
+    (row-major) or (K, M) (``layout_a=COL_MAJOR``); B: stored (K, N) or (N, K)
+    (``layout_b=COL_MAJOR``); C: (M, N) float32 or None.  alpha and beta are
+    rounded to float32 first, as the GPU entry point receives them.
     """
+    full, _ = _entry_points(in_type)
     A, lda, B, ldb, M, N, K = _operands(A, B, layout_a, layout_b)
     alpha = float(np.float32(alpha))
     beta = float(np.float32(beta))
     C, ldc = _as_c(C, M, N, beta)
     ref = np.empty((M, N), dtype=np.float64)
     absdot = np.empty((M, N), dtype=np.float64)
-    _check(_load().oracle_gemm_layout(layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B), ldb,
-                                      _ptr(C), ldc, alpha, beta, _ptr(ref), _ptr(absdot)))
+    _check(full(layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B), ldb,
+                _ptr(C), ldc, alpha, beta, _ptr(ref), _ptr(absdot)))
     return ref, absdot
 
 
 def gemm_entries(A, B, C, alpha: float, beta: float, rows, cols,
-                 layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR):
+                 layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR, in_type: str = "f16"):
     """Selected entries (rows[t], cols[t]).  Returns ``(ref, absdot)`` 1-D.
     Operands as for :func:`gemm`."""
+    _, entries = _entry_points(in_type)
     A, lda, B, ldb, M, N, K = _operands(A, B, layout_a, layout_b)
     alpha = float(np.float32(alpha))
     beta = float(np.float32(beta))
@@ -186,9 +218,9 @@ def gemm_entries(A, B, C, alpha: float, beta: float, rows, cols,
         raise ValueError("rows and cols must be 1-D and equal length")
     ref = np.empty(rows.shape, dtype=np.float64)
     absdot = np.empty(rows.shape, dtype=np.float64)
-    _check(_load().oracle_gemm_layout_entries(layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B), ldb,
-                                              _ptr(C), ldc, alpha, beta, rows.size, _ptr(rows),
-                                              _ptr(cols), _ptr(ref), _ptr(absdot)))
+    _check(entries(layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B), ldb,
+                   _ptr(C), ldc, alpha, beta, rows.size, _ptr(rows),
+                   _ptr(cols), _ptr(ref), _ptr(absdot)))
     return ref, absdot
 
 

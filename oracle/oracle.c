@@ -23,6 +23,13 @@
  *   - beta == 0 means C is not read at all (the output may hold NaN poison,
  *     "02_mixed_precision_gemm", Verification).
  *
+ * BF16 inputs (the other 16-bit tensor-core input type "Tensor cores with
+ * WMMA" lists, section "A warp owns a tile, and no thread owns an element")
+ * go through the *_bf16_* entry points: the same product, with each input
+ * decoded from the bfloat16 format instead (8 significant bits; products of
+ * two are exact in FP64 just the same, and every finite BF16 value and
+ * product is in FP64's range).
+ *
  * Arithmetic: an FP16 value is an integer times 2^-24 with at most 11
  * significant bits, so its FP64 widening is exact and every product of two
  * widened values is exact in FP64 (22 significant bits).  Only the running
@@ -71,11 +78,41 @@ void oracle_f16_to_f64_array(const uint16_t *h, int64_t n, double *out)
 }
 
 /*
+ * bfloat16 -> binary64, from the format's definition: the upper half of an
+ * IEEE binary32, i.e. 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+ *   exponent 0      : zero or subnormal, value = fraction * 2^-133
+ *   exponent 1..254 : normal, value = (128 + fraction) * 2^(exponent - 134)
+ *   exponent 255    : infinity (fraction 0) or NaN (fraction != 0)
+ */
+double oracle_bf16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int exponent = (h >> 7) & 0xff;
+    const int fraction = h & 0x7f;
+    double v;
+    if (exponent == 0) {
+        v = ldexp((double)fraction, -133);
+    } else if (exponent == 255) {
+        v = (fraction == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(128 + fraction), exponent - 134);
+    }
+    return sign ? -v : v;
+}
+
+void oracle_bf16_to_f64_array(const uint16_t *h, int64_t n, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_to_f64(h[i]);
+}
+
+/*
  * Element strides of the two operands: A[i][k] is A[i*a_i + k*a_k] and
  * B[k][j] is B[k*b_k + j*b_j].
  */
 typedef struct {
     int64_t a_i, a_k, b_k, b_j;
+    double (*decode)(uint16_t);  /* FP16 or BF16 bits -> FP64 */
 } strides_t;
 
 #define ORACLE_ROW_MAJOR 0
@@ -88,6 +125,7 @@ static strides_t strides_for(int layout_a, int layout_b, int64_t lda, int64_t ld
     t.a_k = layout_a == ORACLE_COL_MAJOR ? lda : 1;
     t.b_k = layout_b == ORACLE_COL_MAJOR ? 1 : ldb;
     t.b_j = layout_b == ORACLE_COL_MAJOR ? ldb : 1;
+    t.decode = oracle_f16_to_f64;
     return t;
 }
 
@@ -105,8 +143,8 @@ static void entry(int64_t i, int64_t j, int64_t K,
     double s = 0.0;
     double s_abs = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        const double a = oracle_f16_to_f64(A[i * st.a_i + k * st.a_k]);
-        const double b = oracle_f16_to_f64(B[k * st.b_k + j * st.b_j]);
+        const double a = st.decode(A[i * st.a_i + k * st.a_k]);
+        const double b = st.decode(B[k * st.b_k + j * st.b_j]);
         const double p = a * b; /* exact */
         s += p;
         s_abs += fabs(p);
@@ -154,20 +192,22 @@ static int check_args(int layout_a, int layout_b, int64_t M, int64_t N, int64_t 
  * (absdot may be NULL) are M x N, row-major, packed (leading dimension N),
  * owned by the caller.
  */
-int oracle_gemm_layout(int layout_a, int layout_b,
-                       int64_t M, int64_t N, int64_t K,
-                       const uint16_t *A, int64_t lda,
-                       const uint16_t *B, int64_t ldb,
-                       const float *C, int64_t ldc,
-                       double alpha, double beta,
-                       double *ref, double *absdot)
+static int gemm_full(int bf16, int layout_a, int layout_b,
+                     int64_t M, int64_t N, int64_t K,
+                     const uint16_t *A, int64_t lda,
+                     const uint16_t *B, int64_t ldb,
+                     const float *C, int64_t ldc,
+                     double alpha, double beta,
+                     double *ref, double *absdot)
 {
     const int rc = check_args(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, beta);
     if (rc != ORACLE_OK)
         return rc;
     if (M > 0 && N > 0 && ref == NULL)
         return ORACLE_ENULL;
-    const strides_t st = strides_for(layout_a, layout_b, lda, ldb);
+    strides_t st = strides_for(layout_a, layout_b, lda, ldb);
+    if (bf16)
+        st.decode = oracle_bf16_to_f64;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < M; ++i) {
         for (int64_t j = 0; j < N; ++j) {
@@ -176,6 +216,31 @@ int oracle_gemm_layout(int layout_a, int layout_b,
         }
     }
     return ORACLE_OK;
+}
+
+int oracle_gemm_layout(int layout_a, int layout_b,
+                       int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda,
+                       const uint16_t *B, int64_t ldb,
+                       const float *C, int64_t ldc,
+                       double alpha, double beta,
+                       double *ref, double *absdot)
+{
+    return gemm_full(0, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                     ref, absdot);
+}
+
+/* The same product with BF16 inputs. */
+int oracle_gemm_bf16_layout(int layout_a, int layout_b,
+                            int64_t M, int64_t N, int64_t K,
+                            const uint16_t *A, int64_t lda,
+                            const uint16_t *B, int64_t ldb,
+                            const float *C, int64_t ldc,
+                            double alpha, double beta,
+                            double *ref, double *absdot)
+{
+    return gemm_full(1, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                     ref, absdot);
 }
 
 /* Full product, A and B row-major. */
@@ -194,14 +259,14 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
  * Selected entries only: element t of the output is (rows[t], cols[t]).
  * Used where the full product would take too long on the CPU.
  */
-int oracle_gemm_layout_entries(int layout_a, int layout_b,
-                               int64_t M, int64_t N, int64_t K,
-                               const uint16_t *A, int64_t lda,
-                               const uint16_t *B, int64_t ldb,
-                               const float *C, int64_t ldc,
-                               double alpha, double beta,
-                               int64_t count, const int64_t *rows, const int64_t *cols,
-                               double *ref, double *absdot)
+static int gemm_entries(int bf16, int layout_a, int layout_b,
+                        int64_t M, int64_t N, int64_t K,
+                        const uint16_t *A, int64_t lda,
+                        const uint16_t *B, int64_t ldb,
+                        const float *C, int64_t ldc,
+                        double alpha, double beta,
+                        int64_t count, const int64_t *rows, const int64_t *cols,
+                        double *ref, double *absdot)
 {
     const int rc = check_args(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, beta);
     if (rc != ORACLE_OK)
@@ -212,13 +277,41 @@ int oracle_gemm_layout_entries(int layout_a, int layout_b,
         if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)
             return ORACLE_EBADDIM;
     }
-    const strides_t st = strides_for(layout_a, layout_b, lda, ldb);
+    strides_t st = strides_for(layout_a, layout_b, lda, ldb);
+    if (bf16)
+        st.decode = oracle_bf16_to_f64;
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t t = 0; t < count; ++t) {
         entry(rows[t], cols[t], K, A, B, st, C, ldc, alpha, beta,
               &ref[t], absdot ? &absdot[t] : NULL);
     }
     return ORACLE_OK;
+}
+
+int oracle_gemm_layout_entries(int layout_a, int layout_b,
+                               int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda,
+                               const uint16_t *B, int64_t ldb,
+                               const float *C, int64_t ldc,
+                               double alpha, double beta,
+                               int64_t count, const int64_t *rows, const int64_t *cols,
+                               double *ref, double *absdot)
+{
+    return gemm_entries(0, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                        count, rows, cols, ref, absdot);
+}
+
+int oracle_gemm_bf16_layout_entries(int layout_a, int layout_b,
+                                    int64_t M, int64_t N, int64_t K,
+                                    const uint16_t *A, int64_t lda,
+                                    const uint16_t *B, int64_t ldb,
+                                    const float *C, int64_t ldc,
+                                    double alpha, double beta,
+                                    int64_t count, const int64_t *rows, const int64_t *cols,
+                                    double *ref, double *absdot)
+{
+    return gemm_entries(1, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                        count, rows, cols, ref, absdot);
 }
 
 /* Selected entries, A and B row-major. */

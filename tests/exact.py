@@ -16,11 +16,21 @@ def f16_exact(bits_2d):
     return [[Fraction(float(v)) for v in row] for row in vals]
 
 
-def exact_gemm(A_bits, B_bits, C=None, alpha=1.0, beta=0.0):
+def bf16_exact(bits_2d):
+    """BF16 bit patterns -> nested lists of exact Fractions (via torch's own
+    bfloat16 -> float64 conversion, a library routine)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(bits_2d, dtype=np.uint16)).view(np.int16))
+    vals = t.view(torch.bfloat16).to(torch.float64).numpy()
+    return [[Fraction(float(v)) for v in row] for row in vals]
+
+
+def exact_gemm(A_bits, B_bits, C=None, alpha=1.0, beta=0.0, in_type="f16"):
     """Exact result and exact sum|a*b| as float64 arrays (rounded once at the
     end, to nearest) plus the exact Fractions for callers that need them."""
-    A = f16_exact(A_bits)
-    B = f16_exact(B_bits)
+    decode = bf16_exact if in_type == "bf16" else f16_exact
+    A = decode(A_bits)
+    B = decode(B_bits)
     M, K = len(A), (len(A[0]) if A else 0)
     N = len(B[0]) if B else np.asarray(B_bits).shape[1]
     fa = Fraction(float(np.float32(alpha)))

@@ -328,6 +328,104 @@ def test_layout_ignored_is_caught():
 
 
 # ----------------------------------------------------------------------------
+# BF16 inputs ("Tensor cores with WMMA", section "A warp owns a tile, and no
+# thread owns an element": bf16 is the other 16-bit tensor-core input type)
+# ----------------------------------------------------------------------------
+
+def test_bf16_decoder_exhaustive_matches_torch():
+    """All 65,536 bit patterns against torch's bfloat16 -> float64 conversion."""
+    import torch
+    ref = torch.from_numpy(ALL_CODES.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.bf16_to_f64(ALL_CODES)
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.array_equal(got[~both_nan], ref[~both_nan]) and np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+def test_bf16_decoder_format_values():
+    """Values fixed by the format itself (bias 127, 7 fraction bits)."""
+    v = oracle.bf16_to_f64(np.array([0x3F80, 0xBF80, 0x4000, 0x3F00, 0x0080, 0x0001, 0x7F7F, 0x8000],
+                                    dtype=np.uint16))
+    assert v.tolist() == [1.0, -1.0, 2.0, 0.5, 2.0 ** -126, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127, -0.0]
+
+
+def _bf16_bits(X):
+    import torch
+    return X.to(torch.bfloat16).contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_special_mix(M, K, seed):
+    """BF16 bits mixing uniform values with subnormals and far-apart
+    exponents, so every decoder branch and a wide exponent range feed the sum."""
+    import torch
+    rng = np.random.default_rng(seed)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x3F80, 0xBF80,
+                         0x7F7F, 0xFF7F, 0x5000, 0x2000], dtype=np.uint16)
+    base = _bf16_bits(torch.rand(M, K, generator=torch.Generator().manual_seed(seed)) * 2 - 1)
+    mask = rng.random((M, K)) < 0.3
+    pick = specials[rng.integers(0, specials.size, (M, K))]
+    return np.where(mask, pick, base).astype(np.uint16)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (17, 15, 33), (33, 31, 65)])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (1.5, 0.5)])
+def test_bf16_brute_force_exact(M, N, K, alpha, beta):
+    A, B, C = make_inputs(M, N, K, "uniform", seed=3 * M + N + K, c_init="uniform", dtype=torch_bf16())
+    Ab, Bb, Cn = bits(A), bits(B), C.numpy()
+    ref, absdot = oracle.gemm(Ab, Bb, Cn, alpha, beta, in_type="bf16")
+    eref, eabs, _ = exact_gemm(Ab, Bb, Cn, alpha, beta, in_type="bf16")
+    assert np.all(np.abs(ref - eref) <= fp64_sum_bound(K, alpha, beta, eabs, Cn))
+    assert np.allclose(absdot, eabs, rtol=K * 2.0 ** -52, atol=0)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 16), (9, 11, 40)])
+def test_bf16_brute_force_special_values(M, N, K):
+    Ab = _bf16_special_mix(M, K, seed=M * 10 + K)
+    Bb = _bf16_special_mix(K, N, seed=N * 10 + K + 1)
+    ref, _ = oracle.gemm(Ab, Bb, in_type="bf16")
+    eref, eabs, _ = exact_gemm(Ab, Bb, in_type="bf16")
+    assert np.all(np.abs(ref - eref) <= fp64_sum_bound(K, 1.0, 0.0, eabs))
+
+
+def test_bf16_matches_f16_where_both_are_exact():
+    """Small integers are exact in both formats: the two decoders must give
+    the same values, so the two products agree bit for bit."""
+    M, N, K = 41, 37, 300
+    A, B, _ = make_inputs(M, N, K, "smallint", seed=19)
+    r16, s16 = oracle.gemm(bits(A), bits(B))
+    rbf, sbf = oracle.gemm(_bf16_bits(A.float()), _bf16_bits(B.float()), in_type="bf16")
+    assert np.array_equal(r16, rbf) and np.array_equal(s16, sbf)
+    ints = A.numpy().astype(np.int64) @ B.numpy().astype(np.int64)
+    assert np.array_equal(rbf, ints.astype(np.float64))
+
+
+def test_bf16_all_ones_and_layouts():
+    M, N, K = 30, 20, 77
+    A, B, _ = make_inputs(M, N, K, "ones", seed=1, dtype=torch_bf16())
+    ref, _ = oracle.gemm(bits(A), bits(B), in_type="bf16")
+    assert np.all(ref == K)
+    A, B, C = make_inputs(M, N, K, "uniform", seed=20, c_init="uniform", dtype=torch_bf16())
+    r0, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 1.5, 0.5, in_type="bf16")
+    for la, lb in LAYOUTS:
+        r1, _ = oracle.gemm(_stored(bits(A), la), _stored(bits(B), lb), C.numpy(), 1.5, 0.5,
+                            layout_a=la, layout_b=lb, in_type="bf16")
+        assert np.array_equal(r0, r1)
+
+
+def test_bf16_read_as_f16_is_caught():
+    """Decoding BF16 bits with the FP16 decoder (a plausible slip) fails the
+    exact pin."""
+    A, B, _ = make_inputs(9, 7, 13, "uniform", seed=21, dtype=torch_bf16())
+    wrong, _ = oracle.gemm(bits(A), bits(B))   # in_type left at "f16"
+    eref, eabs, _ = exact_gemm(bits(A), bits(B), in_type="bf16")
+    assert not np.all(np.abs(wrong - eref) <= fp64_sum_bound(13, 1.0, 0.0, eabs))
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
+
+
+# ----------------------------------------------------------------------------
 # The acceptance rule
 # ----------------------------------------------------------------------------
 
