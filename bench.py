@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-others", action="store_true", help="time only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-power", dest="power", action="store_false",
+                   help="skip the amd-smi power/clock sample under sustained 8192^3 load")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="after timing, run one plain device copy of this many MiB (a known-size "
                         "kernel for scaling the HBM byte counters of a rocprofv3 --pmc run)")
@@ -88,12 +90,16 @@ def measured_traffic(workload: str, kernel_ms: float):
             "GBps": round((read_b + write_b) / (kernel_ms * 1e-3) / 1e9, 1), "source": os.path.relpath(path, ROOT)}
 
 
-def time_workload(w, steps, warmup, torch, mp):
+def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0):
+    """Time `steps` launches (after `warmup`) on resident inputs.  A column-
+    major operand is stored transposed on the device and passed as the
+    transposed view."""
     from dense_mixed_precision_amd.workloads import workload_inputs
 
     dev = torch.device("cuda:0")
     A, B, C = workload_inputs(w)
-    Ad, Bd = A.to(dev), B.to(dev)
+    Ad = A.t().contiguous().to(dev).t() if layout_a else A.to(dev)
+    Bd = B.t().contiguous().to(dev).t() if layout_b else B.to(dev)
     Cd = C.to(dev) if C is not None else torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     cfg = mp.query_for(Ad, Bd, Cd, w.alpha, w.beta)
@@ -116,6 +122,59 @@ def time_workload(w, steps, warmup, torch, mp):
     wall_ms = (t1 - t0) * 1e3 / steps
     kern_ms = ev0.elapsed_time(ev1) / steps
     return {"A": A, "B": B, "C": C, "Cd": Cd, "cfg": cfg, "wall_ms": wall_ms, "kernel_ms": kern_ms}
+
+
+def _smi_power():
+    """Socket power (W) and mean graphics clock (MHz) from amd-smi, or None."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", "0"], capture_output=True,
+                             text=True, timeout=20).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    power = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", out)
+    clocks = [float(x) for x in re.findall(r"^\s*CLK:\s*([0-9.]+)\s*MHz", out, re.M)]
+    if not power:
+        return None
+    return {"socket_w": float(power[0]),
+            "gfx_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None}
+
+
+def sample_power(w, torch, mp, seconds=2.0):
+    """Run workload `w` back to back for `seconds` and read socket power and
+    the graphics clock in the middle of the run (outside any timed region):
+    evidence for how far the board's power limit pulls the clock down under
+    sustained matrix-core load."""
+    import threading
+
+    from dense_mixed_precision_amd.workloads import workload_inputs
+
+    dev = torch.device("cuda:0")
+    A, B, C = workload_inputs(w)
+    Ad, Bd = A.to(dev), B.to(dev)
+    Cd = C.to(dev) if C is not None else torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    idle = _smi_power()
+    stop = time.perf_counter() + seconds
+    count = [0]
+
+    def loop():
+        while time.perf_counter() < stop:
+            for _ in range(10):
+                mp.gemm(Ad, Bd, Cd, w.alpha, w.beta)
+            torch.cuda.synchronize()
+            count[0] += 10
+
+    t0 = time.perf_counter()
+    th = threading.Thread(target=loop)
+    th.start()
+    time.sleep(seconds * 0.6)
+    busy = _smi_power()
+    th.join()
+    dt = time.perf_counter() - t0
+    return {"workload": w.name, "idle": idle, "busy": busy,
+            "tflops_during_sample": round(w.flop * count[0] / dt / 1e12, 1),
+            "source": "amd-smi metric -p -c (SOCKET_POWER, graphics CLK of each XCD)"}
 
 
 def roofline_entry(w, kernel_ms):
@@ -239,7 +298,25 @@ def main():
                             "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "vec_a", "vec_b", "grid")}}
             del r
             torch.cuda.empty_cache()
+        # the column-major operand modes on the two headline shapes
+        for base in ("square2048", "square8192"):
+            w = WORKLOADS[base]
+            for la, lb, tag in ((0, 1, "Bcol"), (1, 1, "AcolBcol")):
+                name = f"{base}_{tag}"
+                steps = max(5, min(args.steps, 20 if w.flop > 1e12 else args.steps))
+                print(f"# timing {name} ({steps} steps)", file=sys.stderr, flush=True)
+                r = time_workload(w, steps, max(3, args.warmup // 2), torch, mp, la, lb)
+                others[name] = {"tflops": round(w.flop / (r["kernel_ms"] * 1e-3) / 1e12, 2),
+                                "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
+                                "layout": {"A": "col" if la else "row", "B": "col" if lb else "row"},
+                                "pct_of_peak": round(100 * w.flop / (r["kernel_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
+                                "roofline": roofline_entry(w, r["kernel_ms"]),
+                                "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "bk", "vec_a", "vec_b", "grid")}}
+                del r
+                torch.cuda.empty_cache()
         line["workloads"] = others
+    if args.power:
+        line["power"] = sample_power(WORKLOADS["square8192"], torch, mp)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(head, res, args.cpu_seconds)

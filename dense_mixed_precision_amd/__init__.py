@@ -14,12 +14,14 @@ integers holding device addresses, ``stream`` a hipStream_t as an integer,
     mpgemm_f16f32_layout(layout_a, layout_b, M, N, K, ...) -> int   (A and/or B column-major)
     mpgemm_f16f32_layout_query(layout_a, layout_b, M, N, K, ...) -> dict
     mpgemm_f16f32_layout_with_config(cfg, layout_a, layout_b, M, N, K, ...) -> int
+    mpgemm_bf16f32, mpgemm_bf16f32_layout, mpgemm_bf16f32_layout_query,
+    mpgemm_bf16f32_layout_with_config: the same with BF16 inputs
     mpgemm_num_configs(), mpgemm_config_info(id), mpgemm_probe_mfma_layout(shape, out, stream)
     mpgemm_strerror(code), mpgemm_version()
 
 Tensor convenience: ``gemm(A, B, C, alpha, beta)`` for torch tensors on the
-GPU (A, B float16, each row- or column-major, e.g. a transposed view; C
-float32 row-major), launched on torch's current stream.
+GPU (A, B both float16 or both bfloat16, each row- or column-major, e.g. a
+transposed view; C float32 row-major), launched on torch's current stream.
 """
 from __future__ import annotations
 
@@ -33,6 +35,8 @@ from ._binding import (  # noqa: F401
     MPGEMM_ENULL,
     MPGEMM_OK,
     MPGEMM_COL_MAJOR,
+    MPGEMM_IN_BF16,
+    MPGEMM_IN_F16,
     MPGEMM_ROW_MAJOR,
     MpgemmError,
     config_fields,
@@ -46,6 +50,10 @@ from ._binding import (  # noqa: F401
     mpgemm_f16f32_layout,
     mpgemm_f16f32_layout_query,
     mpgemm_f16f32_layout_with_config,
+    mpgemm_bf16f32,
+    mpgemm_bf16f32_layout,
+    mpgemm_bf16f32_layout_query,
+    mpgemm_bf16f32_layout_with_config,
     mpgemm_num_configs,
     mpgemm_probe_mfma_layout,
     mpgemm_strerror,

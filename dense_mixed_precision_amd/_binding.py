@@ -19,12 +19,16 @@ MPGEMM_ELAYOUT = -7
 MPGEMM_ROW_MAJOR = 0
 MPGEMM_COL_MAJOR = 1
 
+MPGEMM_IN_F16 = 0
+MPGEMM_IN_BF16 = 1
+
 
 class MpgemmConfig(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "id", "kind", "bm", "bn", "bk", "waves_m", "waves_n", "wave_m", "wave_n",
         "mfma_m", "mfma_n", "mfma_k", "vec_a", "vec_b", "stages", "threads", "lds_bytes")] + [
-        ("grid", ctypes.c_int64), ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32)]
+        ("grid", ctypes.c_int64), ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32),
+        ("in_type", ctypes.c_int32)]
 
 
 config_fields = [f[0] for f in MpgemmConfig._fields_]
@@ -68,6 +72,16 @@ def load():
     lib.mpgemm_f16f32_layout_query.restype = i32
     lib.mpgemm_f16f32_layout_with_config.argtypes = [i32, i32, i32] + gemm_args + [vp]
     lib.mpgemm_f16f32_layout_with_config.restype = i32
+    for dt in ("bf16",):
+        getattr(lib, f"mpgemm_{dt}f32").argtypes = gemm_args + [vp]
+        getattr(lib, f"mpgemm_{dt}f32").restype = i32
+        getattr(lib, f"mpgemm_{dt}f32_layout").argtypes = [i32, i32] + gemm_args + [vp]
+        getattr(lib, f"mpgemm_{dt}f32_layout").restype = i32
+        getattr(lib, f"mpgemm_{dt}f32_layout_query").argtypes = [i32, i32] + gemm_args + [
+            ctypes.POINTER(MpgemmConfig)]
+        getattr(lib, f"mpgemm_{dt}f32_layout_query").restype = i32
+        getattr(lib, f"mpgemm_{dt}f32_layout_with_config").argtypes = [i32, i32, i32] + gemm_args + [vp]
+        getattr(lib, f"mpgemm_{dt}f32_layout_with_config").restype = i32
     lib.mpgemm_num_configs.argtypes = []
     lib.mpgemm_num_configs.restype = i32
     lib.mpgemm_config_info.argtypes = [i32, ctypes.POINTER(MpgemmConfig)]
@@ -131,6 +145,32 @@ def mpgemm_f16f32_layout_with_config(config_id, layout_a, layout_b, M, N, K, A, 
                                                        lda, B, ldb, C, ldc, alpha, beta, stream))
 
 
+def mpgemm_bf16f32(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream=0) -> int:
+    return int(load().mpgemm_bf16f32(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream))
+
+
+def mpgemm_bf16f32_layout(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                          stream=0) -> int:
+    return int(load().mpgemm_bf16f32_layout(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc,
+                                            alpha, beta, stream))
+
+
+def mpgemm_bf16f32_layout_query(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha,
+                                beta) -> dict:
+    out = MpgemmConfig()
+    rc = load().mpgemm_bf16f32_layout_query(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc,
+                                            alpha, beta, ctypes.byref(out))
+    if rc != MPGEMM_OK:
+        raise MpgemmError(rc, "mpgemm_bf16f32_layout_query")
+    return _cfg_dict(out)
+
+
+def mpgemm_bf16f32_layout_with_config(config_id, layout_a, layout_b, M, N, K, A, lda, B, ldb, C,
+                                      ldc, alpha, beta, stream=0) -> int:
+    return int(load().mpgemm_bf16f32_layout_with_config(config_id, layout_a, layout_b, M, N, K, A,
+                                                        lda, B, ldb, C, ldc, alpha, beta, stream))
+
+
 def mpgemm_num_configs() -> int:
     return int(load().mpgemm_num_configs())
 
@@ -183,8 +223,9 @@ def _check_tensor(t, name, dtype, allow_col_major=False):
 
 def _args(A, B, C):
     import torch
-    la, lda = _check_tensor(A, "A", torch.float16, allow_col_major=True)
-    lb, ldb = _check_tensor(B, "B", torch.float16, allow_col_major=True)
+    dt = A.dtype if isinstance(A, torch.Tensor) and A.dtype == torch.bfloat16 else torch.float16
+    la, lda = _check_tensor(A, "A", dt, allow_col_major=True)
+    lb, ldb = _check_tensor(B, "B", dt, allow_col_major=True)
     _, ldc = _check_tensor(C, "C", torch.float32)
     M, K = A.shape
     K2, N = B.shape
@@ -193,12 +234,17 @@ def _args(A, B, C):
     return M, N, K, la, lda, lb, ldb, ldc
 
 
+def _in_type(A):
+    import torch
+    return MPGEMM_IN_BF16 if A.dtype == torch.bfloat16 else MPGEMM_IN_F16
+
+
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, config: int | None = None, stream=None):
     """C <- alpha*A@B + beta*C in place on the GPU; returns C.
 
-    A (M x K) and B (K x N) may each be row-major or column-major (e.g. the
-    transpose view of a row-major tensor); the storage order is read from the
-    strides.  C must be row-major.
+    A (M x K) and B (K x N): both float16 or both bfloat16, each row-major or
+    column-major (e.g. the transpose view of a row-major tensor); the storage
+    order is read from the strides.  C must be float32 row-major.
     ``stream``: a torch.cuda.Stream or raw handle (default: current stream).
     ``config``: force a table entry (tests and sweeps)."""
     import torch
@@ -206,20 +252,23 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, config: int | None = No
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    bf16 = _in_type(A) == MPGEMM_IN_BF16
     if config is None:
-        rc = mpgemm_f16f32_layout(la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
-                                  C.data_ptr(), ldc, float(alpha), float(beta), handle)
+        fn = mpgemm_bf16f32_layout if bf16 else mpgemm_f16f32_layout
+        rc = fn(la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                float(alpha), float(beta), handle)
     else:
-        rc = mpgemm_f16f32_layout_with_config(int(config), la, lb, M, N, K, A.data_ptr(), lda,
-                                              B.data_ptr(), ldb, C.data_ptr(), ldc, float(alpha),
-                                              float(beta), handle)
+        fn = mpgemm_bf16f32_layout_with_config if bf16 else mpgemm_f16f32_layout_with_config
+        rc = fn(int(config), la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(),
+                ldc, float(alpha), float(beta), handle)
     if rc != MPGEMM_OK:
-        raise MpgemmError(rc, "mpgemm_f16f32_layout" if config is None else f"config {config}")
+        raise MpgemmError(rc, fn.__name__ if config is None else f"config {config}")
     return C
 
 
 def query_for(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> dict:
     """The factory's choice for these tensors (no launch)."""
     M, N, K, la, lda, lb, ldb, ldc = _args(A, B, C)
-    return mpgemm_f16f32_layout_query(la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
-                                      C.data_ptr(), ldc, float(alpha), float(beta))
+    fn = mpgemm_bf16f32_layout_query if _in_type(A) == MPGEMM_IN_BF16 else mpgemm_f16f32_layout_query
+    return fn(la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+              float(alpha), float(beta))

@@ -115,6 +115,24 @@ struct GemmArgs {
     int32_t group_m;
 };
 
+// Input format of A and B: IEEE binary16 or bfloat16.  Both are 16-bit
+// patterns to every copy and LDS read; only the matrix instruction differs.
+constexpr int kInF16 = 0;
+constexpr int kInBF16 = 1;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// acc += A_op * B_op on the 32x32x16 matrix instruction of the input format.
+template <int IN>
+__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 acc)
+{
+    if constexpr (IN == kInBF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+
 // Workgroup id -> (tile row, tile column).  First undo the round-robin XCD
 // dispatch so each XCD owns one contiguous run of tile ids, then walk that
 // run in groups of `group_m` tile rows so the workgroups resident on one XCD
@@ -368,6 +386,7 @@ gemm_tiled(GemmArgs args)
 // ---------------------------------------------------------------------------
 // Direct kernel: 4 waves, 64x64 of C per workgroup, operands from memory.
 // ---------------------------------------------------------------------------
+template <int IN>
 __global__ void __launch_bounds__(256)
 gemm_direct(GemmArgs args)
 {
@@ -394,7 +413,7 @@ gemm_direct(GemmArgs args)
             a[e] = __builtin_bit_cast(_Float16, av);
             b[e] = __builtin_bit_cast(_Float16, bv);
         }
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+        acc = mfma32<IN>(a, b, acc);
     }
     store_tile32(acc, args.C, args.ldc, args.M, args.N, row0, col0, args.alpha, args.beta, lane);
 }
@@ -495,6 +514,7 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRowMajor = 0;
 constexpr int kColMajor = 1;
 
+
 // One operand tile in LDS.  KC = true: K-contiguous rows (BX rows of BK);
 // KC = false: outer-contiguous rows (BK rows of BX).  NW waves share the
 // copies; each copy instruction fills RPI whole LDS rows.
@@ -522,12 +542,13 @@ struct OpTile {
 };
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int VEC_A_, int VEC_B_,
-          int LAYOUT_A_ = kRowMajor, int LAYOUT_B_ = kRowMajor>
+          int LAYOUT_A_ = kRowMajor, int LAYOUT_B_ = kRowMajor, int IN_ = kInF16>
 struct PipeCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int VEC_A = VEC_A_, VEC_B = VEC_B_;
     static constexpr int LAYOUT_A = LAYOUT_A_, LAYOUT_B = LAYOUT_B_;
+    static constexpr int IN = IN_;
     static constexpr int NW = WAVES_M * WAVES_N;
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -812,7 +833,7 @@ gemm_pipe(GemmArgs args)
     auto mfma_group = [&](int set, int i) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[set][i], rb[set][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = mfma32<Cfg::IN>(ra[set][i], rb[set][j], acc[i][j]);
     };
 
     // Make tile t (in buffer buf) visible to the workgroup: this thread's

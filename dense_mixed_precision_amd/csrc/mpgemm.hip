@@ -19,6 +19,8 @@ namespace {
 
 using mpg::GemmArgs;
 using mpg::kColMajor;
+using mpg::kInBF16;
+using mpg::kInF16;
 using mpg::kRowMajor;
 using mpg::PipeCfg;
 using mpg::TileCfg;
@@ -49,9 +51,10 @@ hipError_t launch_pipe(const GemmArgs &a, dim3 grid, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int IN>
 hipError_t launch_direct(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(mpg::gemm_direct, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(mpg::gemm_direct<IN>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -79,6 +82,7 @@ constexpr Entry tiled_entry(int id)
     c.grid = 0;
     c.layout_a = MPGEMM_ROW_MAJOR;
     c.layout_b = MPGEMM_ROW_MAJOR;
+    c.in_type = MPGEMM_IN_F16;
     return Entry{c, &launch_tiled<Cfg>};
 }
 
@@ -106,9 +110,11 @@ constexpr Entry pipe_entry(int id)
     c.grid = 0;
     c.layout_a = Cfg::LAYOUT_A;
     c.layout_b = Cfg::LAYOUT_B;
+    c.in_type = Cfg::IN;
     return Entry{c, &launch_pipe<Cfg>};
 }
 
+template <int IN>
 constexpr Entry direct_entry(int id)
 {
     mpgemm_config c{};
@@ -129,7 +135,8 @@ constexpr Entry direct_entry(int id)
     c.stages = 0;
     c.threads = 256;
     c.lds_bytes = 0;
-    return Entry{c, &launch_direct};
+    c.in_type = IN;
+    return Entry{c, &launch_direct<IN>};
 }
 
 constexpr Entry scale_entry(int id)
@@ -162,11 +169,20 @@ constexpr Entry scale_entry(int id)
         pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 8, 8, LA, LB>>(base + 4),    \
         pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 1, 1, LA, LB>>(base + 5)
 
+#define MPG_BF16_ENTRIES(base, LA, LB)                                                 \
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, LA, LB, kInBF16>>(base + 0),       \
+        pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4, 1, 1, LA, LB, kInBF16>>(base + 1),   \
+        pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, 8, 8, LA, LB, kInBF16>>(base + 2),   \
+        pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3, 1, 1, LA, LB, kInBF16>>(base + 3),   \
+        pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 8, 8, LA, LB, kInBF16>>(base + 4),     \
+        pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 1, 1, LA, LB, kInBF16>>(base + 5),     \
+        pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, LA, LB, kInBF16>>(base + 6)
+
 const Entry kTable[] = {
     MPG_TILE_ENTRIES(0, 256, 256, 64, 2, 2),  // 0..3   register-staged copies
     MPG_TILE_ENTRIES(4, 128, 128, 64, 2, 2),  // 4..7
     MPG_TILE_ENTRIES(8, 64, 64, 64, 2, 2),    // 8..11
-    direct_entry(12),                         // 12     any stride / size
+    direct_entry<kInF16>(12),                 // 12     any stride / size / order
     scale_entry(13),                          // 13     alpha == 0 or K == 0
     MPG_PIPE_ENTRIES(14, 256, 256, 32, 2, 2, 4),  // 14..17 large products
     MPG_PIPE_ENTRIES(18, 128, 128, 64, 2, 2, 3),  // 18..21 2048-class and tall-skinny
@@ -197,9 +213,15 @@ const Entry kTable[] = {
     pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kColMajor, kRowMajor>>(58),
     pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kRowMajor, kColMajor>>(59),
     pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kColMajor, kColMajor>>(60),
+    // BF16 inputs: the same shapes for every storage-order pair
+    MPG_BF16_ENTRIES(61, kRowMajor, kRowMajor),  // 61..67
+    MPG_BF16_ENTRIES(68, kColMajor, kRowMajor),  // 68..74
+    MPG_BF16_ENTRIES(75, kRowMajor, kColMajor),  // 75..81
+    MPG_BF16_ENTRIES(82, kColMajor, kColMajor),  // 82..88
+    direct_entry<kInBF16>(89),                   // 89     BF16 fallback
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
-constexpr int kDirectId = 12;
+constexpr int kDirectIds[2] = {12, 89};  // per input format
 constexpr int kScaleId = 13;
 
 // Tile groups the factory chooses from, largest first, per storage-order
@@ -208,18 +230,24 @@ constexpr int kScaleId = 13;
 // the eight-wave shapes exist for 16-byte aligned operands only and the
 // other pairs fall back to the four-wave form of the same tile; for the
 // column-major pairs every pair but 88 takes the 2-byte (11) entry.
-// 128x128, K tile 128, eight waves, per storage-order pair
-constexpr int kWideKIds[4] = {37, 58, 59, 60};
+// 128x128, K tile 128, eight waves, per input format and storage-order pair
+constexpr int kWideKIds[2][4] = {{37, 58, 59, 60}, {67, 74, 81, 88}};
 struct TileGroup {
     int bm, bn;
     int ids[4];
 };
 constexpr int kNumGroups = 3;
-constexpr TileGroup kGroups[4][kNumGroups] = {
-    {{256, 256, {32, 15, 16, 17}}, {128, 128, {36, 19, 20, 21}}, {64, 64, {22, 23, 24, 25}}},
-    {{256, 256, {40, 41, 41, 41}}, {128, 128, {42, 43, 43, 43}}, {64, 64, {44, 45, 45, 45}}},
-    {{256, 256, {46, 47, 47, 47}}, {128, 128, {48, 49, 49, 49}}, {64, 64, {50, 51, 51, 51}}},
-    {{256, 256, {52, 53, 53, 53}}, {128, 128, {54, 55, 55, 55}}, {64, 64, {56, 57, 57, 57}}},
+#define MPG_GROUPS(b)                                                          \
+    {{256, 256, {b, b + 1, b + 1, b + 1}}, {128, 128, {b + 2, b + 3, b + 3, b + 3}}, \
+     {64, 64, {b + 4, b + 5, b + 5, b + 5}}}
+constexpr TileGroup kGroups[2][4][kNumGroups] = {
+    {
+        {{256, 256, {32, 15, 16, 17}}, {128, 128, {36, 19, 20, 21}}, {64, 64, {22, 23, 24, 25}}},
+        MPG_GROUPS(40),
+        MPG_GROUPS(46),
+        MPG_GROUPS(52),
+    },
+    {MPG_GROUPS(61), MPG_GROUPS(68), MPG_GROUPS(75), MPG_GROUPS(82)},
 };
 
 // ---------------------------------------------------------------------------
@@ -232,6 +260,7 @@ struct Problem {
     const float *C;
     float alpha, beta;
     int la, lb;  // storage orders of A and B
+    int in_type; // MPGEMM_IN_F16 or MPGEMM_IN_BF16
 };
 
 int64_t at_least_one(int64_t v) { return v > 1 ? v : 1; }
@@ -280,6 +309,8 @@ bool entry_fits(const Entry &e, const Problem &p)
     const bool scale_only = p.K == 0 || p.alpha == 0.0f;
     if (c.kind == MPGEMM_KIND_SCALE)
         return scale_only || trivial;
+    if (c.in_type != p.in_type)
+        return false;
     if (c.kind == MPGEMM_KIND_DIRECT)
         return true;
     if (c.layout_a != p.la || c.layout_b != p.lb)
@@ -349,17 +380,17 @@ int select(const Problem &p)
     // 128x128 tiles with both panels reused across tiles (B panels by at
     // least four column tiles) take K steps of 128: half as many barriers.
     // A tall-skinny product streams A once and keeps the deeper 64-wide ring.
-    const int wide = kWideKIds[p.la + 2 * p.lb];
+    const int wide = kWideKIds[p.in_type][p.la + 2 * p.lb];
     if (group == 1 && v == 0 && cdiv(p.N, 128) >= 4 && cdiv(p.M, 128) >= 4 &&
         entry_fits(kTable[wide], p))
         return wide;
-    const TileGroup *groups = kGroups[p.la + 2 * p.lb];
+    const TileGroup *groups = kGroups[p.in_type][p.la + 2 * p.lb];
     for (int g = group; g < kNumGroups; ++g) {
         const int id = groups[g].ids[v];
         if (entry_fits(kTable[id], p))
             return id;
     }
-    return kDirectId;
+    return kDirectIds[p.in_type];
 }
 
 int fill_config(int id, const Problem &p, mpgemm_config *out)
@@ -370,6 +401,7 @@ int fill_config(int id, const Problem &p, mpgemm_config *out)
         c.kind = MPGEMM_KIND_NONE;
         c.layout_a = p.la;
         c.layout_b = p.lb;
+        c.in_type = p.in_type;
         *out = c;
         return MPGEMM_OK;
     }
@@ -377,6 +409,7 @@ int fill_config(int id, const Problem &p, mpgemm_config *out)
     out->grid = grid_for(out[0], p);
     out->layout_a = p.la;
     out->layout_b = p.lb;
+    out->in_type = p.in_type;
     return MPGEMM_OK;
 }
 
@@ -431,42 +464,43 @@ int run(int id, const Problem &p, void *stream)
 
 Problem make_problem(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                      const uint16_t *B, int64_t ldb, const float *C, int64_t ldc,
-                     float alpha, float beta, int la = MPGEMM_ROW_MAJOR, int lb = MPGEMM_ROW_MAJOR)
+                     float alpha, float beta, int la = MPGEMM_ROW_MAJOR, int lb = MPGEMM_ROW_MAJOR,
+                     int in_type = MPGEMM_IN_F16)
 {
-    return Problem{M, N, K, lda, ldb, ldc, A, B, C, alpha, beta, la, lb};
+    return Problem{M, N, K, lda, ldb, ldc, A, B, C, alpha, beta, la, lb, in_type};
 }
 
-int gemm_layout(int la, int lb, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
-                const uint16_t *B, int64_t ldb, float *C, int64_t ldc, float alpha, float beta,
-                void *stream)
+int gemm_layout(int in_type, int la, int lb, int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                int64_t lda, const uint16_t *B, int64_t ldb, float *C, int64_t ldc, float alpha,
+                float beta, void *stream)
 {
-    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb);
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb, in_type);
     const int rc = validate(p);
     if (rc != MPGEMM_OK)
         return rc;
     return run(select(p), p, stream);
 }
 
-int query_layout(int la, int lb, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
-                 const uint16_t *B, int64_t ldb, const float *C, int64_t ldc, float alpha,
-                 float beta, mpgemm_config *out)
+int query_layout(int in_type, int la, int lb, int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                 int64_t lda, const uint16_t *B, int64_t ldb, const float *C, int64_t ldc,
+                 float alpha, float beta, mpgemm_config *out)
 {
     if (out == nullptr)
         return MPGEMM_ENULL;
-    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb);
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb, in_type);
     const int rc = validate(p);
     if (rc != MPGEMM_OK)
         return rc;
     return fill_config(select(p), p, out);
 }
 
-int with_config_layout(int config_id, int la, int lb, int64_t M, int64_t N, int64_t K,
-                       const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float *C,
-                       int64_t ldc, float alpha, float beta, void *stream)
+int with_config_layout(int in_type, int config_id, int la, int lb, int64_t M, int64_t N,
+                       int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                       float *C, int64_t ldc, float alpha, float beta, void *stream)
 {
     if (config_id < 0 || config_id >= kNumEntries)
         return MPGEMM_ECONFIG;
-    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb);
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb, in_type);
     const int rc = validate(p);
     if (rc != MPGEMM_OK)
         return rc;
@@ -485,31 +519,32 @@ int mpgemm_f16f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t ld
                   const uint16_t *B, int64_t ldb, float *C, int64_t ldc, float alpha,
                   float beta, void *stream)
 {
-    return gemm_layout(MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K, A, lda, B, ldb, C, ldc,
-                       alpha, beta, stream);
+    return gemm_layout(MPGEMM_IN_F16, MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K, A, lda, B, ldb,
+                       C, ldc, alpha, beta, stream);
 }
 
 int mpgemm_f16f32_query(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                         const uint16_t *B, int64_t ldb, const float *C, int64_t ldc,
                         float alpha, float beta, mpgemm_config *out)
 {
-    return query_layout(MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K, A, lda, B, ldb, C, ldc,
-                        alpha, beta, out);
+    return query_layout(MPGEMM_IN_F16, MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K, A, lda, B, ldb,
+                        C, ldc, alpha, beta, out);
 }
 
 int mpgemm_f16f32_with_config(int config_id, int64_t M, int64_t N, int64_t K,
                               const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                               float *C, int64_t ldc, float alpha, float beta, void *stream)
 {
-    return with_config_layout(config_id, MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K, A, lda,
-                              B, ldb, C, ldc, alpha, beta, stream);
+    return with_config_layout(MPGEMM_IN_F16, config_id, MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K,
+                              A, lda, B, ldb, C, ldc, alpha, beta, stream);
 }
 
 int mpgemm_f16f32_layout(int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
                          const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                          float *C, int64_t ldc, float alpha, float beta, void *stream)
 {
-    return gemm_layout(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, stream);
+    return gemm_layout(MPGEMM_IN_F16, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha,
+                       beta, stream);
 }
 
 int mpgemm_f16f32_layout_query(int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
@@ -517,7 +552,8 @@ int mpgemm_f16f32_layout_query(int layout_a, int layout_b, int64_t M, int64_t N,
                                const float *C, int64_t ldc, float alpha, float beta,
                                mpgemm_config *out)
 {
-    return query_layout(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, out);
+    return query_layout(MPGEMM_IN_F16, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha,
+                        beta, out);
 }
 
 int mpgemm_f16f32_layout_with_config(int config_id, int layout_a, int layout_b, int64_t M,
@@ -525,8 +561,42 @@ int mpgemm_f16f32_layout_with_config(int config_id, int layout_a, int layout_b, 
                                      const uint16_t *B, int64_t ldb, float *C, int64_t ldc,
                                      float alpha, float beta, void *stream)
 {
-    return with_config_layout(config_id, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc,
-                              alpha, beta, stream);
+    return with_config_layout(MPGEMM_IN_F16, config_id, layout_a, layout_b, M, N, K, A, lda, B, ldb,
+                              C, ldc, alpha, beta, stream);
+}
+
+int mpgemm_bf16f32(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                   const uint16_t *B, int64_t ldb, float *C, int64_t ldc, float alpha,
+                   float beta, void *stream)
+{
+    return gemm_layout(MPGEMM_IN_BF16, MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR, M, N, K, A, lda, B, ldb,
+                       C, ldc, alpha, beta, stream);
+}
+
+int mpgemm_bf16f32_layout(int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
+                          const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                          float *C, int64_t ldc, float alpha, float beta, void *stream)
+{
+    return gemm_layout(MPGEMM_IN_BF16, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha,
+                       beta, stream);
+}
+
+int mpgemm_bf16f32_layout_query(int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
+                                const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                                const float *C, int64_t ldc, float alpha, float beta,
+                                mpgemm_config *out)
+{
+    return query_layout(MPGEMM_IN_BF16, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha,
+                        beta, out);
+}
+
+int mpgemm_bf16f32_layout_with_config(int config_id, int layout_a, int layout_b, int64_t M,
+                                      int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                                      const uint16_t *B, int64_t ldb, float *C, int64_t ldc,
+                                      float alpha, float beta, void *stream)
+{
+    return with_config_layout(MPGEMM_IN_BF16, config_id, layout_a, layout_b, M, N, K, A, lda, B,
+                              ldb, C, ldc, alpha, beta, stream);
 }
 
 int mpgemm_num_configs(void) { return kNumEntries; }
@@ -577,6 +647,6 @@ const char *mpgemm_strerror(int code)
     }
 }
 
-const char *mpgemm_version(void) { return "mpgemm 0.2.0 gfx950"; }
+const char *mpgemm_version(void) { return "mpgemm 0.3.0 gfx950"; }
 
 }  // extern "C"

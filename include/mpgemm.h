@@ -62,6 +62,10 @@ extern "C" {
 #define MPGEMM_ROW_MAJOR 0
 #define MPGEMM_COL_MAJOR 1
 
+/* Input format of A and B (the accumulator and C are always FP32). */
+#define MPGEMM_IN_F16 0        /* IEEE binary16                                   */
+#define MPGEMM_IN_BF16 1       /* bfloat16                                        */
+
 /* Kinds of kernel a config can name. */
 #define MPGEMM_KIND_TILED 0    /* LDS-staged, double-buffered MFMA block tile     */
 #define MPGEMM_KIND_DIRECT 1   /* operands straight from memory; any size/stride  */
@@ -90,6 +94,7 @@ typedef struct mpgemm_config {
     int32_t layout_a;    /* storage order of A the entry reads (MPGEMM_*_MAJOR)   */
     int32_t layout_b;    /* storage order of B; the direct and scale kernels take
                             any order and report the one they were asked for     */
+    int32_t in_type;     /* input format the entry reads (MPGEMM_IN_*)            */
 } mpgemm_config;
 
 /*
@@ -174,6 +179,46 @@ int mpgemm_f16f32_layout_with_config(int config_id, int layout_a, int layout_b,
                                      float alpha, float beta,
                                      void *stream);
 
+/*
+ * The same GEMM with BF16 inputs: A and B hold bfloat16 bit patterns (the
+ * other 16-bit tensor-core input type listed in "Tensor cores with WMMA",
+ * section "A warp owns a tile, and no thread owns an element").  Products
+ * of BF16 values are exact in FP32 and summed in FP32, as for FP16.  Every
+ * other argument, layout rule, error and the semantics are those of the
+ * FP16 entry point of the same form; mpgemm_bf16f32 takes row-major A and B.
+ */
+int mpgemm_bf16f32(int64_t M, int64_t N, int64_t K,
+                   const uint16_t *A, int64_t lda,
+                   const uint16_t *B, int64_t ldb,
+                   float *C, int64_t ldc,
+                   float alpha, float beta,
+                   void *stream);
+
+int mpgemm_bf16f32_layout(int layout_a, int layout_b,
+                          int64_t M, int64_t N, int64_t K,
+                          const uint16_t *A, int64_t lda,
+                          const uint16_t *B, int64_t ldb,
+                          float *C, int64_t ldc,
+                          float alpha, float beta,
+                          void *stream);
+
+int mpgemm_bf16f32_layout_query(int layout_a, int layout_b,
+                                int64_t M, int64_t N, int64_t K,
+                                const uint16_t *A, int64_t lda,
+                                const uint16_t *B, int64_t ldb,
+                                const float *C, int64_t ldc,
+                                float alpha, float beta,
+                                mpgemm_config *out);
+
+/* MPGEMM_ECONFIG also when the entry was compiled for FP16 inputs. */
+int mpgemm_bf16f32_layout_with_config(int config_id, int layout_a, int layout_b,
+                                      int64_t M, int64_t N, int64_t K,
+                                      const uint16_t *A, int64_t lda,
+                                      const uint16_t *B, int64_t ldb,
+                                      float *C, int64_t ldc,
+                                      float alpha, float beta,
+                                      void *stream);
+
 /* Number of entries in the config table. */
 int mpgemm_num_configs(void);
 
@@ -195,7 +240,7 @@ int mpgemm_probe_mfma_layout(int shape, float *out, void *stream);
 /* Static text for an error code (never NULL). */
 const char *mpgemm_strerror(int code);
 
-/* Library version string, e.g. "mpgemm 0.2.0 gfx950". */
+/* Library version string, e.g. "mpgemm 0.3.0 gfx950". */
 const char *mpgemm_version(void);
 
 #ifdef __cplusplus

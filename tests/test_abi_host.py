@@ -228,3 +228,42 @@ def test_layout_factory_choices(la, lb):
     # a stored stage beyond 32-bit offsets leaves only the 64-bit direct kernel
     c = ql(la, lb, 300, 300, 64, lda=(1 << 30), ldb=(1 << 30))
     assert c["kind_name"] == "direct" and (c["layout_a"], c["layout_b"]) == (la, lb)
+
+
+# ----------------------------------------------------------------------------
+# BF16 inputs
+# ----------------------------------------------------------------------------
+
+def qb(la, lb, M, N, K, A=FAKE_A, lda=None, B=FAKE_B, ldb=None, C=FAKE_C, ldc=None,
+       alpha=1.0, beta=0.0):
+    lda = max(M if la else K, 1) if lda is None else lda
+    ldb = max(K if lb else N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return mp.mpgemm_bf16f32_layout_query(la, lb, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta)
+
+
+@pytest.mark.parametrize("la,lb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_bf16_factory_choices(la, lb):
+    c = qb(la, lb, 8192, 8192, 8192)
+    assert (c["kind_name"], c["bm"], c["bn"], c["in_type"]) == ("pipe", 256, 256, mp.MPGEMM_IN_BF16)
+    assert (c["layout_a"], c["layout_b"]) == (la, lb)
+    assert mp.mpgemm_config_info(c["id"])["in_type"] == mp.MPGEMM_IN_BF16
+    c = qb(la, lb, 2048, 2048, 2048)
+    assert (c["bm"], c["bk"], c["in_type"]) == (128, 128, mp.MPGEMM_IN_BF16)
+    c = qb(la, lb, 1000, 800, 617, lda=(1001 if la else 617), ldb=(617 if lb else 800))
+    assert (c["vec_a"], c["vec_b"], c["in_type"]) == (1, 1, mp.MPGEMM_IN_BF16)
+    c = qb(la, lb, 300, 300, 64, lda=(1 << 30), ldb=(1 << 30))
+    assert c["kind_name"] == "direct" and c["in_type"] == mp.MPGEMM_IN_BF16
+    assert qb(la, lb, 64, 64, 0)["kind_name"] == "scale"
+
+
+def test_bf16_and_f16_entries_do_not_mix():
+    f16_id = q(8192, 8192, 8192)["id"]
+    bf16_id = qb(0, 0, 8192, 8192, 8192)["id"]
+    assert f16_id != bf16_id
+    args = (8192, 8192, 8192, FAKE_A, 8192, FAKE_B, 8192, FAKE_C, 8192, 1.0, 0.0, 0)
+    assert mp.mpgemm_bf16f32_layout_with_config(f16_id, 0, 0, *args) == mp.MPGEMM_ECONFIG
+    assert mp.mpgemm_f16f32_layout_with_config(bf16_id, 0, 0, *args) == mp.MPGEMM_ECONFIG
+    assert mp.mpgemm_bf16f32(-1, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0) == mp.MPGEMM_EDIM
+    assert mp.mpgemm_bf16f32_layout(5, 0, 4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0) \
+        == mp.MPGEMM_ELAYOUT

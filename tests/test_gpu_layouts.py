@@ -37,7 +37,8 @@ def _layout_ids():
     out = []
     for i in range(mp.mpgemm_num_configs()):
         c = mp.mpgemm_config_info(i)
-        if c["kind_name"] == "pipe" and (c["layout_a"], c["layout_b"]) != (0, 0):
+        if (c["kind_name"] == "pipe" and (c["layout_a"], c["layout_b"]) != (0, 0)
+                and c["in_type"] == mp.MPGEMM_IN_F16):
             out.append(i)
     return out
 
@@ -114,7 +115,7 @@ def test_same_tile_shape_is_bitwise_identical_across_layouts():
     for i in range(mp.mpgemm_num_configs()):
         c = mp.mpgemm_config_info(i)
         if (c["kind_name"], c["bm"], c["bn"], c["bk"], c["waves_m"], c["waves_n"], c["stages"],
-                c["vec_a"], c["vec_b"]) == ("pipe", 256, 256, 64, 2, 4, 2, 8, 8):
+                c["vec_a"], c["vec_b"], c["in_type"]) == ("pipe", 256, 256, 64, 2, 4, 2, 8, 8, 0):
             ids[(c["layout_a"], c["layout_b"])] = i
     assert set(ids) == {(0, 0), (0, 1), (1, 0), (1, 1)}
     M, N, K = 300, 520, 333
