@@ -82,6 +82,13 @@ def _load():
     lib.oracle_gemm_bf16_layout.restype = ctypes.c_int
     lib.oracle_gemm_bf16_layout_entries.argtypes = lib.oracle_gemm_layout_entries.argtypes
     lib.oracle_gemm_bf16_layout_entries.restype = ctypes.c_int
+    lib.oracle_gemm_ex.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, i64,
+                                   vp, i64, vp, i64, ctypes.c_double, ctypes.c_double, vp, vp, vp]
+    lib.oracle_gemm_ex.restype = ctypes.c_int
+    lib.oracle_gemm_ex_entries.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                           vp, i64, vp, i64, vp, i64, ctypes.c_double,
+                                           ctypes.c_double, vp, i64, vp, vp, vp, vp]
+    lib.oracle_gemm_ex_entries.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -168,13 +175,20 @@ def bf16_to_f64(bits) -> np.ndarray:
 IN_TYPES = ("f16", "bf16")
 
 
-def _entry_points(in_type):
-    lib = _load()
-    if in_type == "f16":
-        return lib.oracle_gemm_layout, lib.oracle_gemm_layout_entries
-    if in_type == "bf16":
-        return lib.oracle_gemm_bf16_layout, lib.oracle_gemm_bf16_layout_entries
-    raise ValueError(f"in_type must be one of {IN_TYPES}")
+def _bf16_flag(in_type):
+    if in_type not in IN_TYPES:
+        raise ValueError(f"in_type must be one of {IN_TYPES}")
+    return 1 if in_type == "bf16" else 0
+
+
+def _as_bias(bias, N):
+    """Per-column bias: None, or N float32 values (contiguous)."""
+    if bias is None:
+        return None
+    bias = np.ascontiguousarray(np.asarray(bias), dtype=np.float32)
+    if bias.shape != (N,):
+        raise ValueError(f"bias must hold N = {N} values")
+    return bias
 
 
 def _check(rc):
@@ -183,32 +197,36 @@ def _check(rc):
 
 
 def gemm(A, B, C=None, alpha: float = 1.0, beta: float = 0.0,
-         layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR, in_type: str = "f16"):
+         layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR, in_type: str = "f16", bias=None):
     """Full product.  Returns ``(ref, absdot)``, both float64 (M, N).
 
     A: 16-bit patterns (FP16, or BF16 with ``in_type="bf16"``) stored (M, K)
     (row-major) or (K, M) (``layout_a=COL_MAJOR``); B: stored (K, N) or (N, K)
-    (``layout_b=COL_MAJOR``); C: (M, N) float32 or None.  alpha and beta are
-    rounded to float32 first, as the GPU entry point receives them.
+    (``layout_b=COL_MAJOR``); C: (M, N) float32 or None; bias: N float32
+    values added to every row, or None.  alpha and beta are rounded to
+    float32 first, as the GPU entry point receives them.
     """
-    full, _ = _entry_points(in_type)
+    flag = _bf16_flag(in_type)
     A, lda, B, ldb, M, N, K = _operands(A, B, layout_a, layout_b)
+    bias = _as_bias(bias, N)
     alpha = float(np.float32(alpha))
     beta = float(np.float32(beta))
     C, ldc = _as_c(C, M, N, beta)
     ref = np.empty((M, N), dtype=np.float64)
     absdot = np.empty((M, N), dtype=np.float64)
-    _check(full(layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B), ldb,
-                _ptr(C), ldc, alpha, beta, _ptr(ref), _ptr(absdot)))
+    _check(_load().oracle_gemm_ex(flag, layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B), ldb,
+                                  _ptr(C), ldc, alpha, beta, _ptr(bias), _ptr(ref), _ptr(absdot)))
     return ref, absdot
 
 
 def gemm_entries(A, B, C, alpha: float, beta: float, rows, cols,
-                 layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR, in_type: str = "f16"):
+                 layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR, in_type: str = "f16",
+                 bias=None):
     """Selected entries (rows[t], cols[t]).  Returns ``(ref, absdot)`` 1-D.
     Operands as for :func:`gemm`."""
-    _, entries = _entry_points(in_type)
+    flag = _bf16_flag(in_type)
     A, lda, B, ldb, M, N, K = _operands(A, B, layout_a, layout_b)
+    bias = _as_bias(bias, N)
     alpha = float(np.float32(alpha))
     beta = float(np.float32(beta))
     C, ldc = _as_c(C, M, N, beta)
@@ -218,9 +236,9 @@ def gemm_entries(A, B, C, alpha: float, beta: float, rows, cols,
         raise ValueError("rows and cols must be 1-D and equal length")
     ref = np.empty(rows.shape, dtype=np.float64)
     absdot = np.empty(rows.shape, dtype=np.float64)
-    _check(entries(layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B), ldb,
-                   _ptr(C), ldc, alpha, beta, rows.size, _ptr(rows),
-                   _ptr(cols), _ptr(ref), _ptr(absdot)))
+    _check(_load().oracle_gemm_ex_entries(flag, layout_a, layout_b, M, N, K, _ptr(A), lda, _ptr(B),
+                                          ldb, _ptr(C), ldc, alpha, beta, _ptr(bias), rows.size,
+                                          _ptr(rows), _ptr(cols), _ptr(ref), _ptr(absdot)))
     return ref, absdot
 
 

@@ -30,6 +30,12 @@
  * two are exact in FP64 just the same, and every finite BF16 value and
  * product is in FP64's range).
  *
+ * A per-column bias (the position-dependent epilogue "Tensor cores with WMMA"
+ * names in section "The habit this API takes away": a bias per column, which
+ * a WMMA fragment cannot place but a documented accumulator layout can) is
+ * taken by the *_ex entry points: ref[i][j] = alpha*s + beta*c + bias[j],
+ * each term in FP64.
+ *
  * Arithmetic: an FP16 value is an integer times 2^-24 with at most 11
  * significant bits, so its FP64 widening is exact and every product of two
  * widened values is exact in FP64 (22 significant bits).  Only the running
@@ -113,6 +119,7 @@ void oracle_bf16_to_f64_array(const uint16_t *h, int64_t n, double *out)
 typedef struct {
     int64_t a_i, a_k, b_k, b_j;
     double (*decode)(uint16_t);  /* FP16 or BF16 bits -> FP64 */
+    const float *bias;           /* per-column bias (N values) or NULL */
 } strides_t;
 
 #define ORACLE_ROW_MAJOR 0
@@ -126,6 +133,7 @@ static strides_t strides_for(int layout_a, int layout_b, int64_t lda, int64_t ld
     t.b_k = layout_b == ORACLE_COL_MAJOR ? 1 : ldb;
     t.b_j = layout_b == ORACLE_COL_MAJOR ? ldb : 1;
     t.decode = oracle_f16_to_f64;
+    t.bias = NULL;
     return t;
 }
 
@@ -152,6 +160,8 @@ static void entry(int64_t i, int64_t j, int64_t K,
     double r = alpha * s;
     if (beta != 0.0)
         r += beta * (double)C[i * ldc + j];
+    if (st.bias)
+        r += (double)st.bias[j];
     *ref = r;
     if (absdot)
         *absdot = s_abs;
@@ -197,7 +207,7 @@ static int gemm_full(int bf16, int layout_a, int layout_b,
                      const uint16_t *A, int64_t lda,
                      const uint16_t *B, int64_t ldb,
                      const float *C, int64_t ldc,
-                     double alpha, double beta,
+                     double alpha, double beta, const float *bias,
                      double *ref, double *absdot)
 {
     const int rc = check_args(layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, beta);
@@ -208,6 +218,7 @@ static int gemm_full(int bf16, int layout_a, int layout_b,
     strides_t st = strides_for(layout_a, layout_b, lda, ldb);
     if (bf16)
         st.decode = oracle_bf16_to_f64;
+    st.bias = bias;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < M; ++i) {
         for (int64_t j = 0; j < N; ++j) {
@@ -226,7 +237,7 @@ int oracle_gemm_layout(int layout_a, int layout_b,
                        double alpha, double beta,
                        double *ref, double *absdot)
 {
-    return gemm_full(0, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+    return gemm_full(0, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, NULL,
                      ref, absdot);
 }
 
@@ -239,7 +250,7 @@ int oracle_gemm_bf16_layout(int layout_a, int layout_b,
                             double alpha, double beta,
                             double *ref, double *absdot)
 {
-    return gemm_full(1, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+    return gemm_full(1, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, NULL,
                      ref, absdot);
 }
 
@@ -264,7 +275,7 @@ static int gemm_entries(int bf16, int layout_a, int layout_b,
                         const uint16_t *A, int64_t lda,
                         const uint16_t *B, int64_t ldb,
                         const float *C, int64_t ldc,
-                        double alpha, double beta,
+                        double alpha, double beta, const float *bias,
                         int64_t count, const int64_t *rows, const int64_t *cols,
                         double *ref, double *absdot)
 {
@@ -280,6 +291,7 @@ static int gemm_entries(int bf16, int layout_a, int layout_b,
     strides_t st = strides_for(layout_a, layout_b, lda, ldb);
     if (bf16)
         st.decode = oracle_bf16_to_f64;
+    st.bias = bias;
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t t = 0; t < count; ++t) {
         entry(rows[t], cols[t], K, A, B, st, C, ldc, alpha, beta,
@@ -297,7 +309,7 @@ int oracle_gemm_layout_entries(int layout_a, int layout_b,
                                int64_t count, const int64_t *rows, const int64_t *cols,
                                double *ref, double *absdot)
 {
-    return gemm_entries(0, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+    return gemm_entries(0, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, NULL,
                         count, rows, cols, ref, absdot);
 }
 
@@ -310,7 +322,7 @@ int oracle_gemm_bf16_layout_entries(int layout_a, int layout_b,
                                     int64_t count, const int64_t *rows, const int64_t *cols,
                                     double *ref, double *absdot)
 {
-    return gemm_entries(1, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+    return gemm_entries(1, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, NULL,
                         count, rows, cols, ref, absdot);
 }
 
@@ -325,6 +337,35 @@ int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
 {
     return oracle_gemm_layout_entries(ORACLE_ROW_MAJOR, ORACLE_ROW_MAJOR, M, N, K, A, lda, B, ldb,
                                       C, ldc, alpha, beta, count, rows, cols, ref, absdot);
+}
+
+/*
+ * Everything at once: input format (bf16 = 0: FP16, 1: BF16), storage
+ * orders, and an optional per-column bias (NULL for none).
+ */
+int oracle_gemm_ex(int bf16, int layout_a, int layout_b,
+                   int64_t M, int64_t N, int64_t K,
+                   const uint16_t *A, int64_t lda,
+                   const uint16_t *B, int64_t ldb,
+                   const float *C, int64_t ldc,
+                   double alpha, double beta, const float *bias,
+                   double *ref, double *absdot)
+{
+    return gemm_full(bf16 != 0, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                     bias, ref, absdot);
+}
+
+int oracle_gemm_ex_entries(int bf16, int layout_a, int layout_b,
+                           int64_t M, int64_t N, int64_t K,
+                           const uint16_t *A, int64_t lda,
+                           const uint16_t *B, int64_t ldb,
+                           const float *C, int64_t ldc,
+                           double alpha, double beta, const float *bias,
+                           int64_t count, const int64_t *rows, const int64_t *cols,
+                           double *ref, double *absdot)
+{
+    return gemm_entries(bf16 != 0, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                        bias, count, rows, cols, ref, absdot);
 }
 
 int oracle_num_threads(void)

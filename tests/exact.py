@@ -25,7 +25,7 @@ def bf16_exact(bits_2d):
     return [[Fraction(float(v)) for v in row] for row in vals]
 
 
-def exact_gemm(A_bits, B_bits, C=None, alpha=1.0, beta=0.0, in_type="f16"):
+def exact_gemm(A_bits, B_bits, C=None, alpha=1.0, beta=0.0, in_type="f16", bias=None):
     """Exact result and exact sum|a*b| as float64 arrays (rounded once at the
     end, to nearest) plus the exact Fractions for callers that need them."""
     decode = bf16_exact if in_type == "bf16" else f16_exact
@@ -49,15 +49,20 @@ def exact_gemm(A_bits, B_bits, C=None, alpha=1.0, beta=0.0, in_type="f16"):
             r = fa * s
             if fb != 0:
                 r += fb * Fraction(float(C[i, j]))
+            if bias is not None:
+                r += Fraction(float(bias[j]))
             exact[i][j] = r
             ref[i, j] = float(r)
             absdot[i, j] = float(sa)
     return ref, absdot, exact
 
 
-def fp64_sum_bound(K, alpha, beta, absdot, C=None):
+def fp64_sum_bound(K, alpha, beta, absdot, C=None, bias=None):
     """Worst-case rounding of an FP64 ascending sum of K exact products plus
-    the alpha/beta combination: (K + 4) * 2^-53 * (|alpha|*S + |beta*c|)."""
+    the alpha/beta (and bias) combination:
+    (K + 5) * 2^-53 * (|alpha|*S + |beta*c| + |bias|)."""
     u = 2.0 ** -53
     extra = 0.0 if (C is None or beta == 0) else np.abs(float(np.float32(beta)) * C.astype(np.float64))
-    return (K + 4) * u * (abs(float(np.float32(alpha))) * absdot + extra) + 1e-300
+    if bias is not None:
+        extra = extra + np.abs(np.asarray(bias, dtype=np.float64))[None, :]
+    return (K + 5) * u * (abs(float(np.float32(alpha))) * absdot + extra) + 1e-300

@@ -420,6 +420,60 @@ def test_bf16_read_as_f16_is_caught():
     assert not np.all(np.abs(wrong - eref) <= fp64_sum_bound(13, 1.0, 0.0, eabs))
 
 
+# ----------------------------------------------------------------------------
+# Per-column bias ("Tensor cores with WMMA", section "The habit this API takes
+# away": a position-dependent epilogue, a bias per column)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("in_type", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 5), (3, 5, 7), (17, 15, 33)])
+def test_bias_exact_brute_force(in_type, M, N, K):
+    import torch
+    dt = torch.bfloat16 if in_type == "bf16" else torch.float16
+    A, B, C = make_inputs(M, N, K, "uniform", seed=M + N + 7 * K, c_init="uniform", dtype=dt)
+    bias = np.random.default_rng(M * N).uniform(-1, 1, N).astype(np.float32)
+    Ab, Bb, Cn = bits(A), bits(B), C.numpy()
+    ref, _ = oracle.gemm(Ab, Bb, Cn, 1.5, 0.5, in_type=in_type, bias=bias)
+    eref, eabs, _ = exact_gemm(Ab, Bb, Cn, 1.5, 0.5, in_type=in_type, bias=bias)
+    assert np.all(np.abs(ref - eref) <= fp64_sum_bound(K, 1.5, 0.5, eabs, Cn, bias))
+
+
+def test_bias_closed_forms_and_layouts():
+    M, N, K = 12, 9, 20
+    A, B, C = make_inputs(M, N, K, "uniform", seed=23, c_init="uniform")
+    bias = np.linspace(-2, 2, N).astype(np.float32)
+    # zero bias: bit for bit the product without one
+    r0, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 1.5, 0.5)
+    rz, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 1.5, 0.5, bias=np.zeros(N, np.float32))
+    assert np.array_equal(r0, rz)
+    # alpha = 0: beta*C + bias, each element one FP64 rounding of two exact terms
+    ra, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 0.0, 0.5, bias=bias)
+    assert np.array_equal(ra, 0.5 * C.numpy().astype(np.float64) + bias.astype(np.float64)[None, :])
+    # storage order does not change a bit
+    for la, lb in LAYOUTS:
+        rl, _ = oracle.gemm(_stored(bits(A), la), _stored(bits(B), lb), C.numpy(), 1.5, 0.5,
+                            layout_a=la, layout_b=lb, bias=bias)
+        rb, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 1.5, 0.5, bias=bias)
+        assert np.array_equal(rl, rb)
+    rows, cols = np.array([0, M - 1, 4]), np.array([N - 1, 0, 3])
+    e, _ = oracle.gemm_entries(bits(A), bits(B), C.numpy(), 1.5, 0.5, rows, cols, bias=bias)
+    assert np.array_equal(e, rb[rows, cols])
+    with pytest.raises(ValueError):
+        oracle.gemm(bits(A), bits(B), bias=bias[:-1])
+
+
+def test_bias_by_row_is_caught():
+    """Adding bias[i] (the row) instead of bias[j] (a plausible slip) fails
+    the exact pin on a non-square output."""
+    M, N, K = 5, 8, 11
+    A, B, _ = make_inputs(M, N, K, "uniform", seed=24)
+    bias = np.arange(N, dtype=np.float32)
+    r, _ = oracle.gemm(bits(A), bits(B))
+    wrong = r + bias[:M, None].astype(np.float64)
+    eref, eabs, _ = exact_gemm(bits(A), bits(B), bias=bias)
+    assert not np.all(np.abs(wrong - eref) <= fp64_sum_bound(K, 1.0, 0.0, eabs, None, bias))
+
+
 def torch_bf16():
     import torch
     return torch.bfloat16
