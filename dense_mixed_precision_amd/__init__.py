@@ -16,6 +16,8 @@ integers holding device addresses, ``stream`` a hipStream_t as an integer,
     mpgemm_f16f32_layout_with_config(cfg, layout_a, layout_b, M, N, K, ...) -> int
     mpgemm_bf16f32, mpgemm_bf16f32_layout, mpgemm_bf16f32_layout_query,
     mpgemm_bf16f32_layout_with_config: the same with BF16 inputs
+    mpgemm_gemm_ex(in_type, layout_a, layout_b, M, N, K, ..., alpha, beta, bias, stream) -> int
+    mpgemm_gemm_ex_with_config(cfg, in_type, layout_a, layout_b, ...) -> int   (per-column bias)
     mpgemm_num_configs(), mpgemm_config_info(id), mpgemm_probe_mfma_layout(shape, out, stream)
     mpgemm_strerror(code), mpgemm_version()
 
@@ -31,6 +33,7 @@ from ._binding import (  # noqa: F401
     MPGEMM_EDIM,
     MPGEMM_ELAUNCH,
     MPGEMM_ELAYOUT,
+    MPGEMM_ETYPE,
     MPGEMM_ELD,
     MPGEMM_ENULL,
     MPGEMM_OK,
@@ -54,6 +57,8 @@ from ._binding import (  # noqa: F401
     mpgemm_bf16f32_layout,
     mpgemm_bf16f32_layout_query,
     mpgemm_bf16f32_layout_with_config,
+    mpgemm_gemm_ex,
+    mpgemm_gemm_ex_with_config,
     mpgemm_num_configs,
     mpgemm_probe_mfma_layout,
     mpgemm_strerror,

@@ -15,6 +15,7 @@ MPGEMM_ELAUNCH = -4
 MPGEMM_ECONFIG = -5
 MPGEMM_EALIGN = -6
 MPGEMM_ELAYOUT = -7
+MPGEMM_ETYPE = -8
 
 MPGEMM_ROW_MAJOR = 0
 MPGEMM_COL_MAJOR = 1
@@ -82,6 +83,10 @@ def load():
         getattr(lib, f"mpgemm_{dt}f32_layout_query").restype = i32
         getattr(lib, f"mpgemm_{dt}f32_layout_with_config").argtypes = [i32, i32, i32] + gemm_args + [vp]
         getattr(lib, f"mpgemm_{dt}f32_layout_with_config").restype = i32
+    lib.mpgemm_gemm_ex.argtypes = [i32, i32, i32] + gemm_args + [vp, vp]
+    lib.mpgemm_gemm_ex.restype = i32
+    lib.mpgemm_gemm_ex_with_config.argtypes = [i32, i32, i32, i32] + gemm_args + [vp, vp]
+    lib.mpgemm_gemm_ex_with_config.restype = i32
     lib.mpgemm_num_configs.argtypes = []
     lib.mpgemm_num_configs.restype = i32
     lib.mpgemm_config_info.argtypes = [i32, ctypes.POINTER(MpgemmConfig)]
@@ -171,6 +176,18 @@ def mpgemm_bf16f32_layout_with_config(config_id, layout_a, layout_b, M, N, K, A,
                                                         lda, B, ldb, C, ldc, alpha, beta, stream))
 
 
+def mpgemm_gemm_ex(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                   bias=0, stream=0) -> int:
+    return int(load().mpgemm_gemm_ex(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc,
+                                     alpha, beta, bias, stream))
+
+
+def mpgemm_gemm_ex_with_config(config_id, in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb,
+                               C, ldc, alpha, beta, bias=0, stream=0) -> int:
+    return int(load().mpgemm_gemm_ex_with_config(config_id, in_type, layout_a, layout_b, M, N, K,
+                                                 A, lda, B, ldb, C, ldc, alpha, beta, bias, stream))
+
+
 def mpgemm_num_configs() -> int:
     return int(load().mpgemm_num_configs())
 
@@ -239,12 +256,25 @@ def _in_type(A):
     return MPGEMM_IN_BF16 if A.dtype == torch.bfloat16 else MPGEMM_IN_F16
 
 
-def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, config: int | None = None, stream=None):
-    """C <- alpha*A@B + beta*C in place on the GPU; returns C.
+def _bias_ptr(bias, N):
+    import torch
+    if bias is None:
+        return 0
+    if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or not bias.is_cuda:
+        raise TypeError("bias must be a float32 tensor on the GPU")
+    if bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1):
+        raise ValueError(f"bias must be a contiguous vector of N = {N} values")
+    return bias.data_ptr()
+
+
+def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, config: int | None = None, stream=None,
+         bias=None):
+    """C <- alpha*A@B + beta*C (+ bias[j]) in place on the GPU; returns C.
 
     A (M x K) and B (K x N): both float16 or both bfloat16, each row-major or
     column-major (e.g. the transpose view of a row-major tensor); the storage
-    order is read from the strides.  C must be float32 row-major.
+    order is read from the strides.  C must be float32 row-major.  ``bias``:
+    optional float32 vector of N values added to every row.
     ``stream``: a torch.cuda.Stream or raw handle (default: current stream).
     ``config``: force a table entry (tests and sweeps)."""
     import torch
@@ -252,7 +282,26 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, config: int | None = No
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    bf16 = _in_type(A) == MPGEMM_IN_BF16
+    in_type = _in_type(A)
+    bf16 = in_type == MPGEMM_IN_BF16
+    if bias is not None:
+        bp = _bias_ptr(bias, N)
+        if config is None:
+            rc = mpgemm_gemm_ex(in_type, la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                C.data_ptr(), ldc, float(alpha), float(beta), bp, handle)
+        else:
+            rc = mpgemm_gemm_ex_with_config(int(config), in_type, la, lb, M, N, K, A.data_ptr(), lda,
+                                            B.data_ptr(), ldb, C.data_ptr(), ldc, float(alpha),
+                                            float(beta), bp, handle)
+        if rc != MPGEMM_OK:
+            raise MpgemmError(rc, "mpgemm_gemm_ex" if config is None else f"config {config}")
+        return C
+    if config is None and not bf16 and (la, lb) == (MPGEMM_ROW_MAJOR, MPGEMM_ROW_MAJOR):
+        rc = mpgemm_f16f32(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
+                           float(alpha), float(beta), handle)
+        if rc != MPGEMM_OK:
+            raise MpgemmError(rc, "mpgemm_f16f32")
+        return C
     if config is None:
         fn = mpgemm_bf16f32_layout if bf16 else mpgemm_f16f32_layout
         rc = fn(la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,

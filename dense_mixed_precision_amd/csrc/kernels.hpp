@@ -111,6 +111,8 @@ struct GemmArgs {
     // (read by the direct kernel; the tiled kernels compile their layout in)
     int64_t a_i, a_k, b_k, b_j;
     float alpha, beta;
+    // optional per-column bias: C[i][j] gains bias[j] (nullptr: none)
+    const float *bias;
     int32_t tiles_m, tiles_n;
     int32_t group_m;
 };
@@ -157,11 +159,12 @@ __device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_n, int ti
 // element is C[row0][col0]: C = alpha*acc + beta*C, C not read when beta == 0.
 __device__ __forceinline__ void store_tile32(const floatx16 &acc, float *C, int64_t ldc,
                                              int64_t M, int64_t N, int64_t row0, int64_t col0,
-                                             float alpha, float beta, int lane)
+                                             float alpha, float beta, const float *bias, int lane)
 {
     const int64_t col = col0 + (lane & 31);
     if (col >= N)
         return;
+    const float bv = bias ? bias[col] : 0.0f;
     const int64_t rbase = row0 + 4 * (lane >> 5);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -169,7 +172,10 @@ __device__ __forceinline__ void store_tile32(const floatx16 &acc, float *C, int6
         if (row < M) {
             float *p = C + row * ldc + col;
             const float s = acc[v];
-            *p = (beta == 0.0f) ? alpha * s : __builtin_fmaf(alpha, s, beta * *p);
+            float val = (beta == 0.0f) ? alpha * s : __builtin_fmaf(alpha, s, beta * *p);
+            if (bias)
+                val += bv;
+            *p = val;
         }
     }
 }
@@ -380,7 +386,7 @@ gemm_tiled(GemmArgs args)
         for (int j = 0; j < FN; ++j)
             store_tile32(acc[i][j], args.C, args.ldc, M, N,
                          m0 + wm * Cfg::WTM + i * 32, n0 + wn * Cfg::WTN + j * 32,
-                         args.alpha, args.beta, lane);
+                         args.alpha, args.beta, args.bias, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -415,19 +421,23 @@ gemm_direct(GemmArgs args)
         }
         acc = mfma32<IN>(a, b, acc);
     }
-    store_tile32(acc, args.C, args.ldc, args.M, args.N, row0, col0, args.alpha, args.beta, lane);
+    store_tile32(acc, args.C, args.ldc, args.M, args.N, row0, col0, args.alpha, args.beta, args.bias,
+                 lane);
 }
 
-// C <- beta*C (beta == 0 writes zeros without reading C).  Grid-stride over
-// rows in y and columns in x.
+// C <- beta*C (+ bias[j]); beta == 0 writes without reading C.  Grid-stride
+// over rows in y and columns in x.
 __global__ void __launch_bounds__(256)
-scale_c(float *C, int64_t M, int64_t N, int64_t ldc, float beta)
+scale_c(float *C, int64_t M, int64_t N, int64_t ldc, float beta, const float *bias)
 {
     for (int64_t i = blockIdx.y; i < M; i += gridDim.y) {
         for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < N;
              j += (int64_t)gridDim.x * blockDim.x) {
             float *p = C + i * ldc + j;
-            *p = (beta == 0.0f) ? 0.0f : beta * *p;
+            float v = (beta == 0.0f) ? 0.0f : beta * *p;
+            if (bias)
+                v += bias[j];
+            *p = v;
         }
     }
 }
@@ -937,6 +947,20 @@ gemm_pipe(GemmArgs args)
         const float alpha = args.alpha, beta = args.beta;
         const int cl = lane & 31;
         const int rl = 4 * (lane >> 5);
+        // the bias of each of this lane's FN columns (0 past the last column)
+        float bv[FN];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            bv[j] = 0.0f;
+        if (args.bias) {
+            const __amdgpu_buffer_rsrc_t rsBias = make_rsrc(args.bias + wcol0);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int c = 32 * j + cl;
+                bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                      rsBias, c < wcols ? (uint32_t)(c * 4) : kOOB, 0, 0));
+            }
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -952,6 +976,8 @@ gemm_pipe(GemmArgs args)
                         val = __builtin_fmaf(beta,
                                              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsC, off, 0, 0)),
                                              val);
+                    if (args.bias)
+                        val += bv[j];
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off, 0, kStoreNT);
                 }
             }

@@ -261,12 +261,15 @@ struct Problem {
     float alpha, beta;
     int la, lb;  // storage orders of A and B
     int in_type; // MPGEMM_IN_F16 or MPGEMM_IN_BF16
+    const float *bias;  // per-column bias or nullptr
 };
 
 int64_t at_least_one(int64_t v) { return v > 1 ? v : 1; }
 
 int validate(const Problem &p)
 {
+    if (p.in_type != MPGEMM_IN_F16 && p.in_type != MPGEMM_IN_BF16)
+        return MPGEMM_ETYPE;
     if ((p.la != MPGEMM_ROW_MAJOR && p.la != MPGEMM_COL_MAJOR) ||
         (p.lb != MPGEMM_ROW_MAJOR && p.lb != MPGEMM_COL_MAJOR))
         return MPGEMM_ELAYOUT;
@@ -285,7 +288,8 @@ int validate(const Problem &p)
     const bool reads_ab = p.K > 0 && p.alpha != 0.0f;
     if (reads_ab && (p.A == nullptr || p.B == nullptr))
         return MPGEMM_ENULL;
-    if ((reinterpret_cast<uintptr_t>(p.C) & 3u) != 0)
+    if ((reinterpret_cast<uintptr_t>(p.C) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(p.bias) & 3u) != 0)
         return MPGEMM_EALIGN;
     if (reads_ab && (((reinterpret_cast<uintptr_t>(p.A) | reinterpret_cast<uintptr_t>(p.B)) & 1u) != 0))
         return MPGEMM_EALIGN;
@@ -425,7 +429,7 @@ int run(int id, const Problem &p, void *stream)
         const int64_t gx = cdiv(p.N, 256) < 64 ? cdiv(p.N, 256) : 64;
         const int64_t gy = p.M < 65535 ? p.M : 65535;
         hipLaunchKernelGGL(mpg::scale_c, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s,
-                           const_cast<float *>(p.C), p.M, p.N, p.ldc, p.beta);
+                           const_cast<float *>(p.C), p.M, p.N, p.ldc, p.beta, p.bias);
         return hipGetLastError() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
     }
     GemmArgs a;
@@ -444,6 +448,7 @@ int run(int id, const Problem &p, void *stream)
     a.b_j = p.lb == MPGEMM_COL_MAJOR ? p.ldb : 1;
     a.alpha = p.alpha;
     a.beta = p.beta;
+    a.bias = p.bias;
     const int64_t grid = grid_for(e.cfg, p);
     if (e.cfg.kind == MPGEMM_KIND_DIRECT) {
         a.tiles_m = (int32_t)cdiv(p.M, 64);
@@ -465,16 +470,17 @@ int run(int id, const Problem &p, void *stream)
 Problem make_problem(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                      const uint16_t *B, int64_t ldb, const float *C, int64_t ldc,
                      float alpha, float beta, int la = MPGEMM_ROW_MAJOR, int lb = MPGEMM_ROW_MAJOR,
-                     int in_type = MPGEMM_IN_F16)
+                     int in_type = MPGEMM_IN_F16, const float *bias = nullptr)
 {
-    return Problem{M, N, K, lda, ldb, ldc, A, B, C, alpha, beta, la, lb, in_type};
+    return Problem{M, N, K, lda, ldb, ldc, A, B, C, alpha, beta, la, lb, in_type, bias};
 }
 
 int gemm_layout(int in_type, int la, int lb, int64_t M, int64_t N, int64_t K, const uint16_t *A,
                 int64_t lda, const uint16_t *B, int64_t ldb, float *C, int64_t ldc, float alpha,
-                float beta, void *stream)
+                float beta, void *stream, const float *bias = nullptr)
 {
-    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb, in_type);
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb, in_type,
+                                   bias);
     const int rc = validate(p);
     if (rc != MPGEMM_OK)
         return rc;
@@ -496,11 +502,13 @@ int query_layout(int in_type, int la, int lb, int64_t M, int64_t N, int64_t K, c
 
 int with_config_layout(int in_type, int config_id, int la, int lb, int64_t M, int64_t N,
                        int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
-                       float *C, int64_t ldc, float alpha, float beta, void *stream)
+                       float *C, int64_t ldc, float alpha, float beta, void *stream,
+                       const float *bias = nullptr)
 {
     if (config_id < 0 || config_id >= kNumEntries)
         return MPGEMM_ECONFIG;
-    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb, in_type);
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, la, lb, in_type,
+                                   bias);
     const int rc = validate(p);
     if (rc != MPGEMM_OK)
         return rc;
@@ -599,6 +607,23 @@ int mpgemm_bf16f32_layout_with_config(int config_id, int layout_a, int layout_b,
                               ldb, C, ldc, alpha, beta, stream);
 }
 
+int mpgemm_gemm_ex(int in_type, int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
+                   const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float *C,
+                   int64_t ldc, float alpha, float beta, const float *bias, void *stream)
+{
+    return gemm_layout(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                       stream, bias);
+}
+
+int mpgemm_gemm_ex_with_config(int config_id, int in_type, int layout_a, int layout_b, int64_t M,
+                               int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                               const uint16_t *B, int64_t ldb, float *C, int64_t ldc, float alpha,
+                               float beta, const float *bias, void *stream)
+{
+    return with_config_layout(in_type, config_id, layout_a, layout_b, M, N, K, A, lda, B, ldb, C,
+                              ldc, alpha, beta, stream, bias);
+}
+
 int mpgemm_num_configs(void) { return kNumEntries; }
 
 int mpgemm_config_info(int config_id, mpgemm_config *out)
@@ -642,11 +667,13 @@ const char *mpgemm_strerror(int code)
         return "A/B are not 2-byte aligned or C is not 4-byte aligned";
     case MPGEMM_ELAYOUT:
         return "a layout is neither MPGEMM_ROW_MAJOR nor MPGEMM_COL_MAJOR";
+    case MPGEMM_ETYPE:
+        return "the input type is neither MPGEMM_IN_F16 nor MPGEMM_IN_BF16";
     default:
         return "unknown error code";
     }
 }
 
-const char *mpgemm_version(void) { return "mpgemm 0.3.0 gfx950"; }
+const char *mpgemm_version(void) { return "mpgemm 0.4.0 gfx950"; }
 
 }  // extern "C"

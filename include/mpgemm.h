@@ -55,8 +55,9 @@ extern "C" {
 #define MPGEMM_ENULL (-3)      /* NULL pointer for an operand that must be read   */
 #define MPGEMM_ELAUNCH (-4)    /* the HIP launch failed                           */
 #define MPGEMM_ECONFIG (-5)    /* unknown config id, or it cannot run these args  */
-#define MPGEMM_EALIGN (-6)     /* A/B not 2-byte aligned or C not 4-byte aligned  */
+#define MPGEMM_EALIGN (-6)     /* A/B not 2-byte aligned, C or bias not 4-byte    */
 #define MPGEMM_ELAYOUT (-7)    /* a layout argument is not one of MPGEMM_*_MAJOR  */
+#define MPGEMM_ETYPE (-8)      /* an input type is not one of MPGEMM_IN_*         */
 
 /* Storage order of A or B (C is always row-major). */
 #define MPGEMM_ROW_MAJOR 0
@@ -219,6 +220,39 @@ int mpgemm_bf16f32_layout_with_config(int config_id, int layout_a, int layout_b,
                                       float alpha, float beta,
                                       void *stream);
 
+/*
+ * Everything in one call: input format (MPGEMM_IN_F16 or MPGEMM_IN_BF16),
+ * storage orders (as for mpgemm_f16f32_layout) and an optional per-column
+ * bias, the position-dependent epilogue of "Tensor cores with WMMA",
+ * section "The habit this API takes away" (a bias per column):
+ *
+ *     C[i][j] <- alpha * sum_k A[i][k] * B[k][j] + beta * C[i][j] + bias[j]
+ *
+ * bias: N floats in device memory, 4-byte aligned, read-only, caller-owned;
+ * NULL means no bias (the other entry points are this call with NULL).  The
+ * bias is added in FP32 after the alpha and beta terms, also when alpha == 0
+ * or K == 0 (then C <- beta*C + bias[j], C not read when beta == 0).
+ * MPGEMM_ETYPE for an unknown input format; other errors as mpgemm_f16f32.
+ */
+int mpgemm_gemm_ex(int in_type, int layout_a, int layout_b,
+                   int64_t M, int64_t N, int64_t K,
+                   const uint16_t *A, int64_t lda,
+                   const uint16_t *B, int64_t ldb,
+                   float *C, int64_t ldc,
+                   float alpha, float beta,
+                   const float *bias,
+                   void *stream);
+
+/* mpgemm_gemm_ex forced onto table entry `config_id` (tests and sweeps). */
+int mpgemm_gemm_ex_with_config(int config_id, int in_type, int layout_a, int layout_b,
+                               int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda,
+                               const uint16_t *B, int64_t ldb,
+                               float *C, int64_t ldc,
+                               float alpha, float beta,
+                               const float *bias,
+                               void *stream);
+
 /* Number of entries in the config table. */
 int mpgemm_num_configs(void);
 
@@ -240,7 +274,7 @@ int mpgemm_probe_mfma_layout(int shape, float *out, void *stream);
 /* Static text for an error code (never NULL). */
 const char *mpgemm_strerror(int code);
 
-/* Library version string, e.g. "mpgemm 0.3.0 gfx950". */
+/* Library version string, e.g. "mpgemm 0.4.0 gfx950". */
 const char *mpgemm_version(void);
 
 #ifdef __cplusplus

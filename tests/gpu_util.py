@@ -149,7 +149,7 @@ def stored(X, col_major):
 
 
 def run_layout(A, B, C0, alpha, beta, layout_a, layout_b, config=None, lda=None, ldb=None,
-               ldc=None, a_off=0, b_off=0, poison=True):
+               ldc=None, a_off=0, b_off=0, poison=True, bias=None):
     """Like run(), with A and/or B stored column-major.  A (M,K) and B (K,N)
     are the logical host matrices; a column-major operand is stored as its
     transpose (leading dimension lda >= M or ldb >= K) and handed to the
@@ -166,6 +166,7 @@ def run_layout(A, B, C0, alpha, beta, layout_a, layout_b, config=None, lda=None,
         gC = Guarded(C0, ld=ldc)
     a_view = gA.view().t() if layout_a else gA.view()
     b_view = gB.view().t() if layout_b else gB.view()
-    mp.gemm(a_view, b_view, gC.view(), alpha, beta, config=config)
+    bias_dev = None if bias is None else torch.as_tensor(bias, dtype=torch.float32).to(device())
+    mp.gemm(a_view, b_view, gC.view(), alpha, beta, config=config, bias=bias_dev)
     torch.cuda.synchronize()
     return gC.result(), gC

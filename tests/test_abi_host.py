@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert "gfx950" in mp.mpgemm_version()
-    for code in range(-6, 1):
+    for code in range(-8, 1):
         assert mp.mpgemm_strerror(code)
     assert mp.mpgemm_strerror(-99) == "unknown error code"
 
@@ -267,3 +267,13 @@ def test_bf16_and_f16_entries_do_not_mix():
     assert mp.mpgemm_bf16f32(-1, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0) == mp.MPGEMM_EDIM
     assert mp.mpgemm_bf16f32_layout(5, 0, 4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0) \
         == mp.MPGEMM_ELAYOUT
+
+
+def test_gemm_ex_validation_before_launch():
+    args = (4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0)
+    assert mp.mpgemm_gemm_ex(2, 0, 0, *args, 0, 0) == mp.MPGEMM_ETYPE
+    assert mp.mpgemm_gemm_ex(0, 2, 0, *args, 0, 0) == mp.MPGEMM_ELAYOUT
+    assert mp.mpgemm_gemm_ex(0, 0, 0, *args, FAKE_C + 0x1000 + 2, 0) == mp.MPGEMM_EALIGN
+    assert mp.mpgemm_gemm_ex(0, 0, 0, -1, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0, 0) \
+        == mp.MPGEMM_EDIM
+    assert mp.mpgemm_gemm_ex_with_config(999, 0, 0, 0, *args, 0, 0) == mp.MPGEMM_ECONFIG
