@@ -90,22 +90,24 @@ def measured_traffic(workload: str, kernel_ms: float):
             "GBps": round((read_b + write_b) / (kernel_ms * 1e-3) / 1e9, 1), "source": os.path.relpath(path, ROOT)}
 
 
-def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0):
+def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=None, bias=False):
     """Time `steps` launches (after `warmup`) on resident inputs.  A column-
     major operand is stored transposed on the device and passed as the
-    transposed view."""
+    transposed view; `dtype` picks FP16 (default) or BF16 inputs; `bias`
+    adds a per-column bias vector to the epilogue."""
     from dense_mixed_precision_amd.workloads import workload_inputs
 
     dev = torch.device("cuda:0")
-    A, B, C = workload_inputs(w)
+    A, B, C = workload_inputs(w, dtype or torch.float16)
     Ad = A.t().contiguous().to(dev).t() if layout_a else A.to(dev)
     Bd = B.t().contiguous().to(dev).t() if layout_b else B.to(dev)
     Cd = C.to(dev) if C is not None else torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     cfg = mp.query_for(Ad, Bd, Cd, w.alpha, w.beta)
+    bias_d = torch.rand(w.N, device=dev) * 2 - 1 if bias else None
 
     def step():
-        mp.gemm(Ad, Bd, Cd, w.alpha, w.beta, stream=stream)
+        mp.gemm(Ad, Bd, Cd, w.alpha, w.beta, stream=stream, bias=bias_d)
 
     for _ in range(warmup):
         step()
@@ -134,11 +136,22 @@ def _smi_power():
     except (OSError, subprocess.SubprocessError):
         return None
     power = re.findall(r"SOCKET_POWER:\s*([0-9.]+)\s*W", out)
-    clocks = [float(x) for x in re.findall(r"^\s*CLK:\s*([0-9.]+)\s*MHz", out, re.M)]
+    # the CLK line of each GFX_<n> section (one per XCD); other clock domains
+    # (memory, video) have sections of their own
+    clocks, section = [], ""
+    for line in out.splitlines():
+        m = re.match(r"^\s*([A-Z]+_?\d*):\s*$", line)
+        if m:
+            section = m.group(1)
+            continue
+        m = re.match(r"^\s*CLK:\s*([0-9.]+)\s*MHz", line)
+        if m and section.startswith("GFX"):
+            clocks.append(float(m.group(1)))
     if not power:
         return None
     return {"socket_w": float(power[0]),
-            "gfx_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None}
+            "gfx_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None,
+            "gfx_sections": len(clocks)}
 
 
 def sample_power(w, torch, mp, seconds=2.0):
@@ -298,17 +311,22 @@ def main():
                             "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "vec_a", "vec_b", "grid")}}
             del r
             torch.cuda.empty_cache()
-        # the column-major operand modes on the two headline shapes
+        # the column-major operand modes, BF16 inputs and the bias epilogue
+        # on the two headline shapes
+        variants = [(0, 1, None, False, "Bcol"), (1, 1, None, False, "AcolBcol"),
+                    (0, 0, torch.bfloat16, False, "bf16"), (0, 1, torch.bfloat16, False, "bf16_Bcol"),
+                    (0, 0, None, True, "bias")]
         for base in ("square2048", "square8192"):
             w = WORKLOADS[base]
-            for la, lb, tag in ((0, 1, "Bcol"), (1, 1, "AcolBcol")):
+            for la, lb, dt, with_bias, tag in variants:
                 name = f"{base}_{tag}"
                 steps = max(5, min(args.steps, 20 if w.flop > 1e12 else args.steps))
                 print(f"# timing {name} ({steps} steps)", file=sys.stderr, flush=True)
-                r = time_workload(w, steps, max(3, args.warmup // 2), torch, mp, la, lb)
+                r = time_workload(w, steps, max(3, args.warmup // 2), torch, mp, la, lb, dt, with_bias)
                 others[name] = {"tflops": round(w.flop / (r["kernel_ms"] * 1e-3) / 1e12, 2),
                                 "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
                                 "layout": {"A": "col" if la else "row", "B": "col" if lb else "row"},
+                                "inputs": "bf16" if dt is not None else "f16", "bias": with_bias,
                                 "pct_of_peak": round(100 * w.flop / (r["kernel_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
                                 "roofline": roofline_entry(w, r["kernel_ms"]),
                                 "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "bk", "vec_a", "vec_b", "grid")}}
