@@ -18,6 +18,7 @@ integers holding device addresses, ``stream`` a hipStream_t as an integer,
     mpgemm_bf16f32_layout_with_config: the same with BF16 inputs
     mpgemm_gemm_ex(in_type, layout_a, layout_b, M, N, K, ..., alpha, beta, bias, stream) -> int
     mpgemm_gemm_ex_with_config(cfg, in_type, layout_a, layout_b, ...) -> int   (per-column bias)
+    mpgemm_splitk_plan(...) -> dict, mpgemm_gemm_splitk(..., splits, workspace, bytes, stream) -> int
     mpgemm_num_configs(), mpgemm_config_info(id), mpgemm_probe_mfma_layout(shape, out, stream)
     mpgemm_strerror(code), mpgemm_version()
 
@@ -33,7 +34,9 @@ from ._binding import (  # noqa: F401
     MPGEMM_EDIM,
     MPGEMM_ELAUNCH,
     MPGEMM_ELAYOUT,
+    MPGEMM_ESPLIT,
     MPGEMM_ETYPE,
+    MPGEMM_EWORKSPACE,
     MPGEMM_ELD,
     MPGEMM_ENULL,
     MPGEMM_OK,
@@ -59,6 +62,10 @@ from ._binding import (  # noqa: F401
     mpgemm_bf16f32_layout_with_config,
     mpgemm_gemm_ex,
     mpgemm_gemm_ex_with_config,
+    mpgemm_splitk_plan,
+    mpgemm_gemm_splitk,
+    gemm_splitk,
+    splitk_plan_for,
     mpgemm_num_configs,
     mpgemm_probe_mfma_layout,
     mpgemm_strerror,

@@ -16,6 +16,8 @@ MPGEMM_ECONFIG = -5
 MPGEMM_EALIGN = -6
 MPGEMM_ELAYOUT = -7
 MPGEMM_ETYPE = -8
+MPGEMM_EWORKSPACE = -9
+MPGEMM_ESPLIT = -10
 
 MPGEMM_ROW_MAJOR = 0
 MPGEMM_COL_MAJOR = 1
@@ -87,6 +89,12 @@ def load():
     lib.mpgemm_gemm_ex.restype = i32
     lib.mpgemm_gemm_ex_with_config.argtypes = [i32, i32, i32, i32] + gemm_args + [vp, vp]
     lib.mpgemm_gemm_ex_with_config.restype = i32
+    lib.mpgemm_splitk_plan.argtypes = [i32, i32, i32, i64, i64, i64, vp, i64, vp, i64, i32,
+                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(i64),
+                                       ctypes.POINTER(ctypes.c_int32)]
+    lib.mpgemm_splitk_plan.restype = i32
+    lib.mpgemm_gemm_splitk.argtypes = [i32, i32, i32] + gemm_args + [vp, i32, vp, i64, vp]
+    lib.mpgemm_gemm_splitk.restype = i32
     lib.mpgemm_num_configs.argtypes = []
     lib.mpgemm_num_configs.restype = i32
     lib.mpgemm_config_info.argtypes = [i32, ctypes.POINTER(MpgemmConfig)]
@@ -186,6 +194,25 @@ def mpgemm_gemm_ex_with_config(config_id, in_type, layout_a, layout_b, M, N, K, 
                                C, ldc, alpha, beta, bias=0, stream=0) -> int:
     return int(load().mpgemm_gemm_ex_with_config(config_id, in_type, layout_a, layout_b, M, N, K,
                                                  A, lda, B, ldb, C, ldc, alpha, beta, bias, stream))
+
+
+def mpgemm_splitk_plan(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb,
+                       splits_requested=0) -> dict:
+    """The split-K plan: {"splits", "workspace_bytes", "config_id"}."""
+    sp, ws, cid = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int32()
+    rc = load().mpgemm_splitk_plan(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb,
+                                   splits_requested, ctypes.byref(sp), ctypes.byref(ws),
+                                   ctypes.byref(cid))
+    if rc != MPGEMM_OK:
+        raise MpgemmError(rc, "mpgemm_splitk_plan")
+    return {"splits": int(sp.value), "workspace_bytes": int(ws.value), "config_id": int(cid.value)}
+
+
+def mpgemm_gemm_splitk(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha, beta,
+                       bias=0, splits_requested=0, workspace=0, workspace_bytes=0, stream=0) -> int:
+    return int(load().mpgemm_gemm_splitk(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb, C,
+                                         ldc, alpha, beta, bias, splits_requested, workspace,
+                                         workspace_bytes, stream))
 
 
 def mpgemm_num_configs() -> int:
@@ -321,3 +348,35 @@ def query_for(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> dict:
     fn = mpgemm_bf16f32_layout_query if _in_type(A) == MPGEMM_IN_BF16 else mpgemm_f16f32_layout_query
     return fn(la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc,
               float(alpha), float(beta))
+
+
+def splitk_plan_for(A, B, C, splits: int = 0) -> dict:
+    """The split-K plan for these tensors (no launch)."""
+    M, N, K, la, lda, lb, ldb, ldc = _args(A, B, C)
+    return mpgemm_splitk_plan(_in_type(A), la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                              int(splits))
+
+
+def gemm_splitk(A, B, C, alpha: float = 1.0, beta: float = 0.0, bias=None, splits: int = 0,
+                workspace=None, stream=None):
+    """Split-K form of :func:`gemm`.  ``splits`` 0 lets the library decide.
+    ``workspace``: a float32 GPU tensor of at least the planned size; when
+    None, one is allocated here (by torch, on the caller's side of the C
+    ABI) for this call."""
+    import torch
+    M, N, K, la, lda, lb, ldb, ldc = _args(A, B, C)
+    plan = mpgemm_splitk_plan(_in_type(A), la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                              int(splits))
+    if workspace is None and plan["workspace_bytes"] > 0:
+        workspace = torch.empty(plan["workspace_bytes"] // 4, dtype=torch.float32, device=C.device)
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    rc = mpgemm_gemm_splitk(_in_type(A), la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                            C.data_ptr(), ldc, float(alpha), float(beta), _bias_ptr(bias, N),
+                            int(splits), ws_ptr, ws_bytes, handle)
+    if rc != MPGEMM_OK:
+        raise MpgemmError(rc, "mpgemm_gemm_splitk")
+    return C

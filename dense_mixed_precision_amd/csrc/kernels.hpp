@@ -115,6 +115,13 @@ struct GemmArgs {
     const float *bias;
     int32_t tiles_m, tiles_n;
     int32_t group_m;
+    // split-K (pipelined kernel only): when splits > 1 the grid holds
+    // `splits` copies of the tile grid; copy s sums k in [s*k_split,
+    // (s+1)*k_split) and writes its unscaled partial tile to ws + s*M*N (rows
+    // of N), which a reduction then combines in a fixed order.
+    int32_t splits;
+    int64_t k_split;
+    float *ws;
 };
 
 // Input format of A and B: IEEE binary16 or bfloat16.  Both are 16-bit
@@ -425,6 +432,31 @@ gemm_direct(GemmArgs args)
                  lane);
 }
 
+// Split-K reduction: C <- alpha * sum_{s<splits} ws[s] + beta*C (+ bias[j]),
+// the partials summed in ascending s (run-to-run deterministic).  ws holds
+// `splits` row-major M x N partial products, rows of N.  Grid-stride over
+// rows in y and columns in x.
+__global__ void __launch_bounds__(256)
+splitk_reduce(float *C, int64_t M, int64_t N, int64_t ldc, const float *ws, int splits,
+              float alpha, float beta, const float *bias)
+{
+    for (int64_t i = blockIdx.y; i < M; i += gridDim.y) {
+        for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < N;
+             j += (int64_t)gridDim.x * blockDim.x) {
+            float acc = 0.0f;
+            for (int s = 0; s < splits; ++s)
+                acc += ws[(int64_t)s * M * N + i * N + j];
+            float *p = C + i * ldc + j;
+            float v = alpha * acc;
+            if (beta != 0.0f)
+                v = __builtin_fmaf(beta, *p, v);
+            if (bias)
+                v += bias[j];
+            *p = v;
+        }
+    }
+}
+
 // C <- beta*C (+ bias[j]); beta == 0 writes without reading C.  Grid-stride
 // over rows in y and columns in x.
 __global__ void __launch_bounds__(256)
@@ -725,7 +757,7 @@ struct OpReader {
 
 template <class Cfg>
 __global__ void __launch_bounds__(Cfg::NT)
-gemm_pipe(GemmArgs args)
+gemm_pipe(GemmArgs args_in)
 {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, S = Cfg::STAGES;
     constexpr int FM = Cfg::FM, FN = Cfg::FN, KS = Cfg::KS;
@@ -747,8 +779,29 @@ gemm_pipe(GemmArgs args)
     const int wm = wave / Cfg::WAVES_N;
     const int wn = wave % Cfg::WAVES_N;
 
+    // Split-K: this workgroup's K range and partial-sum destination; the rest
+    // of the kernel sees an ordinary product over that range.
+    GemmArgs args = args_in;
+    int bid = blockIdx.x, nb = gridDim.x;
+    if (args.splits > 1) {
+        const int ntiles = args.tiles_m * args.tiles_n;
+        const int split = bid / ntiles;
+        bid -= split * ntiles;
+        nb = ntiles;
+        const int64_t k0 = (int64_t)split * args.k_split;
+        const int64_t klen = args.K - k0 < args.k_split ? args.K - k0 : args.k_split;
+        args.A += A_ROW ? k0 : k0 * args.lda;
+        args.B += B_ROW ? k0 * args.ldb : k0;
+        args.K = klen > 0 ? klen : 0;
+        args.C = args.ws + (int64_t)split * args.M * args.N;
+        args.ldc = args.N;
+        args.alpha = 1.0f;
+        args.beta = 0.0f;
+        args.bias = nullptr;
+    }
+
     int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, args.tiles_n, args.tiles_m, args.group_m, tm, tn);
+    tile_coords(bid, nb, args.tiles_n, args.tiles_m, args.group_m, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
     const int64_t K = args.K;

@@ -449,6 +449,9 @@ int run(int id, const Problem &p, void *stream)
     a.alpha = p.alpha;
     a.beta = p.beta;
     a.bias = p.bias;
+    a.splits = 1;
+    a.k_split = 0;
+    a.ws = nullptr;
     const int64_t grid = grid_for(e.cfg, p);
     if (e.cfg.kind == MPGEMM_KIND_DIRECT) {
         a.tiles_m = (int32_t)cdiv(p.M, 64);
@@ -465,6 +468,88 @@ int run(int id, const Problem &p, void *stream)
     (void)hipGetLastError();
     const hipError_t err = e.launch(a, dim3((unsigned)grid), s);
     return err == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K for grids that leave compute units idle
+// ---------------------------------------------------------------------------
+struct SplitPlan {
+    int id;           // table entry of the tile kernel
+    int splits;       // K ranges (1: no split)
+    int64_t k_split;  // elements of K per range, a multiple of the entry's bk
+    int64_t ws_bytes; // workspace the partial products need
+};
+
+// `requested` 0: automatic (split only when the tile grid fills less than
+// half the chip, up to 16 ranges of at least 4 K tiles each); otherwise that
+// many ranges, at most one per K tile.  Empty ranges are never planned.
+SplitPlan plan_split(const Problem &p, int requested)
+{
+    SplitPlan sp{select(p), 1, 0, 0};
+    if (sp.id < 0 || p.K == 0 || p.alpha == 0.0f)
+        return sp;
+    const mpgemm_config &c = kTable[sp.id].cfg;
+    if (c.kind != MPGEMM_KIND_PIPE)
+        return sp;
+    const int64_t tiles = grid_for(c, p);
+    const int64_t ktiles = cdiv(p.K, c.bk);
+    int64_t s;
+    if (requested == 0) {
+        s = tiles >= kNumCu / 2 ? 1 : cdiv(kNumCu, tiles);
+        if (s > 16)
+            s = 16;
+        if (s > ktiles / 4)
+            s = ktiles / 4;
+    } else {
+        s = requested < ktiles ? requested : ktiles;
+    }
+    if (s <= 1)
+        return sp;
+    sp.k_split = cdiv(ktiles, s) * c.bk;
+    sp.splits = (int)cdiv(p.K, sp.k_split);
+    if (sp.splits <= 1 || tiles * sp.splits > 0x7FFFFFFF) {
+        sp.splits = 1;
+        sp.k_split = 0;
+        return sp;
+    }
+    sp.ws_bytes = (int64_t)sp.splits * p.M * p.N * 4;
+    return sp;
+}
+
+int run_split(const SplitPlan &sp, const Problem &p, float *ws, void *stream)
+{
+    const Entry &e = kTable[sp.id];
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    GemmArgs a{};
+    a.A = p.A;
+    a.B = p.B;
+    a.C = const_cast<float *>(p.C);
+    a.M = p.M;
+    a.N = p.N;
+    a.K = p.K;
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.alpha = p.alpha;
+    a.beta = p.beta;
+    a.bias = p.bias;
+    a.tiles_m = (int32_t)cdiv(p.M, e.cfg.bm);
+    a.tiles_n = (int32_t)cdiv(p.N, e.cfg.bn);
+    a.group_m = 8;
+    a.splits = sp.splits;
+    a.k_split = sp.k_split;
+    a.ws = ws;
+    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * sp.splits;
+    (void)hipGetLastError();
+    hipError_t err = e.launch(a, dim3((unsigned)grid), s);
+    if (err != hipSuccess)
+        return MPGEMM_ELAUNCH;
+    const int64_t gx = cdiv(p.N, 256) < 64 ? cdiv(p.N, 256) : 64;
+    const int64_t gy = p.M < 65535 ? p.M : 65535;
+    hipLaunchKernelGGL(mpg::splitk_reduce, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s,
+                       const_cast<float *>(p.C), p.M, p.N, p.ldc, ws, sp.splits, p.alpha, p.beta,
+                       p.bias);
+    return hipGetLastError() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
 }
 
 Problem make_problem(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
@@ -624,6 +709,55 @@ int mpgemm_gemm_ex_with_config(int config_id, int in_type, int layout_a, int lay
                               ldc, alpha, beta, stream, bias);
 }
 
+int mpgemm_splitk_plan(int in_type, int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                       int splits_requested, int32_t *splits, int64_t *workspace_bytes,
+                       int32_t *config_id)
+{
+    if (splits_requested < 0)
+        return MPGEMM_ESPLIT;
+    // C is not touched by planning: any aligned stand-in passes validation
+    static const float c_stand_in = 0.0f;
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, &c_stand_in, N > 1 ? N : 1, 1.0f,
+                                   0.0f, layout_a, layout_b, in_type);
+    const int rc = validate(p);
+    if (rc != MPGEMM_OK)
+        return rc;
+    const SplitPlan sp = plan_split(p, splits_requested);
+    if (splits)
+        *splits = sp.splits;
+    if (workspace_bytes)
+        *workspace_bytes = sp.ws_bytes;
+    if (config_id)
+        *config_id = sp.id;
+    return MPGEMM_OK;
+}
+
+int mpgemm_gemm_splitk(int in_type, int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float *C,
+                       int64_t ldc, float alpha, float beta, const float *bias,
+                       int splits_requested, float *workspace, int64_t workspace_bytes,
+                       void *stream)
+{
+    if (splits_requested < 0)
+        return MPGEMM_ESPLIT;
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, layout_a,
+                                   layout_b, in_type, bias);
+    const int rc = validate(p);
+    if (rc != MPGEMM_OK)
+        return rc;
+    const SplitPlan sp = plan_split(p, splits_requested);
+    if (sp.splits <= 1)
+        return run(sp.id, p, stream);
+    if (workspace == nullptr)
+        return MPGEMM_ENULL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0)
+        return MPGEMM_EALIGN;
+    if (workspace_bytes < sp.ws_bytes)
+        return MPGEMM_EWORKSPACE;
+    return run_split(sp, p, workspace, stream);
+}
+
 int mpgemm_num_configs(void) { return kNumEntries; }
 
 int mpgemm_config_info(int config_id, mpgemm_config *out)
@@ -669,11 +803,15 @@ const char *mpgemm_strerror(int code)
         return "a layout is neither MPGEMM_ROW_MAJOR nor MPGEMM_COL_MAJOR";
     case MPGEMM_ETYPE:
         return "the input type is neither MPGEMM_IN_F16 nor MPGEMM_IN_BF16";
+    case MPGEMM_EWORKSPACE:
+        return "the split-K workspace is smaller than mpgemm_splitk_plan reports";
+    case MPGEMM_ESPLIT:
+        return "a negative split count was requested";
     default:
         return "unknown error code";
     }
 }
 
-const char *mpgemm_version(void) { return "mpgemm 0.4.0 gfx950"; }
+const char *mpgemm_version(void) { return "mpgemm 0.5.0 gfx950"; }
 
 }  // extern "C"

@@ -58,6 +58,8 @@ extern "C" {
 #define MPGEMM_EALIGN (-6)     /* A/B not 2-byte aligned, C or bias not 4-byte    */
 #define MPGEMM_ELAYOUT (-7)    /* a layout argument is not one of MPGEMM_*_MAJOR  */
 #define MPGEMM_ETYPE (-8)      /* an input type is not one of MPGEMM_IN_*         */
+#define MPGEMM_EWORKSPACE (-9) /* split-K workspace smaller than planned          */
+#define MPGEMM_ESPLIT (-10)    /* negative split count requested                  */
 
 /* Storage order of A or B (C is always row-major). */
 #define MPGEMM_ROW_MAJOR 0
@@ -253,6 +255,49 @@ int mpgemm_gemm_ex_with_config(int config_id, int in_type, int layout_a, int lay
                                const float *bias,
                                void *stream);
 
+/*
+ * Split-K for products whose tile grid leaves compute units idle (few
+ * output tiles, long K: the "skinny" 4096 x 16 x 4096 case of "Capstone 4: a
+ * tensor-core GEMM", section "Independent gate").  The K range is cut into
+ * `splits` pieces; each piece's workgroups write their unscaled FP32 partial
+ * product to a caller-provided workspace, and a second kernel sums the
+ * pieces in a fixed order (so results are run-to-run identical) and applies
+ * alpha, beta and the bias:
+ *
+ *     C[i][j] <- alpha * sum_s P_s[i][j] + beta * C[i][j] + bias[j]
+ *
+ * mpgemm_splitk_plan reports, without any HIP call, how many pieces a call
+ * would use (`splits_requested` 0: automatic, split only when the grid
+ * fills less than half the chip; n > 0: n pieces, at most one per K tile of
+ * the chosen kernel), the workspace bytes that needs (splits*M*N*4; 0 when
+ * splits == 1) and the tile kernel's table entry.  Output pointers may be
+ * NULL.  Arguments as for mpgemm_gemm_ex; C, alpha and beta are not needed
+ * to plan.
+ *
+ * mpgemm_gemm_splitk runs it: workspace is device memory the caller owns,
+ * 4-byte aligned, at least the planned size (else MPGEMM_EWORKSPACE; NULL
+ * with a non-zero plan is MPGEMM_ENULL); it may be NULL when the plan is a
+ * single piece, which runs the ordinary path.  Calls that share a workspace
+ * must not overlap in time.
+ */
+int mpgemm_splitk_plan(int in_type, int layout_a, int layout_b,
+                       int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda,
+                       const uint16_t *B, int64_t ldb,
+                       int splits_requested,
+                       int32_t *splits, int64_t *workspace_bytes, int32_t *config_id);
+
+int mpgemm_gemm_splitk(int in_type, int layout_a, int layout_b,
+                       int64_t M, int64_t N, int64_t K,
+                       const uint16_t *A, int64_t lda,
+                       const uint16_t *B, int64_t ldb,
+                       float *C, int64_t ldc,
+                       float alpha, float beta,
+                       const float *bias,
+                       int splits_requested,
+                       float *workspace, int64_t workspace_bytes,
+                       void *stream);
+
 /* Number of entries in the config table. */
 int mpgemm_num_configs(void);
 
@@ -274,7 +319,7 @@ int mpgemm_probe_mfma_layout(int shape, float *out, void *stream);
 /* Static text for an error code (never NULL). */
 const char *mpgemm_strerror(int code);
 
-/* Library version string, e.g. "mpgemm 0.4.0 gfx950". */
+/* Library version string, e.g. "mpgemm 0.5.0 gfx950". */
 const char *mpgemm_version(void);
 
 #ifdef __cplusplus

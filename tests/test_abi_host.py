@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert "gfx950" in mp.mpgemm_version()
-    for code in range(-8, 1):
+    for code in range(-10, 1):
         assert mp.mpgemm_strerror(code)
     assert mp.mpgemm_strerror(-99) == "unknown error code"
 
@@ -277,3 +277,50 @@ def test_gemm_ex_validation_before_launch():
     assert mp.mpgemm_gemm_ex(0, 0, 0, -1, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0, 0) \
         == mp.MPGEMM_EDIM
     assert mp.mpgemm_gemm_ex_with_config(999, 0, 0, 0, *args, 0, 0) == mp.MPGEMM_ECONFIG
+
+
+# ----------------------------------------------------------------------------
+# Split-K plans
+# ----------------------------------------------------------------------------
+
+def plan(M, N, K, splits=0, la=0, lb=0, in_type=0, lda=None, ldb=None):
+    lda = max(M if la else K, 1) if lda is None else lda
+    ldb = max(K if lb else N, 1) if ldb is None else ldb
+    return mp.mpgemm_splitk_plan(in_type, la, lb, M, N, K, FAKE_A, lda, FAKE_B, ldb, splits)
+
+
+def test_splitk_plan_skinny_case_fills_the_chip():
+    p = plan(4096, 16, 4096)     # 64 tiles of 64x64 on 256 compute units
+    c = mp.mpgemm_config_info(p["config_id"])
+    tiles = (4096 // c["bm"]) * 1
+    assert p["splits"] * tiles >= 256 and p["splits"] <= 16
+    assert p["workspace_bytes"] == p["splits"] * 4096 * 16 * 4
+
+
+def test_splitk_plan_keeps_full_grids_whole():
+    for shape in [(2048, 2048, 2048), (8192, 8192, 8192), (32768, 128, 4096)]:
+        p = plan(*shape)
+        assert (p["splits"], p["workspace_bytes"]) == (1, 0), shape
+
+
+def test_splitk_plan_forced_and_capped():
+    p = plan(300, 200, 1234, splits=3)
+    assert p["splits"] == 3 and p["workspace_bytes"] == 3 * 300 * 200 * 4
+    bk = mp.mpgemm_config_info(p["config_id"])["bk"]
+    p = plan(300, 200, 100, splits=64)           # at most one piece per K tile
+    assert p["splits"] == -(-100 // bk)
+    assert plan(300, 200, 1234, splits=1)["splits"] == 1
+    assert plan(300, 200, 0)["splits"] == 1      # K == 0 is the scale path
+    with pytest.raises(mp.MpgemmError) as e:
+        plan(300, 200, 1234, splits=-1)
+    assert e.value.code == mp.MPGEMM_ESPLIT
+    with pytest.raises(mp.MpgemmError) as e:
+        plan(300, 200, 1234, la=3)
+    assert e.value.code == mp.MPGEMM_ELAYOUT
+
+
+def test_splitk_launch_checks_the_workspace_before_hip():
+    args = (0, 0, 0, 4096, 16, 4096, FAKE_A, 4096, FAKE_B, 16, FAKE_C, 16, 1.0, 0.0, 0, 0)
+    assert mp.mpgemm_gemm_splitk(*args, 0, 0, 0) == mp.MPGEMM_ENULL
+    assert mp.mpgemm_gemm_splitk(*args, FAKE_C + 0x100000, 1024, 0) == mp.MPGEMM_EWORKSPACE
+    assert mp.mpgemm_gemm_splitk(*args, FAKE_C + 0x100002, 1 << 30, 0) == mp.MPGEMM_EALIGN
