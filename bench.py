@@ -90,7 +90,8 @@ def measured_traffic(workload: str, kernel_ms: float):
             "GBps": round((read_b + write_b) / (kernel_ms * 1e-3) / 1e9, 1), "source": os.path.relpath(path, ROOT)}
 
 
-def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=None, bias=False):
+def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=None, bias=False,
+                  splitk=False):
     """Time `steps` launches (after `warmup`) on resident inputs.  A column-
     major operand is stored transposed on the device and passed as the
     transposed view; `dtype` picks FP16 (default) or BF16 inputs; `bias`
@@ -105,9 +106,17 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
     stream = torch.cuda.current_stream(dev)
     cfg = mp.query_for(Ad, Bd, Cd, w.alpha, w.beta)
     bias_d = torch.rand(w.N, device=dev) * 2 - 1 if bias else None
+    ws = None
+    if splitk:
+        plan = mp.splitk_plan_for(Ad, Bd, Cd)
+        cfg = dict(cfg, splits=plan["splits"])
+        ws = torch.empty(max(plan["workspace_bytes"] // 4, 1), dtype=torch.float32, device=dev)
 
     def step():
-        mp.gemm(Ad, Bd, Cd, w.alpha, w.beta, stream=stream, bias=bias_d)
+        if splitk:
+            mp.gemm_splitk(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, workspace=ws, stream=stream)
+        else:
+            mp.gemm(Ad, Bd, Cd, w.alpha, w.beta, stream=stream, bias=bias_d)
 
     for _ in range(warmup):
         step()
@@ -332,6 +341,20 @@ def main():
                                 "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "bk", "vec_a", "vec_b", "grid")}}
                 del r
                 torch.cuda.empty_cache()
+        # split-K on the pages' skinny case (64 output tiles for 256 compute units)
+        from dense_mixed_precision_amd.workloads import Workload
+        skinny = Workload("skinny4096x16x4096", 4096, 16, 4096, "uniform", 1.0, 0.0, None, 1005)
+        for tag, sk in (("", False), ("_splitk", True)):
+            name = skinny.name + tag
+            print(f"# timing {name} ({args.steps} steps)", file=sys.stderr, flush=True)
+            r = time_workload(skinny, args.steps, max(3, args.warmup // 2), torch, mp, splitk=sk)
+            others[name] = {"tflops": round(skinny.flop / (r["kernel_ms"] * 1e-3) / 1e12, 2),
+                            "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
+                            "roofline": roofline_entry(skinny, r["kernel_ms"]),
+                            "splits": r["cfg"].get("splits", 1),
+                            "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "bk", "grid")}}
+            del r
+            torch.cuda.empty_cache()
         line["workloads"] = others
     if args.power:
         line["power"] = sample_power(WORKLOADS["square8192"], torch, mp)
