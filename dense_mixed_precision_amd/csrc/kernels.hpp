@@ -583,19 +583,28 @@ struct OpTile {
     }
 };
 
+// KGROUPS > 1 splits the waves of a workgroup into groups that share every
+// LDS tile but take different k-steps of it, each group covering the whole
+// BM x BN block with WAVES_M x WAVES_N waves; the groups' sums are added in
+// LDS at the end.  For a small block this keeps the wave tiles large (fewer
+// LDS bytes per matrix instruction) while two waves per SIMD still hide
+// latency.
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int VEC_A_, int VEC_B_,
-          int LAYOUT_A_ = kRowMajor, int LAYOUT_B_ = kRowMajor, int IN_ = kInF16>
+          int LAYOUT_A_ = kRowMajor, int LAYOUT_B_ = kRowMajor, int IN_ = kInF16, int KGROUPS_ = 1>
 struct PipeCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int VEC_A = VEC_A_, VEC_B = VEC_B_;
     static constexpr int LAYOUT_A = LAYOUT_A_, LAYOUT_B = LAYOUT_B_;
     static constexpr int IN = IN_;
-    static constexpr int NW = WAVES_M * WAVES_N;
+    static constexpr int KGROUPS = KGROUPS_;
+    static constexpr int NWG = WAVES_M * WAVES_N;         // waves per k-group
+    static constexpr int NW = NWG * KGROUPS;              // waves per workgroup
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int KS = BK / 16;                    // MFMA k-steps per tile
+    static constexpr int KSL = KS / KGROUPS;              // ... taken by each k-group
     // row-major A and column-major B are K-contiguous in memory
     using TA = OpTile<BM, BK, LAYOUT_A == kRowMajor, NW>;
     using TB = OpTile<BN, BK, LAYOUT_B == kColMajor, NW>;
@@ -612,7 +621,10 @@ struct PipeCfg {
     // about the rate the memory system serves them, leaving the rest of the
     // tile as slack; deeper rings spread them over a whole tile.
     static constexpr int COPY_WINDOW =
-        STAGES == 2 ? (NCOPY < KS * FM ? (NCOPY > 0 ? NCOPY : 1) : KS * FM) : KS * FM;
+        STAGES == 2 ? (NCOPY < KSL * FM ? (NCOPY > 0 ? NCOPY : 1) : KSL * FM) : KSL * FM;
+    static_assert(KGROUPS >= 1 && KS % KGROUPS == 0, "k-steps must split evenly over k-groups");
+    static_assert(KGROUPS == 1 || NWG * FM * FN * 16 * 64 * 4 <= STAGES * (BM + BN) * BK * 2,
+                  "the k-groups' sums are combined in the LDS ring");
     static_assert(BK == 32 || BK == 64 || BK == 128, "BK must be 32, 64 or 128");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
     static_assert(STAGES >= 2 && STAGES <= 5, "2..5 LDS stages");
@@ -776,8 +788,11 @@ gemm_pipe(GemmArgs args_in)
     // wave index, made explicitly wave-uniform so everything derived from it
     // (copy offsets, M0) stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / Cfg::WAVES_N;
-    const int wn = wave % Cfg::WAVES_N;
+    const int kgroup = wave / Cfg::NWG;              // 0 unless k-groups
+    const int wl = wave - kgroup * Cfg::NWG;         // wave within its k-group
+    const int wm = wl / Cfg::WAVES_N;
+    const int wn = wl % Cfg::WAVES_N;
+    const int ks0 = kgroup * Cfg::KSL;               // this group's first k-step of a tile
 
     // Split-K: this workgroup's K range and partial-sum destination; the rest
     // of the kernel sees an ordinary product over that range.
@@ -942,15 +957,17 @@ gemm_pipe(GemmArgs args_in)
         publish(0, 0, (int)(num_k - 1 < S - 1 ? num_k - 1 : S - 1));
 #pragma unroll
         for (int grp = 0; grp < FM; ++grp)
-            read_group(0, 0, 0, grp);
+            read_group(0, ks0, 0, grp);
     }
     int buf = 0;
     for (int64_t kt = 0; kt < num_k; ++kt) {
         const int nbuf = (buf + 1 == S) ? 0 : buf + 1;
+        // ks counts this k-group's k-steps of the tile (all of them without
+        // k-groups); the LDS rows read are those of k-step ks0 + ks
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < Cfg::KSL; ++ks) {
             const int set = ks & 1;
-            const bool last = ks + 1 == KS;
+            const bool last = ks + 1 == Cfg::KSL;
             if (last && kt + 1 < num_k) {
                 // tiles kt+2 .. kt+S-1 may still be in flight
                 const int64_t newer = num_k - 2 - kt;
@@ -964,9 +981,9 @@ gemm_pipe(GemmArgs args_in)
 #pragma unroll
             for (int grp = 0; grp < FM; ++grp) {
                 if (!last)
-                    read_group(buf, ks + 1, set ^ 1, grp);
+                    read_group(buf, ks0 + ks + 1, set ^ 1, grp);
                 else if (kt + 1 < num_k)
-                    read_group(nbuf, 0, set ^ 1, grp);
+                    read_group(nbuf, ks0, set ^ 1, grp);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -983,6 +1000,32 @@ gemm_pipe(GemmArgs args_in)
             }
         }
         buf = nbuf;
+    }
+
+    // ---- k-groups: group g > 0 hands its sums to group 0 through LDS
+    if constexpr (Cfg::KGROUPS > 1) {
+        static_assert(Cfg::KGROUPS == 2, "two k-groups");
+        float *const xfer = (float *)smem;
+        __syncthreads();  // every wave is past its last read of the ring
+        if (kgroup == 1) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        xfer[(((wl * FM + i) * FN + j) * 16 + v) * 64 + lane] = acc[i][j][v];
+        }
+        __syncthreads();
+        if (kgroup == 1)
+            return;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[i][j][v] += xfer[(((wl * FM + i) * FN + j) * 16 + v) * 64 + lane];
     }
 
     // ---- epilogue: C = alpha*acc + beta*C through buffer stores whose

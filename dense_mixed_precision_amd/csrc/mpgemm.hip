@@ -83,6 +83,7 @@ constexpr Entry tiled_entry(int id)
     c.layout_a = MPGEMM_ROW_MAJOR;
     c.layout_b = MPGEMM_ROW_MAJOR;
     c.in_type = MPGEMM_IN_F16;
+    c.k_groups = 1;
     return Entry{c, &launch_tiled<Cfg>};
 }
 
@@ -111,6 +112,7 @@ constexpr Entry pipe_entry(int id)
     c.layout_a = Cfg::LAYOUT_A;
     c.layout_b = Cfg::LAYOUT_B;
     c.in_type = Cfg::IN;
+    c.k_groups = Cfg::KGROUPS;
     return Entry{c, &launch_pipe<Cfg>};
 }
 
@@ -136,6 +138,7 @@ constexpr Entry direct_entry(int id)
     c.threads = 256;
     c.lds_bytes = 0;
     c.in_type = IN;
+    c.k_groups = 1;
     return Entry{c, &launch_direct<IN>};
 }
 
@@ -145,6 +148,7 @@ constexpr Entry scale_entry(int id)
     c.id = id;
     c.kind = MPGEMM_KIND_SCALE;
     c.threads = 256;
+    c.k_groups = 1;
     return Entry{c, nullptr};
 }
 
@@ -219,6 +223,9 @@ const Entry kTable[] = {
     MPG_BF16_ENTRIES(75, kRowMajor, kColMajor),  // 75..81
     MPG_BF16_ENTRIES(82, kColMajor, kColMajor),  // 82..88
     direct_entry<kInBF16>(89),                   // 89     BF16 fallback
+    // two k-groups of 2x2 waves (64x64 wave tiles) on 128x128 blocks
+    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, 8, 8, kRowMajor, kRowMajor, kInF16, 2>>(90),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3, 8, 8, kRowMajor, kRowMajor, kInF16, 2>>(91),
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
 constexpr int kDirectIds[2] = {12, 89};  // per input format
@@ -406,6 +413,7 @@ int fill_config(int id, const Problem &p, mpgemm_config *out)
         c.layout_a = p.la;
         c.layout_b = p.lb;
         c.in_type = p.in_type;
+        c.k_groups = 1;
         *out = c;
         return MPGEMM_OK;
     }

@@ -98,6 +98,9 @@ typedef struct mpgemm_config {
     int32_t layout_b;    /* storage order of B; the direct and scale kernels take
                             any order and report the one they were asked for     */
     int32_t in_type;     /* input format the entry reads (MPGEMM_IN_*)            */
+    int32_t k_groups;    /* wave groups sharing each LDS tile, each taking its own
+                            k-steps over the whole block; threads =
+                            64 * waves_m * waves_n * k_groups                     */
 } mpgemm_config;
 
 /*

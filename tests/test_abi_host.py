@@ -109,7 +109,7 @@ def test_config_table_is_consistent():
         if c["kind_name"] in ("tiled", "pipe"):
             assert c["bm"] % (32 * c["waves_m"]) == 0 and c["bn"] % (32 * c["waves_n"]) == 0
             assert c["wave_m"] * c["waves_m"] == c["bm"] and c["wave_n"] * c["waves_n"] == c["bn"]
-            assert c["threads"] == 64 * c["waves_m"] * c["waves_n"]
+            assert c["threads"] == 64 * c["waves_m"] * c["waves_n"] * c["k_groups"]
             assert c["lds_bytes"] == c["stages"] * (c["bm"] + c["bn"]) * c["bk"] * 2
             assert c["lds_bytes"] <= 160 * 1024
             assert c["vec_a"] in (1, 8) and c["vec_b"] in (1, 8)
