@@ -27,6 +27,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace mpg {
 
@@ -140,6 +141,17 @@ __device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 acc)
                                                        __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
     else
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+}
+
+// acc += A_op * B_op on the 16x16x32 matrix instruction of the input format.
+template <int IN>
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 acc)
+{
+    if constexpr (IN == kInBF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
 }
 
 // Workgroup id -> (tile row, tile column).  First undo the round-robin XCD
@@ -514,7 +526,8 @@ probe_mfma(float *out, int shape)
 //   K-contiguous: one LDS row of BK values (2*BK bytes) per M row of A
 //     (row-major A) or per N column of B (column-major B).  Operands are read
 //     with ds_read_b128: lane l takes the 8 K-consecutive values of row l%32
-//     at logical chunk 2*ks + l/32.
+//     at logical chunk 2*ks + l/32 (32x32x16 instruction), or of row l%16 at
+//     chunk 4*ks + l/16 (16x16x32).
 //   outer-contiguous: one LDS row of BX values per k, as a row-major B or a
 //     column-major A holds them in memory.  Operands are read with the
 //     transposing ds_read_b64_tr_b16, two per operand.
@@ -527,11 +540,17 @@ probe_mfma(float *out, int shape)
 //     swz(r) = (r >> 1) & 7 gives the 8 rows of each parity 8 distinct chunks;
 //     with 64-byte rows four rows share a window and swz(r) = (r >> 2) & 3; a
 //     256-byte row fills the window by itself and swz(r) = r & 15.
-//   outer-contiguous: one 32-lane group of the transposing read touches 4
-//     consecutive rows x 4 consecutive chunks; swz(k) = 4*(k & 3) moves the
-//     rows to 4 different 64-byte quarters of the window (rows of 256 bytes or
-//     more), or 4*((k >> 1) & 1) for 128-byte rows (BX = 64), where row
-//     parity already selects the window half.
+//   outer-contiguous, 32x32x16 instruction: one 32-lane group of the
+//     transposing read touches 4 consecutive rows x 4 consecutive chunks;
+//     swz(k) = 4*(k & 3) moves the rows to 4 different 64-byte quarters of the
+//     window (rows of 256 bytes or more), or 4*((k >> 1) & 1) for 128-byte
+//     rows (BX = 64), where row parity already selects the window half.
+//   outer-contiguous, 16x16x32 instruction: the group touches rows
+//     {0,1,2,3} and {8,9,10,11} (plus a multiple of 4 that keeps these
+//     bits) x 2 consecutive chunks, the first even; swz(k) = 2*(k & 3) +
+//     8*((k >> 3) & 1) gives the 8 rows 8 distinct chunk pairs (rows of 256
+//     bytes or more), and 2*((k >> 1) & 1) + 4*((k >> 3) & 1) does the same
+//     within each half window for 128-byte rows.
 // Copies: one wave instruction of buffer_load_dwordx4 ... lds writes 64
 // lanes x 16 B to LDS at M0 + 16*lane (a contiguous KiB); the swizzle is
 // applied by choosing which global chunk each lane fetches.  Lanes whose
@@ -560,7 +579,7 @@ constexpr int kColMajor = 1;
 // One operand tile in LDS.  KC = true: K-contiguous rows (BX rows of BK);
 // KC = false: outer-contiguous rows (BK rows of BX).  NW waves share the
 // copies; each copy instruction fills RPI whole LDS rows.
-template <int BX, int BK, bool KC, int NW>
+template <int BX, int BK, bool KC, int NW, int MI = 32>
 struct OpTile {
     static constexpr bool K_CONTIG = KC;
     static constexpr int NWAVES = NW;
@@ -578,8 +597,10 @@ struct OpTile {
     {
         if constexpr (KC)
             return CH == 16 ? (r & 15) : CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
-        else
+        else if constexpr (MI == 32)
             return CH >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+        else
+            return CH >= 16 ? 2 * (r & 3) + 8 * ((r >> 3) & 1) : 2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1);
     }
 };
 
@@ -590,7 +611,8 @@ struct OpTile {
 // LDS bytes per matrix instruction) while two waves per SIMD still hide
 // latency.
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int VEC_A_, int VEC_B_,
-          int LAYOUT_A_ = kRowMajor, int LAYOUT_B_ = kRowMajor, int IN_ = kInF16, int KGROUPS_ = 1>
+          int LAYOUT_A_ = kRowMajor, int LAYOUT_B_ = kRowMajor, int IN_ = kInF16, int KGROUPS_ = 1,
+          int MI_ = 32>
 struct PipeCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
@@ -598,16 +620,21 @@ struct PipeCfg {
     static constexpr int LAYOUT_A = LAYOUT_A_, LAYOUT_B = LAYOUT_B_;
     static constexpr int IN = IN_;
     static constexpr int KGROUPS = KGROUPS_;
+    // matrix instruction: 32 = 32x32x16 (16 accumulators per lane),
+    // 16 = 16x16x32 (4 accumulators per lane)
+    static constexpr int MI = MI_;
+    static constexpr int KD = MI == 32 ? 16 : 32;         // K of one instruction
+    static constexpr int AV = MI == 32 ? 16 : 4;          // accumulators per lane
     static constexpr int NWG = WAVES_M * WAVES_N;         // waves per k-group
     static constexpr int NW = NWG * KGROUPS;              // waves per workgroup
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
-    static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int KS = BK / 16;                    // MFMA k-steps per tile
+    static constexpr int FM = WTM / MI, FN = WTN / MI;
+    static constexpr int KS = BK / KD;                    // MFMA k-steps per tile
     static constexpr int KSL = KS / KGROUPS;              // ... taken by each k-group
     // row-major A and column-major B are K-contiguous in memory
-    using TA = OpTile<BM, BK, LAYOUT_A == kRowMajor, NW>;
-    using TB = OpTile<BN, BK, LAYOUT_B == kColMajor, NW>;
+    using TA = OpTile<BM, BK, LAYOUT_A == kRowMajor, NW, MI>;
+    using TB = OpTile<BN, BK, LAYOUT_B == kColMajor, NW, MI>;
     static constexpr int A_BYTES = TA::BYTES;
     static constexpr int B_BYTES = TB::BYTES;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
@@ -623,10 +650,12 @@ struct PipeCfg {
     static constexpr int COPY_WINDOW =
         STAGES == 2 ? (NCOPY < KSL * FM ? (NCOPY > 0 ? NCOPY : 1) : KSL * FM) : KSL * FM;
     static_assert(KGROUPS >= 1 && KS % KGROUPS == 0, "k-steps must split evenly over k-groups");
-    static_assert(KGROUPS == 1 || NWG * FM * FN * 16 * 64 * 4 <= STAGES * (BM + BN) * BK * 2,
+    static_assert(MI == 32 || MI == 16, "32x32x16 or 16x16x32 matrix instruction");
+    static_assert(KGROUPS == 1 || NWG * FM * FN * AV * 64 * 4 <= STAGES * (BM + BN) * BK * 2,
                   "the k-groups' sums are combined in the LDS ring");
     static_assert(BK == 32 || BK == 64 || BK == 128, "BK must be 32, 64 or 128");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
+    static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be a multiple of the instruction tile");
+    static_assert(KS >= 1, "a K tile holds at least one instruction's K");
     static_assert(STAGES >= 2 && STAGES <= 5, "2..5 LDS stages");
     static_assert(NL * (STAGES - 1) < 64, "vmcnt is 6 bits");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
@@ -701,17 +730,26 @@ template <class T>
 __device__ __forceinline__ void fill_tile(int wave, int lane, const TileSrc &src, lds_u8 *region, bool all)
 {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src.origin);
+    // the tile's extent, clipped to the tile in 32 bits (both are positive)
+    const int rows = (int)(src.row_left < T::ROWS ? src.row_left : T::ROWS);
+    const int elems = (int)(src.chunk_left < 8 * T::CH ? src.chunk_left : 8 * T::CH);
+    // This path runs only for tiles at a ragged edge.  The empty asm makes
+    // the lane index opaque here, so the per-lane addressing below is
+    // computed when the path runs instead of being hoisted out of the
+    // kernel's main loop, where it would hold registers the whole time.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < T::PW; ++i) {
         const int j = i * T::NWAVES + wave;
-        const int r = T::RPI * j + lane / T::CH;
-        const int c = (lane % T::CH) ^ T::swz(r);
-        const int64_t left = src.chunk_left - 8 * c;
-        const int nv = r >= src.row_left ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : (int)left));
+        const int r = T::RPI * j + ln / T::CH;
+        const int c = (ln % T::CH) ^ T::swz(r);
+        const int left = elems - 8 * c;
+        const int nv = r >= rows ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : left));
         if (all || (nv > 0 && nv < 8)) {
             const uint32_t off = (uint32_t)((r * src.ld + 8 * c) * 2);
             const u32x4 v = (nv >= 8) ? load8_full<1>(rs, off) : load8_partial(rs, off, nv);
-            *(lds_u32x4 *)(region + j * 1024 + lane * 16) = v;
+            *(lds_u32x4 *)(region + j * 1024 + ln * 16) = v;
         }
     }
 }
@@ -724,8 +762,9 @@ __device__ __forceinline__ bool has_partial(int64_t chunk_left)
 }
 
 // Per-lane operand read addressing for a wave whose part of the operand
-// starts at outer index `w_off` (wm*WTM for A, wn*WTN for B).
-template <class T>
+// starts at outer index `w_off` (wm*WTM for A, wn*WTN for B), for the
+// 32x32x16 (MI = 32) or 16x16x32 (MI = 16) matrix instruction.
+template <class T, int MI = 32>
 struct OpReader {
     int base;    // byte offset of this lane's first read within the region
     int sw;      // swizzle of this lane's rows
@@ -734,11 +773,11 @@ struct OpReader {
     __device__ __forceinline__ OpReader(int w_off, int lane)
     {
         if constexpr (T::K_CONTIG) {
-            const int row = w_off + (lane & 31);
+            const int row = w_off + (lane & (MI - 1));
             sw = T::swz(row);
             base = row * T::ROWB;
             col = 0;
-        } else {
+        } else if constexpr (MI == 32) {
             // group g = lane/16, index q = lane%16: rows 8*(g/2) + q/4 (+ 16*ks
             // + 4*h, which leave the swizzle unchanged), columns 16*(g%2) + 4*(q%4)
             const int g = lane >> 4, q = lane & 15;
@@ -746,19 +785,29 @@ struct OpReader {
             sw = T::swz(row_l);
             base = row_l * T::ROWB;
             col = w_off + 16 * (g & 1) + 4 * (q & 3);
+        } else {
+            // rows 8*g + q/4 (+ 32*ks + 4*h, which leave the swizzle
+            // unchanged), columns 4*(q%4)
+            const int g = lane >> 4, q = lane & 15;
+            const int row_l = 8 * g + (q >> 2);
+            sw = T::swz(row_l);
+            base = row_l * T::ROWB;
+            col = w_off + 4 * (q & 3);
         }
     }
 
     // The 8 K-consecutive values lane l contributes to MFMA operand f of
-    // k-step ks: outer index (w_off + 32*f + l%32), k = 16*ks + 8*(l/32) + 0..7.
+    // k-step ks: outer index (w_off + MI*f + l%MI), k = KD*ks + 8*(l/MI) + 0..7
+    // with KD = 16 (MI = 32) or 32 (MI = 16).
     __device__ __forceinline__ half8 read(const lds_u8 *region, int ks, int f, int lane) const
     {
+        constexpr int KD = MI == 32 ? 16 : 32;
         if constexpr (T::K_CONTIG) {
-            const int off = base + f * 32 * T::ROWB + (((2 * ks + (lane >> 5)) ^ sw) * 16);
+            const int off = base + f * MI * T::ROWB + ((((KD / 8) * ks + lane / MI) ^ sw) * 16);
             return __builtin_bit_cast(half8, *(const lds_u32x4 *)(region + off));
         } else {
-            const int c = col + 32 * f;
-            const lds_u8 *p0 = region + base + 16 * ks * T::ROWB + (((c >> 3) ^ sw) * 16) + (c & 7) * 2;
+            const int c = col + MI * f;
+            const lds_u8 *p0 = region + base + KD * ks * T::ROWB + (((c >> 3) ^ sw) * 16) + (c & 7) * 2;
             const fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) fp16x4 *)p0);
             const fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
                 (__attribute__((address_space(3))) fp16x4 *)(p0 + 4 * T::ROWB));
@@ -882,11 +931,16 @@ gemm_pipe(GemmArgs args_in)
     };
 
     // ---- operand reads -----------------------------------------------------
-    const OpReader<TA> rd_a(wm * Cfg::WTM, lane);
-    const OpReader<TB> rd_b(wn * Cfg::WTN, lane);
-    half8 ra[2][FM], rb[2][FN];
+    const OpReader<TA, Cfg::MI> rd_a(wm * Cfg::WTM, lane);
+    const OpReader<TB, Cfg::MI> rd_b(wn * Cfg::WTN, lane);
+    // With the 16x16x32 instruction a wave holds twice as many operand
+    // registers per k-step; A operand f is then kept in one register set and
+    // reloaded for the next k-step right after the MFMAs of group f have
+    // issued (still a whole k-step ahead of its use).
+    constexpr bool ROLL_A = Cfg::MI == 16;
+    half8 ra[ROLL_A ? 1 : 2][FM], rb[2][FN];
     auto read_a = [&](int buf, int ks, int set, int f) __attribute__((always_inline)) {
-        ra[set][f] = rd_a.read(lds + buf * Cfg::STAGE_BYTES, ks, f, lane);
+        ra[ROLL_A ? 0 : set][f] = rd_a.read(lds + buf * Cfg::STAGE_BYTES, ks, f, lane);
     };
     auto read_b = [&](int buf, int ks, int set, int f) __attribute__((always_inline)) {
         rb[set][f] = rd_b.read(lds + buf * Cfg::STAGE_BYTES + Cfg::A_BYTES, ks, f, lane);
@@ -901,17 +955,23 @@ gemm_pipe(GemmArgs args_in)
                 read_b(buf, ks, set, f);
     };
 
-    floatx16 acc[FM][FN];
+    constexpr int AV = Cfg::AV;
+    using AccT = typename std::conditional<Cfg::MI == 32, floatx16, floatx4>::type;
+    AccT acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-            acc[i][j] = floatx16{0};
+            acc[i][j] = AccT{0};
 
     auto mfma_group = [&](int set, int i) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            acc[i][j] = mfma32<Cfg::IN>(ra[set][i], rb[set][j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) {
+            if constexpr (Cfg::MI == 32)
+                acc[i][j] = mfma32<Cfg::IN>(ra[set][i], rb[set][j], acc[i][j]);
+            else
+                acc[i][j] = mfma16<Cfg::IN>(ra[ROLL_A ? 0 : set][i], rb[set][j], acc[i][j]);
+        }
     };
 
     // Make tile t (in buffer buf) visible to the workgroup: this thread's
@@ -978,17 +1038,36 @@ gemm_pipe(GemmArgs args_in)
             // All operand reads for the next k-step go out first, a whole
             // k-step (16 MFMAs per wave) ahead of their use; the scheduling
             // barriers keep the compiler from sinking them next to their uses.
+            // (Rolling A: only the B reads go out here.)
 #pragma unroll
             for (int grp = 0; grp < FM; ++grp) {
-                if (!last)
-                    read_group(buf, ks0 + ks + 1, set ^ 1, grp);
-                else if (kt + 1 < num_k)
-                    read_group(nbuf, ks0, set ^ 1, grp);
+                if constexpr (ROLL_A) {
+#pragma unroll
+                    for (int f = 0; f < FN; ++f)
+                        if (f % FM == grp) {
+                            if (!last)
+                                read_b(buf, ks0 + ks + 1, set ^ 1, f);
+                            else if (kt + 1 < num_k)
+                                read_b(nbuf, ks0, set ^ 1, f);
+                        }
+                } else {
+                    if (!last)
+                        read_group(buf, ks0 + ks + 1, set ^ 1, grp);
+                    else if (kt + 1 < num_k)
+                        read_group(nbuf, ks0, set ^ 1, grp);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int grp = 0; grp < FM; ++grp) {
                 mfma_group(set, grp);
+                if constexpr (ROLL_A) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (!last)
+                        read_a(buf, ks0 + ks + 1, set ^ 1, grp);
+                    else if (kt + 1 < num_k)
+                        read_a(nbuf, ks0, set ^ 1, grp);
+                }
                 // The last k-step opens the window of tile kt+S; the others
                 // continue that of tile kt+S-1, which the ring fill issued
                 // whole when kt == 0.
@@ -1013,8 +1092,8 @@ gemm_pipe(GemmArgs args_in)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        xfer[(((wl * FM + i) * FN + j) * 16 + v) * 64 + lane] = acc[i][j][v];
+                    for (int v = 0; v < AV; ++v)
+                        xfer[(((wl * FM + i) * FN + j) * AV + v) * 64 + lane] = acc[i][j][v];
         }
         __syncthreads();
         if (kgroup == 1)
@@ -1024,8 +1103,8 @@ gemm_pipe(GemmArgs args_in)
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    acc[i][j][v] += xfer[(((wl * FM + i) * FN + j) * 16 + v) * 64 + lane];
+                for (int v = 0; v < AV; ++v)
+                    acc[i][j][v] += xfer[(((wl * FM + i) * FN + j) * AV + v) * 64 + lane];
     }
 
     // ---- epilogue: C = alpha*acc + beta*C through buffer stores whose
@@ -1041,8 +1120,11 @@ gemm_pipe(GemmArgs args_in)
         const __amdgpu_buffer_rsrc_t rsC = make_rsrc(args.C + wrow0 * args.ldc + wcol0);
         const int ldc = (int)args.ldc;
         const float alpha = args.alpha, beta = args.beta;
-        const int cl = lane & 31;
-        const int rl = 4 * (lane >> 5);
+        // accumulator v of instruction tile (i, j) holds row
+        // MI*i + rl + (MI == 32 ? 8*(v/4) + v%4 : v), column MI*j + cl
+        constexpr int MI = Cfg::MI;
+        const int cl = lane & (MI - 1);
+        const int rl = 4 * (lane / MI);
         // the bias of each of this lane's FN columns (0 past the last column)
         float bv[FN];
 #pragma unroll
@@ -1052,7 +1134,7 @@ gemm_pipe(GemmArgs args_in)
             const __amdgpu_buffer_rsrc_t rsBias = make_rsrc(args.bias + wcol0);
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int c = 32 * j + cl;
+                const int c = MI * j + cl;
                 bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                       rsBias, c < wcols ? (uint32_t)(c * 4) : kOOB, 0, 0));
             }
@@ -1061,11 +1143,11 @@ gemm_pipe(GemmArgs args_in)
         for (int i = 0; i < FM; ++i) {
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int c = 32 * j + cl;
+                const int c = MI * j + cl;
                 const bool c_ok = c < wcols;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int r = 32 * i + 8 * (v >> 2) + rl + (v & 3);
+                for (int v = 0; v < AV; ++v) {
+                    const int r = MI * i + rl + (MI == 32 ? 8 * (v >> 2) + (v & 3) : v);
                     const uint32_t off = (c_ok && r < wrows) ? (uint32_t)((r * ldc + c) * 4) : kOOB;
                     float val = alpha * acc[i][j][v];
                     if (beta != 0.0f)

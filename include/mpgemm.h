@@ -87,7 +87,7 @@ typedef struct mpgemm_config {
     int32_t waves_n;     /* waves along N                                         */
     int32_t wave_m;      /* rows of C per wave                                    */
     int32_t wave_n;      /* columns of C per wave                                 */
-    int32_t mfma_m, mfma_n, mfma_k; /* matrix-core instruction shape              */
+    int32_t mfma_m, mfma_n, mfma_k; /* matrix instruction: 32x32x16 or 16x16x32   */
     int32_t vec_a;       /* FP16 elements per global load of A (8 or 1)           */
     int32_t vec_b;       /* FP16 elements per global load of B (8 or 1)           */
     int32_t stages;      /* LDS buffers in flight                                 */
@@ -322,7 +322,7 @@ int mpgemm_probe_mfma_layout(int shape, float *out, void *stream);
 /* Static text for an error code (never NULL). */
 const char *mpgemm_strerror(int code);
 
-/* Library version string, e.g. "mpgemm 0.5.0 gfx950". */
+/* Library version string, e.g. "mpgemm 0.6.0 gfx950". */
 const char *mpgemm_version(void);
 
 #ifdef __cplusplus

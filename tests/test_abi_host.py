@@ -107,7 +107,9 @@ def test_config_table_is_consistent():
         assert c["id"] == i
         kinds.add(c["kind_name"])
         if c["kind_name"] in ("tiled", "pipe"):
-            assert c["bm"] % (32 * c["waves_m"]) == 0 and c["bn"] % (32 * c["waves_n"]) == 0
+            assert (c["mfma_m"], c["mfma_n"], c["mfma_k"]) in ((32, 32, 16), (16, 16, 32))
+            assert c["bm"] % (c["mfma_m"] * c["waves_m"]) == 0 and c["bn"] % (c["mfma_n"] * c["waves_n"]) == 0
+            assert c["bk"] % c["mfma_k"] == 0
             assert c["wave_m"] * c["waves_m"] == c["bm"] and c["wave_n"] * c["waves_n"] == c["bn"]
             assert c["threads"] == 64 * c["waves_m"] * c["waves_n"] * c["k_groups"]
             assert c["lds_bytes"] == c["stages"] * (c["bm"] + c["bn"]) * c["bk"] * 2
@@ -126,6 +128,7 @@ def test_factory_choices_for_the_workloads():
     c = _pick(WORKLOADS["square8192"])
     assert (c["kind_name"], c["bm"], c["bn"], c["vec_a"], c["vec_b"]) == ("pipe", 256, 256, 8, 8)
     assert c["grid"] == 32 * 32
+    assert (c["mfma_m"], c["mfma_n"], c["mfma_k"]) == (16, 16, 32)
     c = _pick(WORKLOADS["square2048"])
     assert (c["bm"], c["bn"], c["bk"]) == (128, 128, 128) and c["grid"] == 256
     c = _pick(WORKLOADS["tallskinny32768x128x4096"])
