@@ -754,6 +754,55 @@ __device__ __forceinline__ void fill_tile(int wave, int lane, const TileSrc &src
     }
 }
 
+// The same fill in two halves, so the loads for a tile can go out a whole
+// tile before its values are written to LDS: load() issues them into
+// registers, store() writes the slots load() covered (both take the same
+// `src` and `all`).
+template <class T>
+struct FillRegs {
+    uint32_t h[T::PW][8];
+
+    __device__ __forceinline__ static int valid(int j, int lane, const TileSrc &src, int &r, int &c)
+    {
+        const int rows = (int)(src.row_left < T::ROWS ? src.row_left : T::ROWS);
+        const int elems = (int)(src.chunk_left < 8 * T::CH ? src.chunk_left : 8 * T::CH);
+        r = T::RPI * j + lane / T::CH;
+        c = (lane % T::CH) ^ T::swz(r);
+        const int left = elems - 8 * c;
+        return r >= rows ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : left));
+    }
+
+    __device__ __forceinline__ void load(int wave, int lane, const TileSrc &src, bool all)
+    {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src.origin);
+#pragma unroll
+        for (int i = 0; i < T::PW; ++i) {
+            int r, c;
+            const int nv = valid(i * T::NWAVES + wave, lane, src, r, c);
+            if (all || (nv > 0 && nv < 8)) {
+                const uint32_t off = (uint32_t)((r * src.ld + 8 * c) * 2);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[i][e] = __builtin_amdgcn_raw_buffer_load_b16(rs, e < nv ? off + 2u * e : kOOB, 0, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(int wave, int lane, const TileSrc &src, lds_u8 *region, bool all) const
+    {
+#pragma unroll
+        for (int i = 0; i < T::PW; ++i) {
+            const int j = i * T::NWAVES + wave;
+            int r, c;
+            const int nv = valid(j, lane, src, r, c);
+            if (all || (nv > 0 && nv < 8))
+                *(lds_u32x4 *)(region + j * 1024 + lane * 16) =
+                    u32x4{pack2(h[i][0], h[i][1]), pack2(h[i][2], h[i][3]), pack2(h[i][4], h[i][5]),
+                          pack2(h[i][6], h[i][7])};
+        }
+    }
+};
+
 // Does a tile with this many elements along its rows leave a partial vector?
 template <class T>
 __device__ __forceinline__ bool has_partial(int64_t chunk_left)
@@ -915,14 +964,40 @@ gemm_pipe(GemmArgs args_in)
         }
     };
 
-    // Register fill after this thread's copies of tile kt have landed.
+    // Register fill after this thread's copies of tile kt have landed.  With
+    // two stages and an operand that goes through registers on every tile
+    // (no 16-byte alignment), the fill's loads for tile kt go out right after
+    // tile kt-1 is published, a whole tile ahead of their use (PIPE_FILL);
+    // otherwise they are issued here.
+    constexpr bool PIPE_FILL = S == 2 && (Cfg::VEC_A != 8 || Cfg::VEC_B != 8);
+    FillRegs<TA> fra;
+    FillRegs<TB> frb;
+    auto fill_load = [&](int64_t kt) __attribute__((always_inline)) {
+        if constexpr (PIPE_FILL) {
+            if (kt >= (K + BK - 1) / BK)
+                return;
+            const TileSrc a = src_a(kt), b = src_b(kt);
+            if (Cfg::VEC_A != 8 || has_partial<TA>(a.chunk_left))
+                fra.load(wave, lane, a, Cfg::VEC_A != 8);
+            if (Cfg::VEC_B != 8 || has_partial<TB>(b.chunk_left))
+                frb.load(wave, lane, b, Cfg::VEC_B != 8);
+        }
+    };
     auto fill = [&](int64_t kt, int buf) __attribute__((always_inline)) {
         lds_u8 *const sbase = lds + buf * Cfg::STAGE_BYTES;
         const TileSrc a = src_a(kt), b = src_b(kt);
-        if (Cfg::VEC_A != 8 || has_partial<TA>(a.chunk_left))
-            fill_tile<TA>(wave, lane, a, sbase, Cfg::VEC_A != 8);
-        if (Cfg::VEC_B != 8 || has_partial<TB>(b.chunk_left))
-            fill_tile<TB>(wave, lane, b, sbase + Cfg::A_BYTES, Cfg::VEC_B != 8);
+        if (Cfg::VEC_A != 8 || has_partial<TA>(a.chunk_left)) {
+            if constexpr (PIPE_FILL)
+                fra.store(wave, lane, a, sbase, Cfg::VEC_A != 8);
+            else
+                fill_tile<TA>(wave, lane, a, sbase, Cfg::VEC_A != 8);
+        }
+        if (Cfg::VEC_B != 8 || has_partial<TB>(b.chunk_left)) {
+            if constexpr (PIPE_FILL)
+                frb.store(wave, lane, b, sbase + Cfg::A_BYTES, Cfg::VEC_B != 8);
+            else
+                fill_tile<TB>(wave, lane, b, sbase + Cfg::A_BYTES, Cfg::VEC_B != 8);
+        }
     };
     auto needs_fill = [&](int64_t kt) __attribute__((always_inline)) {
         if (Cfg::VEC_A != 8 || Cfg::VEC_B != 8)
@@ -1014,7 +1089,9 @@ gemm_pipe(GemmArgs args_in)
             for (int c = 0; c < NCOPY; ++c)
                 copy_one(c);
         }
+        fill_load(0);
         publish(0, 0, (int)(num_k - 1 < S - 1 ? num_k - 1 : S - 1));
+        fill_load(1);
 #pragma unroll
         for (int grp = 0; grp < FM; ++grp)
             read_group(0, ks0, 0, grp);
@@ -1033,8 +1110,10 @@ gemm_pipe(GemmArgs args_in)
                 const int64_t newer = num_k - 2 - kt;
                 publish(kt + 1, nbuf, (int)(newer < S - 2 ? newer : S - 2));
             }
-            if (last)
+            if (last) {
                 begin_copies(kt + S, buf);
+                fill_load(kt + S);
+            }
             // All operand reads for the next k-step go out first, a whole
             // k-step (16 MFMAs per wave) ahead of their use; the scheduling
             // barriers keep the compiler from sinking them next to their uses.

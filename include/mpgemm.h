@@ -18,8 +18,9 @@
  * mpgemm_f16f32_layout); C is always row-major.
  * Leading dimensions count elements, not bytes.  Any M, N, K >= 0 is
  * accepted; no padding is needed and none is done.  A and B must be 2-byte
- * aligned and C 4-byte aligned; wider alignment of the pointers and leading
- * dimensions only selects faster load paths.
+ * aligned and C 4-byte aligned.  A and B are read with 16-byte vector loads
+ * whatever their alignment (gfx950 under ROCm serves unaligned vector loads),
+ * so odd leading dimensions and offset pointers take the same fast path.
  *
  * Arithmetic.  Products of FP16 values are exact in FP32 and are summed in
  * FP32 by the matrix cores; alpha and beta are applied in FP32 at the end.
@@ -132,8 +133,9 @@ int mpgemm_f16f32_query(int64_t M, int64_t N, int64_t K,
 /*
  * The GEMM forced onto table entry `config_id` (for tests and tile sweeps).
  * Same arguments and semantics as mpgemm_f16f32.  Returns MPGEMM_ECONFIG if
- * the id is unknown or the entry cannot run these arguments (for example a
- * vec_a = 8 entry on a misaligned A, or the scale-only entry with K > 0).
+ * the id is unknown or the entry cannot run these arguments (for example an
+ * entry for another storage order or input format, or the scale-only entry
+ * with K > 0).
  */
 int mpgemm_f16f32_with_config(int config_id,
                               int64_t M, int64_t N, int64_t K,

@@ -134,18 +134,20 @@ def test_factory_choices_for_the_workloads():
     c = _pick(WORKLOADS["tallskinny32768x128x4096"])
     assert c["kind_name"] == "pipe" and c["grid"] >= 256 and c["bk"] == 64
     c = _pick(WORKLOADS["ragged1000x800x617"])
-    # lda = 617 is odd: A rows are only 2-byte aligned, so A takes the
-    # element-wise path; B (ldb = 800) keeps 16-byte loads.
-    assert c["kind_name"] == "pipe" and c["vec_a"] == 1 and c["vec_b"] == 8
+    # lda = 617 is odd: A rows are only 2-byte aligned, which 16-byte loads
+    # serve on gfx950 (unaligned mode), so A keeps the vector copy path.
+    assert c["kind_name"] == "pipe" and c["vec_a"] == 8 and c["vec_b"] == 8
     c = _pick(WORKLOADS["square256"])
     assert c["kind_name"] == "pipe" and c["grid"] >= 16
 
 
 def test_factory_alignment_and_degenerate_cases():
-    assert q(512, 512, 512, A=FAKE_A + 2)["vec_a"] == 1
-    assert q(512, 512, 512, B=FAKE_B + 8)["vec_b"] == 1
-    assert q(512, 512, 512, lda=516)["vec_a"] == 1
+    # any 2-byte aligned operand takes the 16-byte copy path
+    assert q(512, 512, 512, A=FAKE_A + 2)["vec_a"] == 8
+    assert q(512, 512, 512, B=FAKE_B + 8)["vec_b"] == 8
+    assert q(512, 512, 512, lda=515)["vec_a"] == 8
     assert q(512, 512, 512, lda=520)["vec_a"] == 8
+    assert code(512, 512, 512, A=FAKE_A + 1) == mp.MPGEMM_EALIGN
     assert q(512, 512, 0)["kind_name"] == "scale"
     assert q(512, 512, 64, alpha=0.0, beta=2.0)["kind_name"] == "scale"
     assert q(0, 512, 64)["kind_name"] == "none"
@@ -227,7 +229,7 @@ def test_layout_factory_choices(la, lb):
     c = ql(la, lb, 2048, 2048, 2048)
     assert (c["bm"], c["bn"], c["bk"]) == (128, 128, 128) and c["grid"] == 256
     c = ql(la, lb, 1000, 800, 617, lda=(1001 if la else 617), ldb=(617 if lb else 800))
-    assert c["kind_name"] == "pipe" and (c["vec_a"], c["vec_b"]) == (1, 1)
+    assert c["kind_name"] == "pipe" and (c["vec_a"], c["vec_b"]) == (8, 8)
     # a stored stage beyond 32-bit offsets leaves only the 64-bit direct kernel
     c = ql(la, lb, 300, 300, 64, lda=(1 << 30), ldb=(1 << 30))
     assert c["kind_name"] == "direct" and (c["layout_a"], c["layout_b"]) == (la, lb)
@@ -254,7 +256,7 @@ def test_bf16_factory_choices(la, lb):
     c = qb(la, lb, 2048, 2048, 2048)
     assert (c["bm"], c["bk"], c["in_type"]) == (128, 128, mp.MPGEMM_IN_BF16)
     c = qb(la, lb, 1000, 800, 617, lda=(1001 if la else 617), ldb=(617 if lb else 800))
-    assert (c["vec_a"], c["vec_b"], c["in_type"]) == (1, 1, mp.MPGEMM_IN_BF16)
+    assert (c["vec_a"], c["vec_b"], c["in_type"]) == (8, 8, mp.MPGEMM_IN_BF16)
     c = qb(la, lb, 300, 300, 64, lda=(1 << 30), ldb=(1 << 30))
     assert c["kind_name"] == "direct" and c["in_type"] == mp.MPGEMM_IN_BF16
     assert qb(la, lb, 64, 64, 0)["kind_name"] == "scale"

@@ -130,6 +130,23 @@ def test_every_config_multi_tile(cfg):
     assert np.array_equal(got, ref.astype(np.float32)), f"config {cfg}: not bitwise"
 
 
+def _vector_ids():
+    return [i for i in _tiled_and_direct_ids()
+            if mp.mpgemm_config_info(i)["kind_name"] in ("tiled", "pipe")
+            and (mp.mpgemm_config_info(i)["vec_a"], mp.mpgemm_config_info(i)["vec_b"]) == (8, 8)]
+
+
+@pytest.mark.parametrize("cfg", _vector_ids())
+def test_every_vector_config_on_unaligned_operands(cfg):
+    """The 16-byte copy paths on operands that are only 2-byte aligned:
+    offset base pointers and odd leading dimensions, so every row of A and B
+    starts at a different alignment."""
+    M, N, K = 261, 147, 101
+    A, B, C = make_inputs(M, N, K, "uniform", seed=cfg + 300, c_init="uniform")
+    full_check(f"config {cfg} unaligned", A, B, C, 1.25, -0.75, config=cfg,
+               a_off=1, b_off=3, lda=103, ldb=149, ldc=151)
+
+
 def test_misaligned_pointers_and_odd_leading_dimensions():
     M, N, K = 333, 250, 617
     A, B, C = make_inputs(M, N, K, "uniform", seed=41, c_init="uniform")
