@@ -249,6 +249,8 @@ constexpr int kScaleId = 13;
 // column-major pairs every pair but 88 takes the 2-byte (11) entry.
 // 128x128, K tile 128, eight waves, per input format and storage-order pair
 constexpr int kWideKIds[2][4] = {{37, 58, 59, 60}, {67, 74, 81, 88}};
+// 64x64 tiles, K tile 128, three stages (row-major FP16)
+constexpr int kSmallDeepKId = 39;
 struct TileGroup {
     int bm, bn;
     int ids[4];
@@ -391,7 +393,9 @@ int64_t grid_for(const mpgemm_config &c, const Problem &p)
 
 // The factory.  Largest tile whose grid still fills the chip; smaller tiles
 // when the product is small.  Returns a table id, or -1 for "nothing to do".
-int select(const Problem &p)
+// `small_deep_k` = false keeps 64-deep K tiles for small products (split-K
+// counts its pieces in K tiles).
+int select(const Problem &p, bool small_deep_k = true)
 {
     if (p.M == 0 || p.N == 0)
         return -1;
@@ -417,6 +421,12 @@ int select(const Problem &p)
     if (group == 1 && v == 0 && cdiv(p.N, 128) >= 4 && cdiv(p.M, 128) >= 4 &&
         entry_fits(kTable[wide], p))
         return wide;
+    // Small row-major FP16 products with more than one 64-deep K tile take
+    // 64x64 tiles with K tiles of 128 and a 3-deep ring: half as many
+    // barriers per K (256^3: 4.6 against 4.8 us per call).
+    if (small_deep_k && group == 2 && v == 0 && p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR &&
+        p.lb == MPGEMM_ROW_MAJOR && p.K > 64 && entry_fits(kTable[kSmallDeepKId], p))
+        return kSmallDeepKId;
     const TileGroup *groups = kGroups[p.in_type][p.la + 2 * p.lb];
     for (int g = group; g < kNumGroups; ++g) {
         const int id = groups[g].ids[v];
@@ -518,7 +528,10 @@ SplitPlan plan_split(const Problem &p, int requested)
     SplitPlan sp{select(p), 1, 0, 0};
     if (sp.id < 0 || p.K == 0 || p.alpha == 0.0f)
         return sp;
-    const mpgemm_config &c = kTable[sp.id].cfg;
+    // pieces are whole K tiles: a split takes the 64-deep form of the small
+    // tile; an unsplit plan keeps the factory's own choice
+    const int id = sp.id == kSmallDeepKId ? select(p, false) : sp.id;
+    const mpgemm_config &c = kTable[id].cfg;
     if (c.kind != MPGEMM_KIND_PIPE)
         return sp;
     const int64_t tiles = grid_for(c, p);
@@ -535,13 +548,13 @@ SplitPlan plan_split(const Problem &p, int requested)
     }
     if (s <= 1)
         return sp;
-    sp.k_split = cdiv(ktiles, s) * c.bk;
-    sp.splits = (int)cdiv(p.K, sp.k_split);
-    if (sp.splits <= 1 || tiles * sp.splits > 0x7FFFFFFF) {
-        sp.splits = 1;
-        sp.k_split = 0;
+    const int64_t k_split = cdiv(ktiles, s) * c.bk;
+    const int64_t pieces = cdiv(p.K, k_split);
+    if (pieces <= 1 || tiles * pieces > 0x7FFFFFFF)
         return sp;
-    }
+    sp.id = id;
+    sp.k_split = k_split;
+    sp.splits = (int)pieces;
     sp.ws_bytes = (int64_t)sp.splits * p.M * p.N * 4;
     return sp;
 }

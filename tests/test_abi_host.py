@@ -137,8 +137,12 @@ def test_factory_choices_for_the_workloads():
     # lda = 617 is odd: A rows are only 2-byte aligned, which 16-byte loads
     # serve on gfx950 (unaligned mode), so A keeps the vector copy path.
     assert c["kind_name"] == "pipe" and c["vec_a"] == 8 and c["vec_b"] == 8
+    assert (c["bm"], c["bn"], c["bk"], c["stages"]) == (64, 64, 128, 3)
     c = _pick(WORKLOADS["square256"])
     assert c["kind_name"] == "pipe" and c["grid"] >= 16
+    assert (c["bm"], c["bn"], c["bk"], c["stages"]) == (64, 64, 128, 3)
+    # one K tile of 64 or less keeps the 64-deep tile
+    assert q(256, 256, 64)["bk"] == 64
 
 
 def test_factory_alignment_and_degenerate_cases():
