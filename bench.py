@@ -12,7 +12,10 @@ in the same JSON line.
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize() on both sides (wall clock -> ms_per_step), with HIP
 events recorded on the launch stream around the same region (-> the average
-kernel duration used for the roofline).  FLOP = 2*M*N*K.
+kernel duration used for the roofline).  FLOP = 2*M*N*K.  Each workload also
+reports "graph_us": the per-launch time of the same call captured in a HIP
+graph and replayed, i.e. the kernels' own time without the Python call
+between launches (which bounds the eager rate of the smallest products).
 
 The CPU baseline is the oracle (oracle/, plain C, FP64) timed on a bounded
 sample of the headline workload: a block of whole rows of C, sized to about
@@ -90,8 +93,33 @@ def measured_traffic(workload: str, kernel_ms: float):
             "GBps": round((read_b + write_b) / (kernel_ms * 1e-3) / 1e9, 1), "source": os.path.relpath(path, ROOT)}
 
 
+def graph_time_us(fn, reps, torch):
+    """Per-launch time of `reps` calls captured in one HIP graph and replayed
+    (best of three replays, HIP events on the replay stream): the kernels'
+    own time without the Python call between launches.  `fn` launches on
+    torch's current stream, which is the capture stream while capturing."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    best = float("inf")
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e3 / reps)
+    del g
+    return best
+
+
 def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=None, bias=False,
-                  splitk=False):
+                  splitk=False, graph_reps=0):
     """Time `steps` launches (after `warmup`) on resident inputs.  A column-
     major operand is stored transposed on the device and passed as the
     transposed view; `dtype` picks FP16 (default) or BF16 inputs; `bias`
@@ -132,7 +160,17 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / steps
     kern_ms = ev0.elapsed_time(ev1) / steps
-    return {"A": A, "B": B, "C": C, "Cd": Cd, "cfg": cfg, "wall_ms": wall_ms, "kernel_ms": kern_ms}
+    out = {"A": A, "B": B, "C": C, "Cd": Cd, "cfg": cfg, "wall_ms": wall_ms, "kernel_ms": kern_ms}
+    if graph_reps > 0:
+        # the same call on the current (capture) stream
+        def step_current():
+            if splitk:
+                mp.gemm_splitk(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, workspace=ws)
+            else:
+                mp.gemm(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d)
+
+        out["graph_us"] = graph_time_us(step_current, graph_reps, torch)
+    return out
 
 
 def _smi_power():
@@ -279,7 +317,7 @@ def main():
     mp.load()
     head = WORKLOADS[args.workload]
     print(f"# timing {head.name} ({args.warmup} warm-up + {args.steps} steps)", file=sys.stderr, flush=True)
-    res = time_workload(head, args.steps, args.warmup, torch, mp)
+    res = time_workload(head, args.steps, args.warmup, torch, mp, graph_reps=20)
     value = head.flop / (res["wall_ms"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
@@ -304,6 +342,7 @@ def main():
         "roofline": roofline_entry(head, res["kernel_ms"]),
     }
     line["roofline"]["kernel_ms"] = round(res["kernel_ms"], 5)
+    line["graph_us"] = round(res["graph_us"], 3)
     line["roofline"]["traffic"] = measured_traffic(head.name, res["kernel_ms"])
     others = {}
     if not args.no_others:
@@ -312,9 +351,11 @@ def main():
                 continue
             steps = max(5, min(args.steps, 20 if w.flop > 1e12 else args.steps))
             print(f"# timing {name} ({steps} steps)", file=sys.stderr, flush=True)
-            r = time_workload(w, steps, max(3, args.warmup // 2), torch, mp)
+            r = time_workload(w, steps, max(3, args.warmup // 2), torch, mp,
+                              graph_reps=5 if w.flop > 1e12 else 20)
             others[name] = {"tflops": round(w.flop / (r["kernel_ms"] * 1e-3) / 1e12, 2),
                             "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
+                            "graph_us": round(r["graph_us"], 3),
                             "pct_of_peak": round(100 * w.flop / (r["kernel_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
                             "roofline": roofline_entry(w, r["kernel_ms"]),
                             "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "vec_a", "vec_b", "grid")}}
@@ -331,9 +372,11 @@ def main():
                 name = f"{base}_{tag}"
                 steps = max(5, min(args.steps, 20 if w.flop > 1e12 else args.steps))
                 print(f"# timing {name} ({steps} steps)", file=sys.stderr, flush=True)
-                r = time_workload(w, steps, max(3, args.warmup // 2), torch, mp, la, lb, dt, with_bias)
+                r = time_workload(w, steps, max(3, args.warmup // 2), torch, mp, la, lb, dt, with_bias,
+                                  graph_reps=5 if w.flop > 1e12 else 20)
                 others[name] = {"tflops": round(w.flop / (r["kernel_ms"] * 1e-3) / 1e12, 2),
                                 "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
+                                "graph_us": round(r["graph_us"], 3),
                                 "layout": {"A": "col" if la else "row", "B": "col" if lb else "row"},
                                 "inputs": "bf16" if dt is not None else "f16", "bias": with_bias,
                                 "pct_of_peak": round(100 * w.flop / (r["kernel_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
@@ -347,9 +390,11 @@ def main():
         for tag, sk in (("", False), ("_splitk", True)):
             name = skinny.name + tag
             print(f"# timing {name} ({args.steps} steps)", file=sys.stderr, flush=True)
-            r = time_workload(skinny, args.steps, max(3, args.warmup // 2), torch, mp, splitk=sk)
+            r = time_workload(skinny, args.steps, max(3, args.warmup // 2), torch, mp, splitk=sk,
+                              graph_reps=20)
             others[name] = {"tflops": round(skinny.flop / (r["kernel_ms"] * 1e-3) / 1e12, 2),
                             "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
+                            "graph_us": round(r["graph_us"], 3),
                             "roofline": roofline_entry(skinny, r["kernel_ms"]),
                             "splits": r["cfg"].get("splits", 1),
                             "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "bk", "grid")}}
