@@ -1,0 +1,28 @@
+"""CPU: the benchmark's host-side helpers (no GPU needed)."""
+import bench
+from dense_mixed_precision_amd.workloads import WORKLOADS
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    # ridge = 2516.6 TFLOP/s / 8 TB/s = 315 FLOP/byte
+    assert bench.roofline_entry(WORKLOADS["square8192"], 1.0)["bound"] == "mfma"     # AI 2048
+    assert bench.roofline_entry(WORKLOADS["square2048"], 1.0)["bound"] == "mfma"     # AI 512
+    assert bench.roofline_entry(WORKLOADS["tallskinny32768x128x4096"], 1.0)["bound"] == "hbm"  # AI 120
+    assert bench.roofline_entry(WORKLOADS["ragged1000x800x617"], 1.0)["bound"] == "hbm"
+
+
+def test_roofline_achieved_is_algorithmic_work_over_time():
+    w = WORKLOADS["square2048"]
+    r = bench.roofline_entry(w, 0.025)  # 25 us
+    assert abs(r["achieved"] - 2 * 2048**3 / 25e-6 / 1e12) < 0.01
+    assert abs(r["frac"] - r["achieved"] / bench.PEAK_F16_TFLOPS) < 1e-4
+    w = WORKLOADS["tallskinny32768x128x4096"]
+    r = bench.roofline_entry(w, 0.05)
+    assert abs(r["achieved"] - w.algorithmic_bytes / 50e-6 / 1e9) < 0.1
+    assert r["unit"] == "GB/s" and r["peak"] == bench.PEAK_HBM_GBS
+
+
+def test_secondary_warmup_is_about_40ms_of_gpu_time():
+    assert bench.warmup_for(WORKLOADS["square8192"], 1000) >= 20      # ~1 ms per launch
+    assert bench.warmup_for(WORKLOADS["square2048"], 1000) == 1000    # capped by --warmup
+    assert bench.warmup_for(WORKLOADS["square8192"], 2) == 3          # at least 3
