@@ -264,9 +264,14 @@ def sample_power(w, torch, mp, seconds=2.0):
     busy = _smi_power()
     th.join()
     dt = time.perf_counter() - t0
-    return {"workload": w.name, "idle": idle, "busy": busy,
-            "tflops_during_sample": round(w.flop * count[0] / dt / 1e12, 1),
-            "source": "amd-smi metric -p -c (SOCKET_POWER, graphics CLK of each XCD)"}
+    tflops = w.flop * count[0] / dt / 1e12
+    out = {"workload": w.name, "idle": idle, "busy": busy,
+           "tflops_during_sample": round(tflops, 1),
+           "source": "amd-smi metric -p -c (SOCKET_POWER, graphics CLK of each XCD)"}
+    if busy and busy.get("socket_w"):
+        # work per joule of socket energy: what sets throughput at the power limit
+        out["gflop_per_joule"] = round(tflops * 1e3 / busy["socket_w"], 1)
+    return out
 
 
 def roofline_entry(w, kernel_ms):
