@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--workload", default="square2048")
+    p.add_argument("--config", type=int, default=None,
+                   help="force this config-table entry for the headline workload (tile candidates)")
     p.add_argument("--no-others", action="store_true", help="time only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -122,7 +124,7 @@ def graph_time_us(fn, reps, torch):
 
 
 def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=None, bias=False,
-                  splitk=False, graph_reps=0):
+                  splitk=False, graph_reps=0, config=None):
     """Time `steps` launches (after `warmup`) on resident inputs.  A column-
     major operand is stored transposed on the device and passed as the
     transposed view; `dtype` picks FP16 (default) or BF16 inputs; `bias`
@@ -136,6 +138,8 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
     Cd = C.to(dev) if C is not None else torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     cfg = mp.query_for(Ad, Bd, Cd, w.alpha, w.beta)
+    if config is not None:
+        cfg = dict(mp.mpgemm_config_info(config), grid=cfg["grid"])
     bias_d = torch.rand(w.N, device=dev) * 2 - 1 if bias else None
     ws = None
     if splitk:
@@ -156,13 +160,16 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
     in_type = mp.MPGEMM_IN_BF16 if Ad.dtype == torch.bfloat16 else mp.MPGEMM_IN_F16
     alpha, beta = float(w.alpha), float(w.beta)
     plain = not splitk and not bias and not layout_a and not layout_b and in_type == mp.MPGEMM_IN_F16
-    f16f32, gemm_ex = mp.mpgemm_f16f32, mp.mpgemm_gemm_ex
+    f16f32, gemm_ex, forced = mp.mpgemm_f16f32, mp.mpgemm_gemm_ex, mp.mpgemm_gemm_ex_with_config
 
     def step():
         if splitk:
             mp.gemm_splitk(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, workspace=ws, stream=stream)
             return
-        if plain:
+        if config is not None:
+            rc = forced(config, in_type, layout_a, layout_b, w.M, w.N, w.K, a_ptr, lda, b_ptr, ldb, c_ptr,
+                        w.N, alpha, beta, bias_ptr, handle)
+        elif plain:
             rc = f16f32(w.M, w.N, w.K, a_ptr, lda, b_ptr, ldb, c_ptr, w.N, alpha, beta, handle)
         else:
             rc = gemm_ex(in_type, layout_a, layout_b, w.M, w.N, w.K, a_ptr, lda, b_ptr, ldb, c_ptr,
@@ -191,7 +198,7 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
             if splitk:
                 mp.gemm_splitk(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, workspace=ws)
             else:
-                mp.gemm(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d)
+                mp.gemm(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, config=config)
 
         out["graph_us"] = graph_time_us(step_current, graph_reps, torch)
     return out
@@ -354,7 +361,7 @@ def main():
     mp.load()
     head = WORKLOADS[args.workload]
     print(f"# timing {head.name} ({args.warmup} warm-up + {args.steps} steps)", file=sys.stderr, flush=True)
-    res = time_workload(head, args.steps, args.warmup, torch, mp, graph_reps=20)
+    res = time_workload(head, args.steps, args.warmup, torch, mp, graph_reps=20, config=args.config)
     value = head.flop / (res["wall_ms"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
