@@ -1224,18 +1224,30 @@ gemm_pipe(GemmArgs args_in)
             for (int j = 0; j < FN; ++j) {
                 const int c = MI * j + cl;
                 const bool c_ok = c < wcols;
+                uint32_t off[AV];
 #pragma unroll
                 for (int v = 0; v < AV; ++v) {
                     const int r = MI * i + rl + (MI == 32 ? 8 * (v >> 2) + (v & 3) : v);
-                    const uint32_t off = (c_ok && r < wrows) ? (uint32_t)((r * ldc + c) * 4) : kOOB;
+                    off[v] = (c_ok && r < wrows) ? (uint32_t)((r * ldc + c) * 4) : kOOB;
+                }
+                // With beta != 0 all of the tile's C loads go out before its
+                // first store: the loads and stores share a buffer, so the
+                // compiler keeps them in program order, and loading each
+                // element just before its store would serialize the loads.
+                float cin[AV];
+                if (beta != 0.0f) {
+#pragma unroll
+                    for (int v = 0; v < AV; ++v)
+                        cin[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsC, off[v], 0, 0));
+                }
+#pragma unroll
+                for (int v = 0; v < AV; ++v) {
                     float val = alpha * acc[i][j][v];
                     if (beta != 0.0f)
-                        val = __builtin_fmaf(beta,
-                                             __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsC, off, 0, 0)),
-                                             val);
+                        val = __builtin_fmaf(beta, cin[v], val);
                     if (args.bias)
                         val += bv[j];
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off, 0, kStoreNT);
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off[v], 0, kStoreNT);
                 }
             }
         }
