@@ -917,7 +917,12 @@ gemm_pipe(GemmArgs args_in)
     tile_coords(bid, nb, args.tiles_n, args.tiles_m, args.group_m, tm, tn);
     const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
-    const int64_t K = args.K;
+    // K tail: the copy loop covers the largest multiple of 8 of K, so every
+    // 16-byte vector it copies is either whole or wholly past the edge; the
+    // last K % 8 values are one more matrix-instruction step whose operands
+    // come straight from memory (see tail_load).
+    const int ktail = (int)(args.K & 7);
+    const int64_t K = args.K - ktail;
     const int64_t lda = args.lda, ldb = args.ldb;
     const int64_t rows_left = args.M - m0;  // > 0
     const int64_t cols_left = args.N - n0;  // > 0
@@ -1029,6 +1034,57 @@ gemm_pipe(GemmArgs args_in)
             if (f % FM == grp)
                 read_b(buf, ks, set, f);
     };
+
+    // ---- K tail operands: lane l holds the values of outer index l % MI at
+    // k = K + 8*(l/MI) + 0..7, zero at and past the true K (so only the lanes
+    // with l < MI carry data) and past the M or N edge.  2-byte buffer loads;
+    // the 32-bit offsets stay within the stage span the host checks.  With
+    // small wave tiles the loads go out before the ring fill, the oldest
+    // memory operations of the kernel, so the copy waits cover them and their
+    // latency hides under the K loop; large wave tiles, which have no
+    // registers to spare across the loop, issue them after it.
+    constexpr bool TAIL_EARLY = (FM + FN) * 4 <= 16;
+    half8 ta[FM], tb[FN];
+    auto tail_load = [&]() __attribute__((always_inline)) {
+        constexpr int MI = Cfg::MI;
+        const int li = lane & (MI - 1);
+        const int k8 = 8 * (lane / MI);
+        const int ld_a = (int)lda, ld_b = (int)ldb;
+        const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(args.A + (A_ROW ? m0 * lda + K : K * lda + m0));
+        const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(args.B + (B_ROW ? K * ldb + n0 : n0 * ldb + K));
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+            const int r = wm * Cfg::WTM + MI * f + li;
+            const bool r_ok = r < rows_left;
+            uint32_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = k8 + e;
+                const uint32_t off = (uint32_t)((A_ROW ? r * ld_a + k : k * ld_a + r) * 2);
+                h[e] = __builtin_amdgcn_raw_buffer_load_b16(rs_a, (r_ok && k < ktail) ? off : kOOB, 0, 0);
+            }
+            ta[f] = __builtin_bit_cast(half8, u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]),
+                                                    pack2(h[6], h[7])});
+        }
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+            const int c = wn * Cfg::WTN + MI * f + li;
+            const bool c_ok = c < cols_left;
+            uint32_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int k = k8 + e;
+                const uint32_t off = (uint32_t)((B_ROW ? k * ld_b + c : c * ld_b + k) * 2);
+                h[e] = __builtin_amdgcn_raw_buffer_load_b16(rs_b, (c_ok && k < ktail) ? off : kOOB, 0, 0);
+            }
+            tb[f] = __builtin_bit_cast(half8, u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]),
+                                                    pack2(h[6], h[7])});
+        }
+    };
+    if constexpr (TAIL_EARLY) {
+        if (ktail > 0)
+            tail_load();
+    }
 
     constexpr int AV = Cfg::AV;
     using AccT = typename std::conditional<Cfg::MI == 32, floatx16, floatx4>::type;
@@ -1184,6 +1240,21 @@ gemm_pipe(GemmArgs args_in)
 #pragma unroll
                 for (int v = 0; v < AV; ++v)
                     acc[i][j][v] += xfer[(((wl * FM + i) * FN + j) * AV + v) * 64 + lane];
+    }
+
+    // ---- K tail: one more instruction step on the tail operands
+    if (ktail > 0) {
+        if constexpr (!TAIL_EARLY)
+            tail_load();
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (Cfg::MI == 32)
+                    acc[i][j] = mfma32<Cfg::IN>(ta[i], tb[j], acc[i][j]);
+                else
+                    acc[i][j] = mfma16<Cfg::IN>(ta[i], tb[j], acc[i][j]);
+            }
     }
 
     // ---- epilogue: C = alpha*acc + beta*C through buffer stores whose

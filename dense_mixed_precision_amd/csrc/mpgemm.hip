@@ -538,9 +538,13 @@ SplitPlan plan_split(const Problem &p, int requested)
     const int64_t ktiles = cdiv(p.K, c.bk);
     int64_t s;
     if (requested == 0) {
-        s = tiles >= kNumCu / 2 ? 1 : cdiv(kNumCu, tiles);
-        if (s > 16)
-            s = 16;
+        // About two workgroups per compute unit: the pieces are short, so a
+        // second resident workgroup keeps more copies in flight (measured
+        // best among 1x/2x/4x the unit count on 4096x16x4096,
+        // 512x512x16384 and 256x256x65536).  Pieces of at least 4 K tiles.
+        s = tiles >= kNumCu / 2 ? 1 : cdiv(2 * kNumCu, tiles);
+        if (s > 32)
+            s = 32;
         if (s > ktiles / 4)
             s = ktiles / 4;
     } else {

@@ -273,8 +273,10 @@ int mpgemm_gemm_ex_with_config(int config_id, int in_type, int layout_a, int lay
  *
  * mpgemm_splitk_plan reports, without any HIP call, how many pieces a call
  * would use (`splits_requested` 0: automatic, split only when the grid
- * fills less than half the chip; n > 0: n pieces, at most one per K tile of
- * the chosen kernel), the workspace bytes that needs (splits*M*N*4; 0 when
+ * fills less than half the chip, into enough pieces for about two
+ * workgroups per compute unit, at most 32, each at least 4 K tiles long;
+ * n > 0: n pieces, at most one per K tile of the chosen kernel), the
+ * workspace bytes that needs (splits*M*N*4; 0 when
  * splits == 1) and the tile kernel's table entry.  Output pointers may be
  * NULL.  Arguments as for mpgemm_gemm_ex; C, alpha and beta are not needed
  * to plan.
