@@ -287,6 +287,19 @@ struct Problem {
 
 int64_t at_least_one(int64_t v) { return v > 1 ? v : 1; }
 
+// Products and sums of caller-supplied sizes (all >= 0 once validated),
+// saturated at INT64_MAX instead of overflowing: every size check below
+// compares against limits far below it, so a saturated value simply fails
+// the check.
+int64_t mul_sat(int64_t a, int64_t b)
+{
+    if (a == 0 || b == 0)
+        return 0;
+    return a > INT64_MAX / b ? INT64_MAX : a * b;
+}
+
+int64_t add_sat(int64_t a, int64_t b) { return a > INT64_MAX - b ? INT64_MAX : a + b; }
+
 int validate(const Problem &p)
 {
     if (p.in_type != MPGEMM_IN_F16 && p.in_type != MPGEMM_IN_BF16)
@@ -317,7 +330,7 @@ int validate(const Problem &p)
     return MPGEMM_OK;
 }
 
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 
 // gfx950 under ROCm runs vector memory instructions in unaligned mode: a
 // 16-byte buffer load at any 2-byte aligned address, into registers or
@@ -359,18 +372,18 @@ bool entry_fits(const Entry &e, const Problem &p)
     // Per-stage buffer offsets are 32-bit: a stage spans bm (A row-major) or
     // bk (A column-major) stored rows of lda, and bk (B row-major) or bn (B
     // column-major) stored rows of ldb.
-    const int64_t a_span = p.la == MPGEMM_ROW_MAJOR ? ((int64_t)c.bm * p.lda + c.bk) * 2
-                                                    : ((int64_t)c.bk * p.lda + c.bm) * 2;
-    const int64_t b_span = p.lb == MPGEMM_ROW_MAJOR ? ((int64_t)c.bk * p.ldb + c.bn) * 2
-                                                    : ((int64_t)c.bn * p.ldb + c.bk) * 2;
+    const int64_t a_span = p.la == MPGEMM_ROW_MAJOR ? mul_sat(add_sat(mul_sat(c.bm, p.lda), c.bk), 2)
+                                                    : mul_sat(add_sat(mul_sat(c.bk, p.lda), c.bm), 2);
+    const int64_t b_span = p.lb == MPGEMM_ROW_MAJOR ? mul_sat(add_sat(mul_sat(c.bk, p.ldb), c.bn), 2)
+                                                    : mul_sat(add_sat(mul_sat(c.bn, p.ldb), c.bk), 2);
     if (a_span >= (int64_t)0x7FFFFFF0 || b_span >= (int64_t)0x7FFFFFF0)
         return false;
     // The pipelined kernel's epilogue addresses a wave's C tile with 32-bit
     // buffer offsets as well.
-    const int64_t c_span = ((int64_t)c.bm * p.ldc + c.bn) * 4;
+    const int64_t c_span = mul_sat(add_sat(mul_sat(c.bm, p.ldc), c.bn), 4);
     if (c.kind == MPGEMM_KIND_PIPE && c_span >= (int64_t)0x7FFFFFF0)
         return false;
-    const int64_t tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    const int64_t tiles = mul_sat(cdiv(p.M, c.bm), cdiv(p.N, c.bn));
     if (tiles > 0x7FFFFFFF)
         return false;
     return true;
@@ -381,9 +394,9 @@ int64_t grid_for(const mpgemm_config &c, const Problem &p)
     switch (c.kind) {
     case MPGEMM_KIND_TILED:
     case MPGEMM_KIND_PIPE:
-        return cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+        return mul_sat(cdiv(p.M, c.bm), cdiv(p.N, c.bn));
     case MPGEMM_KIND_DIRECT:
-        return cdiv(p.M, 64) * cdiv(p.N, 64);
+        return mul_sat(cdiv(p.M, 64), cdiv(p.N, 64));
     case MPGEMM_KIND_SCALE:
         return 0;
     default:
@@ -408,9 +421,9 @@ int select(const Problem &p, bool small_deep_k = true)
     // Else 128x128 if that makes at least half a wave of workgroups.
     // Else 64x64.
     int group;
-    if (cdiv(p.M, 256) * cdiv(p.N, 256) >= kNumCu)
+    if (mul_sat(cdiv(p.M, 256), cdiv(p.N, 256)) >= kNumCu)
         group = 0;
-    else if (cdiv(p.M, 128) * cdiv(p.N, 128) >= kNumCu / 2)
+    else if (mul_sat(cdiv(p.M, 128), cdiv(p.N, 128)) >= kNumCu / 2)
         group = 1;
     else
         group = 2;
@@ -552,14 +565,16 @@ SplitPlan plan_split(const Problem &p, int requested)
     }
     if (s <= 1)
         return sp;
-    const int64_t k_split = cdiv(ktiles, s) * c.bk;
+    const int64_t k_split = mul_sat(cdiv(ktiles, s), c.bk);
     const int64_t pieces = cdiv(p.K, k_split);
-    if (pieces <= 1 || tiles * pieces > 0x7FFFFFFF)
+    // the workspace holds one M x N FP32 product per piece
+    const int64_t ws_bytes = mul_sat(mul_sat(mul_sat(pieces, p.M), p.N), 4);
+    if (pieces <= 1 || mul_sat(tiles, pieces) > 0x7FFFFFFF || ws_bytes == INT64_MAX)
         return sp;
     sp.id = id;
     sp.k_split = k_split;
     sp.splits = (int)pieces;
-    sp.ws_bytes = (int64_t)sp.splits * p.M * p.N * 4;
+    sp.ws_bytes = ws_bytes;
     return sp;
 }
 

@@ -168,6 +168,27 @@ def test_factory_falls_back_to_direct_for_huge_strides():
     assert c["kind_name"] == "direct"
 
 
+@pytest.mark.parametrize("ld", [1 << 62, (1 << 63) - 1, (1 << 32) + 3])
+def test_size_checks_do_not_overflow(ld):
+    # bm * lda for these strides is past 2^63: the span checks must see a
+    # huge stage (64-bit direct kernel), not a wrapped-around small one
+    for kw in ({"lda": ld}, {"ldb": ld}, {"ldc": ld}):
+        c = q(1, 1, 64, **kw)
+        assert c["kind_name"] == "direct", (kw, c)
+    for la, lb in [(1, 0), (0, 1), (1, 1)]:
+        c = ql(la, lb, 1, 1, 64, lda=ld, ldb=ld)
+        assert c["kind_name"] == "direct", (la, lb, c)
+    # tile counts past 2^63 and workspaces past 2^63 bytes: no split, and the
+    # only kernel that could take the shape reports a grid it cannot launch
+    big = 1 << 62
+    c = q(big, big, 64, ldc=big)
+    assert c["kind_name"] == "direct" and c["grid"] > 0x7FFFFFFF
+    p = plan(1 << 40, 1 << 40, 1 << 20, ldb=1 << 40)
+    assert p["splits"] == 1 and p["workspace_bytes"] == 0
+    p = plan(64, 64, (1 << 62) + 5, splits=3, la=1)   # A column-major: lda = M
+    assert p["splits"] == 3 and p["workspace_bytes"] == 3 * 64 * 64 * 4
+
+
 # ----------------------------------------------------------------------------
 # Column-major operands
 # ----------------------------------------------------------------------------
