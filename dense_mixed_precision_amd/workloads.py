@@ -81,6 +81,24 @@ def _draw(g: torch.Generator, shape, dist: str, which: str, dtype=torch.float16)
         x = torch.ones(shape, dtype=torch.float32)
     elif dist == "zeros":
         x = torch.zeros(shape, dtype=torch.float32)
+    elif dist == "adversarial":
+        # FP16 edge values, every one exact in FP16 (and so in float32):
+        # 10% +-65504 (the largest finite), 10% subnormals n*2^-24
+        # (n = 1..1023), 10% +-2^-14 (the smallest normal), 5% zeros, the
+        # rest +-(1 + f/1024)*2^e with e uniform over -14..15; signs mixed.
+        # A K-term dot product stays below K*65504^2, far from FP32 overflow.
+        u = torch.rand(shape, generator=g, dtype=torch.float32)
+        sign = torch.where(torch.rand(shape, generator=g) < 0.5, -1.0, 1.0)
+        frac = torch.randint(0, 1024, shape, generator=g).to(torch.float32)
+        expo = torch.randint(-14, 16, shape, generator=g).to(torch.float32)
+        sub = torch.randint(1, 1024, shape, generator=g).to(torch.float32) * 2.0 ** -24
+        x = (1.0 + frac / 1024.0) * torch.exp2(expo)
+        x = torch.where(u < 0.65, x, torch.where(u < 0.75, torch.full_like(x, 65504.0),
+                        torch.where(u < 0.85, sub, torch.where(u < 0.95, torch.full_like(x, 2.0 ** -14),
+                                                               torch.zeros_like(x)))))
+        x = sign * x
+        if dtype != torch.float16:
+            raise ValueError("the adversarial draw is for FP16 inputs")
     else:
         raise ValueError(f"unknown distribution {dist!r}")
     return x.to(dtype)

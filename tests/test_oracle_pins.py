@@ -538,3 +538,17 @@ def test_planted_mistakes_are_caught(mistake):
             return oracle.gemm(Ab, Bb, Cn, beta if Cn is not None else alpha, alpha if Cn is not None else beta)
         raise AssertionError(mistake)
     assert not _pins_pass(7, 7, 17, compute)
+
+
+def test_adversarial_values_against_exact_arithmetic():
+    """The pages' adversarial edge values (+-65504, subnormals, the smallest
+    normal, zeros, mixed signs and exponents) on a ragged shape: the oracle
+    must equal the exact rational result within FP64 summation rounding."""
+    M, N, K = 9, 7, 41
+    A, B, C = make_inputs(M, N, K, "adversarial", seed=21, c_init="uniform")
+    for alpha, beta in ((1.0, 0.0), (1.5, -0.5)):
+        ref, absdot = oracle.gemm(bits(A), bits(B), C.numpy(), alpha, beta)
+        exact, exact_abs, _ = exact_gemm(bits(A), bits(B), C.numpy(), alpha, beta)
+        bound = fp64_sum_bound(K, alpha, beta, exact_abs, C.numpy())
+        assert np.all(np.abs(ref - exact) <= bound)
+        assert np.allclose(absdot, exact_abs, rtol=1e-15, atol=0)
