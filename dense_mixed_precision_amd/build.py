@@ -46,6 +46,28 @@ def build(extra=(), out: str = LIB, verbose: bool = False) -> str:
     return out
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c_abi", "abi_check")
+ROCM = "/opt/rocm"
+
+
+def build_c_check(verbose: bool = False) -> str:
+    """Compile the plain-C caller of the library (a test program: it uses
+    only mpgemm.h and the HIP runtime's allocation calls) with gcc, linked
+    against the in-tree libmpgemm.so through an $ORIGIN-relative rpath."""
+    cc = shutil.which("gcc") or "gcc"
+    cmd = [cc, "-O2", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include"),
+           "-I", os.path.join(ROOT, "include"), C_CHECK_SRC, "-o", C_CHECK_BIN,
+           "-L", HERE, "-lmpgemm", "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../../dense_mixed_precision_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    return C_CHECK_BIN
+
+
 def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True
