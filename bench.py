@@ -401,7 +401,8 @@ def main():
                             "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
                             "graph_us": round(r["graph_us"], 3),
                             "pct_of_peak": round(100 * w.flop / (r["kernel_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
-                            "roofline": roofline_entry(w, r["kernel_ms"]),
+                            "roofline": dict(roofline_entry(w, r["kernel_ms"]),
+                                             traffic=measured_traffic(name, r["kernel_ms"])),
                             "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "vec_a", "vec_b", "grid")}}
             del r
             torch.cuda.empty_cache()

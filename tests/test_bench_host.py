@@ -26,3 +26,21 @@ def test_secondary_warmup_is_about_40ms_of_gpu_time():
     assert bench.warmup_for(WORKLOADS["square8192"], 1000) >= 20      # ~1 ms per launch
     assert bench.warmup_for(WORKLOADS["square2048"], 1000) == 1000    # capped by --warmup
     assert bench.warmup_for(WORKLOADS["square8192"], 2) == 3          # at least 3
+
+
+def test_measured_traffic_follows_the_kernel_source_digest(tmp_path, monkeypatch):
+    """HBM bytes come from a committed counter summary only while the kernel
+    sources it was taken on are unchanged."""
+    digest = bench.kernel_source_digest()
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    text = ("# HBM traffic\nkernel_source_digest: {d}\nhbm_read_bytes_per_launch: 3000\n"
+            "hbm_write_bytes_per_launch: 1000\n")
+    (prof / "hbm_traffic_square2048.txt").write_text(text.format(d=digest))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: digest)
+    t = bench.measured_traffic("square2048", 0.001)
+    assert t["bytes_per_launch"] == 4000 and t["GBps"] == 4.0
+    (prof / "hbm_traffic_square2048.txt").write_text(text.format(d="0" * 16))
+    assert bench.measured_traffic("square2048", 0.001) is None
+    assert bench.measured_traffic("square8192", 0.001) is None
