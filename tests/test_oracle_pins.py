@@ -552,3 +552,34 @@ def test_adversarial_values_against_exact_arithmetic():
         bound = fp64_sum_bound(K, alpha, beta, exact_abs, C.numpy())
         assert np.all(np.abs(ref - exact) <= bound)
         assert np.allclose(absdot, exact_abs, rtol=1e-15, atol=0)
+
+
+def test_nonfinite_inputs_follow_ieee():
+    """NaN and +-Inf inputs (the pages are silent; IEEE semantics decide):
+    the oracle's NaN / +Inf / -Inf pattern equals a plain Python float
+    triple loop (IEEE double arithmetic) on the same values, and the finite
+    entries agree to FP64 rounding."""
+    M, N, K = 6, 5, 9
+    A, B, _ = make_inputs(M, N, K, "uniform", seed=31)
+    A, B = A.clone(), B.clone()
+    A[1, 2] = float("nan")          # row 1 all NaN
+    A[3, 4] = float("inf")          # row 3: +-Inf, or NaN where B[4, j] == 0
+    B[4, 1] = 0.0
+    B[6, 3] = float("-inf")         # column 3: -+Inf, or NaN with row 3's +Inf
+    A[0, 6] = 0.0                   # 0 * -Inf = NaN at (0, 3)
+    ref, _ = oracle.gemm(bits(A), bits(B))
+    a = A.double().tolist()
+    b = B.double().tolist()
+    want = np.empty((M, N))
+    for i in range(M):
+        for j in range(N):
+            s = 0.0
+            for k in range(K):
+                s += a[i][k] * b[k][j]
+            want[i, j] = s
+    assert np.array_equal(np.isnan(ref), np.isnan(want))
+    assert np.array_equal(np.isposinf(ref), np.isposinf(want))
+    assert np.array_equal(np.isneginf(ref), np.isneginf(want))
+    fin = np.isfinite(want)
+    assert np.allclose(ref[fin], want[fin], rtol=1e-13, atol=1e-15)
+    assert np.isnan(ref[1]).all() and np.isnan(ref[0, 3]) and np.isnan(ref[3, 1])
