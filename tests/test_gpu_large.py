@@ -12,9 +12,11 @@ a tensor-core GEMM", section "Capability").
   than 32-bit buffer offsets: the factory falls back to the 64-bit direct
   kernel, which must give the oracle's product; the gaps between the rows
   hold NaN, so a read outside the rows shows up.
+* K = 2^31 + 9 through split-K, exact.
 
-The large buffers are made on the device (nothing of their size goes
-through the host) and freed after each test.
+The large buffers are made on the device and freed after each test; only
+the split-K case copies its two 4.3 GB operands to the host, for the
+oracle.
 """
 import numpy as np
 import pytest
@@ -96,4 +98,49 @@ def test_stage_span_past_32_bit_offsets_takes_the_direct_kernel(which):
     torch.cuda.synchronize()
     ref, absdot = oracle.gemm(bits(A), bits(B), C.numpy(), 1.5, 0.5)
     assert_close(f"huge ld{which.lower()}", Cd.cpu().numpy(), ref, absdot)
+    torch.cuda.empty_cache()
+
+
+def test_k_past_2_31_through_split_k():
+    """K = 2^31 + 9 for a 1 x 1 output, through split-K (one tile, so the plan
+    cuts K into pieces; 64-bit K offsets per piece, a K tail in the last).
+    A is the 1 x K row stored column-major (lda = 1; stored row-major its
+    leading dimension K would put a stage past 32-bit offsets, which the
+    64-bit direct kernel takes unsplit), B is K x 1 row-major.  Values in
+    {-1, 0, 1}: every partial sum is an integer far below 2^24 in magnitude
+    (a random walk of 2^31 steps stays within a few times 4e4), so the FP32
+    result is exact and must equal the oracle's bit for bit."""
+    K = 2 ** 31 + 9
+    dev = device()
+    g = torch.Generator(device=dev)
+    g.manual_seed(2311)
+    # drawn on the device (seeded), copied to the host for the oracle
+    Ad = torch.randint(-1, 2, (K,), generator=g, device=dev, dtype=torch.int8).to(torch.float16)
+    Bd = torch.randint(-1, 2, (K,), generator=g, device=dev, dtype=torch.int8).to(torch.float16)
+    a = Ad.cpu().numpy()
+    b = Bd.cpu().numpy()
+    C = torch.full((1,), float("nan"), device=dev)
+    args = (mp.MPGEMM_IN_F16, mp.MPGEMM_COL_MAJOR, mp.MPGEMM_ROW_MAJOR, 1, 1, K, Ad.data_ptr(), 1,
+            Bd.data_ptr(), 1)
+    plan = mp.mpgemm_splitk_plan(*args, 0)
+    print(f"[K=2^31+9] split-K plan {plan}", flush=True)
+    assert plan["splits"] > 1 and mp.mpgemm_config_info(plan["config_id"])["kind_name"] == "pipe"
+    ws = torch.empty(plan["workspace_bytes"] // 4, dtype=torch.float32, device=dev)
+    rc = mp.mpgemm_gemm_splitk(*args, C.data_ptr(), 1, 1.0, 0.0, 0, 0, ws.data_ptr(), ws.numel() * 4,
+                               torch.cuda.current_stream().cuda_stream)
+    assert rc == mp.MPGEMM_OK, mp.mpgemm_strerror(rc)
+    torch.cuda.synchronize()
+    # The oracle's dot product in 256 blocks of 2^23 values (the diagonal
+    # entries of the block-reshaped product, computed in parallel) plus the
+    # 9-value remainder: integer partial results, so their FP64 sum is exact.
+    R, L = 256, 2 ** 23
+    ab, bb = a.view(np.uint16), b.view(np.uint16)
+    diag = np.arange(R)
+    blocks, _ = oracle.gemm_entries(ab[:R * L].reshape(R, L), bb[:R * L].reshape(R, L), None, 1.0, 0.0,
+                                    diag, diag, layout_b=oracle.COL_MAJOR)
+    rest, _ = oracle.gemm(ab[R * L:].reshape(1, K - R * L), bb[R * L:].reshape(K - R * L, 1))
+    ref = float(np.sum(blocks)) + float(rest[0, 0])
+    got = C.cpu().numpy()
+    assert got[0] == np.float32(ref), (got[0], ref)
+    del Ad, Bd, C, ws
     torch.cuda.empty_cache()
