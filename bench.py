@@ -281,6 +281,70 @@ def sample_power(w, torch, mp, seconds=2.0):
     return out
 
 
+def mfma_ceiling(torch, mp, seconds=1.5):
+    """Matrix-core-only throughput under sustained load: the library's
+    throughput probe (independent matrix instructions, 128 accumulator
+    registers per lane, no memory traffic) on one workgroup of 8 waves per
+    compute unit, run back to back for `seconds` per case with socket power
+    and the graphics clock read in the middle.  Cases: the 8192^3 workload's
+    operand distribution (N(0,1) clipped to +-4) in FP16 on both
+    instructions, constant FP16 operands, and the same random values in
+    BF16.  What the board's power limit leaves for any FP16 kernel before
+    operand traffic."""
+    import threading
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(77)
+    rand = torch.randn(4096, generator=g).clamp_(-4.0, 4.0)
+    cases = [("random_f16_16x16x32", mp.MPGEMM_IN_F16, 16, rand.to(torch.float16)),
+             ("random_f16_32x32x16", mp.MPGEMM_IN_F16, 32, rand.to(torch.float16)),
+             ("constant_f16_16x16x32", mp.MPGEMM_IN_F16, 16, torch.full((4096,), 1.0, dtype=torch.float16)),
+             ("random_bf16_16x16x32", mp.MPGEMM_IN_BF16, 16, rand.to(torch.bfloat16))]
+    wgs, iters = 256, 4000
+    out = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    res = {}
+    for name, in_type, shape, vals in cases:
+        ops = vals.to(dev)
+        per_round = 2 * 32 * 32 * 16 * 8 if shape == 32 else 2 * 16 * 16 * 32 * 32
+        flop = wgs * 8 * iters * per_round
+
+        def launch():
+            rc = mp.mpgemm_probe_mfma_rate(in_type, shape, ops.data_ptr(), ops.numel(), iters, wgs,
+                                           out.data_ptr(), out.numel(), torch.cuda.current_stream().cuda_stream)
+            if rc != mp.MPGEMM_OK:
+                raise mp.MpgemmError(rc, "mpgemm_probe_mfma_rate")
+
+        for _ in range(20):
+            launch()
+        torch.cuda.synchronize()
+        stop = time.perf_counter() + seconds
+        count = [0]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+
+        def loop():
+            e0.record()
+            while time.perf_counter() < stop:
+                for _ in range(10):
+                    launch()
+                count[0] += 10
+                torch.cuda.synchronize()
+            e1.record()
+            torch.cuda.synchronize()
+
+        th = threading.Thread(target=loop)
+        th.start()
+        time.sleep(seconds * 0.6)
+        busy = _smi_power()
+        th.join()
+        ms = e0.elapsed_time(e1)
+        res[name] = {"tflops": round(flop * count[0] / (ms * 1e-3) / 1e12, 1), "launches": count[0],
+                     "socket_w": busy and busy.get("socket_w"), "gfx_mhz_mean": busy and busy.get("gfx_mhz_mean")}
+    res["source"] = ("mpgemm_probe_mfma_rate, 256 workgroups x 8 waves, 4000 rounds per launch; "
+                     "amd-smi metric -p -c in the middle of each run")
+    return res
+
+
 def roofline_entry(w, kernel_ms):
     """MFMA bound for the compute-heavy shapes, HBM bound where the
     arithmetic intensity (FLOP per algorithmic byte) is below the ridge."""
@@ -448,6 +512,8 @@ def main():
         line["workloads"] = others
     if args.power:
         line["power"] = sample_power(WORKLOADS["square8192"], torch, mp)
+        print("# matrix-core ceiling (throughput probe under sustained load)", file=sys.stderr, flush=True)
+        line["mfma_ceiling"] = mfma_ceiling(torch, mp)
     if not args.no_cpu_baseline:
         print("# cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(head, res, args.cpu_seconds)

@@ -20,6 +20,7 @@ integers holding device addresses, ``stream`` a hipStream_t as an integer,
     mpgemm_gemm_ex_with_config(cfg, in_type, layout_a, layout_b, ...) -> int   (per-column bias)
     mpgemm_splitk_plan(...) -> dict, mpgemm_gemm_splitk(..., splits, workspace, bytes, stream) -> int
     mpgemm_num_configs(), mpgemm_config_info(id), mpgemm_probe_mfma_layout(shape, out, stream)
+    mpgemm_probe_mfma_rate(in_type, shape, ops, ops_len, iters, workgroups, out, out_len, stream)
     mpgemm_strerror(code), mpgemm_version()
 
 Tensor convenience: ``gemm(A, B, C, alpha, beta)`` for torch tensors on the
@@ -68,6 +69,7 @@ from ._binding import (  # noqa: F401
     splitk_plan_for,
     mpgemm_num_configs,
     mpgemm_probe_mfma_layout,
+    mpgemm_probe_mfma_rate,
     mpgemm_strerror,
     mpgemm_version,
     query_for,

@@ -101,6 +101,8 @@ def load():
     lib.mpgemm_config_info.restype = i32
     lib.mpgemm_probe_mfma_layout.argtypes = [i32, vp, vp]
     lib.mpgemm_probe_mfma_layout.restype = i32
+    lib.mpgemm_probe_mfma_rate.argtypes = [i32, i32, vp, i64, i64, i32, vp, i64, vp]
+    lib.mpgemm_probe_mfma_rate.restype = i32
     lib.mpgemm_strerror.argtypes = [i32]
     lib.mpgemm_strerror.restype = ctypes.c_char_p
     lib.mpgemm_version.argtypes = []
@@ -229,6 +231,12 @@ def mpgemm_config_info(config_id: int) -> dict:
 
 def mpgemm_probe_mfma_layout(shape: int, out: int, stream=0) -> int:
     return int(load().mpgemm_probe_mfma_layout(shape, out, stream))
+
+
+def mpgemm_probe_mfma_rate(in_type: int, shape: int, ops: int, ops_len: int, iters: int, workgroups: int,
+                           out: int, out_len: int, stream=0) -> int:
+    return int(load().mpgemm_probe_mfma_rate(in_type, shape, ops, ops_len, iters, workgroups, out, out_len,
+                                             stream))
 
 
 def mpgemm_strerror(code: int) -> str:

@@ -13,6 +13,7 @@
 //                     stride and storage order: the universal fallback.
 //   scale_c           C <- beta*C when alpha == 0 or K == 0.
 //   probe_mfma        writes the accumulator lane layout of one instruction.
+//   probe_mfma_rate   sustained matrix-instruction throughput, no memory traffic.
 //
 // Matrix-core lane layouts used here (CDNA3/CDNA4 matrix instruction docs,
 // checked on the device by probe_mfma):
@@ -516,6 +517,53 @@ probe_mfma(float *out, int shape)
         for (int v = 0; v < 4; ++v)
             out[l * 4 + v] = d[v];
     }
+}
+
+// Matrix-core throughput probe.  Every wave loads four operand pairs once
+// (lane l: A values ops[64*(16*q + l)/8 ...], see below) and then issues
+// `iters` rounds of MFMA_N independent matrix instructions, rotating through
+// the four pairs so consecutive instructions see different operand bits, as
+// in the GEMM's inner loop; nothing touches memory inside the loop.  Each
+// lane writes the sum of its accumulators to out[global thread id], so the
+// work is kept.  A diagnostic of the clock and power the matrix cores settle
+// at under sustained load for given operand values.
+// ops: 4 pairs x 64 lanes x 16 values (8 for A, then 8 for B) = 4096 values.
+template <int IN, int MI>
+__global__ void __launch_bounds__(512)
+probe_mfma_rate(const uint16_t *ops, int64_t iters, float *out)
+{
+    const int lane = threadIdx.x & 63;
+    half8 a[4], b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[q][e] = __builtin_bit_cast(_Float16, ops[(q * 64 + lane) * 16 + e]);
+            b[q][e] = __builtin_bit_cast(_Float16, ops[(q * 64 + lane) * 16 + 8 + e]);
+        }
+    // 128 accumulator registers per lane, like the GEMM's wave tiles
+    constexpr int N = MI == 32 ? 8 : 32;
+    using AccT = typename std::conditional<MI == 32, floatx16, floatx4>::type;
+    AccT acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        acc[i] = AccT{0};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if constexpr (MI == 32)
+                acc[i] = mfma32<IN>(a[i & 3], b[(i >> 2) & 3], acc[i]);
+            else
+                acc[i] = mfma16<IN>(a[i & 3], b[(i >> 2) & 3], acc[i]);
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int v = 0; v < (MI == 32 ? 16 : 4); ++v)
+            s += acc[i][v];
+    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
 // ---------------------------------------------------------------------------

@@ -844,6 +844,33 @@ int mpgemm_probe_mfma_layout(int shape, float *out, void *stream)
     return hipGetLastError() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
 }
 
+int mpgemm_probe_mfma_rate(int in_type, int shape, const uint16_t *ops, int64_t ops_len, int64_t iters,
+                           int workgroups, float *out, int64_t out_len, void *stream)
+{
+    if ((in_type != MPGEMM_IN_F16 && in_type != MPGEMM_IN_BF16) || (shape != 32 && shape != 16))
+        return MPGEMM_ECONFIG;
+    if (ops == nullptr || out == nullptr)
+        return MPGEMM_ENULL;
+    if (ops_len < 4096 || iters < 0 || iters > (int64_t)1 << 24 || workgroups < 1 || workgroups > 65535 ||
+        out_len < (int64_t)workgroups * 512)
+        return MPGEMM_EDIM;
+    (void)hipGetLastError();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)workgroups), block(512);
+    if (in_type == MPGEMM_IN_F16) {
+        if (shape == 32)
+            hipLaunchKernelGGL((mpg::probe_mfma_rate<mpg::kInF16, 32>), grid, block, 0, s, ops, iters, out);
+        else
+            hipLaunchKernelGGL((mpg::probe_mfma_rate<mpg::kInF16, 16>), grid, block, 0, s, ops, iters, out);
+    } else {
+        if (shape == 32)
+            hipLaunchKernelGGL((mpg::probe_mfma_rate<mpg::kInBF16, 32>), grid, block, 0, s, ops, iters, out);
+        else
+            hipLaunchKernelGGL((mpg::probe_mfma_rate<mpg::kInBF16, 16>), grid, block, 0, s, ops, iters, out);
+    }
+    return hipGetLastError() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
+}
+
 const char *mpgemm_strerror(int code)
 {
     switch (code) {

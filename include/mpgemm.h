@@ -323,6 +323,27 @@ int mpgemm_config_info(int config_id, mpgemm_config *out);
  */
 int mpgemm_probe_mfma_layout(int shape, float *out, void *stream);
 
+/*
+ * Diagnostic: sustained matrix-core throughput with no memory traffic, for
+ * measuring the clock and power the matrix cores settle at under load for
+ * given operand values (the GEMM's own inner loop is this instruction
+ * stream plus its operand traffic).  `workgroups` workgroups of 8 waves;
+ * every wave loads four operand pairs from `ops` once (device memory,
+ * ops_len >= 4096 16-bit values: pair q, lane l reads 8 A values at
+ * (64*q + l)*16 and 8 B values right after) and issues `iters` rounds of
+ * independent matrix instructions (8 of 32x32x16 for shape 32, 32 of
+ * 16x16x32 for shape 16, i.e. 128 accumulator registers per lane),
+ * rotating through the pairs.  FLOP per call = workgroups * 8 waves *
+ * iters * 2 * 32*32*16 * 8 (shape 32) or * 2 * 16*16*32 * 32 (shape 16).
+ * Each thread writes the sum of its accumulators to out[thread id]
+ * (out_len >= workgroups*512 floats).  in_type MPGEMM_IN_F16 or
+ * MPGEMM_IN_BF16.  MPGEMM_ECONFIG for another format or shape,
+ * MPGEMM_ENULL for NULL buffers, MPGEMM_EDIM for short buffers, iters
+ * outside 0..2^24 or workgroups outside 1..65535 (checked before launch).
+ */
+int mpgemm_probe_mfma_rate(int in_type, int shape, const uint16_t *ops, int64_t ops_len, int64_t iters,
+                           int workgroups, float *out, int64_t out_len, void *stream);
+
 /* Static text for an error code (never NULL). */
 const char *mpgemm_strerror(int code);
 

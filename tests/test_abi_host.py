@@ -354,3 +354,24 @@ def test_splitk_launch_checks_the_workspace_before_hip():
     assert mp.mpgemm_gemm_splitk(*args, 0, 0, 0) == mp.MPGEMM_ENULL
     assert mp.mpgemm_gemm_splitk(*args, FAKE_C + 0x100000, 1024, 0) == mp.MPGEMM_EWORKSPACE
     assert mp.mpgemm_gemm_splitk(*args, FAKE_C + 0x100002, 1 << 30, 0) == mp.MPGEMM_EALIGN
+
+
+def test_mfma_rate_probe_rejects_bad_arguments_before_launch():
+    ok = (mp.MPGEMM_IN_F16, 16, FAKE_A, 4096, 10, 256, FAKE_C, 256 * 512, 0)
+
+    def call(**kw):
+        names = ("in_type", "shape", "ops", "ops_len", "iters", "workgroups", "out", "out_len", "stream")
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return mp.mpgemm_probe_mfma_rate(*(args[n] for n in names))
+
+    assert call(in_type=7) == mp.MPGEMM_ECONFIG
+    assert call(shape=8) == mp.MPGEMM_ECONFIG
+    assert call(ops=0) == mp.MPGEMM_ENULL
+    assert call(out=0) == mp.MPGEMM_ENULL
+    assert call(ops_len=4095) == mp.MPGEMM_EDIM
+    assert call(out_len=256 * 512 - 1) == mp.MPGEMM_EDIM
+    assert call(iters=-1) == mp.MPGEMM_EDIM
+    assert call(iters=(1 << 24) + 1) == mp.MPGEMM_EDIM
+    assert call(workgroups=0) == mp.MPGEMM_EDIM
+    assert call(workgroups=65536) == mp.MPGEMM_EDIM

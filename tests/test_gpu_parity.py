@@ -49,6 +49,23 @@ def test_mfma_layout_probe(shape, nv):
             assert got[lane, v] == row + shape * col, (lane, v, got[lane, v])
 
 
+@pytest.mark.parametrize("fmt", [mp.MPGEMM_IN_F16, mp.MPGEMM_IN_BF16])
+@pytest.mark.parametrize("shape", [32, 16])
+def test_mfma_rate_probe_does_the_work_it_counts(shape, fmt):
+    # all operands 1: every accumulator element gains the instruction's K
+    # (16 or 32) per round, so each lane's sum is exact and known
+    dtype = torch.bfloat16 if fmt == mp.MPGEMM_IN_BF16 else torch.float16
+    ops = torch.ones(4096, dtype=dtype, device=device())
+    wgs, iters = 3, 10
+    out = torch.full((wgs * 512,), -1.0, device=device())
+    rc = mp.mpgemm_probe_mfma_rate(fmt, shape, ops.data_ptr(), ops.numel(), iters, wgs, out.data_ptr(),
+                                   out.numel(), 0)
+    assert rc == mp.MPGEMM_OK
+    torch.cuda.synchronize()
+    per_lane = (8 * 16 * iters * 16) if shape == 32 else (32 * 4 * iters * 32)
+    assert torch.all(out == per_lane)
+
+
 # ----------------------------------------------------------------------------
 # The five workloads
 # ----------------------------------------------------------------------------
