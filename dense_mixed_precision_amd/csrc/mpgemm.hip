@@ -481,6 +481,7 @@ int run(int id, const Problem &p, void *stream)
             return MPGEMM_OK;
         const int64_t gx = cdiv(p.N, 256) < 64 ? cdiv(p.N, 256) : 64;
         const int64_t gy = p.M < 65535 ? p.M : 65535;
+        (void)hipGetLastError();  // not an earlier call's error
         hipLaunchKernelGGL(mpg::scale_c, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s,
                            const_cast<float *>(p.C), p.M, p.N, p.ldc, p.beta, p.bias);
         return hipGetLastError() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;

@@ -232,3 +232,27 @@ def test_non_default_stream():
     A, B, C = make_inputs(M, N, K, "uniform", seed=6, c_init="uniform")
     s = torch.cuda.Stream()
     full_check("side stream", A, B, C, 1.0, 1.0, stream=s)
+
+
+def test_an_earlier_runtime_error_is_not_reported_as_this_calls():
+    """A failed HIP call made before (here an allocation far beyond the
+    device, refused on the host) leaves the runtime's last error set; the
+    library's calls must still report their own outcome, on the scale-only
+    path (alpha = 0) as on the product path."""
+    import ctypes
+
+    hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime already in the process
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipMalloc.restype = ctypes.c_int
+    M, N, K = 70, 50, 40
+    A, B, C = make_inputs(M, N, K, "uniform", seed=77, c_init="uniform")
+    Ad, Bd, Cd = A.to(device()), B.to(device()), C.to(device())
+    for alpha, beta in ((0.0, 0.5), (1.0, 0.5)):
+        ptr = ctypes.c_void_p()
+        assert hip.hipMalloc(ctypes.byref(ptr), 1 << 60) != 0
+        rc = mp.mpgemm_f16f32(M, N, K, Ad.data_ptr(), K, Bd.data_ptr(), N, Cd.data_ptr(), N, alpha, beta,
+                              torch.cuda.current_stream().cuda_stream)
+        assert rc == mp.MPGEMM_OK, (alpha, mp.mpgemm_strerror(rc))
+    torch.cuda.synchronize()
+    ref, absdot = oracle.gemm(bits(A), bits(B), (np.float32(0.5) * C.numpy()), 1.0, 0.5)
+    assert_close("after stale errors", Cd.cpu().numpy(), ref, absdot)
