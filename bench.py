@@ -124,11 +124,12 @@ def graph_time_us(fn, reps, torch):
 
 
 def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=None, bias=False,
-                  splitk=False, graph_reps=0, config=None):
+                  splitk=False, graph_reps=0, config=None, splits=0):
     """Time `steps` launches (after `warmup`) on resident inputs.  A column-
     major operand is stored transposed on the device and passed as the
     transposed view; `dtype` picks FP16 (default) or BF16 inputs; `bias`
-    adds a per-column bias vector to the epilogue."""
+    adds a per-column bias vector to the epilogue; `splitk` goes through the
+    split-K entry point with `splits` pieces (0: the library's plan)."""
     from dense_mixed_precision_amd.workloads import workload_inputs
 
     dev = torch.device("cuda:0")
@@ -143,8 +144,10 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
     bias_d = torch.rand(w.N, device=dev) * 2 - 1 if bias else None
     ws = None
     if splitk:
-        plan = mp.splitk_plan_for(Ad, Bd, Cd)
-        cfg = dict(cfg, splits=plan["splits"])
+        plan = mp.splitk_plan_for(Ad, Bd, Cd, splits)
+        c = mp.mpgemm_config_info(plan["config_id"])
+        tiles = -(-w.M // c["bm"]) * -(-w.N // c["bn"])
+        cfg = dict(c, grid=cfg["grid"] if plan["splits"] == 1 else tiles * plan["splits"], splits=plan["splits"])
         ws = torch.empty(max(plan["workspace_bytes"] // 4, 1), dtype=torch.float32, device=dev)
 
     # The timed calls go through the raw C-ABI binding with the arguments
@@ -164,7 +167,8 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
 
     def step():
         if splitk:
-            mp.gemm_splitk(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, workspace=ws, stream=stream)
+            mp.gemm_splitk(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, workspace=ws, stream=stream,
+                           splits=splits)
             return
         if config is not None:
             rc = forced(config, in_type, layout_a, layout_b, w.M, w.N, w.K, a_ptr, lda, b_ptr, ldb, c_ptr,
@@ -196,7 +200,7 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
         # the same call on the current (capture) stream
         def step_current():
             if splitk:
-                mp.gemm_splitk(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, workspace=ws)
+                mp.gemm_splitk(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, workspace=ws, splits=splits)
             else:
                 mp.gemm(Ad, Bd, Cd, w.alpha, w.beta, bias=bias_d, config=config)
 
@@ -493,20 +497,21 @@ def main():
                                 "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "bk", "vec_a", "vec_b", "grid")}}
                 del r
                 torch.cuda.empty_cache()
-        # split-K on the pages' skinny case (64 output tiles for 256 compute units)
+        # the pages' skinny case: the library's choice (the narrow kernel, one
+        # workgroup per 16 rows) beside the tiled kernel split 8 ways over K
         from dense_mixed_precision_amd.workloads import Workload
         skinny = Workload("skinny4096x16x4096", 4096, 16, 4096, "uniform", 1.0, 0.0, None, 1005)
-        for tag, sk in (("", False), ("_splitk", True)):
+        for tag, sk in (("", 0), ("_splitk8", 8)):
             name = skinny.name + tag
             print(f"# timing {name} ({args.steps} steps)", file=sys.stderr, flush=True)
-            r = time_workload(skinny, args.steps, warmup_for(skinny, args.warmup), torch, mp, splitk=sk,
-                              graph_reps=20)
+            r = time_workload(skinny, args.steps, warmup_for(skinny, args.warmup), torch, mp, splitk=sk > 0,
+                              graph_reps=20, splits=sk)
             others[name] = {"tflops": round(skinny.flop / (r["kernel_ms"] * 1e-3) / 1e12, 2),
                             "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
                             "graph_us": round(r["graph_us"], 3),
                             "roofline": roofline_entry(skinny, r["kernel_ms"]),
                             "splits": r["cfg"].get("splits", 1),
-                            "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "bk", "grid")}}
+                            "kernel": {k: r["cfg"][k] for k in ("id", "kind_name", "bm", "bn", "bk", "grid")}}
             del r
             torch.cuda.empty_cache()
         line["workloads"] = others

@@ -35,7 +35,7 @@ class MpgemmConfig(ctypes.Structure):
 
 
 config_fields = [f[0] for f in MpgemmConfig._fields_]
-KIND_NAMES = {0: "tiled", 1: "direct", 2: "scale", 3: "none", 4: "pipe"}
+KIND_NAMES = {0: "tiled", 1: "direct", 2: "scale", 3: "none", 4: "pipe", 5: "narrow"}
 
 
 class MpgemmError(RuntimeError):

@@ -1373,4 +1373,187 @@ gemm_pipe(GemmArgs args_in)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Narrow kernel: N <= 16 (one 16-column instruction tile), A row-major
+// ---------------------------------------------------------------------------
+// A product with at most 16 columns is a stream over A (the "skinny" shape
+// of the capstone gate): block tiles wide enough to amortize an LDS ring
+// would mostly multiply zeros, and an under-filled grid leaves the memory
+// system idle.  Each workgroup takes 16 rows of C; its 8 waves split the K
+// range into 8 slices.  A wave streams its slice of A straight from memory
+// into operand registers (lane l: row l % 16, 8 consecutive k at
+// 8*(l/16) of each 32-deep step, one 16-byte buffer load; out-of-range rows
+// and K read zero) and loads B beside it: a column-major B with one 16-byte
+// load of the operand's 8 k values; a row-major B with one 16-byte load of
+// 8 consecutive columns of one k row per lane (the k-step's 32 x 16 values
+// in one instruction; a vector that crosses column N is loaded element by
+// element, zero past N), turned into operand layout through a 1 KiB LDS
+// slot of the wave's own and the transposing LDS read.  It accumulates a
+// 16x16 partial tile on the 16x16x32 instruction, with the loads DEPTH
+// k-steps ahead of their use (two loads per k-step, so the 6-bit load
+// counter covers deep rings).  As in the
+// pipelined kernel the main range covers the largest multiple of 8 of K and
+// the last K % 8 values are one more step (wave 0).  The 8 partial tiles
+// are summed through LDS in ascending slice order (run-to-run identical),
+// then wave 0 applies alpha, beta and the bias and stores the tile.
+// 32-bit buffer offsets: the host checks that 16 rows of A, the K (or 16)
+// stored rows of B and 16 rows of C fit them.
+template <int IN, int LB, int DEPTH>
+__global__ void __launch_bounds__(512)
+gemm_narrow(GemmArgs args)
+{
+    constexpr bool B_ROW = LB == 0;
+    __shared__ floatx4 part[8][64];
+    __shared__ u32x4 bslot[8][64];  // row-major B: each wave's transpose slot
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t m0 = (int64_t)blockIdx.x * 16;
+    const int64_t M = args.M, N = args.N;
+    const int ktail = (int)(args.K & 7);
+    const int64_t Km = args.K - ktail;
+    const int r = lane & 15;          // A row / B column of this lane
+    const int kq = 8 * (lane >> 4);   // this lane's 8 k values within a step
+    const bool r_ok = m0 + r < M;
+    const bool n_ok = r < N;
+    const int lda = (int)args.lda, ldb = (int)args.ldb;
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(args.A + m0 * args.lda);
+    const __amdgpu_buffer_rsrc_t rsB = make_rsrc(args.B);
+
+    // this wave's k-steps [s0, s1) of the main range
+    const int64_t steps = (Km + 31) / 32;
+    const int64_t per = (steps + 7) / 8;
+    const int64_t s0 = wave * per;
+    const int64_t s1 = s0 + per < steps ? s0 + per : steps;
+
+    // row-major B: lane j loads columns 8*(j%2)..+7 of k row j/2 of the step
+    const int bk = lane >> 1, bn = 8 * (lane & 1);
+    const bool b_full = bn + 8 <= N;
+    const bool b_some = bn < N;
+    u32x4 ra[DEPTH], rb[DEPTH];
+    auto issue = [&](int d, int64_t s) __attribute__((always_inline)) {
+        const int64_t k = 32 * s + kq;
+        const bool k_ok = k + 8 <= Km;
+        ra[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rsA, (r_ok && k_ok) ? (uint32_t)((r * lda + (int)k) * 2) : kOOB, 0, 0));
+        if constexpr (B_ROW) {
+            const int64_t kr = 32 * s + bk;
+            // used only when row kr is in range (within the span the host checks)
+            const uint32_t off = (uint32_t)((kr * args.ldb + bn) * 2);
+            if (b_full || !b_some || kr >= Km) {
+                rb[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rsB, (b_full && kr < Km) ? off : kOOB, 0, 0));
+            } else {
+                // the vector crosses column N: element by element, zero past N
+                uint32_t h[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    h[e] = __builtin_amdgcn_raw_buffer_load_b16(rsB, bn + e < N ? off + 2u * e : kOOB, 0, 0);
+                rb[d] = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+            }
+        } else {
+            rb[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rsB, (n_ok && k_ok) ? (uint32_t)((r * ldb + (int)k) * 2) : kOOB, 0, 0));
+        }
+    };
+    // the B operand of the step in register set d: lane l needs k = 8*(l/16)
+    // + 0..7 of column l % 16.  Row-major: the 32 k rows of 32 bytes go into
+    // the wave's slot (lane j at byte 16*j = row j/2, half j%2), and two
+    // transposing reads give lane 16*g + i the 4 + 4 values of column i at
+    // rows 8*g + 0..3 and 8*g + 4..7 (in each 16-lane group, lane i's slot
+    // t takes element i%4 of the 8 bytes addressed by lane 4*t + i/4, which
+    // addresses row 8*g + t at column 4*(i/4)).  The slot is the wave's own
+    // and LDS operations of one wave complete in order, so no barrier.
+    auto b_operand = [&](int d) __attribute__((always_inline)) {
+        if constexpr (B_ROW) {
+            *(lds_u32x4 *)&bslot[wave][lane] = rb[d];
+            const int g = lane >> 4, q = lane & 15;
+            const lds_u8 *p0 = (const lds_u8 *)&bslot[wave][0] + (8 * g + (q >> 2)) * 32 + 8 * (q & 3);
+            const fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) fp16x4 *)p0);
+            const fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                (__attribute__((address_space(3))) fp16x4 *)(p0 + 4 * 32));
+            return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            return __builtin_bit_cast(half8, rb[d]);
+        }
+    };
+
+    floatx4 acc = floatx4{0};
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (s0 + d < s1)
+            issue(d, s0 + d);
+    for (int64_t s = s0; s < s1; s += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            if (s + d < s1) {
+                const half8 a = __builtin_bit_cast(half8, ra[d]);
+                acc = mfma16<IN>(a, b_operand(d), acc);
+                if (s + d + DEPTH < s1)
+                    issue(d, s + d + DEPTH);
+            }
+        }
+    }
+
+    // the last K % 8 values: lane l holds k = Km + kq + 0..7, zero at and past K
+    if (wave == 0 && ktail > 0) {
+        uint32_t ha[8], hb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int k = kq + e;
+            const bool ok = k < ktail;
+            const int kk = (int)Km + k;
+            ha[e] = __builtin_amdgcn_raw_buffer_load_b16(rsA, (r_ok && ok) ? (uint32_t)((r * lda + kk) * 2) : kOOB,
+                                                         0, 0);
+            hb[e] = __builtin_amdgcn_raw_buffer_load_b16(
+                rsB, (n_ok && ok) ? (uint32_t)((B_ROW ? kk * ldb + r : r * ldb + kk) * 2) : kOOB, 0, 0);
+        }
+        const half8 a = __builtin_bit_cast(half8, u32x4{pack2(ha[0], ha[1]), pack2(ha[2], ha[3]),
+                                                        pack2(ha[4], ha[5]), pack2(ha[6], ha[7])});
+        const half8 b = __builtin_bit_cast(half8, u32x4{pack2(hb[0], hb[1]), pack2(hb[2], hb[3]),
+                                                        pack2(hb[4], hb[5]), pack2(hb[6], hb[7])});
+        acc = mfma16<IN>(a, b, acc);
+    }
+
+    // sum the 8 partial tiles in ascending slice order
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0)
+        return;
+    floatx4 sum = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < 8; ++w)
+        sum += part[w][lane];
+
+    // epilogue: accumulator v of lane l holds row 4*(l/16) + v, column l % 16
+    const __amdgpu_buffer_rsrc_t rsC = make_rsrc(args.C + m0 * args.ldc);
+    const int ldc = (int)args.ldc;
+    const int col = lane & 15;
+    const bool c_ok = col < N;
+    float bv = 0.0f;
+    if (args.bias && c_ok)
+        bv = args.bias[col];
+    uint32_t off[4];
+    float cin[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int row = 4 * (lane >> 4) + v;
+        off[v] = (c_ok && m0 + row < M) ? (uint32_t)((row * ldc + col) * 4) : kOOB;
+        cin[v] = 0.0f;
+    }
+    if (args.beta != 0.0f) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            cin[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsC, off[v], 0, 0));
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        float val = args.alpha * sum[v];
+        if (args.beta != 0.0f)
+            val = __builtin_fmaf(args.beta, cin[v], val);
+        if (args.bias)
+            val += bv;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off[v], 0, kStoreNT);
+    }
+}
+
 }  // namespace mpg

@@ -51,6 +51,13 @@ hipError_t launch_pipe(const GemmArgs &a, dim3 grid, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int IN, int LB, int DEPTH>
+hipError_t launch_narrow(const GemmArgs &a, dim3 grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((mpg::gemm_narrow<IN, LB, DEPTH>), grid, dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int IN>
 hipError_t launch_direct(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
@@ -114,6 +121,35 @@ constexpr Entry pipe_entry(int id)
     c.in_type = Cfg::IN;
     c.k_groups = Cfg::KGROUPS;
     return Entry{c, &launch_pipe<Cfg>};
+}
+
+// N <= 16 with A row-major: 16 rows of C per workgroup, 8 waves over K.
+template <int IN, int LB, int DEPTH>
+constexpr Entry narrow_entry(int id)
+{
+    mpgemm_config c{};
+    c.id = id;
+    c.kind = MPGEMM_KIND_NARROW;
+    c.bm = 16;
+    c.bn = 16;
+    c.bk = 32;
+    c.waves_m = 1;
+    c.waves_n = 1;
+    c.wave_m = 16;
+    c.wave_n = 16;
+    c.mfma_m = 16;
+    c.mfma_n = 16;
+    c.mfma_k = 32;
+    c.vec_a = 8;
+    c.vec_b = LB == kColMajor ? 8 : 1;
+    c.stages = DEPTH;   // k-steps of loads in flight per wave
+    c.threads = 512;
+    c.lds_bytes = 2 * 8 * 64 * 16;  // partial tiles + row-major B transpose slots
+    c.layout_a = kRowMajor;
+    c.layout_b = LB;
+    c.in_type = IN;
+    c.k_groups = 8;     // waves splitting K
+    return Entry{c, &launch_narrow<IN, LB, DEPTH>};
 }
 
 template <int IN>
@@ -236,6 +272,15 @@ const Entry kTable[] = {
     pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kColMajor, kRowMajor, kInBF16, 1, 16>>(98),
     pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kRowMajor, kColMajor, kInBF16, 1, 16>>(99),
     pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kColMajor, kColMajor, kInBF16, 1, 16>>(100),
+    // N <= 16 with A row-major, per input format and storage order of B;
+    // four k-steps of loads in flight per wave (fewer registers, so more
+    // workgroups share a compute unit when M is large)
+    narrow_entry<kInF16, kRowMajor, 4>(101),
+    narrow_entry<kInF16, kColMajor, 4>(102),
+    narrow_entry<kInBF16, kRowMajor, 4>(103),
+    narrow_entry<kInBF16, kColMajor, 4>(104),
+    // deeper candidate (FP16, B row-major)
+    narrow_entry<kInF16, kRowMajor, 8>(105),
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
 constexpr int kDirectIds[2] = {12, 89};  // per input format
@@ -251,6 +296,13 @@ constexpr int kScaleId = 13;
 constexpr int kWideKIds[2][4] = {{37, 58, 59, 60}, {67, 74, 81, 88}};
 // 64x64 tiles, K tile 128, three stages (row-major FP16)
 constexpr int kSmallDeepKId = 39;
+// narrow kernel (N <= 16, A row-major) per input format and storage order of B
+constexpr int kNarrowIds[2][2] = {{101, 102}, {103, 104}};
+// below this many 16-row workgroups the narrow kernel leaves most compute
+// units idle, and split-K over the tile kernels is faster (256x16x65536:
+// 74 against 38 us); at or above it the narrow kernel leads (1024x16x16384:
+// 21 against 25 us; 4096x16x4096: 7.7 against 16.2)
+constexpr int64_t kNarrowMinGroups = 64;
 struct TileGroup {
     int bm, bn;
     int ids[4];
@@ -365,6 +417,16 @@ bool entry_fits(const Entry &e, const Problem &p)
         return false;
     if (trivial || scale_only)
         return true;  // the tiled kernel also handles these; the factory never picks it for them
+    if (c.kind == MPGEMM_KIND_NARROW) {
+        // 16 stored rows of A, the stored rows of B (K of them row-major, N <= 16
+        // column-major) and 16 rows of C within 32-bit buffer offsets
+        const int64_t a_span = mul_sat(add_sat(mul_sat(16, p.lda), p.K), 2);
+        const int64_t b_span = p.lb == MPGEMM_ROW_MAJOR ? mul_sat(add_sat(mul_sat(p.K, p.ldb), 16), 2)
+                                                        : mul_sat(add_sat(mul_sat(16, p.ldb), p.K), 2);
+        const int64_t c_span = mul_sat(add_sat(mul_sat(16, p.ldc), 16), 4);
+        return p.N <= 16 && a_span < (int64_t)0x7FFFFFF0 && b_span < (int64_t)0x7FFFFFF0 &&
+               c_span < (int64_t)0x7FFFFFF0 && cdiv(p.M, 16) <= 0x7FFFFFFF;
+    }
     if (c.vec_a == 8 && vec_for(p.A, p.lda) != 8)
         return false;
     if (c.vec_b == 8 && vec_for(p.B, p.ldb) != 8)
@@ -397,6 +459,8 @@ int64_t grid_for(const mpgemm_config &c, const Problem &p)
         return mul_sat(cdiv(p.M, c.bm), cdiv(p.N, c.bn));
     case MPGEMM_KIND_DIRECT:
         return mul_sat(cdiv(p.M, 64), cdiv(p.N, 64));
+    case MPGEMM_KIND_NARROW:
+        return cdiv(p.M, 16);
     case MPGEMM_KIND_SCALE:
         return 0;
     default:
@@ -408,12 +472,19 @@ int64_t grid_for(const mpgemm_config &c, const Problem &p)
 // when the product is small.  Returns a table id, or -1 for "nothing to do".
 // `small_deep_k` = false keeps 64-deep K tiles for small products (split-K
 // counts its pieces in K tiles).
-int select(const Problem &p, bool small_deep_k = true)
+int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
 {
     if (p.M == 0 || p.N == 0)
         return -1;
     if (p.K == 0 || p.alpha == 0.0f)
         return kScaleId;
+    // At most 16 columns with A row-major: a stream over A, taken by the
+    // narrow kernel (16 rows per workgroup, K split over its waves).
+    if (allow_narrow && p.N <= 16 && p.la == MPGEMM_ROW_MAJOR) {
+        const int nid = kNarrowIds[p.in_type][p.lb];
+        if (entry_fits(kTable[nid], p))
+            return nid;
+    }
     const int va = vec_for(p.A, p.lda) == 8 ? 0 : 1;
     const int vb = vec_for(p.B, p.ldb) == 8 ? 0 : 2;
     const int v = va + vb;
@@ -510,6 +581,9 @@ int run(int id, const Problem &p, void *stream)
     if (e.cfg.kind == MPGEMM_KIND_DIRECT) {
         a.tiles_m = (int32_t)cdiv(p.M, 64);
         a.tiles_n = (int32_t)cdiv(p.N, 64);
+    } else if (e.cfg.kind == MPGEMM_KIND_NARROW) {
+        a.tiles_m = (int32_t)cdiv(p.M, 16);
+        a.tiles_n = 1;
     } else {
         a.tiles_m = (int32_t)cdiv(p.M, e.cfg.bm);
         a.tiles_n = (int32_t)cdiv(p.N, e.cfg.bn);
@@ -539,12 +613,21 @@ struct SplitPlan {
 // many ranges, at most one per K tile.  Empty ranges are never planned.
 SplitPlan plan_split(const Problem &p, int requested)
 {
+    // an unsplit plan keeps the factory's own choice
     SplitPlan sp{select(p), 1, 0, 0};
     if (sp.id < 0 || p.K == 0 || p.alpha == 0.0f)
         return sp;
-    // pieces are whole K tiles: a split takes the 64-deep form of the small
-    // tile; an unsplit plan keeps the factory's own choice
-    const int id = sp.id == kSmallDeepKId ? select(p, false) : sp.id;
+    // The narrow kernel splits K inside its workgroups: the automatic plan
+    // keeps it unless its grid has few 16-row workgroups, where split-K over
+    // the tile kernels is faster; a requested piece count splits a tile
+    // kernel.  Pieces are whole K tiles: a split takes the 64-deep form of
+    // the small tile.
+    const bool narrow = kTable[sp.id].cfg.kind == MPGEMM_KIND_NARROW;
+    if (narrow && requested == 0 && cdiv(p.M, 16) >= kNarrowMinGroups)
+        return sp;
+    int id = narrow ? select(p, true, false) : sp.id;
+    if (id == kSmallDeepKId)
+        id = select(p, false, false);
     const mpgemm_config &c = kTable[id].cfg;
     if (c.kind != MPGEMM_KIND_PIPE)
         return sp;

@@ -78,6 +78,10 @@ extern "C" {
 #define MPGEMM_KIND_PIPE 4     /* LDS ring filled by direct-to-LDS copies; operands
                                   stored along M or N read with the transposing
                                   LDS load; the fast path                         */
+#define MPGEMM_KIND_NARROW 5   /* N <= 16, A row-major: 16 rows of C per workgroup,
+                                  8 waves splitting K, operands straight from
+                                  memory into registers, partial tiles summed in
+                                  LDS                                             */
 
 /* One entry of the kernel-config table, as reported by the factory. */
 typedef struct mpgemm_config {
@@ -275,9 +279,10 @@ int mpgemm_gemm_ex_with_config(int config_id, int in_type, int layout_a, int lay
  * would use (`splits_requested` 0: automatic, split only when the grid
  * fills less than half the chip, into enough pieces for about two
  * workgroups per compute unit, at most 32, each at least 4 K tiles long;
- * n > 0: n pieces, at most one per K tile of the chosen kernel), the
- * workspace bytes that needs (splits*M*N*4; 0 when
- * splits == 1) and the tile kernel's table entry.  Output pointers may be
+ * a product the factory gives the narrow kernel stays whole when it has at
+ * least 64 groups of 16 rows; n > 0: n pieces of a tile kernel, at most one
+ * per K tile), the workspace bytes that needs (splits*M*N*4; 0 when
+ * splits == 1) and the kernel's table entry.  Output pointers may be
  * NULL.  Arguments as for mpgemm_gemm_ex; C, alpha and beta are not needed
  * to plan.
  *

@@ -320,11 +320,22 @@ def plan(M, N, K, splits=0, la=0, lb=0, in_type=0, lda=None, ldb=None):
 
 
 def test_splitk_plan_skinny_case_fills_the_chip():
-    p = plan(4096, 16, 4096)     # 64 tiles of 64x64 on 256 compute units
+    # 4096 x 16 x 4096: the narrow kernel (256 workgroups of 16 rows, K split
+    # over each one's 8 waves) fills the chip in one launch, so no pieces
+    p = plan(4096, 16, 4096)
+    assert mp.mpgemm_config_info(p["config_id"])["kind_name"] == "narrow"
+    assert (p["splits"], p["workspace_bytes"]) == (1, 0)
+    # 256 x 16 x 65536: 16 narrow workgroups would leave the chip idle, so
+    # the plan splits a tile kernel into enough pieces for ~2 workgroups per
+    # compute unit, at most 32
+    p = plan(256, 16, 65536)
     c = mp.mpgemm_config_info(p["config_id"])
-    tiles = (4096 // c["bm"]) * 1
-    assert p["splits"] * tiles >= 2 * 256 and p["splits"] <= 32
-    assert p["workspace_bytes"] == p["splits"] * 4096 * 16 * 4
+    tiles = -(-256 // c["bm"])
+    assert c["kind_name"] == "pipe" and p["splits"] == min(32, -(-2 * 256 // tiles))
+    assert p["workspace_bytes"] == p["splits"] * 256 * 16 * 4
+    # a requested piece count splits a tile kernel whatever the shape
+    p = plan(4096, 16, 4096, splits=4)
+    assert p["splits"] == 4 and mp.mpgemm_config_info(p["config_id"])["kind_name"] == "pipe"
 
 
 def test_splitk_plan_keeps_full_grids_whole():
@@ -350,7 +361,8 @@ def test_splitk_plan_forced_and_capped():
 
 
 def test_splitk_launch_checks_the_workspace_before_hip():
-    args = (0, 0, 0, 4096, 16, 4096, FAKE_A, 4096, FAKE_B, 16, FAKE_C, 16, 1.0, 0.0, 0, 0)
+    # a shape the plan splits (four 64-row tiles, deep K)
+    args = (0, 0, 0, 256, 16, 65536, FAKE_A, 65536, FAKE_B, 16, FAKE_C, 16, 1.0, 0.0, 0, 0)
     assert mp.mpgemm_gemm_splitk(*args, 0, 0, 0) == mp.MPGEMM_ENULL
     assert mp.mpgemm_gemm_splitk(*args, FAKE_C + 0x100000, 1024, 0) == mp.MPGEMM_EWORKSPACE
     assert mp.mpgemm_gemm_splitk(*args, FAKE_C + 0x100002, 1 << 30, 0) == mp.MPGEMM_EALIGN

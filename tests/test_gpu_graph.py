@@ -59,14 +59,14 @@ def test_graph_replay_split_k_and_bias():
     Ad, Bd = A.to(dev), B.to(dev)
     bias = torch.linspace(-1, 1, N, device=dev)
     C = torch.full((M, N), float("nan"), device=dev)
-    plan = mp.splitk_plan_for(Ad, Bd, C)
-    assert plan["splits"] > 1
+    plan = mp.splitk_plan_for(Ad, Bd, C, 8)
+    assert plan["splits"] == 8
     ws = torch.empty(plan["workspace_bytes"] // 4, device=dev)
-    mp.gemm_splitk(Ad, Bd, C, 1.0, 0.0, bias=bias, workspace=ws)
+    mp.gemm_splitk(Ad, Bd, C, 1.0, 0.0, bias=bias, workspace=ws, splits=8)
     torch.cuda.synchronize()
     eager = C.clone()
     ref, absdot = oracle.gemm(bits(A), bits(B), None, 1.0, 0.0, bias=bias.cpu().numpy())
     assert_close("graph split-K", eager.cpu().numpy(), ref, absdot)
     print(f"[graph] split-K {plan['splits']} pieces", flush=True)
-    _replays_match(lambda: mp.gemm_splitk(Ad, Bd, C, 1.0, 0.0, bias=bias, workspace=ws), C, eager)
+    _replays_match(lambda: mp.gemm_splitk(Ad, Bd, C, 1.0, 0.0, bias=bias, workspace=ws, splits=8), C, eager)
     assert np.isfinite(C.cpu().numpy()).all()

@@ -52,10 +52,23 @@ def check(label, A, B, C0, alpha, beta, la=0, lb=0, splits=0, bias=None, ldc=Non
 
 
 def test_skinny_case_from_the_pages():
-    """4096 x 16 x 4096, symmetric uniform: 64 tiles, split to fill the chip."""
+    """4096 x 16 x 4096, symmetric uniform: the plan keeps the narrow kernel
+    whole (256 row groups of 16 already fill the chip); forced pieces run the
+    tiled kernel split, and both match the oracle."""
     A, B, _ = make_inputs(4096, 16, 4096, "uniform", seed=81)
     print("[splitk] skinny", flush=True)
-    check("skinny", A, B, None, 1.0, 0.0)
+    _, plan = check("skinny", A, B, None, 1.0, 0.0, want_split=False)
+    assert plan["splits"] == 1 and mp.mpgemm_config_info(plan["config_id"])["kind_name"] == "narrow"
+    _, plan = check("skinny forced", A, B, None, 1.0, 0.0, splits=16)
+    assert plan["splits"] == 16 and mp.mpgemm_config_info(plan["config_id"])["kind_name"] == "pipe"
+
+
+def test_short_skinny_deep_k_splits_by_itself():
+    """256 x 16 x 65536: 16 row groups cannot fill the chip, so the plan
+    splits K across a tiled kernel."""
+    A, B, C = make_inputs(256, 16, 65536, "uniform", seed=83, c_init="uniform")
+    _, plan = check("short skinny", A, B, C, 0.5, 2.0)
+    assert mp.mpgemm_config_info(plan["config_id"])["kind_name"] == "pipe"
 
 
 @pytest.mark.parametrize("splits", [2, 3, 5, 7, 16])
@@ -111,9 +124,9 @@ def test_single_piece_is_the_ordinary_path():
 
 def test_workspace_errors_on_the_device_path():
     dev = device()
-    A = torch.zeros(4096, 4096, dtype=torch.float16, device=dev)
-    B = torch.zeros(4096, 16, dtype=torch.float16, device=dev)
-    C = torch.zeros(4096, 16, device=dev)
+    A = torch.zeros(256, 65536, dtype=torch.float16, device=dev)
+    B = torch.zeros(65536, 16, dtype=torch.float16, device=dev)
+    C = torch.zeros(256, 16, device=dev)
     small = torch.empty(16, device=dev)
     with pytest.raises(mp.MpgemmError) as e:
         mp.gemm_splitk(A, B, C, workspace=small)

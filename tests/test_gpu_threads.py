@@ -1,8 +1,8 @@
 """Concurrent calls: the library keeps no per-call state, so host threads may
 call it at once, each on its own stream (mpgemm.h, "Ownership and
-concurrency").  Four threads, each with its own stream, buffers and shapes
+concurrency").  Five threads, each with its own stream, buffers and shapes
 (different kernel configs, ragged edges, beta != 0, column-major B, BF16,
-split-K), call the library repeatedly at the same time; every result must
+split-K, the narrow kernel), call the library repeatedly at the same time; every result must
 equal the same call made alone, bit for bit (each call is deterministic)."""
 import threading
 
@@ -20,7 +20,8 @@ CASES = [
     dict(M=1000, N=800, K=617, dtype=torch.float16, col_b=False, splitk=False, beta=0.5),
     dict(M=2048, N=1024, K=512, dtype=torch.float16, col_b=True, splitk=False, beta=0.0),
     dict(M=513, N=257, K=1031, dtype=torch.bfloat16, col_b=False, splitk=False, beta=-1.0),
-    dict(M=4096, N=16, K=4096, dtype=torch.float16, col_b=False, splitk=True, beta=0.0),
+    dict(M=256, N=16, K=65536, dtype=torch.float16, col_b=False, splitk=True, beta=0.0),
+    dict(M=4096, N=16, K=4096, dtype=torch.float16, col_b=False, splitk=False, beta=0.5),   # narrow
 ]
 
 

@@ -55,12 +55,12 @@ def test_m0_is_only_written_by_the_copy_sequence(device_asm):
 
 
 def test_no_private_scratch_in_pipelined_kernels(device_asm):
-    """The pipelined kernels (every large-product choice of the factory) keep
-    all their state in registers and LDS."""
+    """The pipelined and narrow kernels (every choice of the factory but the
+    fallback) keep all their state in registers and LDS."""
     text = "\n".join(device_asm)
     kernels = [(n, b) for n, b in re.findall(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.S)
-               if "gemm_pipe" in n]
-    assert len(kernels) >= 20
+               if "gemm_pipe" in n or "gemm_narrow" in n]
+    assert len(kernels) >= 20 and any("gemm_narrow" in n for n, _ in kernels)
     for name, body in kernels:
         size = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body).group(1))
         assert size == 0, f"{name} spills to scratch ({size} bytes)"
