@@ -471,7 +471,8 @@ def main():
                             "pct_of_peak": round(100 * w.flop / (r["kernel_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
                             "roofline": dict(roofline_entry(w, r["kernel_ms"]),
                                              traffic=measured_traffic(name, r["kernel_ms"])),
-                            "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "vec_a", "vec_b", "grid")}}
+                            "kernel": {k: r["cfg"][k] for k in ("id", "kind_name", "bm", "bn", "vec_a", "vec_b",
+                                                                "grid")}}
             del r
             torch.cuda.empty_cache()
         # the column-major operand modes, BF16 inputs and the bias epilogue
@@ -497,14 +498,13 @@ def main():
                                 "kernel": {k: r["cfg"][k] for k in ("id", "bm", "bn", "bk", "vec_a", "vec_b", "grid")}}
                 del r
                 torch.cuda.empty_cache()
-        # the pages' skinny case: the library's choice (the narrow kernel, one
-        # workgroup per 16 rows) beside the tiled kernel split 8 ways over K
-        from dense_mixed_precision_amd.workloads import Workload
-        skinny = Workload("skinny4096x16x4096", 4096, 16, 4096, "uniform", 1.0, 0.0, None, 1005)
-        for tag, sk in (("", 0), ("_splitk8", 8)):
+        # the pages' skinny case on the tiled kernel split 8 ways over K, beside
+        # the library's choice above (the narrow kernel)
+        skinny = WORKLOADS["skinny4096x16x4096"]
+        for tag, sk in (("_splitk8", 8),):
             name = skinny.name + tag
             print(f"# timing {name} ({args.steps} steps)", file=sys.stderr, flush=True)
-            r = time_workload(skinny, args.steps, warmup_for(skinny, args.warmup), torch, mp, splitk=sk > 0,
+            r = time_workload(skinny, args.steps, warmup_for(skinny, args.warmup), torch, mp, splitk=True,
                               graph_reps=20, splits=sk)
             others[name] = {"tflops": round(skinny.flop / (r["kernel_ms"] * 1e-3) / 1e12, 2),
                             "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),

@@ -51,7 +51,7 @@ class Workload:
         return 2 * self.M * self.K + 2 * self.K * self.N + c + (c if self.beta != 0 else 0)
 
 
-#: The five workloads this library is measured and checked on.
+#: The six workloads this library is measured and checked on.
 WORKLOADS = {
     w.name: w
     for w in (
@@ -65,6 +65,8 @@ WORKLOADS = {
                  "compute-bound roofline shape"),
         Workload("tallskinny32768x128x4096", 32768, 128, 4096, "uniform", 1.0, 0.0, None, 1004,
                  "low reuse in N; HBM bound"),
+        Workload("skinny4096x16x4096", 4096, 16, 4096, "uniform", 1.0, 0.0, None, 1005,
+                 "the pages' skinny gate shape; N <= 16, an HBM stream of A"),
     )
 }
 

@@ -67,10 +67,10 @@ def test_mfma_rate_probe_does_the_work_it_counts(shape, fmt):
 
 
 # ----------------------------------------------------------------------------
-# The five workloads
+# The six workloads
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["square256", "ragged1000x800x617"])
+@pytest.mark.parametrize("name", ["square256", "ragged1000x800x617", "skinny4096x16x4096"])
 def test_workload_every_element(name):
     w = WORKLOADS[name]
     A, B, C = workload_inputs(w)
