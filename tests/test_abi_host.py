@@ -387,3 +387,24 @@ def test_mfma_rate_probe_rejects_bad_arguments_before_launch():
     assert call(iters=(1 << 24) + 1) == mp.MPGEMM_EDIM
     assert call(workgroups=0) == mp.MPGEMM_EDIM
     assert call(workgroups=65536) == mp.MPGEMM_EDIM
+
+
+def test_factory_gives_narrow_products_the_narrow_kernel():
+    """N <= 16 with A row-major takes the narrow kernel of the call's input
+    format and B storage order, one workgroup per 16 rows; N = 17, a
+    column-major A, or 16 rows of A past 32-bit offsets take another kind."""
+    for N in (1, 2, 8, 15, 16):
+        for lb in (0, 1):
+            if lb and N == 1:
+                continue
+            c = ql(0, lb, 1000, N, 617)
+            assert c["kind_name"] == "narrow" and c["layout_b"] == lb and c["grid"] == -(-1000 // 16), (N, lb, c)
+            assert c["in_type"] == mp.MPGEMM_IN_F16
+            c = mp.mpgemm_bf16f32_layout_query(0, lb, 1000, N, 617, FAKE_A, 617, FAKE_B, 617 if lb else N,
+                                               FAKE_C, N, 1.0, 0.0)
+            assert c["kind_name"] == "narrow" and c["in_type"] == mp.MPGEMM_IN_BF16 and c["layout_b"] == lb
+    assert ql(0, 0, 1000, 17, 617)["kind_name"] == "pipe"
+    assert ql(1, 0, 1000, 16, 617)["kind_name"] != "narrow"
+    assert ql(0, 0, 1000, 16, 617, lda=1 << 27)["kind_name"] == "direct"
+    assert ql(0, 0, 0, 16, 617)["kind_name"] == "none"
+    assert ql(0, 0, 1000, 16, 0)["kind_name"] == "scale"
