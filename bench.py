@@ -11,11 +11,19 @@ in the same JSON line.
 
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize() on both sides (wall clock -> ms_per_step), with HIP
-events recorded on the launch stream around the same region (-> the average
-kernel duration used for the roofline).  FLOP = 2*M*N*K.  Each workload also
-reports "graph_us": the per-launch time of the same call captured in a HIP
-graph and replayed, i.e. the kernels' own time without the Python call
-between launches (which bounds the eager rate of the smallest products).
+events recorded on the launch stream before the first step and after each
+(-> the average kernel duration used for the roofline, and the median and
+coefficient of variation per step under "timing"); then, outside the timed
+region, the pages' 5 runs x 20 launches (median of the runs, CV across
+them).  FLOP = 2*M*N*K.  Each workload also reports "graph_us": the
+per-launch time of the same call captured in a HIP graph and replayed, i.e.
+the kernels' own time without the Python call between launches (which bounds
+the eager rate of the smallest products).
+
+For the 2048^3 headline the bench also measures the L2 fill and hit rates
+per XCD with the diagnostics library's fill probe, and derives from them an
+attainable time for that product on its tiling ("attainable"), reported
+next to the spec-peak fraction.
 
 The CPU baseline is the oracle (oracle/, plain C, FP64) timed on a bounded
 sample of the headline workload: a block of whole rows of C, sized to about
@@ -52,6 +60,11 @@ def parse():
     p.add_argument("--workload", default="square2048")
     p.add_argument("--config", type=int, default=None,
                    help="force this config-table entry for the headline workload (tile candidates)")
+    p.add_argument("--candidates", action="store_true",
+                   help="load the candidates build of the library (the product entries plus the "
+                        "sweep-only tile shapes; python -m dense_mixed_precision_amd.build --candidates)")
+    p.add_argument("--no-fill", dest="fill", action="store_false",
+                   help="skip the L2 fill-rate probe and the attainable bound derived from it")
     p.add_argument("--no-others", action="store_true", help="time only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -76,10 +89,12 @@ def kernel_source_digest() -> str:
 
 
 def measured_traffic(workload: str, kernel_ms: float):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary for this
-    workload (FETCH_SIZE and WRITE_SIZE, each scaled by the reading of a plain
-    copy of known size), or None if there is none or the kernels changed since."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    """Bytes per launch that leave the L2 caches for memory, from the committed
+    rocprofv3 --pmc summary for this workload (FETCH_SIZE and WRITE_SIZE, each
+    scaled by what it reads for a plain copy of known size), or None if there
+    is none or the kernels changed since.  They count L2 misses, part of which
+    the memory-side cache serves: an upper bound on DRAM bytes."""
+    path = os.path.join(ROOT, "profiles", f"l2_miss_bytes_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -90,12 +105,14 @@ def measured_traffic(workload: str, kernel_ms: float):
     if vals.get("kernel_source_digest") != kernel_source_digest():
         return None
     try:
-        read_b = float(vals["hbm_read_bytes_per_launch"])
-        write_b = float(vals["hbm_write_bytes_per_launch"])
+        read_b = float(vals["l2_miss_read_bytes_per_launch"])
+        write_b = float(vals["l2_miss_write_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
     return {"bytes_per_launch": read_b + write_b, "read_bytes": read_b, "write_bytes": write_b,
-            "GBps": round((read_b + write_b) / (kernel_ms * 1e-3) / 1e9, 1), "source": os.path.relpath(path, ROOT)}
+            "GBps": round((read_b + write_b) / (kernel_ms * 1e-3) / 1e9, 1),
+            "counts": "L2-to-memory requests (FETCH_SIZE, WRITE_SIZE), an upper bound on DRAM bytes",
+            "source": os.path.relpath(path, ROOT)}
 
 
 def graph_time_us(fn, reps, torch):
@@ -123,9 +140,21 @@ def graph_time_us(fn, reps, torch):
     return best
 
 
+def spread(ms):
+    """Median, mean and coefficient of variation (stdev / mean) of per-launch
+    times in ms, reported in microseconds."""
+    import statistics
+
+    mean = statistics.fmean(ms)
+    cv = statistics.pstdev(ms) / mean if len(ms) > 1 and mean > 0 else 0.0
+    return {"median_us": round(statistics.median(ms) * 1e3, 3), "mean_us": round(mean * 1e3, 3),
+            "cv": round(cv, 4), "n": len(ms)}
+
+
 def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=None, bias=False,
-                  splitk=False, graph_reps=0, config=None, splits=0):
-    """Time `steps` launches (after `warmup`) on resident inputs.  A column-
+                  splitk=False, graph_reps=0, config=None, splits=0, runs=0, iters=20):
+    """Time `steps` launches (after `warmup`) on resident inputs, then
+    (`runs` > 0) `runs` more runs of `iters` launches each.  A column-
     major operand is stored transposed on the device and passed as the
     transposed view; `dtype` picks FP16 (default) or BF16 inputs; `bias`
     adds a per-column bias vector to the epilogue; `splitk` goes through the
@@ -183,19 +212,36 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
 
     for _ in range(warmup):
         step()
+    # one HIP event before the timed steps and one after each, all on the
+    # launch stream: per-step kernel times for the median and spread
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(steps):
+    events[0].record(stream)
+    for i in range(steps):
         step()
-    ev1.record(stream)
+        events[i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / steps
-    kern_ms = ev0.elapsed_time(ev1) / steps
-    out = {"A": A, "B": B, "C": C, "Cd": Cd, "cfg": cfg, "wall_ms": wall_ms, "kernel_ms": kern_ms}
+    kern_ms = events[0].elapsed_time(events[-1]) / steps
+    per_step = [events[i].elapsed_time(events[i + 1]) for i in range(steps)]
+    out = {"A": A, "B": B, "C": C, "Cd": Cd, "cfg": cfg, "wall_ms": wall_ms, "kernel_ms": kern_ms,
+           "step_stats": spread(per_step)}
+    if runs > 0:
+        # the pages' method: `runs` runs of `iters` back-to-back launches,
+        # each run's mean per launch; the median over runs and their spread
+        run_ms = []
+        for _ in range(runs):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(iters):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            run_ms.append(e0.elapsed_time(e1) / iters)
+        out["run_stats"] = dict(spread(run_ms), runs=runs, iters=iters)
     if graph_reps > 0:
         # the same call on the current (capture) stream
         def step_current():
@@ -349,6 +395,82 @@ def mfma_ceiling(torch, mp, seconds=1.5):
     return res
 
 
+def fill_rate(torch, mp):
+    """L2 fill and hit rates per XCD from the diagnostics library's fill probe
+    (256 workgroups of 8 waves, workgroup b on XCD b % 8; each XCD sweeps its
+    own region of the buffer, every byte once per pass).  A 6 MiB region per
+    XCD -- the footprint of a 2048^3 launch on one XCD, more than its 4 MiB
+    L2 -- misses on every pass, so it measures the fill from the memory-side
+    cache, which holds the whole 48 MiB buffer; a 2 MiB region stays in L2
+    and measures hits.  Cases: the GEMM's copy form (16 bytes per lane into
+    LDS) and 16- and 4-byte loads into registers at 1..16 requests in
+    flight per wave; the copy form with every XCD reading the same region,
+    and with each byte requested by 8 compute units of the XCD at once, as
+    the 2048^3 kernel's workgroups sharing a panel do.  Best of 3 timed
+    launches after one untimed; GB/s per XCD of unique bytes."""
+    dev = torch.device("cuda:0")
+    MiB = 1 << 20
+    buf = torch.ones(48 * MiB // 4, dtype=torch.float32, device=dev)
+    wgs = 256
+    sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    names = {mp.MPGEMM_FILL_LDS16: "lds16", mp.MPGEMM_FILL_REG16: "reg16", mp.MPGEMM_FILL_REG4: "reg4"}
+
+    def measure(mode, depth, footprint, shared=0, replicas=1):
+        passes = max(4, int(64 * 6 * MiB // footprint))
+        args = (mode, depth, buf.data_ptr(), buf.numel() * 4, footprint, shared, replicas, passes, wgs,
+                sink.data_ptr(), sink.numel(), stream.cuda_stream)
+        rc = mp.mpgemm_probe_fill(*args)
+        if rc != mp.MPGEMM_OK:
+            raise mp.MpgemmError(rc, "mpgemm_probe_fill")
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            mp.mpgemm_probe_fill(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        return round(footprint * passes / best / 1e9, 1)
+
+    out = {"per_xcd_GBps": {}, "unit": "GB/s per XCD (unique bytes)"}
+    for mode in (mp.MPGEMM_FILL_LDS16, mp.MPGEMM_FILL_REG16, mp.MPGEMM_FILL_REG4):
+        for depth in (1, 2, 4, 8, 16):
+            out["per_xcd_GBps"][f"fill_6MiB_{names[mode]}_d{depth}"] = measure(mode, depth, 6 * MiB)
+    out["per_xcd_GBps"]["fill_6MiB_lds16_d8_shared"] = measure(mp.MPGEMM_FILL_LDS16, 8, 6 * MiB, shared=1)
+    out["per_xcd_GBps"]["fill_6MiB_lds16_d8_x8cu"] = measure(mp.MPGEMM_FILL_LDS16, 8, 6 * MiB, replicas=8)
+    for depth in (4, 8, 16):
+        out["per_xcd_GBps"][f"hit_2MiB_lds16_d{depth}"] = measure(mp.MPGEMM_FILL_LDS16, depth, 2 * MiB)
+    vals = out["per_xcd_GBps"]
+    out["best_fill_GBps"] = max(v for k, v in vals.items() if k.startswith("fill_6MiB_") and "_x8cu" not in k)
+    out["best_hit_GBps"] = max(v for k, v in vals.items() if k.startswith("hit_"))
+    out["source"] = "mpgemm_probe_fill (libmpgemm_probes.so), 256 workgroups x 8 waves, best of 3"
+    del buf, sink
+    return out
+
+
+def attainable_2048(w, fill, k128_us):
+    """An attainable time for the 2048^3 product on 128x128 tiles from measured
+    rates: the one-K-tile product (launch, first tile, C write) plus, for each
+    of the other 15 K tiles, the longer of (a) filling the tile's A and B
+    lines into each XCD's L2 (the 32 concurrent tiles of one XCD, an 8x4
+    block, need 1024 rows of A and 512 columns of B: 384 KiB per K tile of
+    128) at the best measured fill rate and (b) serving the 32 tiles' 64 KiB
+    each from L2 at the best measured hit rate.  Bounds the kernel, not the
+    matrix cores: a fraction of the MFMA peak no kernel on this tiling can
+    exceed on this board, reported next to the spec-peak fraction."""
+    KiB = 1024
+    fill_us = 384 * KiB / (fill["best_fill_GBps"] * 1e9) * 1e6
+    hit_us = 32 * 64 * KiB / (fill["best_hit_GBps"] * 1e9) * 1e6
+    per_tile = max(fill_us, hit_us)
+    bound_us = k128_us + 15 * per_tile
+    tflops = w.flop / (bound_us * 1e-6) / 1e12
+    return {"k128_us": round(k128_us, 3), "fill_us_per_k_tile": round(fill_us, 3),
+            "hit_us_per_k_tile": round(hit_us, 3), "bound_us": round(bound_us, 3),
+            "tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_F16_TFLOPS, 4)}
+
+
 def roofline_entry(w, kernel_ms):
     """MFMA bound for the compute-heavy shapes, HBM bound where the
     arithmetic intensity (FLOP per algorithmic byte) is below the ridge."""
@@ -361,6 +483,15 @@ def roofline_entry(w, kernel_ms):
     achieved = w.algorithmic_bytes / (kernel_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+
+
+def with_traffic(roof, traffic):
+    """`roof` with its traffic entry: the measured L2-miss bytes per launch
+    (or None) and their detail."""
+    roof = dict(roof)
+    roof["traffic"] = traffic["bytes_per_launch"] if traffic else None
+    roof["traffic_detail"] = traffic
+    return roof
 
 
 def cpu_baseline(w, res, seconds):
@@ -404,12 +535,29 @@ def cpu_baseline(w, res, seconds):
            "sample": f"rows 0..{rows - 1} of {w.M} ({rows} rows x {w.N} cols x K={w.K}) "
                      f"of {w.name}; {dt:.1f} s of oracle time",
            "seconds": round(dt, 2)}
+    out["cpu_model"] = cpu_model()
     if got is not None:
         ok = oracle.tolerance_ok(got[r0:r0 + rows], ref, absdot)
         err = np.abs(got[r0:r0 + rows] - ref) / (oracle.TOL_REL * absdot + oracle.TOL_ABS)
         out["gpu_rows_match"] = bool(ok.all())
         out["gpu_rows_worst_err_over_tol"] = float(err.max())
+        # the error against the worst case of an FP32 running sum (at most 1
+        # for FP32 accumulation; an FP16 running sum exceeds it)
+        out["gpu_rows_accumulation_ratio"] = oracle.accumulation_ratio(got[r0:r0 + rows], ref, absdot, w.K,
+                                                                       w.alpha)
     return out
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first "model name" of /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def main():
@@ -426,10 +574,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    mp.load()
+    mp.load(mp.CANDIDATES_PATH if args.candidates else None)
+    if args.config is not None and not 0 <= args.config < mp.mpgemm_num_configs():
+        print(f"config {args.config} is not in {mp.lib_path()} ({mp.mpgemm_num_configs()} entries; the "
+              "sweep-only shapes need --candidates)", file=sys.stderr)
+        sys.exit(2)
     head = WORKLOADS[args.workload]
     print(f"# timing {head.name} ({args.warmup} warm-up + {args.steps} steps)", file=sys.stderr, flush=True)
-    res = time_workload(head, args.steps, args.warmup, torch, mp, graph_reps=20, config=args.config)
+    res = time_workload(head, args.steps, args.warmup, torch, mp, graph_reps=20, config=args.config, runs=5,
+                        iters=20)
     value = head.flop / (res["wall_ms"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
@@ -454,8 +607,25 @@ def main():
         "roofline": roofline_entry(head, res["kernel_ms"]),
     }
     line["roofline"]["kernel_ms"] = round(res["kernel_ms"], 5)
+    traffic = measured_traffic(head.name, res["kernel_ms"])
+    line["roofline"]["traffic"] = traffic["bytes_per_launch"] if traffic else None
+    line["roofline"]["traffic_detail"] = traffic
+    line["timing"] = {"steps": res["step_stats"], "runs_5x20": res["run_stats"],
+                      "note": "per-launch kernel time from HIP events on the launch stream: over the timed "
+                              "steps (one event after each step), and over 5 further runs of 20 launches "
+                              "(median of the runs' means, CV across runs)"}
     line["graph_us"] = round(res["graph_us"], 3)
-    line["roofline"]["traffic"] = measured_traffic(head.name, res["kernel_ms"])
+    if args.fill and head.name == "square2048" and args.config is None:
+        print("# L2 fill-rate probe and the 2048^3 attainable bound", file=sys.stderr, flush=True)
+        fill = fill_rate(torch, mp)
+        from dense_mixed_precision_amd.workloads import Workload
+        k128 = Workload("square2048_k128", 2048, 2048, 128, "uniform", 1.0, 0.0, None, 1001)
+        r = time_workload(k128, 200, 200, torch, mp)
+        line["fill_rate"] = fill
+        line["attainable"] = attainable_2048(head, fill, r["kernel_ms"] * 1e3)
+        line["attainable"]["kernel_frac_of_attainable"] = round(
+            line["roofline"]["achieved"] / line["attainable"]["tflops"], 4)
+        del r
     others = {}
     if not args.no_others:
         for name, w in WORKLOADS.items():
@@ -469,8 +639,9 @@ def main():
                             "kernel_ms": round(r["kernel_ms"], 5), "wall_ms": round(r["wall_ms"], 5),
                             "graph_us": round(r["graph_us"], 3),
                             "pct_of_peak": round(100 * w.flop / (r["kernel_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
-                            "roofline": dict(roofline_entry(w, r["kernel_ms"]),
-                                             traffic=measured_traffic(name, r["kernel_ms"])),
+                            "roofline": with_traffic(roofline_entry(w, r["kernel_ms"]),
+                                                     measured_traffic(name, r["kernel_ms"])),
+                            "timing": r["step_stats"],
                             "kernel": {k: r["cfg"][k] for k in ("id", "kind_name", "bm", "bn", "vec_a", "vec_b",
                                                                 "grid")}}
             del r

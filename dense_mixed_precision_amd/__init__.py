@@ -1,7 +1,8 @@
 """dense_mixed_precision_amd -- FP16-input, FP32-accumulate GEMM for gfx950.
 
 Thin Python binding over the C ABI in ``include/mpgemm.h`` (library
-``libmpgemm.so``, built in-tree by ``build.build()``).  Every step of the
+``libmpgemm.so``, built in-tree by ``build.build()``) and over the
+diagnostics of ``include/mpgemm_probes.h`` (``libmpgemm_probes.so``).  Every step of the
 product runs in the HIP kernels; Python only marshals arguments.  There is no
 CPU or library fallback: if the shared library is missing, every call raises.
 
@@ -19,9 +20,12 @@ integers holding device addresses, ``stream`` a hipStream_t as an integer,
     mpgemm_gemm_ex(in_type, layout_a, layout_b, M, N, K, ..., alpha, beta, bias, stream) -> int
     mpgemm_gemm_ex_with_config(cfg, in_type, layout_a, layout_b, ...) -> int   (per-column bias)
     mpgemm_splitk_plan(...) -> dict, mpgemm_gemm_splitk(..., splits, workspace, bytes, stream) -> int
-    mpgemm_num_configs(), mpgemm_config_info(id), mpgemm_probe_mfma_layout(shape, out, stream)
+    mpgemm_num_configs(), mpgemm_config_info(id), mpgemm_strerror(code), mpgemm_version()
+Diagnostics (libmpgemm_probes.so):
+    mpgemm_probe_mfma_layout(shape, out, stream)
     mpgemm_probe_mfma_rate(in_type, shape, ops, ops_len, iters, workgroups, out, out_len, stream)
-    mpgemm_strerror(code), mpgemm_version()
+    mpgemm_probe_fill(mode, depth, buf, buf_bytes, footprint, shared, replicas, passes, workgroups,
+                      sink, sink_len, stream)
 
 Tensor convenience: ``gemm(A, B, C, alpha, beta)`` for torch tensors on the
 GPU (A, B both float16 or both bfloat16, each row- or column-major, e.g. a
@@ -45,11 +49,16 @@ from ._binding import (  # noqa: F401
     MPGEMM_IN_BF16,
     MPGEMM_IN_F16,
     MPGEMM_ROW_MAJOR,
+    MPGEMM_FILL_LDS16,
+    MPGEMM_FILL_REG16,
+    MPGEMM_FILL_REG4,
+    CANDIDATES_PATH,
     MpgemmError,
     config_fields,
     gemm,
     lib_path,
     load,
+    load_probes,
     mpgemm_config_info,
     mpgemm_f16f32,
     mpgemm_f16f32_query,
@@ -70,6 +79,7 @@ from ._binding import (  # noqa: F401
     mpgemm_num_configs,
     mpgemm_probe_mfma_layout,
     mpgemm_probe_mfma_rate,
+    mpgemm_probe_fill,
     mpgemm_strerror,
     mpgemm_version,
     query_for,

@@ -1,4 +1,5 @@
-"""ctypes binding for libmpgemm.so (argument marshalling only)."""
+"""ctypes binding for libmpgemm.so and libmpgemm_probes.so (argument
+marshalling only: every step of the product runs in the HIP library)."""
 from __future__ import annotations
 
 import ctypes
@@ -6,6 +7,9 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmpgemm.so")
+_PROBES_PATH = os.path.join(_HERE, "libmpgemm_probes.so")
+#: the product library plus the sweep-only tile shapes (built on request)
+CANDIDATES_PATH = os.path.join(_HERE, "libmpgemm_candidates.so")
 
 MPGEMM_OK = 0
 MPGEMM_EDIM = -1
@@ -35,7 +39,11 @@ class MpgemmConfig(ctypes.Structure):
 
 
 config_fields = [f[0] for f in MpgemmConfig._fields_]
-KIND_NAMES = {0: "tiled", 1: "direct", 2: "scale", 3: "none", 4: "pipe", 5: "narrow"}
+KIND_NAMES = {1: "direct", 2: "scale", 3: "none", 4: "pipe", 5: "narrow"}
+
+MPGEMM_FILL_LDS16 = 0
+MPGEMM_FILL_REG16 = 1
+MPGEMM_FILL_REG4 = 2
 
 
 class MpgemmError(RuntimeError):
@@ -45,22 +53,29 @@ class MpgemmError(RuntimeError):
 
 
 _lib = None
+_lib_path = None
+_probes = None
 
 
 def lib_path() -> str:
-    return _LIB_PATH
+    return _lib_path or _LIB_PATH
 
 
-def load():
-    """Load the in-tree libmpgemm.so.  Raises if it has not been built."""
-    global _lib
+def load(path: str | None = None):
+    """Load the in-tree libmpgemm.so (or, once, before anything else is
+    loaded, the library at `path`: the candidates build for tile sweeps).
+    Raises if it has not been built; there is no fallback path."""
+    global _lib, _lib_path
     if _lib is not None:
+        if path is not None and os.path.abspath(path) != _lib_path:
+            raise RuntimeError(f"{_lib_path} is already loaded; cannot switch to {path}")
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    path = os.path.abspath(path or _LIB_PATH)
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
-            "or `python -m dense_mixed_precision_amd.build` (no fallback path exists)")
-    lib = ctypes.CDLL(_LIB_PATH)
+            f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python -m dense_mixed_precision_amd.build [--candidates]` (no fallback path exists)")
+    lib = ctypes.CDLL(path)
     i64, f32, vp, i32 = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
     gemm_args = [i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, f32]
     lib.mpgemm_f16f32.argtypes = gemm_args + [vp]
@@ -99,15 +114,31 @@ def load():
     lib.mpgemm_num_configs.restype = i32
     lib.mpgemm_config_info.argtypes = [i32, ctypes.POINTER(MpgemmConfig)]
     lib.mpgemm_config_info.restype = i32
-    lib.mpgemm_probe_mfma_layout.argtypes = [i32, vp, vp]
-    lib.mpgemm_probe_mfma_layout.restype = i32
-    lib.mpgemm_probe_mfma_rate.argtypes = [i32, i32, vp, i64, i64, i32, vp, i64, vp]
-    lib.mpgemm_probe_mfma_rate.restype = i32
     lib.mpgemm_strerror.argtypes = [i32]
     lib.mpgemm_strerror.restype = ctypes.c_char_p
     lib.mpgemm_version.argtypes = []
     lib.mpgemm_version.restype = ctypes.c_char_p
     _lib = lib
+    _lib_path = path
+    return lib
+
+
+def load_probes():
+    """Load the in-tree diagnostics library libmpgemm_probes.so."""
+    global _probes
+    if _probes is not None:
+        return _probes
+    if not os.path.exists(_PROBES_PATH):
+        raise RuntimeError(f"{_PROBES_PATH} is not built; run `python -m dense_mixed_precision_amd.build`")
+    lib = ctypes.CDLL(_PROBES_PATH)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.mpgemm_probe_mfma_layout.argtypes = [i32, vp, vp]
+    lib.mpgemm_probe_mfma_layout.restype = i32
+    lib.mpgemm_probe_mfma_rate.argtypes = [i32, i32, vp, i64, i64, i32, vp, i64, vp]
+    lib.mpgemm_probe_mfma_rate.restype = i32
+    lib.mpgemm_probe_fill.argtypes = [i32, i32, vp, i64, i64, i32, i32, i64, i32, vp, i64, vp]
+    lib.mpgemm_probe_fill.restype = i32
+    _probes = lib
     return lib
 
 
@@ -230,13 +261,19 @@ def mpgemm_config_info(config_id: int) -> dict:
 
 
 def mpgemm_probe_mfma_layout(shape: int, out: int, stream=0) -> int:
-    return int(load().mpgemm_probe_mfma_layout(shape, out, stream))
+    return int(load_probes().mpgemm_probe_mfma_layout(shape, out, stream))
 
 
 def mpgemm_probe_mfma_rate(in_type: int, shape: int, ops: int, ops_len: int, iters: int, workgroups: int,
                            out: int, out_len: int, stream=0) -> int:
-    return int(load().mpgemm_probe_mfma_rate(in_type, shape, ops, ops_len, iters, workgroups, out, out_len,
-                                             stream))
+    return int(load_probes().mpgemm_probe_mfma_rate(in_type, shape, ops, ops_len, iters, workgroups, out,
+                                                    out_len, stream))
+
+
+def mpgemm_probe_fill(mode: int, depth: int, buf: int, buf_bytes: int, footprint: int, shared: int,
+                      replicas: int, passes: int, workgroups: int, sink: int, sink_len: int, stream=0) -> int:
+    return int(load_probes().mpgemm_probe_fill(mode, depth, buf, buf_bytes, footprint, shared, replicas,
+                                               passes, workgroups, sink, sink_len, stream))
 
 
 def mpgemm_strerror(code: int) -> str:
@@ -266,9 +303,18 @@ def _check_tensor(t, name, dtype, allow_col_major=False):
         raise ValueError(f"{name} must be on the GPU")
     rows, cols = t.shape
     if cols <= 1 or t.stride(1) == 1:
-        return MPGEMM_ROW_MAJOR, (max(t.stride(0), max(cols, 1)) if rows > 1 else max(cols, 1))
+        if rows <= 1:
+            return MPGEMM_ROW_MAJOR, max(cols, 1)
+        # rows that share memory (a broadcast or overlapping view) would be
+        # read wrongly or, for C, written out of bounds: refuse them
+        if t.stride(0) < max(cols, 1):
+            raise ValueError(f"{name}: its rows overlap (row stride {t.stride(0)} < {cols} columns)")
+        return MPGEMM_ROW_MAJOR, t.stride(0)
     if allow_col_major and (rows <= 1 or t.stride(0) == 1):
-        return MPGEMM_COL_MAJOR, max(t.stride(1), max(rows, 1))
+        # here cols > 1: the columns are the stored rows
+        if t.stride(1) < max(rows, 1):
+            raise ValueError(f"{name}: its columns overlap (column stride {t.stride(1)} < {rows} rows)")
+        return MPGEMM_COL_MAJOR, t.stride(1)
     raise ValueError(f"{name} must have unit stride along one dimension"
                      + ("" if allow_col_major else " (row-major)"))
 
@@ -368,11 +414,18 @@ def splitk_plan_for(A, B, C, splits: int = 0) -> dict:
 def gemm_splitk(A, B, C, alpha: float = 1.0, beta: float = 0.0, bias=None, splits: int = 0,
                 workspace=None, stream=None):
     """Split-K form of :func:`gemm`.  ``splits`` 0 lets the library decide.
-    ``workspace``: a float32 GPU tensor of at least the planned size; when
-    None, one is allocated here (by torch, on the caller's side of the C
-    ABI) for this call."""
+    ``workspace``: a contiguous float32 tensor on C's GPU of at least the
+    planned size; when None, one is allocated here (by torch, on the
+    caller's side of the C ABI) for this call."""
     import torch
     M, N, K, la, lda, lb, ldb, ldc = _args(A, B, C)
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.float32 or not workspace.is_cuda:
+            raise TypeError("workspace must be a float32 tensor on the GPU")
+        if workspace.device != C.device:
+            raise ValueError(f"workspace is on {workspace.device}, C on {C.device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous (the kernels write it as one flat array)")
     plan = mpgemm_splitk_plan(_in_type(A), la, lb, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
                               int(splits))
     if workspace is None and plan["workspace_bytes"] > 0:

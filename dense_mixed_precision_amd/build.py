@@ -1,21 +1,38 @@
-"""Build step for the gfx950 GEMM library (``libmpgemm.so``, in-tree).
+"""Build step for the gfx950 GEMM libraries (in-tree).
 
-``build()`` always recompiles ``csrc/mpgemm.hip`` with hipcc for gfx950.
+``build()`` always recompiles, with hipcc for gfx950:
+
+* ``libmpgemm.so`` -- the product library (``csrc/mpgemm.hip``, C ABI in
+  ``include/mpgemm.h``): the config entries the factory chooses from and the
+  fallbacks;
+* ``libmpgemm_probes.so`` -- the diagnostics (``csrc/probes.hip``, C ABI in
+  ``include/mpgemm_probes.h``);
+* with ``candidates=True`` also ``libmpgemm_candidates.so``: the product
+  library plus the alternative tile shapes of tile sweeps
+  (``-DMPGEMM_CANDIDATES``), which the factory never picks.
+
 Packed FP32 VALU instructions are disabled on the device side
-(``-target-feature -packed-fp32-ops``); hipcc's host pass warns that it
-does not know the feature, which is harmless.
+(``-target-feature -packed-fp32-ops``); hipcc's host pass warns that it does
+not know the feature, which is harmless.
+
+    python -m dense_mixed_precision_amd.build [--candidates]
 """
 from __future__ import annotations
 
 import os
 import shutil
 import subprocess
+import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "mpgemm.hip")
-DEPS = [SRC, os.path.join(HERE, "csrc", "kernels.hpp"), os.path.join(ROOT, "include", "mpgemm.h")]
+CSRC = os.path.join(HERE, "csrc")
+SRC = os.path.join(CSRC, "mpgemm.hip")
+PROBES_SRC = os.path.join(CSRC, "probes.hip")
+DEPS = [SRC, os.path.join(CSRC, "kernels.hpp"), os.path.join(ROOT, "include", "mpgemm.h")]
 LIB = os.path.join(HERE, "libmpgemm.so")
+PROBES_LIB = os.path.join(HERE, "libmpgemm_probes.so")
+CANDIDATES_LIB = os.path.join(HERE, "libmpgemm_candidates.so")
 ARCH = "gfx950"
 
 
@@ -33,16 +50,41 @@ def flags(extra=()):
             *extra]
 
 
-def build(extra=(), out: str = LIB, verbose: bool = False) -> str:
-    """Compile the library to ``out`` (default: in-tree ``libmpgemm.so``)."""
+def _start(src, out, extra, verbose):
     tmp = out + ".tmp"
-    cmd = [hipcc(), *flags(extra), SRC, "-o", tmp]
+    cmd = [hipcc(), *flags(extra), src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True), tmp, out
+
+
+def _finish(job):
+    proc, tmp, out = job
+    stdout, stderr = proc.communicate()
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}) for {out}:\n{stdout}\n{stderr}")
     os.replace(tmp, out)
+    return out
+
+
+def build(extra=(), out: str = LIB, verbose: bool = False, probes: bool = True,
+          candidates: bool = False) -> str:
+    """Compile the product library to ``out`` (default: in-tree
+    ``libmpgemm.so``), the diagnostics library, and optionally the
+    candidates library, in parallel.  Returns ``out``."""
+    jobs = [_start(SRC, out, extra, verbose)]
+    if probes:
+        jobs.append(_start(PROBES_SRC, PROBES_LIB, extra, verbose))
+    if candidates:
+        jobs.append(_start(SRC, CANDIDATES_LIB, (*extra, "-DMPGEMM_CANDIDATES"), verbose))
+    errors = []
+    for job in jobs:
+        try:
+            _finish(job)
+        except RuntimeError as e:
+            errors.append(str(e))
+    if errors:
+        raise RuntimeError("\n".join(errors))
     return out
 
 
@@ -76,4 +118,4 @@ def is_stale() -> bool:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, candidates="--candidates" in sys.argv[1:]))

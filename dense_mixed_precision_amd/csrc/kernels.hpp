@@ -3,20 +3,22 @@
 // "Capstone 4: a tensor-core GEMM", sections "Capability" and "Minimal model").
 //
 // Kernels:
-//   gemm_tiled<Cfg>   block tile staged through a two-deep LDS ring, wave tiles
-//                     on v_mfma_f32_32x32x16_f16, bounds-checked alpha/beta
-//                     epilogue.  The pages' staged-tile design ("Worked path",
-//                     and the double-buffered copy of "02_mixed_precision_gemm",
+//   gemm_pipe<Cfg>    block tile staged through an LDS ring of K tiles filled by
+//                     direct-to-LDS buffer loads, wave tiles on
+//                     v_mfma_f32_32x32x16_f16 or v_mfma_f32_16x16x32_f16,
+//                     bounds-checked alpha/beta (+ bias) epilogue.  The pages'
+//                     staged-tile design ("Capstone 4", Worked path, and the
+//                     double-buffered copy of "02_mixed_precision_gemm",
 //                     Summary) is the prior art; the layout below is gfx950's.
+//   gemm_narrow       N <= 16: 16 rows of C per workgroup, K split over waves.
 //   gemm_direct       one 32x32 MFMA tile per wave with operands loaded
 //                     straight from memory, 64-bit addressing, any size,
 //                     stride and storage order: the universal fallback.
+//   splitk_reduce     sums split-K partial products in a fixed order.
 //   scale_c           C <- beta*C when alpha == 0 or K == 0.
-//   probe_mfma        writes the accumulator lane layout of one instruction.
-//   probe_mfma_rate   sustained matrix-instruction throughput, no memory traffic.
 //
 // Matrix-core lane layouts used here (CDNA3/CDNA4 matrix instruction docs,
-// checked on the device by probe_mfma):
+// checked on the device by the layout probe of the diagnostics library):
 //   v_mfma_f32_32x32x16_f16: lane l supplies A[l%32][8*(l/32) + 0..7] and
 //     B[8*(l/32) + 0..7][l%32]; accumulator v (0..15) of lane l holds
 //     D[8*(v/4) + 4*(l/32) + v%4][l%32].
@@ -64,24 +66,6 @@ __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi)
     return (lo & 0xFFFFu) | (hi << 16);
 }
 
-// Eight consecutive FP16 values starting at byte offset `off` (or kOOB).
-// VEC = 8: one 16-byte load (offset 16-byte aligned).  VEC = 1: eight
-// 2-byte loads (any 2-byte alignment).
-template <int VEC>
-__device__ __forceinline__ u32x4 load8_full(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    if constexpr (VEC == 8) {
-        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    } else {
-        static_assert(VEC == 1, "vector width must be 8 or 1");
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            h[e] = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2u * e, 0, 0);
-        return u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-    }
-}
-
 // Same, but only the first `nvalid` (1..7) elements are in range; the rest
 // read as zero.  Used where a vector straddles the end of a row.
 __device__ __forceinline__ u32x4 load8_partial(__amdgpu_buffer_rsrc_t r, uint32_t off, int nvalid)
@@ -91,16 +75,6 @@ __device__ __forceinline__ u32x4 load8_partial(__amdgpu_buffer_rsrc_t r, uint32_
     for (int e = 0; e < 8; ++e)
         h[e] = __builtin_amdgcn_raw_buffer_load_b16(r, e < nvalid ? off + 2u * e : kOOB, 0, 0);
     return u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
-}
-
-// nvalid >= 8: whole vector; <= 0: zeros; otherwise partial.
-template <int VEC>
-__device__ __forceinline__ u32x4 load8(__amdgpu_buffer_rsrc_t r, uint32_t off, int nvalid)
-{
-    u32x4 v = load8_full<VEC>(r, nvalid >= 8 ? off : kOOB);
-    if (nvalid > 0 && nvalid < 8)
-        v = load8_partial(r, off, nvalid);
-    return v;
 }
 
 struct GemmArgs {
@@ -201,215 +175,6 @@ __device__ __forceinline__ void store_tile32(const floatx16 &acc, float *C, int6
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel
-// ---------------------------------------------------------------------------
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int VEC_A_, int VEC_B_>
-struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_;
-    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int VEC_A = VEC_A_, VEC_B = VEC_B_;
-    static constexpr int NT = 64 * WAVES_M * WAVES_N;
-    static constexpr int WTM = BM / WAVES_M;       // rows of C per wave
-    static constexpr int WTN = BN / WAVES_N;       // columns of C per wave
-    static constexpr int FM = WTM / 32;            // 32x32 MFMA tiles per wave, along M
-    static constexpr int FN = WTN / 32;            // ... along N
-    static constexpr int KS = BK / 16;             // MFMA k-steps per stage
-    static constexpr int CH = BK / 8;              // 16-byte chunks per LDS row
-    static constexpr int ROWB = BK * 2;            // bytes per LDS row
-    static constexpr int A_CHUNKS = BM * CH / NT;  // 16-byte A chunks each thread copies per stage
-    static constexpr int KB = BK * BN / (8 * NT);  // B rows per thread per stage (8-column block)
-    static constexpr int A_BYTES = BM * ROWB;
-    static constexpr int B_BYTES = BN * ROWB;
-    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-
-    static_assert(BK == 64 || BK == 128, "LDS swizzle is laid out for 64 or 128 K per stage");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32x32");
-    static_assert((BM * CH) % NT == 0, "A stage must split evenly over the threads");
-    static_assert(KB == 2 || KB == 4 || KB == 8, "B stage must split into 8-column blocks of 2, 4 or 8 rows");
-    static_assert((BN / 8) * (BK / KB) == NT, "B blocks must cover the stage exactly");
-    static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
-};
-
-// XOR swizzle of the 16-byte chunk index inside an LDS row.  Reads take 8
-// consecutive rows at one logical chunk; the transposed B writes take rows
-// 8 apart.  (r ^ r>>3) & 7 sends both patterns to 8 distinct 16-byte bank
-// slots, so neither the ds_read_b128 nor the ds_write_b128 conflicts.
-__device__ __forceinline__ int swz(int row)
-{
-    return (row ^ (row >> 3)) & 7;
-}
-
-template <class Cfg>
-__global__ void __launch_bounds__(Cfg::NT)
-gemm_tiled(GemmArgs args)
-{
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
-    constexpr int FM = Cfg::FM, FN = Cfg::FN, KS = Cfg::KS, CH = Cfg::CH, ROWB = Cfg::ROWB;
-    constexpr int NT = Cfg::NT, KB = Cfg::KB, A_CHUNKS = Cfg::A_CHUNKS;
-
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Cfg::LDS_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / Cfg::WAVES_N;
-    const int wn = wave % Cfg::WAVES_N;
-
-    int tm, tn;
-    tile_coords(blockIdx.x, gridDim.x, args.tiles_n, args.tiles_m, args.group_m, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
-    const int64_t M = args.M, N = args.N, K = args.K;
-    const int64_t lda = args.lda, ldb = args.ldb;
-
-    // ---- per-thread copy assignment -------------------------------------
-    // A: chunk q = tid + NT*i covers row q/CH, elements 8*(q%CH) .. +7.
-    uint32_t a_off[A_CHUNKS];
-    int a_row_ok[A_CHUNKS];
-    int a_col[A_CHUNKS];
-    uint32_t a_lds[A_CHUNKS];
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-        const int q = tid + NT * i;
-        const int r = q / CH, c = q % CH;
-        a_off[i] = (uint32_t)((r * lda + 8 * c) * 2);
-        a_row_ok[i] = (m0 + r) < M;
-        a_col[i] = 8 * c;
-        a_lds[i] = r * ROWB + ((c ^ swz(r)) * 16);
-    }
-    // B: thread owns the 8-column block nc and rows KB*kq .. KB*kq+KB-1.
-    const int nc = tid % (BN / 8);
-    const int kq = tid / (BN / 8);
-    const int64_t b_cols_left = N - (n0 + 8 * nc);
-    const int b_nvalid = b_cols_left >= 8 ? 8 : (b_cols_left <= 0 ? 0 : (int)b_cols_left);
-    uint32_t b_off[KB];
-#pragma unroll
-    for (int rr = 0; rr < KB; ++rr)
-        b_off[rr] = (uint32_t)(((KB * kq + rr) * ldb + 8 * nc) * 2);
-    // LDS destination of transposed column j of the block: row 8*nc + j,
-    // k offset KB*kq inside that row.
-    uint32_t b_lds[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int n = 8 * nc + j;
-        const int kk = KB * kq;
-        b_lds[j] = Cfg::A_BYTES + n * ROWB + (((kk >> 3) ^ swz(n)) * 16) + (kk & 7) * 2;
-    }
-
-    u32x4 ra[A_CHUNKS];
-    u32x4 rb[KB];
-
-    auto load_stage = [&](int64_t k0) {
-        const __amdgpu_buffer_rsrc_t rsA = make_rsrc(args.A + m0 * lda + k0);
-        const __amdgpu_buffer_rsrc_t rsB = make_rsrc(args.B + k0 * ldb + n0);
-        const int64_t k_left = K - k0;
-#pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) {
-            const int64_t left = k_left - a_col[i];
-            const int nv = !a_row_ok[i] ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : (int)left));
-            ra[i] = load8<Cfg::VEC_A>(rsA, a_off[i], nv);
-        }
-#pragma unroll
-        for (int rr = 0; rr < KB; ++rr) {
-            const int nv = (KB * kq + rr) < k_left ? b_nvalid : 0;
-            rb[rr] = load8<Cfg::VEC_B>(rsB, b_off[rr], nv);
-        }
-    };
-
-    auto store_stage = [&](int stage) {
-        uint8_t *base = smem + stage * Cfg::STAGE_BYTES;
-#pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i)
-            *reinterpret_cast<u32x4 *>(base + a_lds[i]) = ra[i];
-        // 8 x KB block -> KB x 8: column j gathers element j of each row.
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint32_t col[KB / 2];
-#pragma unroll
-            for (int p = 0; p < KB / 2; ++p) {
-                const uint32_t lo = rb[2 * p][j >> 1];
-                const uint32_t hi = rb[2 * p + 1][j >> 1];
-                col[p] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-            }
-            if constexpr (KB == 8)
-                *reinterpret_cast<u32x4 *>(base + b_lds[j]) = u32x4{col[0], col[1], col[2], col[3]};
-            else if constexpr (KB == 4)
-                *reinterpret_cast<u32x2 *>(base + b_lds[j]) = u32x2{col[0], col[1]};
-            else
-                *reinterpret_cast<uint32_t *>(base + b_lds[j]) = col[0];
-        }
-    };
-
-    // ---- operand read offsets (bytes inside a stage) ---------------------
-    uint32_t a_rd[FM], b_rd[FN];
-    int a_sw[FM], b_sw[FN];
-#pragma unroll
-    for (int f = 0; f < FM; ++f) {
-        const int r = wm * Cfg::WTM + f * 32 + (lane & 31);
-        a_rd[f] = r * ROWB;
-        a_sw[f] = swz(r);
-    }
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-        const int n = wn * Cfg::WTN + f * 32 + (lane & 31);
-        b_rd[f] = Cfg::A_BYTES + n * ROWB;
-        b_sw[f] = swz(n);
-    }
-    const int khalf = lane >> 5;
-
-    floatx16 acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            acc[i][j] = floatx16{0};
-
-    const int64_t num_k = (K + BK - 1) / BK;
-    if (num_k > 0) {
-        load_stage(0);
-        store_stage(0);
-        __syncthreads();
-    }
-    for (int64_t kt = 0; kt < num_k; ++kt) {
-        const int stage = (int)(kt & 1);
-        const bool has_next = kt + 1 < num_k;
-        if (has_next)
-            load_stage((kt + 1) * BK);
-        const uint8_t *base = smem + stage * Cfg::STAGE_BYTES;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int c = 2 * ks + khalf;
-            half8 a[FM], b[FN];
-#pragma unroll
-            for (int f = 0; f < FM; ++f)
-                a[f] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(
-                                                     base + a_rd[f] + ((c ^ a_sw[f]) * 16)));
-#pragma unroll
-            for (int f = 0; f < FN; ++f)
-                b[f] = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4 *>(
-                                                     base + b_rd[f] + ((c ^ b_sw[f]) * 16)));
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-        if (has_next)
-            store_stage(stage ^ 1);
-        __syncthreads();
-    }
-
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-            store_tile32(acc[i][j], args.C, args.ldc, M, N,
-                         m0 + wm * Cfg::WTM + i * 32, n0 + wn * Cfg::WTN + j * 32,
-                         args.alpha, args.beta, args.bias, lane);
-}
-
-// ---------------------------------------------------------------------------
 // Direct kernel: 4 waves, 64x64 of C per workgroup, operands from memory.
 // ---------------------------------------------------------------------------
 template <int IN>
@@ -487,85 +252,6 @@ scale_c(float *C, int64_t M, int64_t N, int64_t ldc, float beta, const float *bi
     }
 }
 
-// One wave.  A[i][0] = i, A[i][1] = 1, B[0][j] = 1, B[1][j] = S*j, the rest
-// zero, so D[i][j] = i + S*j; each lane writes its accumulators in order.
-__global__ void __launch_bounds__(64)
-probe_mfma(float *out, int shape)
-{
-    const int l = threadIdx.x;
-    half8 a = half8{0}, b = half8{0};
-    if (shape == 32) {
-        if (l < 32) {  // k = 0..7 held by lanes 0..31
-            a[0] = (_Float16)(float)(l & 31);
-            a[1] = (_Float16)1.0f;
-            b[0] = (_Float16)1.0f;
-            b[1] = (_Float16)(float)(32 * (l & 31));
-        }
-        floatx16 d = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, floatx16{0}, 0, 0, 0);
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-            out[l * 16 + v] = d[v];
-    } else {
-        if (l < 16) {  // k = 0..7 held by lanes 0..15
-            a[0] = (_Float16)(float)(l & 15);
-            a[1] = (_Float16)1.0f;
-            b[0] = (_Float16)1.0f;
-            b[1] = (_Float16)(float)(16 * (l & 15));
-        }
-        floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, floatx4{0}, 0, 0, 0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            out[l * 4 + v] = d[v];
-    }
-}
-
-// Matrix-core throughput probe.  Every wave loads four operand pairs once
-// (lane l: A values ops[64*(16*q + l)/8 ...], see below) and then issues
-// `iters` rounds of MFMA_N independent matrix instructions, rotating through
-// the four pairs so consecutive instructions see different operand bits, as
-// in the GEMM's inner loop; nothing touches memory inside the loop.  Each
-// lane writes the sum of its accumulators to out[global thread id], so the
-// work is kept.  A diagnostic of the clock and power the matrix cores settle
-// at under sustained load for given operand values.
-// ops: 4 pairs x 64 lanes x 16 values (8 for A, then 8 for B) = 4096 values.
-template <int IN, int MI>
-__global__ void __launch_bounds__(512)
-probe_mfma_rate(const uint16_t *ops, int64_t iters, float *out)
-{
-    const int lane = threadIdx.x & 63;
-    half8 a[4], b[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            a[q][e] = __builtin_bit_cast(_Float16, ops[(q * 64 + lane) * 16 + e]);
-            b[q][e] = __builtin_bit_cast(_Float16, ops[(q * 64 + lane) * 16 + 8 + e]);
-        }
-    // 128 accumulator registers per lane, like the GEMM's wave tiles
-    constexpr int N = MI == 32 ? 8 : 32;
-    using AccT = typename std::conditional<MI == 32, floatx16, floatx4>::type;
-    AccT acc[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        acc[i] = AccT{0};
-    for (int64_t it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            if constexpr (MI == 32)
-                acc[i] = mfma32<IN>(a[i & 3], b[(i >> 2) & 3], acc[i]);
-            else
-                acc[i] = mfma16<IN>(a[i & 3], b[(i >> 2) & 3], acc[i]);
-        }
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-#pragma unroll
-        for (int v = 0; v < (MI == 32 ? 16 : 4); ++v)
-            s += acc[i][v];
-    out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
-}
-
 // ---------------------------------------------------------------------------
 // Pipelined kernel: global -> LDS with buffer_load ... lds
 // ---------------------------------------------------------------------------
@@ -603,8 +289,15 @@ probe_mfma_rate(const uint16_t *ops, int64_t iters, float *out)
 // lanes x 16 B to LDS at M0 + 16*lane (a contiguous KiB); the swizzle is
 // applied by choosing which global chunk each lane fetches.  Lanes whose
 // chunk is outside the matrix get an offset past num_records and write
-// zeros.  Vectors that straddle the end of a row, and operands without
-// 16-byte alignment, are filled through registers instead.
+// zeros.  Vectors that straddle the end of a row are filled through
+// registers instead.  The 16-byte loads need only the operands' 2-byte
+// alignment: under ROCm, gfx9-family devices run vector memory in unaligned
+// mode (the kernel driver sets it for every process), where a 16-byte buffer
+// load at any 2-byte aligned address returns exactly the bytes there, into
+// registers and through the LDS-DMA form alike.  Without that mode the
+// hardware would drop the low address bits and read the wrong bytes; the GPU
+// tests on 2-byte aligned operands (offset pointers, odd leading
+// dimensions) check it on every device they run on.
 //
 // Schedule (per wave, per K tile of BK): each k-step first issues every
 // operand read of the next k-step (into the other register set), then runs
@@ -658,13 +351,12 @@ struct OpTile {
 // LDS at the end.  For a small block this keeps the wave tiles large (fewer
 // LDS bytes per matrix instruction) while two waves per SIMD still hide
 // latency.
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_, int VEC_A_, int VEC_B_,
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_,
           int LAYOUT_A_ = kRowMajor, int LAYOUT_B_ = kRowMajor, int IN_ = kInF16, int KGROUPS_ = 1,
           int MI_ = 32>
 struct PipeCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
-    static constexpr int VEC_A = VEC_A_, VEC_B = VEC_B_;
     static constexpr int LAYOUT_A = LAYOUT_A_, LAYOUT_B = LAYOUT_B_;
     static constexpr int IN = IN_;
     static constexpr int KGROUPS = KGROUPS_;
@@ -688,7 +380,7 @@ struct PipeCfg {
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static constexpr int APW = TA::PW, BPW = TB::PW;      // copies per wave per tile
-    static constexpr int NL = (VEC_A == 8 ? APW : 0) + (VEC_B == 8 ? BPW : 0);  // vmcnt per tile
+    static constexpr int NL = APW + BPW;                   // vmcnt per tile
     static constexpr int NCOPY = APW + BPW;                // copy instructions per wave per tile
     // MFMA groups (FM per k-step) over which a tile's copies are spread,
     // counted from the barrier that frees their buffer.  With two stages the
@@ -770,12 +462,12 @@ __device__ __forceinline__ void copy_slot(int i, int wave, int lane, i32x4 rs, c
     dma16(rs, region + j * 1024, ok ? voff : kOOB, (uint32_t)(T::RPI * j * src.ld * 2));
 }
 
-// Register fill of one operand tile: every slot when `all` (operands without
-// 16-byte alignment, which the copies skip), else only the vectors that
-// straddle the end of a row (the copies wrote zeros there).  Runs after this
-// thread's copies for the tile have landed.
+// Register fill of the vectors of one operand tile that straddle the end of
+// a row (the copies wrote zeros there): element loads, zero past the edge,
+// written to the slot the copy would have filled.  Runs after this thread's
+// copies for the tile have landed.
 template <class T>
-__device__ __forceinline__ void fill_tile(int wave, int lane, const TileSrc &src, lds_u8 *region, bool all)
+__device__ __forceinline__ void fill_tile(int wave, int lane, const TileSrc &src, lds_u8 *region)
 {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src.origin);
     // the tile's extent, clipped to the tile in 32 bits (both are positive)
@@ -794,62 +486,12 @@ __device__ __forceinline__ void fill_tile(int wave, int lane, const TileSrc &src
         const int c = (ln % T::CH) ^ T::swz(r);
         const int left = elems - 8 * c;
         const int nv = r >= rows ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : left));
-        if (all || (nv > 0 && nv < 8)) {
+        if (nv > 0 && nv < 8) {
             const uint32_t off = (uint32_t)((r * src.ld + 8 * c) * 2);
-            const u32x4 v = (nv >= 8) ? load8_full<1>(rs, off) : load8_partial(rs, off, nv);
-            *(lds_u32x4 *)(region + j * 1024 + ln * 16) = v;
+            *(lds_u32x4 *)(region + j * 1024 + ln * 16) = load8_partial(rs, off, nv);
         }
     }
 }
-
-// The same fill in two halves, so the loads for a tile can go out a whole
-// tile before its values are written to LDS: load() issues them into
-// registers, store() writes the slots load() covered (both take the same
-// `src` and `all`).
-template <class T>
-struct FillRegs {
-    uint32_t h[T::PW][8];
-
-    __device__ __forceinline__ static int valid(int j, int lane, const TileSrc &src, int &r, int &c)
-    {
-        const int rows = (int)(src.row_left < T::ROWS ? src.row_left : T::ROWS);
-        const int elems = (int)(src.chunk_left < 8 * T::CH ? src.chunk_left : 8 * T::CH);
-        r = T::RPI * j + lane / T::CH;
-        c = (lane % T::CH) ^ T::swz(r);
-        const int left = elems - 8 * c;
-        return r >= rows ? 0 : (left >= 8 ? 8 : (left <= 0 ? 0 : left));
-    }
-
-    __device__ __forceinline__ void load(int wave, int lane, const TileSrc &src, bool all)
-    {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src.origin);
-#pragma unroll
-        for (int i = 0; i < T::PW; ++i) {
-            int r, c;
-            const int nv = valid(i * T::NWAVES + wave, lane, src, r, c);
-            if (all || (nv > 0 && nv < 8)) {
-                const uint32_t off = (uint32_t)((r * src.ld + 8 * c) * 2);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    h[i][e] = __builtin_amdgcn_raw_buffer_load_b16(rs, e < nv ? off + 2u * e : kOOB, 0, 0);
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store(int wave, int lane, const TileSrc &src, lds_u8 *region, bool all) const
-    {
-#pragma unroll
-        for (int i = 0; i < T::PW; ++i) {
-            const int j = i * T::NWAVES + wave;
-            int r, c;
-            const int nv = valid(j, lane, src, r, c);
-            if (all || (nv > 0 && nv < 8))
-                *(lds_u32x4 *)(region + j * 1024 + lane * 16) =
-                    u32x4{pack2(h[i][0], h[i][1]), pack2(h[i][2], h[i][3]), pack2(h[i][4], h[i][5]),
-                          pack2(h[i][6], h[i][7])};
-        }
-    }
-};
 
 // Does a tile with this many elements along its rows leave a partial vector?
 template <class T>
@@ -1008,53 +650,23 @@ gemm_pipe(GemmArgs args_in)
     auto copy_one = [&](int q) __attribute__((always_inline)) {
         if (!copy_live)
             return;
-        if (q < APW) {
-            if constexpr (Cfg::VEC_A == 8)
-                copy_slot<TA>(q, wave, lane, rsA, cpa, copy_region);
-        } else {
-            if constexpr (Cfg::VEC_B == 8)
-                copy_slot<TB>(q - APW, wave, lane, rsB, cpb, copy_region + Cfg::A_BYTES);
-        }
+        if (q < APW)
+            copy_slot<TA>(q, wave, lane, rsA, cpa, copy_region);
+        else
+            copy_slot<TB>(q - APW, wave, lane, rsB, cpb, copy_region + Cfg::A_BYTES);
     };
 
-    // Register fill after this thread's copies of tile kt have landed.  With
-    // two stages and an operand that goes through registers on every tile
-    // (no 16-byte alignment), the fill's loads for tile kt go out right after
-    // tile kt-1 is published, a whole tile ahead of their use (PIPE_FILL);
-    // otherwise they are issued here.
-    constexpr bool PIPE_FILL = S == 2 && (Cfg::VEC_A != 8 || Cfg::VEC_B != 8);
-    FillRegs<TA> fra;
-    FillRegs<TB> frb;
-    auto fill_load = [&](int64_t kt) __attribute__((always_inline)) {
-        if constexpr (PIPE_FILL) {
-            if (kt >= (K + BK - 1) / BK)
-                return;
-            const TileSrc a = src_a(kt), b = src_b(kt);
-            if (Cfg::VEC_A != 8 || has_partial<TA>(a.chunk_left))
-                fra.load(wave, lane, a, Cfg::VEC_A != 8);
-            if (Cfg::VEC_B != 8 || has_partial<TB>(b.chunk_left))
-                frb.load(wave, lane, b, Cfg::VEC_B != 8);
-        }
-    };
+    // Register fill of the vectors that straddle a row end, after this
+    // thread's copies of tile kt have landed.
     auto fill = [&](int64_t kt, int buf) __attribute__((always_inline)) {
         lds_u8 *const sbase = lds + buf * Cfg::STAGE_BYTES;
         const TileSrc a = src_a(kt), b = src_b(kt);
-        if (Cfg::VEC_A != 8 || has_partial<TA>(a.chunk_left)) {
-            if constexpr (PIPE_FILL)
-                fra.store(wave, lane, a, sbase, Cfg::VEC_A != 8);
-            else
-                fill_tile<TA>(wave, lane, a, sbase, Cfg::VEC_A != 8);
-        }
-        if (Cfg::VEC_B != 8 || has_partial<TB>(b.chunk_left)) {
-            if constexpr (PIPE_FILL)
-                frb.store(wave, lane, b, sbase + Cfg::A_BYTES, Cfg::VEC_B != 8);
-            else
-                fill_tile<TB>(wave, lane, b, sbase + Cfg::A_BYTES, Cfg::VEC_B != 8);
-        }
+        if (has_partial<TA>(a.chunk_left))
+            fill_tile<TA>(wave, lane, a, sbase);
+        if (has_partial<TB>(b.chunk_left))
+            fill_tile<TB>(wave, lane, b, sbase + Cfg::A_BYTES);
     };
     auto needs_fill = [&](int64_t kt) __attribute__((always_inline)) {
-        if (Cfg::VEC_A != 8 || Cfg::VEC_B != 8)
-            return true;
         return has_partial<TA>(src_a(kt).chunk_left) || has_partial<TB>(src_b(kt).chunk_left);
     };
 
@@ -1193,9 +805,7 @@ gemm_pipe(GemmArgs args_in)
             for (int c = 0; c < NCOPY; ++c)
                 copy_one(c);
         }
-        fill_load(0);
         publish(0, 0, (int)(num_k - 1 < S - 1 ? num_k - 1 : S - 1));
-        fill_load(1);
 #pragma unroll
         for (int grp = 0; grp < FM; ++grp)
             read_group(0, ks0, 0, grp);
@@ -1214,10 +824,8 @@ gemm_pipe(GemmArgs args_in)
                 const int64_t newer = num_k - 2 - kt;
                 publish(kt + 1, nbuf, (int)(newer < S - 2 ? newer : S - 2));
             }
-            if (last) {
+            if (last)
                 begin_copies(kt + S, buf);
-                fill_load(kt + S);
-            }
             // All operand reads for the next k-step go out first, a whole
             // k-step (16 MFMAs per wave) ahead of their use; the scheduling
             // barriers keep the compiler from sinking them next to their uses.

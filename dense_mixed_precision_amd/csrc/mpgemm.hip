@@ -4,10 +4,10 @@
 //
 // The factory is the gfx950 form of the "kernel factory" of the
 // "GEMM kernels 1-7 + Tensor Cores" visualizer (kernel 7: the host picks the
-// tile shape per configuration): a small table of compiled block/wave tiles,
-// chosen per shape so that the grid fills the 256 compute units, and per
-// pointer/leading-dimension alignment so that 16-byte loads are used only
-// where every vector is 16-byte aligned.
+// tile shape per configuration): a small table of compiled block/wave tiles
+// per input format and storage-order pair, chosen per shape so that the grid
+// fills the 256 compute units, with the 64-bit direct kernel for whatever
+// the tiled kernels' 32-bit buffer offsets cannot address.
 #include "mpgemm.h"
 
 #include <hip/hip_runtime.h>
@@ -23,7 +23,6 @@ using mpg::kInBF16;
 using mpg::kInF16;
 using mpg::kRowMajor;
 using mpg::PipeCfg;
-using mpg::TileCfg;
 
 constexpr int kNumCu = 256;
 
@@ -36,13 +35,6 @@ struct Entry {
     mpgemm_config cfg;
     launch_fn launch;
 };
-
-template <class Cfg>
-hipError_t launch_tiled(const GemmArgs &a, dim3 grid, hipStream_t s)
-{
-    hipLaunchKernelGGL(mpg::gemm_tiled<Cfg>, grid, dim3(Cfg::NT), 0, s, a);
-    return hipGetLastError();
-}
 
 template <class Cfg>
 hipError_t launch_pipe(const GemmArgs &a, dim3 grid, hipStream_t s)
@@ -66,35 +58,6 @@ hipError_t launch_direct(const GemmArgs &a, dim3 grid, hipStream_t s)
 }
 
 template <class Cfg>
-constexpr Entry tiled_entry(int id)
-{
-    mpgemm_config c{};
-    c.id = id;
-    c.kind = MPGEMM_KIND_TILED;
-    c.bm = Cfg::BM;
-    c.bn = Cfg::BN;
-    c.bk = Cfg::BK;
-    c.waves_m = Cfg::WAVES_M;
-    c.waves_n = Cfg::WAVES_N;
-    c.wave_m = Cfg::WTM;
-    c.wave_n = Cfg::WTN;
-    c.mfma_m = 32;
-    c.mfma_n = 32;
-    c.mfma_k = 16;
-    c.vec_a = Cfg::VEC_A;
-    c.vec_b = Cfg::VEC_B;
-    c.stages = 2;
-    c.threads = Cfg::NT;
-    c.lds_bytes = Cfg::LDS_BYTES;
-    c.grid = 0;
-    c.layout_a = MPGEMM_ROW_MAJOR;
-    c.layout_b = MPGEMM_ROW_MAJOR;
-    c.in_type = MPGEMM_IN_F16;
-    c.k_groups = 1;
-    return Entry{c, &launch_tiled<Cfg>};
-}
-
-template <class Cfg>
 constexpr Entry pipe_entry(int id)
 {
     mpgemm_config c{};
@@ -110,8 +73,8 @@ constexpr Entry pipe_entry(int id)
     c.mfma_m = Cfg::MI;
     c.mfma_n = Cfg::MI;
     c.mfma_k = Cfg::KD;
-    c.vec_a = Cfg::VEC_A;
-    c.vec_b = Cfg::VEC_B;
+    c.vec_a = 8;
+    c.vec_b = 8;
     c.stages = Cfg::STAGES;
     c.threads = Cfg::NT;
     c.lds_bytes = Cfg::LDS_BYTES;
@@ -141,7 +104,7 @@ constexpr Entry narrow_entry(int id)
     c.mfma_n = 16;
     c.mfma_k = 32;
     c.vec_a = 8;
-    c.vec_b = LB == kColMajor ? 8 : 1;
+    c.vec_b = 8;
     c.stages = DEPTH;   // k-steps of loads in flight per wave
     c.threads = 512;
     c.lds_bytes = 2 * 8 * 64 * 16;  // partial tiles + row-major B transpose slots
@@ -188,140 +151,73 @@ constexpr Entry scale_entry(int id)
     return Entry{c, nullptr};
 }
 
-// Tile shapes.  Each is compiled for the four (vec_a, vec_b) combinations.
-#define MPG_TILE_ENTRIES(base, BM, BN, BK, WM, WN)                     \
-    tiled_entry<TileCfg<BM, BN, BK, WM, WN, 8, 8>>(base + 0),          \
-        tiled_entry<TileCfg<BM, BN, BK, WM, WN, 1, 8>>(base + 1),      \
-        tiled_entry<TileCfg<BM, BN, BK, WM, WN, 8, 1>>(base + 2),      \
-        tiled_entry<TileCfg<BM, BN, BK, WM, WN, 1, 1>>(base + 3)
+// The tile shapes the factory chooses from, for one input format and
+// storage-order pair (entries base .. base+3):
+//   big   256x256x64, 2 stages, 8 waves of 128x64 on 16x16x32: products with
+//         enough 256x256 tiles for every compute unit (under the board's
+//         power limit this instruction does 3-8% more work per joule than
+//         32x32x16);
+//   mid   128x128x64, 3 stages, 8 waves: the 128x128 class when a panel is
+//         streamed once (tall-skinny), where the deeper ring streams A better;
+//   wide  128x128x128, 2 stages, 8 waves: the 128x128 class with reused
+//         panels (half as many barriers per K);
+//   small 64x64x64, 2 stages, 4 waves: small products.
+#define MPG_FAMILY(base, IN, LA, LB)                                                     \
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, LA, LB, IN, 1, 16>>(base + 0),            \
+        pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, LA, LB, IN>>(base + 1),               \
+        pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, LA, LB, IN>>(base + 2),              \
+        pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, LA, LB, IN>>(base + 3)
 
-#define MPG_PIPE_ENTRIES(base, BM, BN, BK, WM, WN, S)                  \
-    pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 8, 8>>(base + 0),        \
-        pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 1, 8>>(base + 1),    \
-        pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 8, 1>>(base + 2),    \
-        pipe_entry<PipeCfg<BM, BN, BK, WM, WN, S, 1, 1>>(base + 3)
-
-#define MPG_LAYOUT_ENTRIES(base, LA, LB)                                     \
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, LA, LB>>(base + 0),      \
-        pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4, 1, 1, LA, LB>>(base + 1),  \
-        pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, 8, 8, LA, LB>>(base + 2),  \
-        pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3, 1, 1, LA, LB>>(base + 3),  \
-        pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 8, 8, LA, LB>>(base + 4),    \
-        pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 1, 1, LA, LB>>(base + 5)
-
-#define MPG_BF16_ENTRIES(base, LA, LB)                                                 \
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, LA, LB, kInBF16>>(base + 0),       \
-        pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4, 1, 1, LA, LB, kInBF16>>(base + 1),   \
-        pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, 8, 8, LA, LB, kInBF16>>(base + 2),   \
-        pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3, 1, 1, LA, LB, kInBF16>>(base + 3),   \
-        pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 8, 8, LA, LB, kInBF16>>(base + 4),     \
-        pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, 1, 1, LA, LB, kInBF16>>(base + 5),     \
-        pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, LA, LB, kInBF16>>(base + 6)
+enum : int { kBig = 0, kMid = 1, kWide = 2, kSmall = 3 };
 
 const Entry kTable[] = {
-    MPG_TILE_ENTRIES(0, 256, 256, 64, 2, 2),  // 0..3   register-staged copies
-    MPG_TILE_ENTRIES(4, 128, 128, 64, 2, 2),  // 4..7
-    MPG_TILE_ENTRIES(8, 64, 64, 64, 2, 2),    // 8..11
-    direct_entry<kInF16>(12),                 // 12     any stride / size / order
-    scale_entry(13),                          // 13     alpha == 0 or K == 0
-    MPG_PIPE_ENTRIES(14, 256, 256, 32, 2, 2, 4),  // 14..17 large products
-    MPG_PIPE_ENTRIES(18, 128, 128, 64, 2, 2, 3),  // 18..21 2048-class and tall-skinny
-    MPG_PIPE_ENTRIES(22, 64, 64, 64, 2, 2, 2),    // 22..25 small or ragged products
-    // alternative shapes (16-byte aligned operands only), for tile sweeps
-    pipe_entry<PipeCfg<256, 256, 64, 2, 2, 2, 8, 8>>(26),
-    pipe_entry<PipeCfg<256, 256, 32, 2, 2, 5, 8, 8>>(27),
-    pipe_entry<PipeCfg<256, 128, 64, 2, 2, 3, 8, 8>>(28),
-    pipe_entry<PipeCfg<128, 128, 32, 2, 2, 4, 8, 8>>(29),
-    pipe_entry<PipeCfg<128, 128, 64, 2, 2, 2, 8, 8>>(30),
-    pipe_entry<PipeCfg<64, 64, 32, 2, 2, 4, 8, 8>>(31),
-    // eight waves per workgroup (two per SIMD)
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8>>(32),
-    pipe_entry<PipeCfg<256, 256, 32, 2, 4, 4, 8, 8>>(33),
-    pipe_entry<PipeCfg<256, 256, 32, 2, 4, 3, 8, 8>>(34),
-    pipe_entry<PipeCfg<256, 128, 64, 4, 2, 3, 8, 8>>(35),
-    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, 8, 8>>(36),
-    // K tiles of 128: half as many barriers per K for the narrower tiles
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8>>(37),
-    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, 8, 8>>(38),
-    pipe_entry<PipeCfg<64, 64, 128, 2, 2, 3, 8, 8>>(39),
-    // A and/or B column-major: the three tile groups, each for 16-byte
-    // aligned operands and for any 2-byte alignment
-    MPG_LAYOUT_ENTRIES(40, kColMajor, kRowMajor),  // 40..45
-    MPG_LAYOUT_ENTRIES(46, kRowMajor, kColMajor),  // 46..51
-    MPG_LAYOUT_ENTRIES(52, kColMajor, kColMajor),  // 52..57
-    // 128x128 tiles with K tiles of 128 for the column-major pairs
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kColMajor, kRowMajor>>(58),
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kRowMajor, kColMajor>>(59),
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kColMajor, kColMajor>>(60),
-    // BF16 inputs: the same shapes for every storage-order pair
-    MPG_BF16_ENTRIES(61, kRowMajor, kRowMajor),  // 61..67
-    MPG_BF16_ENTRIES(68, kColMajor, kRowMajor),  // 68..74
-    MPG_BF16_ENTRIES(75, kRowMajor, kColMajor),  // 75..81
-    MPG_BF16_ENTRIES(82, kColMajor, kColMajor),  // 82..88
-    direct_entry<kInBF16>(89),                   // 89     BF16 fallback
-    // two k-groups of 2x2 waves (64x64 wave tiles) on 128x128 blocks
-    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, 8, 8, kRowMajor, kRowMajor, kInF16, 2>>(90),
-    pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3, 8, 8, kRowMajor, kRowMajor, kInF16, 2>>(91),
-    // the 16x16x32 matrix instruction on the large and 2048-class shapes
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kRowMajor, kRowMajor, kInF16, 1, 16>>(92),
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, 8, 8, kRowMajor, kRowMajor, kInF16, 1, 16>>(93),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kColMajor, kRowMajor, kInF16, 1, 16>>(94),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kRowMajor, kColMajor, kInF16, 1, 16>>(95),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kColMajor, kColMajor, kInF16, 1, 16>>(96),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kRowMajor, kRowMajor, kInBF16, 1, 16>>(97),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kColMajor, kRowMajor, kInBF16, 1, 16>>(98),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kRowMajor, kColMajor, kInBF16, 1, 16>>(99),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, 8, 8, kColMajor, kColMajor, kInBF16, 1, 16>>(100),
+    direct_entry<kInF16>(0),   // 0      any stride / size / order
+    direct_entry<kInBF16>(1),  // 1      BF16 fallback
+    scale_entry(2),            // 2      alpha == 0 or K == 0
+    MPG_FAMILY(3, kInF16, kRowMajor, kRowMajor),    // 3..6
+    MPG_FAMILY(7, kInF16, kColMajor, kRowMajor),    // 7..10
+    MPG_FAMILY(11, kInF16, kRowMajor, kColMajor),   // 11..14
+    MPG_FAMILY(15, kInF16, kColMajor, kColMajor),   // 15..18
+    MPG_FAMILY(19, kInBF16, kRowMajor, kRowMajor),  // 19..22
+    MPG_FAMILY(23, kInBF16, kColMajor, kRowMajor),  // 23..26
+    MPG_FAMILY(27, kInBF16, kRowMajor, kColMajor),  // 27..30
+    MPG_FAMILY(31, kInBF16, kColMajor, kColMajor),  // 31..34
+    // small row-major FP16 products with more than one 64-deep K tile:
+    // 64x64 tiles with K tiles of 128 and a 3-deep ring
+    pipe_entry<PipeCfg<64, 64, 128, 2, 2, 3>>(35),
     // N <= 16 with A row-major, per input format and storage order of B;
-    // four k-steps of loads in flight per wave (fewer registers, so more
-    // workgroups share a compute unit when M is large)
-    narrow_entry<kInF16, kRowMajor, 4>(101),
-    narrow_entry<kInF16, kColMajor, 4>(102),
-    narrow_entry<kInBF16, kRowMajor, 4>(103),
-    narrow_entry<kInBF16, kColMajor, 4>(104),
-    // deeper candidate (FP16, B row-major)
-    narrow_entry<kInF16, kRowMajor, 8>(105),
+    // four k-steps of loads in flight per wave
+    narrow_entry<kInF16, kRowMajor, 4>(36),
+    narrow_entry<kInF16, kColMajor, 4>(37),
+    narrow_entry<kInBF16, kRowMajor, 4>(38),
+    narrow_entry<kInBF16, kColMajor, 4>(39),
+#ifdef MPGEMM_CANDIDATES
+    // Alternatives the factory does not choose, compiled only into the
+    // candidates build for tile sweeps (FP16, A and B row-major).
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2>>(40),                   // 32x32x16 on the big tile
+    pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4>>(41),                   // 4 waves of 128x128
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16>>(42),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, kRowMajor, kRowMajor, kInF16, 2>>(43),  // 2 k-groups
+    pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3>>(44),                   // 4 waves
+    pipe_entry<PipeCfg<256, 128, 64, 4, 2, 3>>(45),
+    pipe_entry<PipeCfg<128, 128, 32, 2, 2, 4>>(46),
+    narrow_entry<kInF16, kRowMajor, 8>(47),                           // 8 k-steps in flight
+#endif
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
-constexpr int kDirectIds[2] = {12, 89};  // per input format
-constexpr int kScaleId = 13;
-
-// Tile groups the factory chooses from, largest first, per storage-order
-// pair (layout_a + 2*layout_b).  ids[] holds the table entry for each
-// (vec_a, vec_b) pair in the order 88, 18, 81, 11.  For row-major operands
-// the eight-wave shapes exist for 16-byte aligned operands only and the
-// other pairs fall back to the four-wave form of the same tile; for the
-// column-major pairs every pair but 88 takes the 2-byte (11) entry.
-// 128x128, K tile 128, eight waves, per input format and storage-order pair
-constexpr int kWideKIds[2][4] = {{37, 58, 59, 60}, {67, 74, 81, 88}};
+constexpr int kDirectIds[2] = {0, 1};  // per input format
+constexpr int kScaleId = 2;
+// first entry of the family of input format `in` and storage orders (la, lb)
+constexpr int family(int in, int la, int lb) { return 3 + 16 * in + 4 * (la + 2 * lb); }
 // 64x64 tiles, K tile 128, three stages (row-major FP16)
-constexpr int kSmallDeepKId = 39;
+constexpr int kSmallDeepKId = 35;
 // narrow kernel (N <= 16, A row-major) per input format and storage order of B
-constexpr int kNarrowIds[2][2] = {{101, 102}, {103, 104}};
+constexpr int kNarrowIds[2][2] = {{36, 37}, {38, 39}};
 // below this many 16-row workgroups the narrow kernel leaves most compute
 // units idle, and split-K over the tile kernels is faster (256x16x65536:
 // 74 against 38 us); at or above it the narrow kernel leads (1024x16x16384:
 // 21 against 25 us; 4096x16x4096: 7.7 against 16.2)
 constexpr int64_t kNarrowMinGroups = 64;
-struct TileGroup {
-    int bm, bn;
-    int ids[4];
-};
-constexpr int kNumGroups = 3;
-// The 256x256 shape uses the 16x16x32 instruction (entry `big`): under the
-// board's power limit it does 3-8% more work per joule than 32x32x16.
-#define MPG_GROUPS(b, big)                                                          \
-    {{256, 256, {big, b + 1, b + 1, b + 1}}, {128, 128, {b + 2, b + 3, b + 3, b + 3}}, \
-     {64, 64, {b + 4, b + 5, b + 5, b + 5}}}
-constexpr TileGroup kGroups[2][4][kNumGroups] = {
-    {
-        {{256, 256, {92, 15, 16, 17}}, {128, 128, {36, 19, 20, 21}}, {64, 64, {22, 23, 24, 25}}},
-        MPG_GROUPS(40, 94),
-        MPG_GROUPS(46, 95),
-        MPG_GROUPS(52, 96),
-    },
-    {MPG_GROUPS(61, 97), MPG_GROUPS(68, 98), MPG_GROUPS(75, 99), MPG_GROUPS(82, 100)},
-};
 
 // ---------------------------------------------------------------------------
 // Validation and selection (pure host code, no HIP calls)
@@ -384,22 +280,12 @@ int validate(const Problem &p)
 
 int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0); }
 
-// gfx950 under ROCm runs vector memory instructions in unaligned mode: a
-// 16-byte buffer load at any 2-byte aligned address, into registers or
-// through the LDS-DMA form, returns exactly the 16 bytes there (probed on
-// the device; the parity tests with odd leading dimensions and offset
-// pointers run through these paths).  So every valid (2-byte aligned)
-// operand takes the 16-byte copy path; the element-wise (vec 1) entries stay
-// in the table for tests and for a device without that mode, where
-// kUnalignedVectors = false restores 16-byte alignment as the condition.
-constexpr bool kUnalignedVectors = true;
-
-int vec_for(const void *ptr, int64_t ld)
-{
-    if (kUnalignedVectors)
-        return 8;
-    return ((reinterpret_cast<uintptr_t>(ptr) & 15u) == 0 && (ld % 8) == 0) ? 8 : 1;
-}
+// Every valid operand (2-byte aligned, any leading dimension) takes the
+// 16-byte copy path: under ROCm, gfx9-family devices run vector memory in
+// unaligned mode, where a 16-byte buffer load at any 2-byte aligned address,
+// into registers or through the LDS-DMA form, returns exactly the 16 bytes
+// there (probed on the device; the parity tests with odd leading dimensions
+// and offset pointers run through these paths on every device they run on).
 
 // Can table entry `e` run problem `p`?
 bool entry_fits(const Entry &e, const Problem &p)
@@ -427,10 +313,6 @@ bool entry_fits(const Entry &e, const Problem &p)
         return p.N <= 16 && a_span < (int64_t)0x7FFFFFF0 && b_span < (int64_t)0x7FFFFFF0 &&
                c_span < (int64_t)0x7FFFFFF0 && cdiv(p.M, 16) <= 0x7FFFFFFF;
     }
-    if (c.vec_a == 8 && vec_for(p.A, p.lda) != 8)
-        return false;
-    if (c.vec_b == 8 && vec_for(p.B, p.ldb) != 8)
-        return false;
     // Per-stage buffer offsets are 32-bit: a stage spans bm (A row-major) or
     // bk (A column-major) stored rows of lda, and bk (B row-major) or bn (B
     // column-major) stored rows of ldb.
@@ -454,7 +336,6 @@ bool entry_fits(const Entry &e, const Problem &p)
 int64_t grid_for(const mpgemm_config &c, const Problem &p)
 {
     switch (c.kind) {
-    case MPGEMM_KIND_TILED:
     case MPGEMM_KIND_PIPE:
         return mul_sat(cdiv(p.M, c.bm), cdiv(p.N, c.bn));
     case MPGEMM_KIND_DIRECT:
@@ -485,38 +366,34 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
         if (entry_fits(kTable[nid], p))
             return nid;
     }
-    const int va = vec_for(p.A, p.lda) == 8 ? 0 : 1;
-    const int vb = vec_for(p.B, p.ldb) == 8 ? 0 : 2;
-    const int v = va + vb;
     // Enough 256x256 tiles for every CU: large products.
     // Else 128x128 if that makes at least half a wave of workgroups.
     // Else 64x64.
-    int group;
-    if (mul_sat(cdiv(p.M, 256), cdiv(p.N, 256)) >= kNumCu)
-        group = 0;
-    else if (mul_sat(cdiv(p.M, 128), cdiv(p.N, 128)) >= kNumCu / 2)
-        group = 1;
-    else
-        group = 2;
-    // 128x128 tiles with both panels reused across tiles (B panels by at
-    // least four column tiles) take K steps of 128: half as many barriers.
-    // A tall-skinny product streams A once and keeps the deeper 64-wide ring.
-    const int wide = kWideKIds[p.in_type][p.la + 2 * p.lb];
-    if (group == 1 && v == 0 && cdiv(p.N, 128) >= 4 && cdiv(p.M, 128) >= 4 &&
-        entry_fits(kTable[wide], p))
-        return wide;
-    // Small row-major FP16 products with more than one 64-deep K tile take
-    // 64x64 tiles with K tiles of 128 and a 3-deep ring: half as many
-    // barriers per K (256^3: 4.6 against 4.8 us per call).
-    if (small_deep_k && group == 2 && v == 0 && p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR &&
-        p.lb == MPGEMM_ROW_MAJOR && p.K > 64 && entry_fits(kTable[kSmallDeepKId], p))
-        return kSmallDeepKId;
-    const TileGroup *groups = kGroups[p.in_type][p.la + 2 * p.lb];
-    for (int g = group; g < kNumGroups; ++g) {
-        const int id = groups[g].ids[v];
-        if (entry_fits(kTable[id], p))
-            return id;
+    const int fam = family(p.in_type, p.la, p.lb);
+    int order[4];
+    int n = 0;
+    if (mul_sat(cdiv(p.M, 256), cdiv(p.N, 256)) >= kNumCu) {
+        order[n++] = fam + kBig;
+        order[n++] = fam + kMid;
+    } else if (mul_sat(cdiv(p.M, 128), cdiv(p.N, 128)) >= kNumCu / 2) {
+        // 128x128 tiles with both panels reused across tiles (B panels by at
+        // least four column tiles) take K steps of 128: half as many
+        // barriers.  A tall-skinny product streams A once and keeps the
+        // deeper 64-wide ring.
+        if (cdiv(p.N, 128) >= 4 && cdiv(p.M, 128) >= 4)
+            order[n++] = fam + kWide;
+        order[n++] = fam + kMid;
+    } else if (small_deep_k && p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR &&
+               p.lb == MPGEMM_ROW_MAJOR && p.K > 64) {
+        // Small row-major FP16 products with more than one 64-deep K tile
+        // take 64x64 tiles with K tiles of 128 and a 3-deep ring: half as
+        // many barriers per K (256^3: 4.6 against 4.8 us per call).
+        order[n++] = kSmallDeepKId;
     }
+    order[n++] = fam + kSmall;
+    for (int i = 0; i < n; ++i)
+        if (entry_fits(kTable[order[i]], p))
+            return order[i];
     return kDirectIds[p.in_type];
 }
 
@@ -916,45 +793,6 @@ int mpgemm_config_info(int config_id, mpgemm_config *out)
     return MPGEMM_OK;
 }
 
-int mpgemm_probe_mfma_layout(int shape, float *out, void *stream)
-{
-    if (shape != 32 && shape != 16)
-        return MPGEMM_ECONFIG;
-    if (out == nullptr)
-        return MPGEMM_ENULL;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(mpg::probe_mfma, dim3(1), dim3(64), 0,
-                       reinterpret_cast<hipStream_t>(stream), out, shape);
-    return hipGetLastError() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
-}
-
-int mpgemm_probe_mfma_rate(int in_type, int shape, const uint16_t *ops, int64_t ops_len, int64_t iters,
-                           int workgroups, float *out, int64_t out_len, void *stream)
-{
-    if ((in_type != MPGEMM_IN_F16 && in_type != MPGEMM_IN_BF16) || (shape != 32 && shape != 16))
-        return MPGEMM_ECONFIG;
-    if (ops == nullptr || out == nullptr)
-        return MPGEMM_ENULL;
-    if (ops_len < 4096 || iters < 0 || iters > (int64_t)1 << 24 || workgroups < 1 || workgroups > 65535 ||
-        out_len < (int64_t)workgroups * 512)
-        return MPGEMM_EDIM;
-    (void)hipGetLastError();
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)workgroups), block(512);
-    if (in_type == MPGEMM_IN_F16) {
-        if (shape == 32)
-            hipLaunchKernelGGL((mpg::probe_mfma_rate<mpg::kInF16, 32>), grid, block, 0, s, ops, iters, out);
-        else
-            hipLaunchKernelGGL((mpg::probe_mfma_rate<mpg::kInF16, 16>), grid, block, 0, s, ops, iters, out);
-    } else {
-        if (shape == 32)
-            hipLaunchKernelGGL((mpg::probe_mfma_rate<mpg::kInBF16, 32>), grid, block, 0, s, ops, iters, out);
-        else
-            hipLaunchKernelGGL((mpg::probe_mfma_rate<mpg::kInBF16, 16>), grid, block, 0, s, ops, iters, out);
-    }
-    return hipGetLastError() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
-}
-
 const char *mpgemm_strerror(int code)
 {
     switch (code) {
@@ -985,6 +823,6 @@ const char *mpgemm_strerror(int code)
     }
 }
 
-const char *mpgemm_version(void) { return "mpgemm 0.6.0 gfx950"; }
+const char *mpgemm_version(void) { return "mpgemm 0.7.0 gfx950"; }
 
 }  // extern "C"

@@ -70,8 +70,7 @@ extern "C" {
 #define MPGEMM_IN_F16 0        /* IEEE binary16                                   */
 #define MPGEMM_IN_BF16 1       /* bfloat16                                        */
 
-/* Kinds of kernel a config can name. */
-#define MPGEMM_KIND_TILED 0    /* LDS-staged, double-buffered MFMA block tile     */
+/* Kinds of kernel a config can name (0 is not used). */
 #define MPGEMM_KIND_DIRECT 1   /* operands straight from memory; any size/stride  */
 #define MPGEMM_KIND_SCALE 2    /* C <- beta*C only (alpha == 0 or K == 0)         */
 #define MPGEMM_KIND_NONE 3     /* nothing to do (M == 0 or N == 0)                */
@@ -93,8 +92,10 @@ typedef struct mpgemm_config {
     int32_t wave_m;      /* rows of C per wave                                    */
     int32_t wave_n;      /* columns of C per wave                                 */
     int32_t mfma_m, mfma_n, mfma_k; /* matrix instruction: 32x32x16 or 16x16x32   */
-    int32_t vec_a;       /* FP16 elements per global load of A (8 or 1)           */
-    int32_t vec_b;       /* FP16 elements per global load of B (8 or 1)           */
+    int32_t vec_a;       /* 16-bit elements per global load of A: 8 for the tiled
+                            kernels (16-byte loads at any 2-byte alignment), 1
+                            for the direct kernel (element loads)                 */
+    int32_t vec_b;       /* the same for B                                        */
     int32_t stages;      /* LDS buffers in flight                                 */
     int32_t threads;     /* threads per workgroup                                 */
     int32_t lds_bytes;   /* LDS per workgroup                                     */
@@ -316,43 +317,10 @@ int mpgemm_num_configs(void);
 /* Table entry `config_id` into *out (grid = 0).  MPGEMM_ECONFIG if unknown. */
 int mpgemm_config_info(int config_id, mpgemm_config *out);
 
-/*
- * Diagnostic: runs one matrix-core instruction on known operands and writes
- * where each output element landed, so the documented lane layout can be
- * checked on the device.  shape 32 uses the 32x32x16 FP16 instruction,
- * shape 16 the 16x16x32 one.  Operands: A[i][0] = i, A[i][1] = 1,
- * B[0][j] = 1, B[1][j] = S*j (S = 32 or 16), every other entry 0, so
- * D[i][j] = i + S*j exactly.  `out` is device memory for 64*16 floats
- * (shape 32) or 64*4 floats (shape 16): out[lane*V + v] = lane's v-th
- * accumulator.  MPGEMM_ECONFIG for another shape.
- */
-int mpgemm_probe_mfma_layout(int shape, float *out, void *stream);
-
-/*
- * Diagnostic: sustained matrix-core throughput with no memory traffic, for
- * measuring the clock and power the matrix cores settle at under load for
- * given operand values (the GEMM's own inner loop is this instruction
- * stream plus its operand traffic).  `workgroups` workgroups of 8 waves;
- * every wave loads four operand pairs from `ops` once (device memory,
- * ops_len >= 4096 16-bit values: pair q, lane l reads 8 A values at
- * (64*q + l)*16 and 8 B values right after) and issues `iters` rounds of
- * independent matrix instructions (8 of 32x32x16 for shape 32, 32 of
- * 16x16x32 for shape 16, i.e. 128 accumulator registers per lane),
- * rotating through the pairs.  FLOP per call = workgroups * 8 waves *
- * iters * 2 * 32*32*16 * 8 (shape 32) or * 2 * 16*16*32 * 32 (shape 16).
- * Each thread writes the sum of its accumulators to out[thread id]
- * (out_len >= workgroups*512 floats).  in_type MPGEMM_IN_F16 or
- * MPGEMM_IN_BF16.  MPGEMM_ECONFIG for another format or shape,
- * MPGEMM_ENULL for NULL buffers, MPGEMM_EDIM for short buffers, iters
- * outside 0..2^24 or workgroups outside 1..65535 (checked before launch).
- */
-int mpgemm_probe_mfma_rate(int in_type, int shape, const uint16_t *ops, int64_t ops_len, int64_t iters,
-                           int workgroups, float *out, int64_t out_len, void *stream);
-
 /* Static text for an error code (never NULL). */
 const char *mpgemm_strerror(int code);
 
-/* Library version string, e.g. "mpgemm 0.6.0 gfx950". */
+/* Library version string, e.g. "mpgemm 0.7.0 gfx950". */
 const char *mpgemm_version(void);
 
 #ifdef __cplusplus

@@ -9,11 +9,14 @@ with gcc into ``liboracle.so`` and called here through ctypes.
 What it computes is the plain definition of the product ("Capstone 4: a
 tensor-core GEMM", Minimal model and Compare like with like): FP16 inputs
 widened exactly to FP64, products exact, the sum carried in FP64 in ascending
-k, then ``alpha*s + beta*c`` with C not read when ``beta == 0``.
+k, then ``alpha*s + beta*c`` with C not read when ``beta == 0``, and A and B
+not read when ``alpha == 0`` or ``K == 0`` (then the result is ``beta*c``).
 
 The acceptance rule for a GPU result ``c`` against this oracle is
 ``|c - ref| <= 1e-3 * sum_k|a_ik*b_kj| + 1e-5`` elementwise (see
 :func:`tolerance_ok`); the oracle returns that sum alongside the result.
+:func:`accumulation_ratio` is a second, diagnostic check: the error against
+the worst case of an FP32 running sum, which an FP16 running sum exceeds.
 """
 from __future__ import annotations
 
@@ -252,6 +255,52 @@ def tolerance_ok(got, ref, absdot):
     err = np.abs(got - ref)
     tol = TOL_REL * absdot + TOL_ABS
     return err <= tol
+
+
+#: FP32 unit roundoff (round to nearest) and smallest normal.
+U_FP32 = 2.0 ** -24
+TINY_FP32 = 2.0 ** -126
+
+
+def accumulation_bound(ref, absdot, K: int, alpha: float, extra_adds: int = 64):
+    """Worst-case error of an FP32 running sum of exact products (recursive
+    summation, gamma_n = n*u/(1 - n*u) with u = 2^-24) plus the epilogue's
+    own roundings:
+
+        gamma_n * |alpha| * S + 2u * |ref| + K * 2^-126 + 2^-149,   n = K + extra_adds
+
+    S = sum_k |a_ik b_kj| (the oracle's ``absdot``).  ``extra_adds`` covers
+    the additions a kernel makes beyond the K of the product (partial sums
+    of split pieces or of K slices, the alpha scaling, the beta and bias
+    terms); the last term allows for FP32 partial sums below the normal
+    range being flushed (2^-149, the smallest FP32 value, keeps the bound
+    positive).  This is a diagnostic, not the acceptance rule:
+    an FP32-accumulating kernel stays below it on any data, while an FP16
+    (or BF16) running sum exceeds it by orders of magnitude on ordinary
+    data, although the acceptance rule can still pass it ("Capstone 4: a
+    tensor-core GEMM", Common failures: the accumulator must not be FP16;
+    "Tensor cores with WMMA", Exercise: an FP16 accumulator passed that
+    page's checks)."""
+    n = K + extra_adds
+    gamma = n * U_FP32 / (1.0 - n * U_FP32)
+    alpha = abs(float(np.float32(alpha)))
+    return (gamma * alpha * np.asarray(absdot) + 2 * U_FP32 * np.abs(ref) + K * TINY_FP32
+            + 2.0 ** -149)
+
+
+def accumulation_ratio(got, ref, absdot, K: int, alpha: float, extra_adds: int = 64) -> float:
+    """max |got - ref| / accumulation_bound(...) over the finite entries of
+    ``ref`` (NaN/Inf in ``got`` there count as infinitely far); 0 for no
+    entries.  At most 1 for an FP32-accumulating kernel."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = np.isfinite(ref)
+    if not fin.any():
+        return 0.0
+    err = np.abs(got[fin] - ref[fin])
+    err = np.where(np.isfinite(err), err, np.inf)
+    bound = accumulation_bound(ref[fin], np.asarray(absdot)[fin], K, alpha, extra_adds)
+    return float(np.max(err / bound))
 
 
 def worst(got, ref, absdot):

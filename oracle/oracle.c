@@ -141,6 +141,13 @@ static strides_t strides_for(int layout_a, int layout_b, int64_t lda, int64_t ld
  * One output element: the dot product of row i of A with column j of B in
  * ascending k, then alpha*s + beta*c.  Also returns sum_k |a_ik * b_kj|, the
  * scale the acceptance rule is written against.
+ *
+ * When alpha == 0 or K == 0 the product term is not formed at all and A and
+ * B are not read: the result is beta*c (+ bias), and the sum of |a*b| is 0.
+ * The pages say nothing about this case; the reading taken is the usual
+ * convention of matrix-product interfaces (the counterpart of "beta == 0
+ * means C is not read"), so a NaN or Inf in A or B, or a non-finite alpha
+ * with K == 0, does not reach the result.
  */
 static void entry(int64_t i, int64_t j, int64_t K,
                   const uint16_t *A, const uint16_t *B, strides_t st,
@@ -148,18 +155,24 @@ static void entry(int64_t i, int64_t j, int64_t K,
                   double alpha, double beta,
                   double *ref, double *absdot)
 {
+    const int product = alpha != 0.0 && K > 0;
     double s = 0.0;
     double s_abs = 0.0;
-    for (int64_t k = 0; k < K; ++k) {
+    for (int64_t k = 0; product && k < K; ++k) {
         const double a = st.decode(A[i * st.a_i + k * st.a_k]);
         const double b = st.decode(B[k * st.b_k + j * st.b_j]);
         const double p = a * b; /* exact */
         s += p;
         s_abs += fabs(p);
     }
-    double r = alpha * s;
-    if (beta != 0.0)
-        r += beta * (double)C[i * ldc + j];
+    double r;
+    if (product) {
+        r = alpha * s;
+        if (beta != 0.0)
+            r += beta * (double)C[i * ldc + j];
+    } else {
+        r = beta != 0.0 ? beta * (double)C[i * ldc + j] : 0.0;
+    }
     if (st.bias)
         r += (double)st.bias[j];
     *ref = r;

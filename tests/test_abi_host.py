@@ -14,14 +14,15 @@ from dense_mixed_precision_amd.workloads import WORKLOADS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mpgemm.h")
+PROBES_HEADER = os.path.join(ROOT, "include", "mpgemm_probes.h")
 
 FAKE_A = 0x7F0000000000   # 256-byte aligned fake device addresses
 FAKE_B = 0x7F1000000000
 FAKE_C = 0x7F2000000000
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mpgemm_\w+)\s*\(", text)))
 
@@ -37,6 +38,15 @@ def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(mp.lib_path())
     missing = [n for n in declared_functions() if not hasattr(lib, n)]
     assert not missing, missing
+
+
+def test_probes_library_exports_its_header_and_the_product_none_of_it():
+    probes = declared_functions(PROBES_HEADER)
+    assert {"mpgemm_probe_mfma_layout", "mpgemm_probe_mfma_rate", "mpgemm_probe_fill"} <= set(probes)
+    lib = mp.load_probes()
+    assert not [n for n in probes if not hasattr(lib, n)]
+    product = ctypes.CDLL(mp.lib_path())
+    assert not [n for n in probes if hasattr(product, n)]
 
 
 def test_version_and_strerror():
@@ -106,7 +116,7 @@ def test_config_table_is_consistent():
         c = mp.mpgemm_config_info(i)
         assert c["id"] == i
         kinds.add(c["kind_name"])
-        if c["kind_name"] in ("tiled", "pipe"):
+        if c["kind_name"] == "pipe":
             assert (c["mfma_m"], c["mfma_n"], c["mfma_k"]) in ((32, 32, 16), (16, 16, 32))
             assert c["bm"] % (c["mfma_m"] * c["waves_m"]) == 0 and c["bn"] % (c["mfma_n"] * c["waves_n"]) == 0
             assert c["bk"] % c["mfma_k"] == 0
@@ -114,8 +124,8 @@ def test_config_table_is_consistent():
             assert c["threads"] == 64 * c["waves_m"] * c["waves_n"] * c["k_groups"]
             assert c["lds_bytes"] == c["stages"] * (c["bm"] + c["bn"]) * c["bk"] * 2
             assert c["lds_bytes"] <= 160 * 1024
-            assert c["vec_a"] in (1, 8) and c["vec_b"] in (1, 8)
-    assert {"tiled", "pipe", "direct", "scale"} <= kinds
+            assert (c["vec_a"], c["vec_b"]) == (8, 8)
+    assert kinds == {"pipe", "direct", "scale", "narrow"}
     with pytest.raises(mp.MpgemmError):
         mp.mpgemm_config_info(n)
 
@@ -228,7 +238,8 @@ def test_layout_validation_codes(args, kw, expect):
 def test_layout_launch_validates_before_hip():
     rc = mp.mpgemm_f16f32_layout(3, 0, 4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4, 1.0, 0.0, 0)
     assert rc == mp.MPGEMM_ELAYOUT
-    rc = mp.mpgemm_f16f32_layout_with_config(32, 1, 0, 4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4,
+    rowmajor_id = q(8192, 8192, 8192)["id"]
+    rc = mp.mpgemm_f16f32_layout_with_config(rowmajor_id, 1, 0, 4, 4, 4, FAKE_A, 4, FAKE_B, 4, FAKE_C, 4,
                                              1.0, 0.0, 0)
     assert rc == mp.MPGEMM_ECONFIG  # a row-major entry asked to read a column-major A
 
@@ -238,8 +249,6 @@ def test_every_layout_pair_has_pipelined_entries():
     for i in range(mp.mpgemm_num_configs()):
         c = mp.mpgemm_config_info(i)
         assert c["layout_a"] in (0, 1) and c["layout_b"] in (0, 1)
-        if c["kind_name"] == "tiled":
-            assert (c["layout_a"], c["layout_b"]) == (0, 0)
         if c["kind_name"] == "pipe":
             pairs.setdefault((c["layout_a"], c["layout_b"]), set()).add((c["bm"], c["bn"]))
     for pair in [(0, 0), (0, 1), (1, 0), (1, 1)]:
@@ -389,6 +398,31 @@ def test_mfma_rate_probe_rejects_bad_arguments_before_launch():
     assert call(workgroups=65536) == mp.MPGEMM_EDIM
 
 
+def test_fill_probe_rejects_bad_arguments_before_launch():
+    names = ("mode", "depth", "buf", "buf_bytes", "footprint", "shared", "replicas", "passes", "workgroups",
+             "sink", "sink_len", "stream")
+    ok = dict(zip(names, (mp.MPGEMM_FILL_LDS16, 8, FAKE_A, 8 << 20, 1 << 20, 0, 1, 4, 256, FAKE_C,
+                          256 * 512, 0)))
+
+    def call(**kw):
+        args = dict(ok)
+        args.update(kw)
+        return mp.mpgemm_probe_fill(*(args[n] for n in names))
+
+    assert call(mode=3) == mp.MPGEMM_ECONFIG
+    assert call(depth=3) == mp.MPGEMM_ECONFIG
+    assert call(buf=0) == mp.MPGEMM_ENULL
+    assert call(sink=0) == mp.MPGEMM_ENULL
+    assert call(buf=FAKE_A + 8) == mp.MPGEMM_EALIGN
+    assert call(workgroups=252) == mp.MPGEMM_EDIM          # not a multiple of 8
+    assert call(replicas=3) == mp.MPGEMM_EDIM              # does not divide 32 per XCD
+    assert call(footprint=(1 << 20) + 1024) == mp.MPGEMM_EDIM
+    assert call(footprint=2 << 20) == mp.MPGEMM_EDIM       # 8 distinct regions exceed the buffer
+    assert call(buf_bytes=1 << 31, footprint=1 << 20) == mp.MPGEMM_EDIM
+    assert call(passes=0) == mp.MPGEMM_EDIM
+    assert call(sink_len=256 * 512 - 1) == mp.MPGEMM_EDIM
+
+
 def test_factory_gives_narrow_products_the_narrow_kernel():
     """N <= 16 with A row-major takes the narrow kernel of the call's input
     format and B storage order, one workgroup per 16 rows; N = 17, a
@@ -408,3 +442,121 @@ def test_factory_gives_narrow_products_the_narrow_kernel():
     assert ql(0, 0, 1000, 16, 617, lda=1 << 27)["kind_name"] == "direct"
     assert ql(0, 0, 0, 16, 617)["kind_name"] == "none"
     assert ql(0, 0, 1000, 16, 0)["kind_name"] == "scale"
+
+
+def test_product_table_holds_what_the_factory_can_choose():
+    """Every table entry except the scale-only one is the factory's choice
+    for some call (the direct kernels by huge strides, the tile entries by
+    shape, the narrow ones by N <= 16), so nothing in the product library is
+    unreachable."""
+    chosen = set()
+    for in_type in (0, 1):
+        for la in (0, 1):
+            for lb in (0, 1):
+                f = mp.mpgemm_bf16f32_layout_query if in_type else mp.mpgemm_f16f32_layout_query
+                for M, N, K in [(8192, 8192, 8192), (2048, 2048, 2048), (32768, 128, 4096), (256, 256, 256),
+                                (256, 256, 64), (1000, 16, 617), (300, 300, 64)]:
+                    lda = M if la else K
+                    ldb = K if lb else N
+                    chosen.add(f(la, lb, M, N, K, FAKE_A, lda, FAKE_B, ldb, FAKE_C, N, 1.0, 0.0)["id"])
+                chosen.add(f(la, lb, 300, 300, 64, FAKE_A, 1 << 30, FAKE_B, 1 << 30, FAKE_C, 300, 1.0, 0.0)["id"])
+    chosen.add(q(64, 64, 0)["id"])
+    assert chosen == set(range(mp.mpgemm_num_configs()))
+
+
+def test_candidates_library_extends_the_product_table():
+    """The candidates build (tile sweeps) holds the product entries with the
+    same ids and fields, then the sweep-only shapes."""
+    path = mp.CANDIDATES_PATH
+    if not os.path.exists(path):
+        pytest.skip("candidates library not built (python -m dense_mixed_precision_amd.build --candidates)")
+    lib = ctypes.CDLL(path)
+    lib.mpgemm_num_configs.restype = ctypes.c_int
+    lib.mpgemm_config_info.argtypes = [ctypes.c_int, ctypes.POINTER(mp._binding.MpgemmConfig)]
+    n = lib.mpgemm_num_configs()
+    assert n > mp.mpgemm_num_configs()
+    for i in range(n):
+        out = mp._binding.MpgemmConfig()
+        assert lib.mpgemm_config_info(i, ctypes.byref(out)) == 0
+        d = mp._binding._cfg_dict(out)
+        if i < mp.mpgemm_num_configs():
+            assert d == mp.mpgemm_config_info(i)
+        else:
+            assert d["id"] == i and d["kind_name"] in ("pipe", "narrow")
+
+
+# ----------------------------------------------------------------------------
+# The tensor binding refuses what the library would misread
+# ----------------------------------------------------------------------------
+
+@pytest.fixture
+def fake_cuda(monkeypatch):
+    """Host tensors pass the binding's is-on-the-GPU checks (there is no GPU
+    here), except those tagged ``_host_for_test``; nothing reaches the GPU
+    because the library entry points are replaced in each test."""
+    import torch
+    monkeypatch.setattr(torch.Tensor, "is_cuda", property(lambda t: not getattr(t, "_host_for_test", False)))
+
+
+def test_binding_refuses_overlapping_rows(fake_cuda):
+    import torch
+    from dense_mixed_precision_amd import _binding as b
+
+    ok = torch.zeros(8, 16, dtype=torch.float32)
+    assert b._check_tensor(ok, "C", torch.float32) == (0, 16)
+    # a broadcast C: every row is the same 16 floats
+    bcast = torch.zeros(1, 16).expand(4096, 16)
+    with pytest.raises(ValueError, match="overlap"):
+        b._check_tensor(bcast, "C", torch.float32)
+    # overlapping rows of A (stride 4 < 16 columns) and a broadcast column
+    over = torch.as_strided(torch.zeros(64, dtype=torch.float16), (8, 16), (4, 1))
+    with pytest.raises(ValueError, match="overlap"):
+        b._check_tensor(over, "A", torch.float16, allow_col_major=True)
+    col = torch.zeros(1, dtype=torch.float16).expand(8, 1)
+    with pytest.raises(ValueError, match="overlap"):
+        b._check_tensor(col, "B", torch.float16, allow_col_major=True)
+    # column-major views: overlapping columns refused, a padded one accepted
+    over_t = torch.as_strided(torch.zeros(64, dtype=torch.float16), (16, 8), (1, 4))
+    with pytest.raises(ValueError, match="overlap"):
+        b._check_tensor(over_t, "A", torch.float16, allow_col_major=True)
+    padded_t = torch.zeros(8, 20, dtype=torch.float16)[:, :16].t()
+    assert b._check_tensor(padded_t, "A", torch.float16, allow_col_major=True) == (1, 20)
+
+
+def test_binding_refuses_overlaps_before_the_c_abi(fake_cuda, monkeypatch):
+    """gemm() with an expanded C raises before any library call."""
+    import torch
+    from dense_mixed_precision_amd import _binding as b
+
+    called = []
+    monkeypatch.setattr(b, "mpgemm_f16f32", lambda *a: called.append(a) or 0)
+    A = torch.zeros(4096, 8, dtype=torch.float16)
+    B = torch.zeros(8, 16, dtype=torch.float16)
+    C = torch.zeros(1, 16).expand(4096, 16)
+    with pytest.raises(ValueError, match="overlap"):
+        b.gemm(A, B, C, stream=0)
+    assert not called
+
+
+def test_splitk_binding_checks_the_workspace(fake_cuda, monkeypatch):
+    import torch
+    from dense_mixed_precision_amd import _binding as b
+
+    called = []
+    monkeypatch.setattr(b, "mpgemm_gemm_splitk", lambda *a: called.append(a) or 0)
+    monkeypatch.setattr(b, "mpgemm_splitk_plan", lambda *a: {"splits": 4, "workspace_bytes": 4096,
+                                                                "config_id": 3})
+    A = torch.zeros(64, 256, dtype=torch.float16)
+    B = torch.zeros(256, 16, dtype=torch.float16)
+    C = torch.zeros(64, 16)
+    host = torch.zeros(1024)
+    host._host_for_test = True
+    with pytest.raises(TypeError, match="GPU"):
+        b.gemm_splitk(A, B, C, workspace=host, stream=0)
+    with pytest.raises(TypeError, match="float32"):
+        b.gemm_splitk(A, B, C, workspace=torch.zeros(2048, dtype=torch.float16), stream=0)
+    with pytest.raises(ValueError, match="contiguous"):
+        b.gemm_splitk(A, B, C, workspace=torch.zeros(2048)[::2], stream=0)
+    assert not called
+    b.gemm_splitk(A, B, C, workspace=torch.zeros(1024), stream=0)
+    assert len(called) == 1

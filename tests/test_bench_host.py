@@ -29,18 +29,41 @@ def test_secondary_warmup_is_about_40ms_of_gpu_time():
 
 
 def test_measured_traffic_follows_the_kernel_source_digest(tmp_path, monkeypatch):
-    """HBM bytes come from a committed counter summary only while the kernel
-    sources it was taken on are unchanged."""
+    """L2-miss bytes come from a committed counter summary only while the
+    kernel sources it was taken on are unchanged."""
     digest = bench.kernel_source_digest()
     prof = tmp_path / "profiles"
     prof.mkdir()
-    text = ("# HBM traffic\nkernel_source_digest: {d}\nhbm_read_bytes_per_launch: 3000\n"
-            "hbm_write_bytes_per_launch: 1000\n")
-    (prof / "hbm_traffic_square2048.txt").write_text(text.format(d=digest))
+    text = ("# L2-miss bytes\nkernel_source_digest: {d}\nl2_miss_read_bytes_per_launch: 3000\n"
+            "l2_miss_write_bytes_per_launch: 1000\n")
+    (prof / "l2_miss_bytes_square2048.txt").write_text(text.format(d=digest))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_digest", lambda: digest)
     t = bench.measured_traffic("square2048", 0.001)
     assert t["bytes_per_launch"] == 4000 and t["GBps"] == 4.0
-    (prof / "hbm_traffic_square2048.txt").write_text(text.format(d="0" * 16))
+    roof = bench.with_traffic(bench.roofline_entry(WORKLOADS["square2048"], 0.025), t)
+    assert roof["traffic"] == 4000 and roof["traffic_detail"]["read_bytes"] == 3000
+    (prof / "l2_miss_bytes_square2048.txt").write_text(text.format(d="0" * 16))
     assert bench.measured_traffic("square2048", 0.001) is None
     assert bench.measured_traffic("square8192", 0.001) is None
+    assert bench.with_traffic({"bound": "mfma"}, None)["traffic"] is None
+
+
+def test_spread_reports_median_and_cv():
+    s = bench.spread([0.010, 0.012, 0.011, 0.011])
+    assert s["median_us"] == 11.0 and s["n"] == 4
+    assert abs(s["cv"] - (0.0007071 / 0.011)) < 1e-3
+    assert bench.spread([0.02])["cv"] == 0.0
+
+
+def test_attainable_bound_uses_the_slower_of_fill_and_hit():
+    w = WORKLOADS["square2048"]
+    fill = {"best_fill_GBps": 393.216, "best_hit_GBps": 3355.4432}   # 384 KiB in 1 us, 2 MiB in 0.625 us
+    a = bench.attainable_2048(w, fill, 6.0)
+    assert abs(a["fill_us_per_k_tile"] - 1.0) < 1e-3 and abs(a["hit_us_per_k_tile"] - 0.625) < 1e-3
+    assert abs(a["bound_us"] - 21.0) < 1e-2
+    assert abs(a["tflops"] - w.flop / 21e-6 / 1e12) < 0.1
+
+
+def test_cpu_model_is_reported():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()

@@ -59,7 +59,7 @@ def test_bench_variant_sampled_and_freivalds(name, la, lb, fmt, with_bias):
     rows, cols = tile_samples(w.M, w.N, tile=128, per_tile=1, seed=w.seed + la + 2 * lb)
     ref, absdot = oracle.gemm_entries(bits(stored(A, la)), bits(stored(B, lb)), None, w.alpha, w.beta, rows,
                                       cols, layout_a=la, layout_b=lb, in_type=fmt, bias=bias)
-    assert_close(label, got[rows, cols], ref, absdot, rows, cols)
+    assert_close(label, got[rows, cols], ref, absdot, rows, cols, K=w.K, alpha=w.alpha)
     ok, ratio = freivalds(got, A, B, w.alpha, bias, seed=w.seed)
     print(f"[{label}] {rows.size} sampled entries ok; Freivalds worst ratio {ratio:.3g}", flush=True)
     assert ok, f"{label}: Freivalds check failed (worst err/bound {ratio:.3g})"

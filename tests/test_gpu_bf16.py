@@ -29,7 +29,7 @@ def oracle_bf16(A, B, C0, alpha, beta, la, lb):
 def full_check(label, A, B, C0, alpha, beta, la, lb, **kw):
     got, gC = run_layout(A, B, C0, alpha, beta, la, lb, **kw)
     ref, absdot = oracle_bf16(A, B, C0, alpha, beta, la, lb)
-    assert_close(label, got, ref, absdot)
+    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha)
     assert gC.untouched_outside_window(), f"{label}: wrote outside the M x N window"
 
 
@@ -93,6 +93,6 @@ def test_2048_sampled_and_freivalds():
     assert np.all(np.isfinite(got))
     rows, cols = tile_samples(M, N, tile=128, per_tile=1, seed=9)
     ref, absdot = oracle.gemm_entries(bits(A), bits(B), None, 1.0, 0.0, rows, cols, in_type="bf16")
-    assert_close("2048 bf16", got[rows, cols], ref, absdot, rows, cols)
+    assert_close("2048 bf16", got[rows, cols], ref, absdot, rows, cols, K=K, alpha=1.0)
     ok, ratio = freivalds_ok(got, A.float(), B.float(), None, 1.0, 0.0, seed=9)
     assert ok, f"Freivalds failed (worst {ratio:.3g})"

@@ -4,8 +4,8 @@ away"), through mpgemm_gemm_ex against the oracle's biased product:
 
     C[i][j] <- alpha * sum_k A[i][k] B[k][j] + beta * C[i][j] + bias[j]
 
-Every kernel kind adds the bias: the pipelined kernels, the register-staged
-tiled kernels, the direct fallback and the scale-only path (alpha == 0 or
+Every kernel kind adds the bias: the pipelined kernels, the narrow kernel,
+the direct fallback and the scale-only path (alpha == 0 or
 K == 0).  Acceptance: |C_gpu - C_ref| <= 1e-3 * sum_k |a_ik b_kj| + 1e-5;
 the bias (|bias| <= 2 here) is added once in FP32, a rounding of at most
 2^-24 of the result, far inside the absolute term.
@@ -32,7 +32,7 @@ def check(label, A, B, C0, alpha, beta, la, lb, bias, **kw):
     ref, absdot = oracle.gemm(bits(stored(A, la)), bits(stored(B, lb)),
                               None if C0 is None else C0.numpy(), alpha, beta,
                               layout_a=la, layout_b=lb, in_type=in_type, bias=bias)
-    assert_close(label, got, ref, absdot)
+    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha)
     assert gC.untouched_outside_window(), f"{label}: wrote outside the M x N window"
 
 

@@ -29,7 +29,7 @@ def test_gate_shape_every_element(name, M, N, K, dist):
     for alpha, beta, c0 in ((1.0, 0.0, None), (1.5, 0.5, C)):
         got, gC = run(A, B, c0, alpha, beta)
         ref, absdot = oracle.gemm(bits(A), bits(B), None if c0 is None else c0.numpy(), alpha, beta)
-        assert_close(f"{name} alpha={alpha} beta={beta}", got, ref, absdot)
+        assert_close(f"{name} alpha={alpha} beta={beta}", got, ref, absdot, K=K, alpha=alpha)
         assert gC.untouched_outside_window()
 
 
@@ -42,6 +42,6 @@ def test_gate_shape_4096_sampled_and_freivalds():
         assert np.all(np.isfinite(got))
         ref, absdot = oracle.gemm_entries(bits(A), bits(B), None if c0 is None else c0.numpy(), alpha, beta,
                                           rows, cols)
-        assert_close(f"4096 beta={beta}", got[rows, cols], ref, absdot, rows, cols)
+        assert_close(f"4096 beta={beta}", got[rows, cols], ref, absdot, rows, cols, K=K, alpha=alpha)
         ok, ratio = freivalds_ok(got, A, B, c0, alpha, beta, seed=4096)
         assert ok, f"4096 beta={beta}: Freivalds failed (worst {ratio:.3g})"

@@ -57,14 +57,14 @@ def test_output_past_2_31_elements():
     assert bool(torch.isfinite(C).all()), "non-finite output"
     assert bool(torch.isnan(flat.view(M, ldc)[:, N:]).all()), "wrote between N and ldc"
     got = C[ri, ci].cpu().numpy()
-    assert_close("large C beta=0", got, ref, absdot, rows, cols)
+    assert_close("large C beta=0", got, ref, absdot, rows, cols, K=K, alpha=1.5)
 
     # beta = 0.5 on a constant C: the reference is alpha*AB + 0.5*0.25
     C.fill_(0.25)
     mp.gemm(Ad, Bd, C, 1.5, 0.5)
     torch.cuda.synchronize()
     got = C[ri, ci].cpu().numpy()
-    assert_close("large C beta=.5", got, ref + 0.125, absdot, rows, cols)
+    assert_close("large C beta=.5", got, ref + 0.125, absdot, rows, cols, K=K, alpha=1.5)
     del flat, C
     torch.cuda.empty_cache()
 
@@ -97,7 +97,7 @@ def test_stage_span_past_32_bit_offsets_takes_the_direct_kernel(which):
     mp.gemm(Ad, Bd, Cd, 1.5, 0.5)
     torch.cuda.synchronize()
     ref, absdot = oracle.gemm(bits(A), bits(B), C.numpy(), 1.5, 0.5)
-    assert_close(f"huge ld{which.lower()}", Cd.cpu().numpy(), ref, absdot)
+    assert_close(f"huge ld{which.lower()}", Cd.cpu().numpy(), ref, absdot, K=K, alpha=1.5)
     torch.cuda.empty_cache()
 
 

@@ -28,7 +28,7 @@ def oracle_layout(A, B, C0, alpha, beta, la, lb):
 def full_check(label, A, B, C0, alpha, beta, la, lb, **kw):
     got, gC = run_layout(A, B, C0, alpha, beta, la, lb, **kw)
     ref, absdot = oracle_layout(A, B, C0, alpha, beta, la, lb)
-    assert_close(label, got, ref, absdot)
+    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha)
     assert gC.untouched_outside_window(), f"{label}: wrote outside the M x N window"
     return got
 
@@ -104,7 +104,10 @@ def test_misaligned_and_odd_leading_dimensions(la, lb):
 def test_direct_kernel_any_layout(la, lb):
     M, N, K = 97, 70, 45
     A, B, C = make_inputs(M, N, K, "uniform", seed=51 + la + 2 * lb, c_init="uniform")
-    full_check(f"direct {la}{lb}", A, B, C, 0.5, 1.5, la, lb, config=12)
+    direct = [i for i in range(mp.mpgemm_num_configs())
+              if mp.mpgemm_config_info(i)["kind_name"] == "direct"
+              and mp.mpgemm_config_info(i)["in_type"] == mp.MPGEMM_IN_F16]
+    full_check(f"direct {la}{lb}", A, B, C, 0.5, 1.5, la, lb, config=direct[0])
 
 
 def test_same_tile_shape_is_bitwise_identical_across_layouts():
@@ -139,6 +142,6 @@ def test_2048_sampled_and_freivalds(la, lb):
     rows, cols = tile_samples(M, N, tile=128, per_tile=1, seed=5)
     ref, absdot = oracle.gemm_entries(bits(stored(A, la)), bits(stored(B, lb)), None, 1.0, 0.0,
                                       rows, cols, layout_a=la, layout_b=lb)
-    assert_close(f"2048 {la}{lb}", got[rows, cols], ref, absdot, rows, cols)
+    assert_close(f"2048 {la}{lb}", got[rows, cols], ref, absdot, rows, cols, K=K, alpha=1.0)
     ok, ratio = freivalds_ok(got, A, B, None, 1.0, 0.0, seed=5)
     assert ok, f"Freivalds failed (worst {ratio:.3g})"

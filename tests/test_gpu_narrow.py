@@ -7,7 +7,9 @@ depth) on ragged M, N from 1 to 16, K below 8 (the tail alone), K with and
 without a tail, K spanning many k-steps per wave and fewer k-steps than
 waves; operands padded past their rows with a NaN pattern; exact small
 integers bit for bit, uniform inputs with beta != 0 within tolerance; a
-bias; and the entry refusing N > 16 or a column-major A.
+bias; and the entry refusing N > 16 or a column-major A.  A one-column B
+stored column-major (which the tensor binding sees as row-major) goes
+through the C ABI directly.
 """
 import numpy as np
 import pytest
@@ -16,7 +18,7 @@ import torch
 import dense_mixed_precision_amd as mp
 import oracle
 from dense_mixed_precision_amd.workloads import bits, make_inputs
-from tests.gpu_util import assert_close, device, run_layout, stored
+from tests.gpu_util import Guarded, assert_close, device, run_layout, stored
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +31,30 @@ SHAPES = [(16, 16, 32), (17, 1, 5), (33, 7, 1), (255, 16, 64), (513, 9, 1031), (
           (1000, 16, 616), (4096, 16, 4096), (40, 16, 8200)]
 
 
+def run_abi(A, B, C0, alpha, beta, la, lb, config, lda, ldb, ldc=None):
+    """Like run_layout, through mpgemm_gemm_ex_with_config with raw device
+    pointers: A row-major, B stored in order `lb`, guarded buffers."""
+    assert la == 0
+    M, K = A.shape
+    N = B.shape[1]
+    gA = Guarded(A, ld=lda)
+    gB = Guarded(stored(B, lb), ld=ldb)
+    if C0 is None:
+        gC = Guarded(torch.zeros((M, N), dtype=torch.float32), ld=ldc, fill=float("nan"))
+    else:
+        gC = Guarded(C0, ld=ldc)
+    in_type = mp.MPGEMM_IN_BF16 if A.dtype == torch.bfloat16 else mp.MPGEMM_IN_F16
+
+    def ptr(g):
+        return g.flat.data_ptr() + g.start * g.flat.element_size()
+
+    rc = mp.mpgemm_gemm_ex_with_config(config, in_type, 0, lb, M, N, K, ptr(gA), gA.ld, ptr(gB), gB.ld, ptr(gC),
+                                       gC.ld, alpha, beta, 0, torch.cuda.current_stream().cuda_stream)
+    assert rc == mp.MPGEMM_OK, mp.mpgemm_strerror(rc)
+    torch.cuda.synchronize()
+    return gC.result(), gC
+
+
 def _ref(A, B, C0, alpha, beta, lb, fmt, bias=None):
     return oracle.gemm(bits(A), bits(stored(B, lb)), None if C0 is None else C0.numpy(), alpha, beta,
                        layout_b=lb, in_type=fmt, bias=bias)
@@ -39,20 +65,22 @@ def _ref(A, B, C0, alpha, beta, lb, fmt, bias=None):
 def test_narrow_config(cfg, M, N, K):
     c = mp.mpgemm_config_info(cfg)
     lb = c["layout_b"]
-    if lb and N == 1:
-        pytest.skip("a one-column B is row-major to the binding (either order describes the same bytes)")
+    # A one-column B describes the same bytes in either storage order, and
+    # the tensor binding passes it as row-major; the column-major entries
+    # are called through the C ABI directly for it.
+    runner = run_abi if (lb and N == 1) else run_layout
     fmt = "bf16" if c["in_type"] == mp.MPGEMM_IN_BF16 else "f16"
     dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
     lda, ldb = K + 3, (K if lb else N) + 5
     A, B, _ = make_inputs(M, N, K, "smallint", seed=cfg * 13 + M + N + K, dtype=dtype)
-    got, gC = run_layout(A, B, None, 1.0, 0.0, 0, lb, config=cfg, lda=lda, ldb=ldb)
+    got, gC = runner(A, B, None, 1.0, 0.0, 0, lb, config=cfg, lda=lda, ldb=ldb)
     ref, _ = _ref(A, B, None, 1.0, 0.0, lb, fmt)
     assert np.array_equal(got, ref.astype(np.float32)), f"config {cfg} {M}x{N}x{K}: not bitwise"
     assert gC.untouched_outside_window()
     A, B, C = make_inputs(M, N, K, "uniform", seed=cfg * 17 + M + N + K, c_init="uniform", dtype=dtype)
-    got, gC = run_layout(A, B, C, 1.5, 0.5, 0, lb, config=cfg, lda=lda, ldb=ldb, ldc=N + 2)
+    got, gC = runner(A, B, C, 1.5, 0.5, 0, lb, config=cfg, lda=lda, ldb=ldb, ldc=N + 2)
     ref, absdot = _ref(A, B, C, 1.5, 0.5, lb, fmt)
-    assert_close(f"config {cfg} {M}x{N}x{K} beta=.5", got, ref, absdot)
+    assert_close(f"config {cfg} {M}x{N}x{K} beta=.5", got, ref, absdot, K=K, alpha=1.5)
     assert gC.untouched_outside_window()
 
 
@@ -67,7 +95,7 @@ def test_narrow_bias_and_scale(cfg):
     bias = np.linspace(-1.0, 1.0, N).astype(np.float32)
     got, _ = run_layout(A, B, C, 0.75, -1.25, 0, lb, config=cfg, bias=bias)
     ref, absdot = _ref(A, B, C, 0.75, -1.25, lb, fmt, bias=bias)
-    assert_close(f"config {cfg} bias", got, ref, absdot)
+    assert_close(f"config {cfg} bias", got, ref, absdot, K=K, alpha=0.75)
 
 
 def test_narrow_entries_refuse_what_they_cannot_run():

@@ -48,4 +48,5 @@ def test_nonfinite_pattern_matches_the_oracle(cfg):
     assert np.isnan(ref[5]).all() and np.isnan(ref[130, 7]) and np.isnan(ref[M - 1, N - 1])
     fin = np.isfinite(ref)
     assert oracle.tolerance_ok(got[fin], ref[fin], absdot[fin]).all(), f"{label}: finite entries out of tolerance"
+    assert oracle.accumulation_ratio(got[fin], ref[fin], absdot[fin], K, 1.0) <= 1.0
     assert gC.untouched_outside_window()

@@ -1,9 +1,11 @@
 """GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
 
 Acceptance (elementwise): |C_gpu - C_ref| <= 1e-3 * sum_k |a_ik b_kj| + 1e-5,
-NaN/Inf fail.  Small and ragged products are compared on every element; the
-large workloads on sampled entries (at least one in every 128x128 block, the
-last row and column, the corners) plus Freivalds' whole-output check.
+NaN/Inf fail, and the accumulation diagnostic at most 1.  Small and ragged
+products are compared on every element here; the large workloads on every
+element or whole tiles in test_gpu_fullsize.py, and here also on sampled
+entries (one in every 128x128 block, the last row and column, the corners)
+plus Freivalds' whole-output check.
 Exact-integer, all-ones and identity inputs must match bit for bit.
 """
 import numpy as np
@@ -13,7 +15,7 @@ import torch
 import dense_mixed_precision_amd as mp
 import oracle
 from dense_mixed_precision_amd.workloads import WORKLOADS, bits, make_inputs, workload_inputs
-from tests.gpu_util import (Guarded, assert_close, device, freivalds_ok, run, tile_samples)
+from tests.gpu_util import (Guarded, assert_close, device, freivalds_ok, run, run_layout, tile_samples)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +27,7 @@ def _c_np(C):
 def full_check(label, A, B, C0, alpha, beta, **kw):
     got, gC = run(A, B, C0, alpha, beta, **kw)
     ref, absdot = oracle.gemm(bits(A), bits(B), _c_np(C0), alpha, beta)
-    assert_close(label, got, ref, absdot)
+    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha)
     assert gC.untouched_outside_window(), f"{label}: wrote outside the M x N window"
     return got, ref
 
@@ -79,7 +81,7 @@ def test_workload_every_element(name):
     full_check(name, A, B, C, w.alpha, w.beta)
 
 
-@pytest.mark.parametrize("name", ["square2048", "tallskinny32768x128x4096", "square8192"])
+@pytest.mark.parametrize("name", ["square2048", "tallskinny32768x128x4096"])
 def test_workload_sampled_and_freivalds(name):
     w = WORKLOADS[name]
     print(f"[{name}] generating inputs", flush=True)
@@ -88,7 +90,7 @@ def test_workload_sampled_and_freivalds(name):
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
     rows, cols = tile_samples(w.M, w.N, tile=128, per_tile=1, seed=w.seed)
     ref, absdot = oracle.gemm_entries(bits(A), bits(B), _c_np(C), w.alpha, w.beta, rows, cols)
-    assert_close(name, got[rows, cols], ref, absdot, rows, cols)
+    assert_close(name, got[rows, cols], ref, absdot, rows, cols, K=w.K, alpha=w.alpha)
     ok, ratio = freivalds_ok(got, A, B, C, w.alpha, w.beta, seed=w.seed)
     print(f"[{name}] {rows.size} sampled entries ok; Freivalds worst ratio {ratio:.3g}", flush=True)
     assert ok, f"{name}: Freivalds check failed (worst err/bound {ratio:.3g})"
@@ -114,18 +116,18 @@ def test_edge_shapes_factory(M, N, K):
     full_check(f"{M}x{N}x{K} beta=.5", A, B, C, 1.5, 0.5)
 
 
-def _tiled_and_direct_ids():
+def _pipe_and_direct_ids():
     ids = []
     for i in range(mp.mpgemm_num_configs()):
         c = mp.mpgemm_config_info(i)
         # row-major entries; the column-major ones have their own tests
-        if (c["kind_name"] in ("tiled", "pipe", "direct") and (c["layout_a"], c["layout_b"]) == (0, 0)
+        if (c["kind_name"] in ("pipe", "direct") and (c["layout_a"], c["layout_b"]) == (0, 0)
                 and c["in_type"] == mp.MPGEMM_IN_F16):
             ids.append(i)
     return ids
 
 
-@pytest.mark.parametrize("cfg", _tiled_and_direct_ids())
+@pytest.mark.parametrize("cfg", _pipe_and_direct_ids())
 def test_every_config_on_ragged_strided_input(cfg):
     """M, N, K fit no tile; lda/ldb are multiples of 8 (so the 16-byte load
     variants apply) but K % 8 and N % 8 leave partial vectors at the edges;
@@ -136,7 +138,7 @@ def test_every_config_on_ragged_strided_input(cfg):
     full_check(f"config {cfg} beta=0", A, B, None, 1.0, 0.0, config=cfg, lda=112, ldb=160, ldc=149)
 
 
-@pytest.mark.parametrize("cfg", _tiled_and_direct_ids())
+@pytest.mark.parametrize("cfg", _pipe_and_direct_ids())
 def test_every_config_multi_tile(cfg):
     """Several tiles of every size in both directions and a K loop longer
     than the LDS ring, with exact small integers: must match bit for bit."""
@@ -148,8 +150,8 @@ def test_every_config_multi_tile(cfg):
 
 
 def _vector_ids():
-    return [i for i in _tiled_and_direct_ids()
-            if mp.mpgemm_config_info(i)["kind_name"] in ("tiled", "pipe")
+    return [i for i in _pipe_and_direct_ids()
+            if mp.mpgemm_config_info(i)["kind_name"] == "pipe"
             and (mp.mpgemm_config_info(i)["vec_a"], mp.mpgemm_config_info(i)["vec_b"]) == (8, 8)]
 
 
@@ -208,6 +210,45 @@ def test_alpha_zero_and_k_zero_scale_C():
     assert np.all(got == 0)
 
 
+def test_alpha_zero_and_k_zero_do_not_read_A_or_B():
+    """alpha == 0 (or K == 0, whatever alpha is) means A and B are not read:
+    NaN and Inf in them do not reach C, which becomes beta*C (+ bias), as
+    the oracle computes it (the reading both take where the pages are
+    silent), bit for bit.  Through the plain, the bias and the split-K
+    entry points."""
+    M, N, K = 130, 70, 33
+    A, B, C = make_inputs(M, N, K, "uniform", seed=13, c_init="uniform")
+    A, B = A.clone(), B.clone()
+    A[3, 5] = float("nan")
+    A[100, 0] = float("inf")
+    B[7, 69] = float("-inf")
+    B[32, 1] = float("nan")
+    for beta in (0.5, -2.0):
+        ref, absdot = oracle.gemm(bits(A), bits(B), C.numpy(), 0.0, beta)
+        assert np.all(absdot == 0)
+        got, _ = run(A, B, C, 0.0, beta)
+        assert np.array_equal(got, ref.astype(np.float32)), f"beta={beta}: differs from beta*C"
+    bias = np.linspace(-1, 1, N).astype(np.float32)
+    ref, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 0.0, 0.5, bias=bias)
+    got, _ = run_layout(A, B, C, 0.0, 0.5, 0, 0, bias=bias)
+    assert np.array_equal(got, ref.astype(np.float32))
+    # split-K entry point: a product it would split, with alpha == 0
+    Ad, Bd = A.to(device()), B.to(device())
+    Cd = C.to(device())
+    mp.gemm_splitk(Ad, Bd, Cd, 0.0, 0.5, splits=4)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 0.0, 0.5)
+    assert np.array_equal(Cd.cpu().numpy(), ref.astype(np.float32))
+    # K == 0 with a non-finite alpha: C <- beta*C; beta == 0 writes zeros over NaN
+    A0, B0, _ = make_inputs(M, N, 0, "uniform", seed=14)
+    for alpha in (float("inf"), float("nan")):
+        ref, _ = oracle.gemm(bits(A0), bits(B0), C.numpy(), alpha, 0.25)
+        got, _ = run(A0, B0, C, alpha, 0.25)
+        assert np.array_equal(got, ref.astype(np.float32)), alpha
+    got, _ = run(A, B, None, 0.0, 0.0, poison=True)
+    assert np.all(got == 0)
+
+
 def test_nan_poisoned_C_is_not_read_when_beta_is_zero():
     M, N, K = 257, 255, 129
     A, B, _ = make_inputs(M, N, K, "uniform", seed=4)
@@ -255,4 +296,4 @@ def test_an_earlier_runtime_error_is_not_reported_as_this_calls():
         assert rc == mp.MPGEMM_OK, (alpha, mp.mpgemm_strerror(rc))
     torch.cuda.synchronize()
     ref, absdot = oracle.gemm(bits(A), bits(B), (np.float32(0.5) * C.numpy()), 1.0, 0.5)
-    assert_close("after stale errors", Cd.cpu().numpy(), ref, absdot)
+    assert_close("after stale errors", Cd.cpu().numpy(), ref, absdot, K=K, alpha=1.0)

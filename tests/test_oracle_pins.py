@@ -128,6 +128,39 @@ def test_zero_A_and_zero_alpha_give_beta_C():
     assert np.array_equal(ref2, 0.5 * c64)
 
 
+def test_alpha_zero_does_not_read_A_or_B():
+    """alpha == 0: the product term is not formed and A and B are not read
+    (the counterpart of beta == 0 not reading C), so NaN and Inf in A and B
+    do not reach the result: C <- beta*C exactly, sum|ab| reported as 0."""
+    M, N, K = 5, 6, 13
+    A, B, C = make_inputs(M, N, K, "uniform", seed=8, c_init="uniform")
+    A, B = A.clone(), B.clone()
+    A[1, 3] = float("nan")
+    A[2, 0] = float("inf")
+    B[4, 5] = float("-inf")
+    B[0, 2] = float("nan")
+    c64 = C.numpy().astype(np.float64)
+    ref, absdot = oracle.gemm(bits(A), bits(B), C.numpy(), 0.0, 0.5)
+    assert np.array_equal(ref, 0.5 * c64) and np.all(absdot == 0)
+    poison = np.full((M, N), np.nan, dtype=np.float32)
+    ref, _ = oracle.gemm(bits(A), bits(B), poison, 0.0, 0.0)
+    assert np.all(ref == 0)
+    bias = np.linspace(-1, 1, N, dtype=np.float32)
+    ref, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 0.0, -2.0, bias=bias)
+    assert np.array_equal(ref, -2.0 * c64 + bias.astype(np.float64)[None, :])
+    # with alpha != 0 the same inputs do reach the result
+    ref, _ = oracle.gemm(bits(A), bits(B), C.numpy(), 1.0, 0.5)
+    assert np.isnan(ref[1]).all() and np.isnan(ref[:, 2]).all()
+
+
+def test_k_zero_ignores_alpha():
+    """K == 0: no product term, whatever alpha is (Inf or NaN included)."""
+    A, B, C = make_inputs(4, 3, 0, "uniform", seed=9, c_init="uniform")
+    for alpha in (float("inf"), float("nan"), -3.0):
+        ref, absdot = oracle.gemm(bits(A), bits(B), C.numpy(), alpha, 0.25)
+        assert np.array_equal(ref, 0.25 * C.numpy().astype(np.float64)) and np.all(absdot == 0)
+
+
 def test_beta_zero_does_not_read_C():
     """NaN-poisoned C with beta == 0 must not leak into the result."""
     M, N, K = 8, 8, 8
@@ -583,3 +616,54 @@ def test_nonfinite_inputs_follow_ieee():
     fin = np.isfinite(want)
     assert np.allclose(ref[fin], want[fin], rtol=1e-13, atol=1e-15)
     assert np.isnan(ref[1]).all() and np.isnan(ref[0, 3]) and np.isnan(ref[3, 1])
+
+
+# ----------------------------------------------------------------------------
+# The accumulation diagnostic
+# ----------------------------------------------------------------------------
+
+def _running_sum(A_bits, B_bits, acc_dtype):
+    """C = A @ B with exact products (FP16 x FP16 fits FP32) added one k at a
+    time into a running sum rounded to `acc_dtype` after every addition."""
+    a = A_bits.view(np.float16).astype(np.float32)
+    b = B_bits.view(np.float16).astype(np.float32)
+    acc = np.zeros((a.shape[0], b.shape[1]), dtype=acc_dtype)
+    for k in range(a.shape[1]):
+        acc = (acc.astype(np.float32) + a[:, k:k + 1] * b[k:k + 1, :]).astype(acc_dtype)
+    return acc.astype(np.float64)
+
+
+def test_accumulation_diagnostic_separates_fp32_from_fp16_sums():
+    """The pages found that an FP16 accumulator passes the usual checks; the
+    acceptance rule is as blind, but the accumulation diagnostic is not.  An
+    FP32 running sum stays within the bound; an FP16 running sum of the same
+    products passes the acceptance rule on most entries and exceeds the
+    bound by far."""
+    for dist, K, min_pass in (("uniform", 2048, 1.0), ("normal4", 8192, 0.99)):
+        M, N = 8, 32
+        A, B, _ = make_inputs(M, N, K, dist, seed=41)
+        Ab, Bb = bits(A), bits(B)
+        ref, absdot = oracle.gemm(Ab, Bb)
+        fp32 = _running_sum(Ab, Bb, np.float32)
+        assert oracle.tolerance_ok(fp32, ref, absdot).all()
+        assert oracle.accumulation_ratio(fp32, ref, absdot, K, 1.0) <= 0.01
+        fp16 = _running_sum(Ab, Bb, np.float16)
+        assert oracle.tolerance_ok(fp16, ref, absdot).mean() >= min_pass
+        assert oracle.accumulation_ratio(fp16, ref, absdot, K, 1.0) > 2.0
+
+
+def test_accumulation_bound_terms():
+    """Exact results give 0; the bound grows with K, |alpha| and S; NaN in
+    the result counts as unbounded; entries whose reference is not finite
+    are skipped."""
+    ref = np.array([1.0, -2.0, np.inf])
+    absdot = np.array([3.0, 3.0, 3.0])
+    assert oracle.accumulation_ratio(ref, ref, absdot, 100, 1.5) == 0.0
+    b1 = oracle.accumulation_bound(ref[:2], absdot[:2], 100, 1.0)
+    assert np.all(oracle.accumulation_bound(ref[:2], absdot[:2], 200, 1.0) > b1)
+    assert np.all(oracle.accumulation_bound(ref[:2], absdot[:2], 100, -2.0) > b1)
+    got = ref.copy(); got[0] += b1[0] * 0.5
+    assert oracle.accumulation_ratio(got, ref, absdot, 100, 1.0) == pytest.approx(0.5)
+    got[1] = np.nan
+    assert oracle.accumulation_ratio(got, ref, absdot, 100, 1.0) == np.inf
+    assert oracle.accumulation_ratio(np.zeros(2), np.zeros(2), np.zeros(2), 0, 1.0) == 0.0

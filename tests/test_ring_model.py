@@ -12,16 +12,15 @@ This model replays the kernel's schedule for one wave (every wave of a
 workgroup runs the same schedule; a barrier orders everything before it in
 every wave before everything after it) and checks, for every table entry,
 every K-tile count up to a few times the ring depth, with and without a
-register fill on every tile and with and without early K-tail loads:
+register fill of partial vectors on every tile and with and without early
+K-tail loads:
 
-* when a tile is published, every copy of it and every register-fill load
-  for it has completed and all of its copy positions were issued;
+* when a tile is published, every copy of it has completed and all of its
+  copy positions were issued;
 * every operand read of a tile comes after the barrier that published it
   and reads the buffer that tile was copied into;
 * no copy or fill store into a buffer is issued before a barrier that
   follows every read of the tile previously held there;
-* the register-fill slot (two-stage rings with element-wise operands) is
-  stored before it is loaded again;
 * every wait count fits the 6-bit counter.
 
 The per-config quantities (copies per wave, waits per tile, copy window)
@@ -57,14 +56,12 @@ def params(c):
     APW = pw(c["bm"], c["layout_a"] == mp.MPGEMM_ROW_MAJOR)
     BPW = pw(c["bn"], c["layout_b"] == mp.MPGEMM_COL_MAJOR)
     NCOPY = APW + BPW
-    NL = (APW if c["vec_a"] == 8 else 0) + (BPW if c["vec_b"] == 8 else 0)
+    NL = APW + BPW
     if S == 2:
         W = (max(NCOPY, 1) if NCOPY < KSL * FM else KSL * FM)
     else:
         W = KSL * FM
-    return dict(S=S, KSL=KSL, FM=FM, APW=APW, BPW=BPW, NCOPY=NCOPY, NL=NL, W=W,
-                vec_a=c["vec_a"], vec_b=c["vec_b"], roll_a=MI == 16,
-                pipe_fill=S == 2 and (c["vec_a"] != 8 or c["vec_b"] != 8))
+    return dict(S=S, KSL=KSL, FM=FM, APW=APW, BPW=BPW, NCOPY=NCOPY, NL=NL, W=W, roll_a=MI == 16)
 
 
 def wait_count(p, newer):
@@ -90,7 +87,6 @@ def simulate(p, num_k, fill_every, tail_early, wait_slack=0, copy_before_barrier
     buf_tile = [None] * S
     published = set()
     cur = {"t": None, "b": None, "live": False}
-    fra = [None]         # register-fill slot (two-stage rings, element-wise operands)
 
     def wait(n):
         assert 0 <= n < 64, f"vmcnt {n} does not fit 6 bits"
@@ -113,31 +109,20 @@ def simulate(p, num_k, fill_every, tail_early, wait_slack=0, copy_before_barrier
         assert c < NCOPY
         calls[t] += 1
         events.append(("copy", t, b))
-        if (c < APW and p["vec_a"] == 8) or (c >= APW and p["vec_b"] == 8):
-            q.append(("copy", t))
+        q.append(("copy", t))
 
     def copy_slice(pos):
         for c in range(NCOPY):
             if -(-pos * NCOPY // W) <= c < -(-(pos + 1) * NCOPY // W):
                 copy_one(c)
 
-    def fill_load(t):
-        if not p["pipe_fill"] or t >= num_k:
-            return
-        assert fra[0] is None, f"fill slot still holds tile {fra[0]} when tile {t} is loaded"
-        fra[0] = t
-        q.append(("fill", t))
-
     def publish(t, b, newer):
         if fill_every:
             wait(0)
-            if p["pipe_fill"]:
-                assert fra[0] == t, f"fill slot holds {fra[0]}, publishing {t}"
-                fra[0] = None
             events.append(("fillstore", t, b))
         else:
             wait(max(0, wait_count(p, newer) + wait_slack))
-        assert not any(op[0] in ("copy", "fill") and op[1] == t for op in q), f"tile {t} published before it landed"
+        assert not any(op[0] == "copy" and op[1] == t for op in q), f"tile {t} published before it landed"
         assert calls.get(t) == NCOPY, f"tile {t} published with {calls.get(t)} of {NCOPY} copies issued"
         events.append(("barrier",))
         published.add(t)
@@ -154,9 +139,7 @@ def simulate(p, num_k, fill_every, tail_early, wait_slack=0, copy_before_barrier
             begin_copies(t, t)
             for c in range(NCOPY):
                 copy_one(c)
-        fill_load(0)
         publish(0, 0, min(num_k - 1, S - 1))
-        fill_load(1)
         for _ in range(FM):
             read(0, 0)
     buf = 0
@@ -166,13 +149,11 @@ def simulate(p, num_k, fill_every, tail_early, wait_slack=0, copy_before_barrier
             last = ks + 1 == KSL
             if copy_before_barrier and last:
                 begin_copies(kt + S, buf)
-                fill_load(kt + S)
                 copy_slice(0)
             if last and kt + 1 < num_k:
                 publish(kt + 1, nbuf, min(num_k - 2 - kt, S - 2))
             if last and not copy_before_barrier:
                 begin_copies(kt + S, buf)
-                fill_load(kt + S)
             # operand reads of the next k-step (B only when A rolls)
             for _ in range(FM):
                 if not last:
@@ -219,17 +200,16 @@ def _pipe_configs():
 def test_ring_protocol_every_pipe_config(cid):
     p = params(mp.mpgemm_config_info(cid))
     assert p["NL"] * (p["S"] - 1) < 64
-    fills = (False, True) if (p["vec_a"], p["vec_b"]) == (8, 8) else (True,)
     for num_k in range(1, 3 * p["S"] + 4):
-        for fill_every in fills:
+        for fill_every in (False, True):
             for tail in (False, True):
                 simulate(p, num_k, fill_every, tail)
 
 
 def _deep_config():
-    # a three-stage entry with 16-byte copies of both operands
+    # a three-stage entry
     for c in _pipe_configs():
-        if c["stages"] == 3 and (c["vec_a"], c["vec_b"]) == (8, 8):
+        if c["stages"] == 3:
             return params(c)
     raise AssertionError("no three-stage entry")
 
@@ -250,4 +230,4 @@ def test_model_rejects_copies_before_the_barrier():
 def test_model_rejects_a_window_wider_than_the_k_steps():
     p = _deep_config()
     with pytest.raises(AssertionError, match="copy window left|published with|published before it landed"):
-        simulate(p, 8, False, False, window_extra=p["FM"])
+        simulate(p, 8, False, False, window_extra=p["W"])   # twice as wide
