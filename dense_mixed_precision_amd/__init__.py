@@ -20,6 +20,7 @@ integers holding device addresses, ``stream`` a hipStream_t as an integer,
     mpgemm_gemm_ex(in_type, layout_a, layout_b, M, N, K, ..., alpha, beta, bias, stream) -> int
     mpgemm_gemm_ex_with_config(cfg, in_type, layout_a, layout_b, ...) -> int   (per-column bias)
     mpgemm_splitk_plan(...) -> dict, mpgemm_gemm_splitk(..., splits, workspace, bytes, stream) -> int
+    mpgemm_gemm_splitk_static(..., bias, splits, stream) -> int   (no workspace, allocates nothing)
     mpgemm_num_configs(), mpgemm_config_info(id), mpgemm_strerror(code), mpgemm_version()
 Diagnostics (libmpgemm_probes.so):
     mpgemm_probe_mfma_layout(shape, out, stream)
@@ -40,6 +41,8 @@ from ._binding import (  # noqa: F401
     MPGEMM_ELAUNCH,
     MPGEMM_ELAYOUT,
     MPGEMM_ESPLIT,
+    MPGEMM_ESCRATCH,
+    MPGEMM_STATIC_SCRATCH_BYTES,
     MPGEMM_ETYPE,
     MPGEMM_EWORKSPACE,
     MPGEMM_ELD,
@@ -74,6 +77,7 @@ from ._binding import (  # noqa: F401
     mpgemm_gemm_ex_with_config,
     mpgemm_splitk_plan,
     mpgemm_gemm_splitk,
+    mpgemm_gemm_splitk_static,
     gemm_splitk,
     splitk_plan_for,
     mpgemm_num_configs,

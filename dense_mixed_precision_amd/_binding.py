@@ -22,6 +22,9 @@ MPGEMM_ELAYOUT = -7
 MPGEMM_ETYPE = -8
 MPGEMM_EWORKSPACE = -9
 MPGEMM_ESPLIT = -10
+MPGEMM_ESCRATCH = -11
+#: bytes of the static split-K scratch of mpgemm_gemm_splitk_static
+MPGEMM_STATIC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 MPGEMM_ROW_MAJOR = 0
 MPGEMM_COL_MAJOR = 1
@@ -110,6 +113,8 @@ def load(path: str | None = None):
     lib.mpgemm_splitk_plan.restype = i32
     lib.mpgemm_gemm_splitk.argtypes = [i32, i32, i32] + gemm_args + [vp, i32, vp, i64, vp]
     lib.mpgemm_gemm_splitk.restype = i32
+    lib.mpgemm_gemm_splitk_static.argtypes = [i32, i32, i32] + gemm_args + [vp, i32, vp]
+    lib.mpgemm_gemm_splitk_static.restype = i32
     lib.mpgemm_num_configs.argtypes = []
     lib.mpgemm_num_configs.restype = i32
     lib.mpgemm_config_info.argtypes = [i32, ctypes.POINTER(MpgemmConfig)]
@@ -246,6 +251,12 @@ def mpgemm_gemm_splitk(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, 
     return int(load().mpgemm_gemm_splitk(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb, C,
                                          ldc, alpha, beta, bias, splits_requested, workspace,
                                          workspace_bytes, stream))
+
+
+def mpgemm_gemm_splitk_static(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb, C, ldc, alpha,
+                              beta, bias=0, splits_requested=0, stream=0) -> int:
+    return int(load().mpgemm_gemm_splitk_static(in_type, layout_a, layout_b, M, N, K, A, lda, B, ldb, C,
+                                                ldc, alpha, beta, bias, splits_requested, stream))
 
 
 def mpgemm_num_configs() -> int:

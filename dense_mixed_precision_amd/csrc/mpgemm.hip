@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace {
@@ -627,6 +629,50 @@ int with_config_layout(int in_type, int config_id, int la, int lb, int64_t M, in
     return run(config_id, p, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Static split-K scratch for callers that cannot allocate
+// ---------------------------------------------------------------------------
+// The array itself (`scratch`, at file scope below the namespace) exists
+// once per device: the code object is loaded on every device the library
+// runs on, and each holds its own copy until the process ends.  Host code
+// never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr int64_t kScratchBytes = MPGEMM_STATIC_SCRATCH_BYTES;
+int scratch_address(void **out);
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address into *out (looked up on its first
+// use on that device).  MPGEMM_ELAUNCH if the runtime refuses.
+int scratch_for_current_device(float **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return MPGEMM_ELAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (scratch_address(&ptr) != MPGEMM_OK || ptr == nullptr)
+            return MPGEMM_ELAUNCH;
+        g_scratch_ptr[dev] = static_cast<float *>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return MPGEMM_OK;
+}
+
+}  // namespace
+
+// Partial products of mpgemm_gemm_splitk_static (file scope, one per device).
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+namespace {
+// The current device's address of `scratch`.
+int scratch_address(void **out)
+{
+    return hipGetSymbolAddress(out, HIP_SYMBOL(scratch)) == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
+}
 }  // namespace
 
 extern "C" {
@@ -781,6 +827,30 @@ int mpgemm_gemm_splitk(int in_type, int layout_a, int layout_b, int64_t M, int64
     return run_split(sp, p, workspace, stream);
 }
 
+int mpgemm_gemm_splitk_static(int in_type, int layout_a, int layout_b, int64_t M, int64_t N, int64_t K,
+                              const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, float *C,
+                              int64_t ldc, float alpha, float beta, const float *bias,
+                              int splits_requested, void *stream)
+{
+    if (splits_requested < 0)
+        return MPGEMM_ESPLIT;
+    const Problem p = make_problem(M, N, K, A, lda, B, ldb, C, ldc, alpha, beta, layout_a,
+                                   layout_b, in_type, bias);
+    const int rc = validate(p);
+    if (rc != MPGEMM_OK)
+        return rc;
+    const SplitPlan sp = plan_split(p, splits_requested);
+    if (sp.splits <= 1)
+        return run(sp.id, p, stream);
+    if (sp.ws_bytes > kScratchBytes)
+        return MPGEMM_ESCRATCH;
+    float *ws = nullptr;
+    const int src = scratch_for_current_device(&ws);
+    if (src != MPGEMM_OK)
+        return src;
+    return run_split(sp, p, ws, stream);
+}
+
 int mpgemm_num_configs(void) { return kNumEntries; }
 
 int mpgemm_config_info(int config_id, mpgemm_config *out)
@@ -818,6 +888,8 @@ const char *mpgemm_strerror(int code)
         return "the split-K workspace is smaller than mpgemm_splitk_plan reports";
     case MPGEMM_ESPLIT:
         return "a negative split count was requested";
+    case MPGEMM_ESCRATCH:
+        return "the split-K plan needs more than the static scratch (MPGEMM_STATIC_SCRATCH_BYTES)";
     default:
         return "unknown error code";
     }

@@ -61,6 +61,7 @@ extern "C" {
 #define MPGEMM_ETYPE (-8)      /* an input type is not one of MPGEMM_IN_*         */
 #define MPGEMM_EWORKSPACE (-9) /* split-K workspace smaller than planned          */
 #define MPGEMM_ESPLIT (-10)    /* negative split count requested                  */
+#define MPGEMM_ESCRATCH (-11)  /* split-K plan larger than the static scratch     */
 
 /* Storage order of A or B (C is always row-major). */
 #define MPGEMM_ROW_MAJOR 0
@@ -310,6 +311,36 @@ int mpgemm_gemm_splitk(int in_type, int layout_a, int layout_b,
                        int splits_requested,
                        float *workspace, int64_t workspace_bytes,
                        void *stream);
+
+/*
+ * Split-K that allocates nothing, for callers that cannot call hipMalloc
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): mpgemm_gemm_splitk with the partial products in a static
+ * array of MPGEMM_STATIC_SCRATCH_BYTES bytes that the library's code object
+ * holds on each device it is loaded on, until the process ends, instead of
+ * a caller workspace.  The plan is the one mpgemm_splitk_plan reports; a
+ * plan of one piece runs the ordinary path and touches no scratch.  A plan
+ * whose workspace exceeds MPGEMM_STATIC_SCRATCH_BYTES returns
+ * MPGEMM_ESCRATCH before any HIP call; other errors as mpgemm_gemm_splitk.
+ * The scratch is the current device's, so `stream` must belong to the
+ * current device.  Every call on a device shares that device's scratch and
+ * leaves its partial products there (each call writes every partial it then
+ * reads, so nothing needs clearing): calls on one device whose kernels can
+ * overlap in time (different streams without ordering between them) race
+ * on it and give wrong results.  Thread-safe otherwise; the first call on a
+ * device looks up the scratch's address there.
+ */
+#define MPGEMM_STATIC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+int mpgemm_gemm_splitk_static(int in_type, int layout_a, int layout_b,
+                              int64_t M, int64_t N, int64_t K,
+                              const uint16_t *A, int64_t lda,
+                              const uint16_t *B, int64_t ldb,
+                              float *C, int64_t ldc,
+                              float alpha, float beta,
+                              const float *bias,
+                              int splits_requested,
+                              void *stream);
 
 /* Number of entries in the config table. */
 int mpgemm_num_configs(void);

@@ -51,7 +51,7 @@ def test_probes_library_exports_its_header_and_the_product_none_of_it():
 
 def test_version_and_strerror():
     assert "gfx950" in mp.mpgemm_version()
-    for code in range(-10, 1):
+    for code in range(-11, 1):
         assert mp.mpgemm_strerror(code)
     assert mp.mpgemm_strerror(-99) == "unknown error code"
 
@@ -367,6 +367,21 @@ def test_splitk_plan_forced_and_capped():
     with pytest.raises(mp.MpgemmError) as e:
         plan(300, 200, 1234, la=3)
     assert e.value.code == mp.MPGEMM_ELAYOUT
+
+
+def test_static_splitk_refuses_before_hip():
+    """The allocation-free split-K checks its arguments and the plan's size
+    against the static scratch before any HIP call."""
+    args = (0, 0, 0, 256, 16, 65536, FAKE_A, 65536, FAKE_B, 16, FAKE_C, 16, 1.0, 0.0, 0)
+    assert mp.mpgemm_gemm_splitk_static(*args, -1, 0) == mp.MPGEMM_ESPLIT
+    assert mp.mpgemm_gemm_splitk_static(3, *args[1:], 0, 0) == mp.MPGEMM_ETYPE
+    assert mp.mpgemm_gemm_splitk_static(0, 0, 0, 256, 16, 65536, FAKE_A, 65536, FAKE_B, 16, FAKE_C + 2, 16,
+                                        1.0, 0.0, 0, 0, 0) == mp.MPGEMM_EALIGN
+    # 4 pieces of 2048 x 2048: 64 MiB of partial products
+    big = (0, 0, 0, 2048, 2048, 8192, FAKE_A, 8192, FAKE_B, 2048, FAKE_C, 2048, 1.0, 0.0, 0)
+    assert plan(2048, 2048, 8192, splits=4)["workspace_bytes"] > mp.MPGEMM_STATIC_SCRATCH_BYTES
+    assert mp.mpgemm_gemm_splitk_static(*big, 4, 0) == mp.MPGEMM_ESCRATCH
+    assert mp.mpgemm_strerror(mp.MPGEMM_ESCRATCH) != "unknown error code"
 
 
 def test_splitk_launch_checks_the_workspace_before_hip():
