@@ -11,19 +11,16 @@ in the same JSON line.
 
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize() on both sides (wall clock -> ms_per_step), with HIP
-events recorded on the launch stream before the first step and after each
-(-> the average kernel duration used for the roofline, and the median and
-coefficient of variation per step under "timing"); then, outside the timed
-region, the pages' 5 runs x 20 launches (median of the runs, CV across
-them).  FLOP = 2*M*N*K.  Each workload also reports "graph_us": the
+events recorded on the launch stream around the same region (-> the average
+kernel duration used for the roofline); then, outside the timed region, the
+pages' 5 runs x 20 launches ("timing": median of the runs' means and their
+coefficient of variation).  FLOP = 2*M*N*K.  Each workload also reports "graph_us": the
 per-launch time of the same call captured in a HIP graph and replayed, i.e.
 the kernels' own time without the Python call between launches (which bounds
 the eager rate of the smallest products).
 
 For the 2048^3 headline the bench also measures the L2 fill and hit rates
-per XCD with the diagnostics library's fill probe, and derives from them an
-attainable time for that product on its tiling ("attainable"), reported
-next to the spec-peak fraction.
+per XCD with the diagnostics library's fill probe ("fill_rate").
 
 The CPU baseline is the oracle (oracle/, plain C, FP64) timed on a bounded
 sample of the headline workload: a block of whole rows of C, sized to about
@@ -64,7 +61,7 @@ def parse():
                    help="load the candidates build of the library (the product entries plus the "
                         "sweep-only tile shapes; python -m dense_mixed_precision_amd.build --candidates)")
     p.add_argument("--no-fill", dest="fill", action="store_false",
-                   help="skip the L2 fill-rate probe and the attainable bound derived from it")
+                   help="skip the L2 fill-rate probe")
     p.add_argument("--no-others", action="store_true", help="time only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -212,22 +209,21 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
 
     for _ in range(warmup):
         step()
-    # one HIP event before the timed steps and one after each, all on the
-    # launch stream: per-step kernel times for the median and spread
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # HIP events on the launch stream around the timed steps only: an event
+    # recorded between steps costs about 2 us of queue time per 2048^3 step
     torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    events[0].record(stream)
-    for i in range(steps):
+    ev0.record(stream)
+    for _ in range(steps):
         step()
-        events[i + 1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / steps
-    kern_ms = events[0].elapsed_time(events[-1]) / steps
-    per_step = [events[i].elapsed_time(events[i + 1]) for i in range(steps)]
-    out = {"A": A, "B": B, "C": C, "Cd": Cd, "cfg": cfg, "wall_ms": wall_ms, "kernel_ms": kern_ms,
-           "step_stats": spread(per_step)}
+    kern_ms = ev0.elapsed_time(ev1) / steps
+    out = {"A": A, "B": B, "C": C, "Cd": Cd, "cfg": cfg, "wall_ms": wall_ms, "kernel_ms": kern_ms}
     if runs > 0:
         # the pages' method: `runs` runs of `iters` back-to-back launches,
         # each run's mean per launch; the median over runs and their spread
@@ -450,27 +446,6 @@ def fill_rate(torch, mp):
     return out
 
 
-def attainable_2048(w, fill, k128_us):
-    """An attainable time for the 2048^3 product on 128x128 tiles from measured
-    rates: the one-K-tile product (launch, first tile, C write) plus, for each
-    of the other 15 K tiles, the longer of (a) filling the tile's A and B
-    lines into each XCD's L2 (the 32 concurrent tiles of one XCD, an 8x4
-    block, need 1024 rows of A and 512 columns of B: 384 KiB per K tile of
-    128) at the best measured fill rate and (b) serving the 32 tiles' 64 KiB
-    each from L2 at the best measured hit rate.  Bounds the kernel, not the
-    matrix cores: a fraction of the MFMA peak no kernel on this tiling can
-    exceed on this board, reported next to the spec-peak fraction."""
-    KiB = 1024
-    fill_us = 384 * KiB / (fill["best_fill_GBps"] * 1e9) * 1e6
-    hit_us = 32 * 64 * KiB / (fill["best_hit_GBps"] * 1e9) * 1e6
-    per_tile = max(fill_us, hit_us)
-    bound_us = k128_us + 15 * per_tile
-    tflops = w.flop / (bound_us * 1e-6) / 1e12
-    return {"k128_us": round(k128_us, 3), "fill_us_per_k_tile": round(fill_us, 3),
-            "hit_us_per_k_tile": round(hit_us, 3), "bound_us": round(bound_us, 3),
-            "tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_F16_TFLOPS, 4)}
-
-
 def roofline_entry(w, kernel_ms):
     """MFMA bound for the compute-heavy shapes, HBM bound where the
     arithmetic intensity (FLOP per algorithmic byte) is below the ridge."""
@@ -610,22 +585,14 @@ def main():
     traffic = measured_traffic(head.name, res["kernel_ms"])
     line["roofline"]["traffic"] = traffic["bytes_per_launch"] if traffic else None
     line["roofline"]["traffic_detail"] = traffic
-    line["timing"] = {"steps": res["step_stats"], "runs_5x20": res["run_stats"],
-                      "note": "per-launch kernel time from HIP events on the launch stream: over the timed "
-                              "steps (one event after each step), and over 5 further runs of 20 launches "
-                              "(median of the runs' means, CV across runs)"}
+    line["timing"] = {"runs_5x20": res["run_stats"],
+                      "note": "per-launch kernel time from HIP events on the launch stream over 5 runs of 20 "
+                              "back-to-back launches after the timed steps: median of the runs' means, CV "
+                              "across runs (the pages' medians of 5 x 20)"}
     line["graph_us"] = round(res["graph_us"], 3)
     if args.fill and head.name == "square2048" and args.config is None:
-        print("# L2 fill-rate probe and the 2048^3 attainable bound", file=sys.stderr, flush=True)
-        fill = fill_rate(torch, mp)
-        from dense_mixed_precision_amd.workloads import Workload
-        k128 = Workload("square2048_k128", 2048, 2048, 128, "uniform", 1.0, 0.0, None, 1001)
-        r = time_workload(k128, 200, 200, torch, mp)
-        line["fill_rate"] = fill
-        line["attainable"] = attainable_2048(head, fill, r["kernel_ms"] * 1e3)
-        line["attainable"]["kernel_frac_of_attainable"] = round(
-            line["roofline"]["achieved"] / line["attainable"]["tflops"], 4)
-        del r
+        print("# L2 fill-rate probe", file=sys.stderr, flush=True)
+        line["fill_rate"] = fill_rate(torch, mp)
     others = {}
     if not args.no_others:
         for name, w in WORKLOADS.items():
@@ -641,7 +608,6 @@ def main():
                             "pct_of_peak": round(100 * w.flop / (r["kernel_ms"] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 2),
                             "roofline": with_traffic(roofline_entry(w, r["kernel_ms"]),
                                                      measured_traffic(name, r["kernel_ms"])),
-                            "timing": r["step_stats"],
                             "kernel": {k: r["cfg"][k] for k in ("id", "kind_name", "bm", "bn", "vec_a", "vec_b",
                                                                 "grid")}}
             del r

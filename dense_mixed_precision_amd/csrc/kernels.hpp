@@ -353,13 +353,19 @@ struct OpTile {
 // latency.
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int STAGES_,
           int LAYOUT_A_ = kRowMajor, int LAYOUT_B_ = kRowMajor, int IN_ = kInF16, int KGROUPS_ = 1,
-          int MI_ = 32>
+          int MI_ = 32, int STAGGER_ = 0>
 struct PipeCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, STAGES = STAGES_;
     static constexpr int LAYOUT_A = LAYOUT_A_, LAYOUT_B = LAYOUT_B_;
     static constexpr int IN = IN_;
     static constexpr int KGROUPS = KGROUPS_;
+    // K order (0: every workgroup walks the K tiles from the first; 1: the
+    // workgroups at odd (tile row + tile column) start one K tile later and
+    // wrap around), so half of the workgroups that share an A or B panel in
+    // an XCD's L2 request its lines one K tile after the others instead of
+    // all at once
+    static constexpr int STAGGER = STAGGER_;
     // matrix instruction: 32 = 32x32x16 (16 accumulators per lane),
     // 16 = 16x16x32 (4 accumulators per lane)
     static constexpr int MI = MI_;
@@ -398,6 +404,7 @@ struct PipeCfg {
     static_assert(KS >= 1, "a K tile holds at least one instruction's K");
     static_assert(STAGES >= 2 && STAGES <= 5, "2..5 LDS stages");
     static_assert(NL * (STAGES - 1) < 64, "vmcnt is 6 bits");
+    static_assert(STAGGER == 0 || STAGGER == 1, "K order 0 or 1");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 };
 
@@ -617,16 +624,30 @@ gemm_pipe(GemmArgs args_in)
     const int64_t rows_left = args.M - m0;  // > 0
     const int64_t cols_left = args.N - n0;  // > 0
 
+    // K tile t of the loop is K tile (t + koff) mod num_kt of the matrices
+    // (see PipeCfg::STAGGER).  Only the order of the K tiles changes; the K
+    // tail stays the last step.
+    const int64_t num_kt = (K + BK - 1) / BK;
+    int64_t koff = 0;
+    if constexpr (Cfg::STAGGER != 0)
+        koff = (num_kt > 1 && ((tm + tn) & 1)) ? 1 : 0;
+    auto kmem = [&](int64_t t) __attribute__((always_inline)) {
+        if constexpr (Cfg::STAGGER == 0)
+            return t;
+        else
+            return t + koff < num_kt ? t + koff : t + koff - num_kt;
+    };
+
     // The A and B tiles of K tile t as windows of the stored matrices.
     auto src_a = [&](int64_t t) __attribute__((always_inline)) {
-        const int64_t k0 = t * BK;
+        const int64_t k0 = kmem(t) * BK;
         if constexpr (A_ROW)
             return TileSrc{args.A + m0 * lda + k0, lda, rows_left, K - k0};
         else
             return TileSrc{args.A + k0 * lda + m0, lda, K - k0, rows_left};
     };
     auto src_b = [&](int64_t t) __attribute__((always_inline)) {
-        const int64_t k0 = t * BK;
+        const int64_t k0 = kmem(t) * BK;
         if constexpr (B_ROW)
             return TileSrc{args.B + k0 * ldb + n0, ldb, K - k0, cols_left};
         else
@@ -813,6 +834,7 @@ gemm_pipe(GemmArgs args_in)
     int buf = 0;
     for (int64_t kt = 0; kt < num_k; ++kt) {
         const int nbuf = (buf + 1 == S) ? 0 : buf + 1;
+
         // ks counts this k-group's k-steps of the tile (all of them without
         // k-groups); the LDS rows read are those of k-step ks0 + ks
 #pragma unroll

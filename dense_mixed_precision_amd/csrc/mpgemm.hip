@@ -167,7 +167,7 @@ constexpr Entry scale_entry(int id)
 #define MPG_FAMILY(base, IN, LA, LB)                                                     \
     pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, LA, LB, IN, 1, 16>>(base + 0),            \
         pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, LA, LB, IN>>(base + 1),               \
-        pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, LA, LB, IN>>(base + 2),              \
+        pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, LA, LB, IN, 1, 32, 1>>(base + 2),     \
         pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, LA, LB, IN>>(base + 3)
 
 enum : int { kBig = 0, kMid = 1, kWide = 2, kSmall = 3 };
@@ -184,26 +184,34 @@ const Entry kTable[] = {
     MPG_FAMILY(23, kInBF16, kColMajor, kRowMajor),  // 23..26
     MPG_FAMILY(27, kInBF16, kRowMajor, kColMajor),  // 27..30
     MPG_FAMILY(31, kInBF16, kColMajor, kColMajor),  // 31..34
-    // small row-major FP16 products with more than one 64-deep K tile:
-    // 64x64 tiles with K tiles of 128 and a 3-deep ring
-    pipe_entry<PipeCfg<64, 64, 128, 2, 2, 3>>(35),
+    // small row-major FP16 products with more than one 64-deep K tile: K
+    // tiles of 128 on 8 waves of 16x16x32 instructions, 64x64 with a 2-deep
+    // ring, or 32x64 with a 3-deep ring when 64x64 tiles would leave more
+    // than half of the compute units idle
+    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16>>(35),
+    pipe_entry<PipeCfg<32, 64, 128, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(36),
     // N <= 16 with A row-major, per input format and storage order of B;
     // four k-steps of loads in flight per wave
-    narrow_entry<kInF16, kRowMajor, 4>(36),
-    narrow_entry<kInF16, kColMajor, 4>(37),
-    narrow_entry<kInBF16, kRowMajor, 4>(38),
-    narrow_entry<kInBF16, kColMajor, 4>(39),
+    narrow_entry<kInF16, kRowMajor, 4>(37),
+    narrow_entry<kInF16, kColMajor, 4>(38),
+    narrow_entry<kInBF16, kRowMajor, 4>(39),
+    narrow_entry<kInBF16, kColMajor, 4>(40),
 #ifdef MPGEMM_CANDIDATES
     // Alternatives the factory does not choose, compiled only into the
     // candidates build for tile sweeps (FP16, A and B row-major).
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2>>(40),                   // 32x32x16 on the big tile
-    pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4>>(41),                   // 4 waves of 128x128
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16>>(42),
-    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, kRowMajor, kRowMajor, kInF16, 2>>(43),  // 2 k-groups
-    pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3>>(44),                   // 4 waves
-    pipe_entry<PipeCfg<256, 128, 64, 4, 2, 3>>(45),
-    pipe_entry<PipeCfg<128, 128, 32, 2, 2, 4>>(46),
-    narrow_entry<kInF16, kRowMajor, 8>(47),                           // 8 k-steps in flight
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2>>(41),                   // 32x32x16 on the big tile
+    pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4>>(42),                   // 4 waves of 128x128
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 1>>(43),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, kRowMajor, kRowMajor, kInF16, 2, 32, 1>>(44),  // 2 k-groups
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2>>(45),                  // ascending K order
+    pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3>>(46),                   // 4 waves
+    pipe_entry<PipeCfg<256, 128, 64, 4, 2, 3>>(47),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 32, 1>>(48),
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 1>>(49),
+    pipe_entry<PipeCfg<64, 64, 128, 2, 2, 3>>(50),                    // 4 waves of 32x32x16
+    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(51),
+    pipe_entry<PipeCfg<32, 64, 128, 2, 2, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(52),
+    narrow_entry<kInF16, kRowMajor, 8>(53),                           // 8 k-steps in flight
 #endif
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
@@ -211,10 +219,11 @@ constexpr int kDirectIds[2] = {0, 1};  // per input format
 constexpr int kScaleId = 2;
 // first entry of the family of input format `in` and storage orders (la, lb)
 constexpr int family(int in, int la, int lb) { return 3 + 16 * in + 4 * (la + 2 * lb); }
-// 64x64 tiles, K tile 128, three stages (row-major FP16)
+// small row-major FP16 products, K tiles of 128: 64x64 and 32x64
 constexpr int kSmallDeepKId = 35;
+constexpr int kTinyDeepKId = 36;
 // narrow kernel (N <= 16, A row-major) per input format and storage order of B
-constexpr int kNarrowIds[2][2] = {{36, 37}, {38, 39}};
+constexpr int kNarrowIds[2][2] = {{37, 38}, {39, 40}};
 // below this many 16-row workgroups the narrow kernel leaves most compute
 // units idle, and split-K over the tile kernels is faster (256x16x65536:
 // 74 against 38 us); at or above it the narrow kernel leads (1024x16x16384:
@@ -388,8 +397,12 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
     } else if (small_deep_k && p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR &&
                p.lb == MPGEMM_ROW_MAJOR && p.K > 64) {
         // Small row-major FP16 products with more than one 64-deep K tile
-        // take 64x64 tiles with K tiles of 128 and a 3-deep ring: half as
-        // many barriers per K (256^3: 4.6 against 4.8 us per call).
+        // take K tiles of 128 (half as many barriers per K) on 8 waves:
+        // 32x64 tiles when 64x64 ones would fill less than half the chip
+        // (256^3: 3.6 against 4.1 us per call), else 64x64 (ragged
+        // 1000x800x617: 7.1 against 7.3 us).
+        if (mul_sat(cdiv(p.M, 64), cdiv(p.N, 64)) < kNumCu / 2)
+            order[n++] = kTinyDeepKId;
         order[n++] = kSmallDeepKId;
     }
     order[n++] = fam + kSmall;
@@ -505,7 +518,7 @@ SplitPlan plan_split(const Problem &p, int requested)
     if (narrow && requested == 0 && cdiv(p.M, 16) >= kNarrowMinGroups)
         return sp;
     int id = narrow ? select(p, true, false) : sp.id;
-    if (id == kSmallDeepKId)
+    if (id == kSmallDeepKId || id == kTinyDeepKId)
         id = select(p, false, false);
     const mpgemm_config &c = kTable[id].cfg;
     if (c.kind != MPGEMM_KIND_PIPE)

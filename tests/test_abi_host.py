@@ -147,12 +147,17 @@ def test_factory_choices_for_the_workloads():
     # lda = 617 is odd: A rows are only 2-byte aligned, which 16-byte loads
     # serve on gfx950 (unaligned mode), so A keeps the vector copy path.
     assert c["kind_name"] == "pipe" and c["vec_a"] == 8 and c["vec_b"] == 8
-    assert (c["bm"], c["bn"], c["bk"], c["stages"]) == (64, 64, 128, 3)
+    # 208 tiles of 64x64 fill more than half the chip: 64x64, 8 waves, 2 stages
+    assert (c["bm"], c["bn"], c["bk"], c["stages"], c["threads"], c["mfma_m"]) == (64, 64, 128, 2, 512, 16)
     c = _pick(WORKLOADS["square256"])
-    assert c["kind_name"] == "pipe" and c["grid"] >= 16
-    assert (c["bm"], c["bn"], c["bk"], c["stages"]) == (64, 64, 128, 3)
+    # 16 tiles of 64x64 would leave most of the chip idle: 32x64 tiles
+    assert c["kind_name"] == "pipe" and c["grid"] == 32
+    assert (c["bm"], c["bn"], c["bk"], c["stages"], c["threads"]) == (32, 64, 128, 3, 512)
     # one K tile of 64 or less keeps the 64-deep tile
     assert q(256, 256, 64)["bk"] == 64
+    # the 2048-class tile (128x128x128) is chosen by panel reuse
+    c = _pick(WORKLOADS["square2048"])
+    assert (c["bm"], c["bn"], c["bk"], c["stages"]) == (128, 128, 128, 2)
 
 
 def test_factory_alignment_and_degenerate_cases():
@@ -469,7 +474,7 @@ def test_product_table_holds_what_the_factory_can_choose():
         for la in (0, 1):
             for lb in (0, 1):
                 f = mp.mpgemm_bf16f32_layout_query if in_type else mp.mpgemm_f16f32_layout_query
-                for M, N, K in [(8192, 8192, 8192), (2048, 2048, 2048), (32768, 128, 4096), (256, 256, 256),
+                for M, N, K in [(8192, 8192, 8192), (2048, 2048, 2048), (32768, 128, 4096), (256, 256, 256), (1000, 800, 617),
                                 (256, 256, 64), (1000, 16, 617), (300, 300, 64)]:
                     lda = M if la else K
                     ldb = K if lb else N

@@ -56,14 +56,5 @@ def test_spread_reports_median_and_cv():
     assert bench.spread([0.02])["cv"] == 0.0
 
 
-def test_attainable_bound_uses_the_slower_of_fill_and_hit():
-    w = WORKLOADS["square2048"]
-    fill = {"best_fill_GBps": 393.216, "best_hit_GBps": 3355.4432}   # 384 KiB in 1 us, 2 MiB in 0.625 us
-    a = bench.attainable_2048(w, fill, 6.0)
-    assert abs(a["fill_us_per_k_tile"] - 1.0) < 1e-3 and abs(a["hit_us_per_k_tile"] - 0.625) < 1e-3
-    assert abs(a["bound_us"] - 21.0) < 1e-2
-    assert abs(a["tflops"] - w.flop / 21e-6 / 1e12) < 0.1
-
-
 def test_cpu_model_is_reported():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
