@@ -953,6 +953,76 @@ gemm_pipe(GemmArgs args_in)
         constexpr int MI = Cfg::MI;
         const int cl = lane & (MI - 1);
         const int rl = 4 * (lane / MI);
+        if constexpr (MI == 16 && FN % 2 == 0) {
+            // Full-line stores.  Accumulator v of lane l holds row 4*(l/16)
+            // + v of a 16-column instruction tile, so one store covers 64
+            // bytes of each of four rows (half lines), which cost about a
+            // fifth more write traffic.  Tiles 2p and 2p+1 are adjacent:
+            // swapping the odd 16-lane rows of tile 2p's value with the even
+            // rows of tile 2p+1's (v_permlane16_swap) leaves lane l with row
+            // v + 8*(l/32) (first value) and 4 + v + 8*(l/32) (second) of
+            // column 32p + l%32, so each store writes two whole 128-byte
+            // lines.
+            const int cp = lane & 31;
+            const int rp = 8 * (lane >> 5);
+            float bp[FN / 2];
+#pragma unroll
+            for (int p = 0; p < FN / 2; ++p)
+                bp[p] = 0.0f;
+            if (args.bias) {
+                const __amdgpu_buffer_rsrc_t rsBias = make_rsrc(args.bias + wcol0);
+#pragma unroll
+                for (int p = 0; p < FN / 2; ++p) {
+                    const int c = 32 * p + cp;
+                    bp[p] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          rsBias, c < wcols ? (uint32_t)(c * 4) : kOOB, 0, 0));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                for (int p = 0; p < FN / 2; ++p) {
+                    const int c = 32 * p + cp;
+                    const bool c_ok = c < wcols;
+                    uint32_t off[2][AV];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int v = 0; v < AV; ++v) {
+                            const int r = MI * i + 4 * h + v + rp;
+                            off[h][v] = (c_ok && r < wrows) ? (uint32_t)((r * ldc + c) * 4) : kOOB;
+                        }
+                    float cin[2][AV];
+                    if (beta != 0.0f) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int v = 0; v < AV; ++v)
+                                cin[h][v] = __builtin_bit_cast(
+                                    float, __builtin_amdgcn_raw_buffer_load_b32(rsC, off[h][v], 0, 0));
+                    }
+#pragma unroll
+                    for (int v = 0; v < AV; ++v) {
+                        // (scalar copies first: a bit cast applied to a vector
+                        // element directly reads element 0 with this compiler)
+                        const float x0 = acc[i][2 * p][v], x1 = acc[i][2 * p + 1][v];
+                        const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x0),
+                                                                         __builtin_bit_cast(uint32_t, x1), false,
+                                                                         false);
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            float val = alpha * __builtin_bit_cast(float, (uint32_t)sw[h]);
+                            if (beta != 0.0f)
+                                val = __builtin_fmaf(beta, cin[h][v], val);
+                            if (args.bias)
+                                val += bp[p];
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC,
+                                                                  off[h][v], 0, kStoreNT);
+                        }
+                    }
+                }
+            }
+        } else {
         // the bias of each of this lane's FN columns (0 past the last column)
         float bv[FN];
 #pragma unroll
@@ -999,6 +1069,7 @@ gemm_pipe(GemmArgs args_in)
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off[v], 0, kStoreNT);
                 }
             }
+        }
         }
     }
 }
