@@ -1087,12 +1087,13 @@ gemm_pipe(GemmArgs args_in)
 // and K read zero) and loads B beside it: a column-major B with one 16-byte
 // load of the operand's 8 k values; a row-major B with one 16-byte load of
 // 8 consecutive columns of one k row per lane (the k-step's 32 x 16 values
-// in one instruction; a vector that crosses column N is loaded element by
-// element, zero past N), turned into operand layout through a 1 KiB LDS
+// in one instruction; columns past N only reach output columns that are
+// never stored), turned into operand layout through a 1 KiB LDS
 // slot of the wave's own and the transposing LDS read.  It accumulates a
 // 16x16 partial tile on the 16x16x32 instruction, with the loads DEPTH
-// k-steps ahead of their use (two loads per k-step, so the 6-bit load
-// counter covers deep rings).  As in the
+// k-steps ahead of their use (two loads per k-step except where a row-major
+// B vector would run past B's last element, so the 6-bit load counter covers
+// deep rings).  As in the
 // pipelined kernel the main range covers the largest multiple of 8 of K and
 // the last K % 8 values are one more step (wave 0).  The 8 partial tiles
 // are summed through LDS in ascending slice order (run-to-run identical),
@@ -1127,9 +1128,18 @@ gemm_narrow(GemmArgs args)
     const int64_t s1 = s0 + per < steps ? s0 + per : steps;
 
     // row-major B: lane j loads columns 8*(j%2)..+7 of k row j/2 of the step
+    // with one 16-byte load.  Values it brings in from columns at or past N
+    // (row padding, or the next row) land in operand columns >= N, which
+    // only feed output columns >= N: those are never stored, so they need
+    // no zeroing.  Only a vector that would run past B's last stored element
+    // (kr*ldb + bn + 7 > (K-1)*ldb + N-1: the last rows of a packed B
+    // narrower than 8 columns) is loaded element by element instead.
     const int bk = lane >> 1, bn = 8 * (lane & 1);
     const bool b_full = bn + 8 <= N;
     const bool b_some = bn < N;
+    // index of B's last stored element, (K-1)*ldb + N-1: below 2^30, since
+    // the host checks that B's stored rows span fewer than 2^31 bytes
+    const int b_last = (int)((args.K - 1) * args.ldb + N - 1);
     u32x4 ra[DEPTH], rb[DEPTH];
     auto issue = [&](int d, int64_t s) __attribute__((always_inline)) {
         const int64_t k = 32 * s + kq;
@@ -1140,11 +1150,11 @@ gemm_narrow(GemmArgs args)
             const int64_t kr = 32 * s + bk;
             // used only when row kr is in range (within the span the host checks)
             const uint32_t off = (uint32_t)((kr * args.ldb + bn) * 2);
-            if (b_full || !b_some || kr >= Km) {
+            if (b_full || !b_some || kr >= Km || (int)kr * ldb + bn + 7 <= b_last) {
                 rb[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                      rsB, (b_full && kr < Km) ? off : kOOB, 0, 0));
+                                                      rsB, (b_some && kr < Km) ? off : kOOB, 0, 0));
             } else {
-                // the vector crosses column N: element by element, zero past N
+                // the vector would run past B's last element: element by element
                 uint32_t h[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)

@@ -84,6 +84,24 @@ def test_narrow_config(cfg, M, N, K):
     assert gC.untouched_outside_window()
 
 
+@pytest.mark.parametrize("M,N,K", [(40, 1, 5), (40, 3, 12), (70, 7, 40), (70, 9, 33), (100, 13, 617),
+                                   (33, 16, 9)])
+@pytest.mark.parametrize("cfg", [i for i in _narrow_ids() if mp.mpgemm_config_info(i)["layout_b"] == 0])
+def test_narrow_packed_row_major_b(cfg, M, N, K):
+    """Row-major B stored packed (ldb = N) and ending at the end of its buffer
+    region (guard sentinels, NaN, right after it): the 16-byte loads of the
+    last k rows must not take values past B's last element, and columns at
+    or past N must read as zero, so the exact product comes out bit for bit."""
+    c = mp.mpgemm_config_info(cfg)
+    fmt = "bf16" if c["in_type"] == mp.MPGEMM_IN_BF16 else "f16"
+    dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
+    A, B, _ = make_inputs(M, N, K, "smallint", seed=cfg * 7 + M + N + K, dtype=dtype)
+    got, gC = run_layout(A, B, None, 1.0, 0.0, 0, 0, config=cfg, lda=K, ldb=N)
+    ref, _ = _ref(A, B, None, 1.0, 0.0, 0, fmt)
+    assert np.array_equal(got, ref.astype(np.float32)), f"config {cfg} {M}x{N}x{K}: not bitwise"
+    assert gC.untouched_outside_window()
+
+
 @pytest.mark.parametrize("cfg", _narrow_ids())
 def test_narrow_bias_and_scale(cfg):
     c = mp.mpgemm_config_info(cfg)
