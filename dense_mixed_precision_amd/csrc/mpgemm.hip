@@ -85,6 +85,7 @@ constexpr Entry pipe_entry(int id)
     c.layout_b = Cfg::LAYOUT_B;
     c.in_type = Cfg::IN;
     c.k_groups = Cfg::KGROUPS;
+    c.k_order = Cfg::STAGGER;
     return Entry{c, &launch_pipe<Cfg>};
 }
 
