@@ -360,11 +360,12 @@ struct PipeCfg {
     static constexpr int LAYOUT_A = LAYOUT_A_, LAYOUT_B = LAYOUT_B_;
     static constexpr int IN = IN_;
     static constexpr int KGROUPS = KGROUPS_;
-    // K order (0: every workgroup walks the K tiles from the first; 1: the
-    // workgroups at odd (tile row + tile column) start one K tile later and
-    // wrap around), so half of the workgroups that share an A or B panel in
-    // an XCD's L2 request its lines one K tile after the others instead of
-    // all at once
+    // K order.  0: every workgroup walks the K tiles from the first.  D >= 2:
+    // the workgroup at tile row tm, tile column tn starts at K tile
+    // (tm + tn) mod min(D, K tiles) and wraps around, so the workgroups of
+    // an XCD that share an A or B panel request its lines at D different
+    // times instead of all at once: one of them misses in the L2 and the
+    // others, up to D - 1 K tiles later, hit.
     static constexpr int STAGGER = STAGGER_;
     // matrix instruction: 32 = 32x32x16 (16 accumulators per lane),
     // 16 = 16x16x32 (4 accumulators per lane)
@@ -404,7 +405,7 @@ struct PipeCfg {
     static_assert(KS >= 1, "a K tile holds at least one instruction's K");
     static_assert(STAGES >= 2 && STAGES <= 5, "2..5 LDS stages");
     static_assert(NL * (STAGES - 1) < 64, "vmcnt is 6 bits");
-    static_assert(STAGGER == 0 || STAGGER == 1, "K order 0 or 1");
+    static_assert(STAGGER == 0 || (STAGGER >= 2 && STAGGER <= 64), "K order: 0, or 2..64 start offsets");
     static_assert(LDS_BYTES <= 160 * 1024, "gfx950 has 160 KiB of LDS per workgroup");
 };
 
@@ -629,8 +630,10 @@ gemm_pipe(GemmArgs args_in)
     // tail stays the last step.
     const int64_t num_kt = (K + BK - 1) / BK;
     int64_t koff = 0;
-    if constexpr (Cfg::STAGGER != 0)
-        koff = (num_kt > 1 && ((tm + tn) & 1)) ? 1 : 0;
+    if constexpr (Cfg::STAGGER != 0) {
+        const int spread = num_kt < Cfg::STAGGER ? (int)num_kt : Cfg::STAGGER;
+        koff = spread > 1 ? (tm + tn) % spread : 0;
+    }
     auto kmem = [&](int64_t t) __attribute__((always_inline)) {
         if constexpr (Cfg::STAGGER == 0)
             return t;
@@ -716,20 +719,27 @@ gemm_pipe(GemmArgs args_in)
                 read_b(buf, ks, set, f);
     };
 
-    // ---- K tail operands: lane l holds the values of outer index l % MI at
-    // k = K + 8*(l/MI) + 0..7, zero at and past the true K (so only the lanes
-    // with l < MI carry data) and past the M or N edge.  2-byte buffer loads;
-    // the 32-bit offsets stay within the stage span the host checks.  With
-    // small wave tiles the loads go out before the ring fill, the oldest
-    // memory operations of the kernel, so the copy waits cover them and their
-    // latency hides under the K loop; large wave tiles, which have no
-    // registers to spare across the loop, issue them after it.
+    // ---- K tail operands.  The instruction sums over all of its K
+    // positions, so where a tail value sits among them does not matter as
+    // long as A and B put it in the same place: tail value j (0 <= j <
+    // ktail <= 7) goes to lane group g = j % G (lanes MI*g .. MI*g + MI - 1,
+    // G = 64 / MI groups) at element j / G of the group's 8, the other
+    // elements stay zero.  Every lane then loads NS = ceil(7 / G) values (2
+    // for 16x16x32, 4 for 32x32x16) instead of one lane group loading all 8.
+    // Values at and past the true K, and past the M or N edge, read as zero.
+    // 2-byte buffer loads; the 32-bit offsets stay within the stage span the
+    // host checks.  With small wave tiles the loads go out before the ring
+    // fill, the oldest memory operations of the kernel, so the copy waits
+    // cover them and their latency hides under the K loop; large wave tiles,
+    // which have no registers to spare across the loop, issue them after it.
     constexpr bool TAIL_EARLY = (FM + FN) * 4 <= 16;
+    constexpr int TG = 64 / Cfg::MI;
+    constexpr int TNS = (7 + TG - 1) / TG;
     half8 ta[FM], tb[FN];
     auto tail_load = [&]() __attribute__((always_inline)) {
         constexpr int MI = Cfg::MI;
         const int li = lane & (MI - 1);
-        const int k8 = 8 * (lane / MI);
+        const int g = lane / MI;
         const int ld_a = (int)lda, ld_b = (int)ldb;
         const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(args.A + (A_ROW ? m0 * lda + K : K * lda + m0));
         const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(args.B + (B_ROW ? K * ldb + n0 : n0 * ldb + K));
@@ -737,10 +747,10 @@ gemm_pipe(GemmArgs args_in)
         for (int f = 0; f < FM; ++f) {
             const int r = wm * Cfg::WTM + MI * f + li;
             const bool r_ok = r < rows_left;
-            uint32_t h[8];
+            uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int k = k8 + e;
+            for (int e = 0; e < TNS; ++e) {
+                const int k = TG * e + g;
                 const uint32_t off = (uint32_t)((A_ROW ? r * ld_a + k : k * ld_a + r) * 2);
                 h[e] = __builtin_amdgcn_raw_buffer_load_b16(rs_a, (r_ok && k < ktail) ? off : kOOB, 0, 0);
             }
@@ -751,10 +761,10 @@ gemm_pipe(GemmArgs args_in)
         for (int f = 0; f < FN; ++f) {
             const int c = wn * Cfg::WTN + MI * f + li;
             const bool c_ok = c < cols_left;
-            uint32_t h[8];
+            uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int k = k8 + e;
+            for (int e = 0; e < TNS; ++e) {
+                const int k = TG * e + g;
                 const uint32_t off = (uint32_t)((B_ROW ? k * ld_b + c : c * ld_b + k) * 2);
                 h[e] = __builtin_amdgcn_raw_buffer_load_b16(rs_b, (c_ok && k < ktail) ? off : kOOB, 0, 0);
             }

@@ -168,7 +168,7 @@ constexpr Entry scale_entry(int id)
 #define MPG_FAMILY(base, IN, LA, LB)                                                     \
     pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, LA, LB, IN, 1, 16>>(base + 0),            \
         pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, LA, LB, IN>>(base + 1),               \
-        pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, LA, LB, IN, 1, 32, 1>>(base + 2),     \
+        pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, LA, LB, IN, 1, 32, 2>>(base + 2),     \
         pipe_entry<PipeCfg<64, 64, 64, 2, 2, 2, LA, LB, IN>>(base + 3)
 
 enum : int { kBig = 0, kMid = 1, kWide = 2, kSmall = 3 };
@@ -202,17 +202,27 @@ const Entry kTable[] = {
     // candidates build for tile sweeps (FP16, A and B row-major).
     pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2>>(41),                   // 32x32x16 on the big tile
     pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4>>(42),                   // 4 waves of 128x128
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 1>>(43),
-    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, kRowMajor, kRowMajor, kInF16, 2, 32, 1>>(44),  // 2 k-groups
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 2>>(43),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, kRowMajor, kRowMajor, kInF16, 2, 32, 2>>(44),  // 2 k-groups
     pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2>>(45),                  // ascending K order
     pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3>>(46),                   // 4 waves
     pipe_entry<PipeCfg<256, 128, 64, 4, 2, 3>>(47),
-    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 32, 1>>(48),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 1>>(49),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 32, 2>>(48),
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 2>>(49),
     pipe_entry<PipeCfg<64, 64, 128, 2, 2, 3>>(50),                    // 4 waves of 32x32x16
     pipe_entry<PipeCfg<64, 64, 128, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(51),
     pipe_entry<PipeCfg<32, 64, 128, 2, 2, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(52),
     narrow_entry<kInF16, kRowMajor, 8>(53),                           // 8 k-steps in flight
+    // K orders with more start offsets
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 32, 4>>(54),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 32, 8>>(55),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 32, 16>>(56),
+    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 64>>(57),
+    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 2>>(58),
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 4>>(59),
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 8>>(60),
+    pipe_entry<PipeCfg<32, 64, 128, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16, 64>>(61),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 32, 4>>(62),
 #endif
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);

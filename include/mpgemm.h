@@ -108,11 +108,12 @@ typedef struct mpgemm_config {
     int32_t k_groups;    /* wave groups sharing each LDS tile, each taking its own
                             k-steps over the whole block; threads =
                             64 * waves_m * waves_n * k_groups                     */
-    int32_t k_order;     /* order of K tiles: 0 ascending in every workgroup; 1
-                            staggered, where a workgroup whose tile row plus tile
-                            column is odd starts one K tile later and wraps
-                            round (the sum over K is taken in another order, so
-                            its rounding differs from the ascending entry's)    */
+    int32_t k_order;     /* order of K tiles: 0 ascending in every workgroup; D >= 2
+                            staggered: the workgroup at tile row tm, tile column
+                            tn starts at K tile (tm + tn) mod min(D, K tiles)
+                            and wraps round (its sum over K is taken in another
+                            order, so its rounding differs from the ascending
+                            entry's)                                            */
 } mpgemm_config;
 
 /*

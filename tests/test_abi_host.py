@@ -126,7 +126,7 @@ def test_config_table_is_consistent():
             assert c["lds_bytes"] <= 160 * 1024
             assert (c["vec_a"], c["vec_b"]) == (8, 8)
             # only the 128x128x128 tile staggers its K order
-            assert c["k_order"] == (1 if (c["bm"], c["bn"], c["bk"]) == (128, 128, 128) else 0)
+            assert c["k_order"] == (2 if (c["bm"], c["bn"], c["bk"]) == (128, 128, 128) else 0)
         else:
             assert c["k_order"] == 0
     assert kinds == {"pipe", "direct", "scale", "narrow"}
@@ -161,7 +161,7 @@ def test_factory_choices_for_the_workloads():
     assert q(256, 256, 64)["bk"] == 64
     # the 2048-class tile (128x128x128) is chosen by panel reuse
     c = _pick(WORKLOADS["square2048"])
-    assert (c["bm"], c["bn"], c["bk"], c["stages"], c["k_order"]) == (128, 128, 128, 2, 1)
+    assert (c["bm"], c["bn"], c["bk"], c["stages"], c["k_order"]) == (128, 128, 128, 2, 2)
 
 
 def test_factory_alignment_and_degenerate_cases():
