@@ -62,6 +62,8 @@ def parse():
                         "sweep-only tile shapes; python -m dense_mixed_precision_amd.build --candidates)")
     p.add_argument("--no-fill", dest="fill", action="store_false",
                    help="skip the L2 fill-rate probe")
+    p.add_argument("--no-timeline", dest="timeline", action="store_false",
+                   help="skip the per-workgroup timeline of the headline workload (timeline build)")
     p.add_argument("--no-others", action="store_true", help="time only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -402,8 +404,10 @@ def fill_rate(torch, mp):
     LDS) and 16- and 4-byte loads into registers at 1..16 requests in
     flight per wave; the copy form with every XCD reading the same region,
     and with each byte requested by 8 compute units of the XCD at once, as
-    the 2048^3 kernel's workgroups sharing a panel do.  Best of 3 timed
-    launches after one untimed; GB/s per XCD of unique bytes."""
+    the 2048^3 kernel's workgroups sharing a panel do.  Per compute unit:
+    the copy form with one workgroup per XCD (a lone compute unit's copy
+    path) and the all-CU hit rate divided by 32.  Best of 3 timed launches
+    after one untimed; GB/s per XCD (per CU) of unique bytes."""
     dev = torch.device("cuda:0")
     MiB = 1 << 20
     buf = torch.ones(48 * MiB // 4, dtype=torch.float32, device=dev)
@@ -412,9 +416,9 @@ def fill_rate(torch, mp):
     stream = torch.cuda.current_stream()
     names = {mp.MPGEMM_FILL_LDS16: "lds16", mp.MPGEMM_FILL_REG16: "reg16", mp.MPGEMM_FILL_REG4: "reg4"}
 
-    def measure(mode, depth, footprint, shared=0, replicas=1):
-        passes = max(4, int(64 * 6 * MiB // footprint))
-        args = (mode, depth, buf.data_ptr(), buf.numel() * 4, footprint, shared, replicas, passes, wgs,
+    def measure(mode, depth, footprint, shared=0, replicas=1, workgroups=wgs):
+        passes = max(4, int(64 * 6 * MiB // footprint)) if workgroups == wgs else 16
+        args = (mode, depth, buf.data_ptr(), buf.numel() * 4, footprint, shared, replicas, passes, workgroups,
                 sink.data_ptr(), sink.numel(), stream.cuda_stream)
         rc = mp.mpgemm_probe_fill(*args)
         if rc != mp.MPGEMM_OK:
@@ -436,13 +440,173 @@ def fill_rate(torch, mp):
             out["per_xcd_GBps"][f"fill_6MiB_{names[mode]}_d{depth}"] = measure(mode, depth, 6 * MiB)
     out["per_xcd_GBps"]["fill_6MiB_lds16_d8_shared"] = measure(mp.MPGEMM_FILL_LDS16, 8, 6 * MiB, shared=1)
     out["per_xcd_GBps"]["fill_6MiB_lds16_d8_x8cu"] = measure(mp.MPGEMM_FILL_LDS16, 8, 6 * MiB, replicas=8)
-    for depth in (4, 8, 16):
+    for depth in (2, 4, 8, 16):
         out["per_xcd_GBps"][f"hit_2MiB_lds16_d{depth}"] = measure(mp.MPGEMM_FILL_LDS16, depth, 2 * MiB)
+    # one workgroup per XCD: what a single compute unit's copy path moves
+    out["per_cu_GBps"] = {}
+    for depth in (1, 2, 4, 8, 16):
+        out["per_cu_GBps"][f"hit_2MiB_lds16_d{depth}_1cu"] = measure(mp.MPGEMM_FILL_LDS16, depth, 2 * MiB,
+                                                                      workgroups=8)
+    for depth in (2, 8):
+        out["per_cu_GBps"][f"hit_2MiB_lds16_d{depth}_32cu"] = round(
+            out["per_xcd_GBps"][f"hit_2MiB_lds16_d{depth}"] / 32, 1)
     vals = out["per_xcd_GBps"]
     out["best_fill_GBps"] = max(v for k, v in vals.items() if k.startswith("fill_6MiB_") and "_x8cu" not in k)
     out["best_hit_GBps"] = max(v for k, v in vals.items() if k.startswith("hit_"))
-    out["source"] = "mpgemm_probe_fill (libmpgemm_probes.so), 256 workgroups x 8 waves, best of 3"
+    out["best_per_cu_GBps"] = max(out["per_cu_GBps"].values())
+    out["source"] = ("mpgemm_probe_fill (libmpgemm_probes.so), 256 workgroups x 8 waves (per_cu: 8 "
+                     "workgroups, one per XCD), best of 3")
     del buf, sink
+    return out
+
+
+def ragged_breakdown(torch, mp, rounds=3, reps=50):
+    """Where the ragged workload's time goes: graph-replayed per-launch time
+    of the 1000x800x617 product (alpha 1.5, beta 0.5, lda 617) and of
+    variants that each remove one of its features -- the C read (beta 0),
+    the odd row stride of A (rows padded to 624 elements, 16-byte aligned),
+    the K tail (K 616, a multiple of 8) -- beside the same product with one
+    K tile (K 128), a single 64x64 workgroup with 5 and 1 K tiles, and the
+    launch floor (a 16x16 product with K 0: the scale kernel alone).  The
+    cases are timed in `rounds` interleaved rounds; best per case, in us.
+    Inputs: the ragged workload's A, B and C (A copied into padded rows)."""
+    from dense_mixed_precision_amd.workloads import WORKLOADS, workload_inputs
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["ragged1000x800x617"]
+    A, B, C = workload_inputs(w)
+    a617 = A.to(dev)
+    a624 = torch.zeros((w.M, 624), dtype=A.dtype, device=dev)
+    a624[:, :w.K] = a617
+    Bd = B.to(dev)
+    C0 = C.to(dev)
+    Cd = C0.clone()
+    handle = torch.cuda.current_stream(dev).cuda_stream
+    cases = {
+        "workload": (w.M, w.N, 617, a617, 617, w.alpha, w.beta),
+        "beta0": (w.M, w.N, 617, a617, 617, w.alpha, 0.0),
+        "beta0_lda624": (w.M, w.N, 617, a624, 624, w.alpha, 0.0),
+        "beta0_lda624_k616": (w.M, w.N, 616, a624, 624, w.alpha, 0.0),
+        "beta0_lda624_k128": (w.M, w.N, 128, a624, 624, w.alpha, 0.0),
+        "one_workgroup_k616": (64, 64, 616, a624, 624, w.alpha, 0.0),
+        "one_workgroup_k128": (64, 64, 128, a624, 624, w.alpha, 0.0),
+        "launch_floor_k0": (16, 16, 0, a624, 624, w.alpha, 0.0),
+    }
+    best = {k: float("inf") for k in cases}
+    for _ in range(rounds):
+        for name, (M, N, K, a, lda, alpha, beta) in cases.items():
+            def step(M=M, N=N, K=K, a=a, lda=lda, alpha=alpha, beta=beta):
+                rc = mp.mpgemm_f16f32(M, N, K, a.data_ptr(), lda, Bd.data_ptr(), w.N, Cd.data_ptr(), w.N,
+                                      alpha, beta, handle)
+                if rc != mp.MPGEMM_OK:
+                    raise mp.MpgemmError(rc, f"ragged breakdown {name}")
+            Cd.copy_(C0)
+            for _ in range(300):
+                step()
+            torch.cuda.synchronize()
+            best[name] = min(best[name], graph_time_us(step, reps, torch))
+    t = {k: round(v, 3) for k, v in best.items()}
+    return {
+        "us": t,
+        "c_read_us": round(t["workload"] - t["beta0"], 3),
+        "odd_row_stride_us": round(t["beta0"] - t["beta0_lda624"], 3),
+        "k_tail_us": round(t["beta0_lda624"] - t["beta0_lda624_k616"], 3),
+        "per_k_tile_us": round((t["beta0_lda624_k616"] - t["beta0_lda624_k128"]) / 4, 3),
+        "per_k_tile_one_workgroup_us": round((t["one_workgroup_k616"] - t["one_workgroup_k128"]) / 4, 3),
+        "launch_floor_us": t["launch_floor_k0"],
+        "note": "graph-replayed per-launch times, best of interleaved rounds; K tiles are 128 deep (5 for "
+                "K 616/617, 1 for K 128)",
+    }
+
+
+def timeline_summary(rec, nwg):
+    """Summary of one launch's timeline records (uint64 array of shape
+    [>= nwg, 48], layout in include/mpgemm_timeline.h).  Each workgroup's
+    shader clock is its shader-clock span over its 100 MHz-clock span; its
+    intervals are converted with its own clock.  Medians over the
+    workgroups of: the start skew, the wait from the start to the first
+    published K tile, the interval between consecutive publishes (per tile
+    index, for the tiles recorded), the time from the last recorded publish
+    to the end of the K loop, and the epilogue; plus each XCD's median end.
+    Times in microseconds."""
+    import numpy as np
+
+    r = np.asarray(rec[:nwg], dtype=np.uint64).astype(np.int64)
+    clk = (r[:, 45] - r[:, 1]) / ((r[:, 46] - r[:, 0]) / 100e6)
+
+    def us(a, b):
+        return (r[:, b] - r[:, a]) / clk * 1e6
+
+    def med(x):
+        return round(float(np.median(x)), 3)
+
+    t0 = r[:, 0].min()
+    start = (r[:, 0] - t0) / 100.0
+    end = (r[:, 46] - t0) / 100.0
+    ntiles = int(r[0, 43])
+    nrec = min(ntiles, 41)
+    intervals = [med(us(1 + t, 2 + t)) for t in range(1, nrec)]
+    last = 1 + nrec
+    xcd = (r[:, 47] >> 32) & 0xF
+    return {
+        "workgroups": int(nwg),
+        "k_tiles": ntiles,
+        "shader_clock_GHz": round(float(np.median(clk)) / 1e9, 3),
+        "start_skew_us": {"median": med(start), "max": round(float(start.max()), 3)},
+        "first_tile_us": med(us(1, 2)),
+        "tile_interval_us": intervals,
+        "steady_tile_interval_us": med(np.array(intervals[2:] or intervals or [0.0])),
+        "last_recorded_tile_to_loop_end_us": med(us(last, 44)),
+        "tiles_after_last_recorded": ntiles - nrec,
+        "epilogue_us": med(us(44, 45)),
+        "workgroup_us": med(us(1, 45)),
+        "launch_span_us": round(float(end.max()), 3),
+        "xcd_end_us": {int(x): med(end[xcd == x]) for x in sorted(set(xcd.tolist()))},
+    }
+
+
+def timeline(w, torch, mp, warm=200, launches=3):
+    """Per-workgroup timeline of the factory's kernel for `w` from the
+    timeline build (libmpgemm_timeline.so, loaded beside the product): after
+    `warm` back-to-back launches the records of the last one are read, three
+    times; the summary of the median launch (by span) is returned.  None
+    when the factory picks a kernel other than the pipelined one."""
+    import numpy as np
+
+    from dense_mixed_precision_amd.workloads import workload_inputs
+
+    dev = torch.device("cuda:0")
+    A, B, C = workload_inputs(w)
+    Ad, Bd = A.to(dev), B.to(dev)
+    Cd = C.to(dev) if C is not None else torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    cfg = mp.query_for(Ad, Bd, Cd, w.alpha, w.beta)
+    if cfg["kind_name"] != "pipe":
+        return None
+    lib = mp.load_timeline()
+    nwg = min(int(cfg["grid"]), 4096)
+    handle = torch.cuda.current_stream(dev).cuda_stream
+    if lib.mpgemm_timeline_clear() != mp.MPGEMM_OK:
+        raise mp.MpgemmError(mp.MPGEMM_ELAUNCH, "mpgemm_timeline_clear")
+    rec = np.zeros((nwg, mp.TIMELINE_SLOTS), dtype=np.uint64)
+    runs = []
+    for _ in range(launches):
+        if C is not None:
+            Cd.copy_(C.to(dev))
+        for _ in range(warm):
+            rc = lib.mpgemm_f16f32(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), w.N, Cd.data_ptr(), w.N,
+                                   float(w.alpha), float(w.beta), handle)
+            if rc != mp.MPGEMM_OK:
+                raise mp.MpgemmError(rc, "timeline build launch")
+        rc = lib.mpgemm_timeline_read(rec.ctypes.data, rec.size)
+        if rc != mp.MPGEMM_OK:
+            raise mp.MpgemmError(rc, "mpgemm_timeline_read")
+        runs.append(timeline_summary(rec, nwg))
+    runs.sort(key=lambda d: d["launch_span_us"])
+    out = runs[len(runs) // 2]
+    out["kernel"] = {k: cfg[k] for k in ("id", "bm", "bn", "bk", "stages", "mfma_m", "k_order", "grid")}
+    out["source"] = ("libmpgemm_timeline.so (the product source with -DMPGEMM_TIMELINE): thread 0 of each "
+                     f"workgroup stamps the shader clock; last of {warm} back-to-back launches, median of "
+                     f"{launches}")
     return out
 
 
@@ -590,6 +754,12 @@ def main():
                               "back-to-back launches after the timed steps: median of the runs' means, CV "
                               "across runs (the pages' medians of 5 x 20)"}
     line["graph_us"] = round(res["graph_us"], 3)
+    if args.timeline and args.config is None:
+        print("# per-workgroup timeline (timeline build)", file=sys.stderr, flush=True)
+        line["timeline"] = timeline(head, torch, mp, warm=max(5, min(200, int(2e13 / head.flop))))
+    if (head.name == "ragged1000x800x617" or not args.no_others) and args.config is None:
+        print("# ragged breakdown", file=sys.stderr, flush=True)
+        line["ragged_breakdown"] = ragged_breakdown(torch, mp)
     if args.fill and head.name == "square2048" and args.config is None:
         print("# L2 fill-rate probe", file=sys.stderr, flush=True)
         line["fill_rate"] = fill_rate(torch, mp)

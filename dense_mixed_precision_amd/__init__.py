@@ -28,6 +28,11 @@ Diagnostics (libmpgemm_probes.so):
     mpgemm_probe_fill(mode, depth, buf, buf_bytes, footprint, shared, replicas, passes, workgroups,
                       sink, sink_len, stream)
 
+Timeline build (libmpgemm_timeline.so, include/mpgemm_timeline.h), loaded
+beside the product by ``load_timeline()``: mpgemm_f16f32 plus
+mpgemm_timeline_entries(), mpgemm_timeline_read(out, entries) and
+mpgemm_timeline_clear() -- per-workgroup stamps of the pipelined kernel.
+
 Tensor convenience: ``gemm(A, B, C, alpha, beta)`` for torch tensors on the
 GPU (A, B both float16 or both bfloat16, each row- or column-major, e.g. a
 transposed view; C float32 row-major), launched on torch's current stream.
@@ -56,12 +61,15 @@ from ._binding import (  # noqa: F401
     MPGEMM_FILL_REG16,
     MPGEMM_FILL_REG4,
     CANDIDATES_PATH,
+    TIMELINE_PATH,
+    TIMELINE_SLOTS,
     MpgemmError,
     config_fields,
     gemm,
     lib_path,
     load,
     load_probes,
+    load_timeline,
     mpgemm_config_info,
     mpgemm_f16f32,
     mpgemm_f16f32_query,

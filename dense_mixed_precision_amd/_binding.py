@@ -1,5 +1,6 @@
-"""ctypes binding for libmpgemm.so and libmpgemm_probes.so (argument
-marshalling only: every step of the product runs in the HIP library)."""
+"""ctypes binding for libmpgemm.so and the diagnostics libraries
+libmpgemm_probes.so and libmpgemm_timeline.so (argument marshalling only:
+every step of the product runs in the HIP library)."""
 from __future__ import annotations
 
 import ctypes
@@ -10,6 +11,10 @@ _LIB_PATH = os.path.join(_HERE, "libmpgemm.so")
 _PROBES_PATH = os.path.join(_HERE, "libmpgemm_probes.so")
 #: the product library plus the sweep-only tile shapes (built on request)
 CANDIDATES_PATH = os.path.join(_HERE, "libmpgemm_candidates.so")
+#: the product library with the per-workgroup timeline (include/mpgemm_timeline.h)
+TIMELINE_PATH = os.path.join(_HERE, "libmpgemm_timeline.so")
+#: uint64 stamps per workgroup record of the timeline build
+TIMELINE_SLOTS = 48
 
 MPGEMM_OK = 0
 MPGEMM_EDIM = -1
@@ -144,6 +149,32 @@ def load_probes():
     lib.mpgemm_probe_fill.argtypes = [i32, i32, vp, i64, i64, i32, i32, i64, i32, vp, i64, vp]
     lib.mpgemm_probe_fill.restype = i32
     _probes = lib
+    return lib
+
+
+_timeline = None
+
+
+def load_timeline():
+    """Load the timeline build (libmpgemm_timeline.so) on its own, beside the
+    product library: a ctypes handle with mpgemm_f16f32 and the three
+    mpgemm_timeline_* entry points typed."""
+    global _timeline
+    if _timeline is not None:
+        return _timeline
+    if not os.path.exists(TIMELINE_PATH):
+        raise RuntimeError(f"{TIMELINE_PATH} is not built; run `python -m dense_mixed_precision_amd.build`")
+    lib = ctypes.CDLL(TIMELINE_PATH)
+    i64, vp, i32, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.mpgemm_f16f32.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, f32, f32, vp]
+    lib.mpgemm_f16f32.restype = i32
+    lib.mpgemm_timeline_entries.argtypes = []
+    lib.mpgemm_timeline_entries.restype = i64
+    lib.mpgemm_timeline_read.argtypes = [vp, i64]
+    lib.mpgemm_timeline_read.restype = i32
+    lib.mpgemm_timeline_clear.argtypes = []
+    lib.mpgemm_timeline_clear.restype = i32
+    _timeline = lib
     return lib
 
 

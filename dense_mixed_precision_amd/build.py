@@ -7,6 +7,9 @@
   fallbacks;
 * ``libmpgemm_probes.so`` -- the diagnostics (``csrc/probes.hip``, C ABI in
   ``include/mpgemm_probes.h``);
+* ``libmpgemm_timeline.so`` -- the product library built with
+  ``-DMPGEMM_TIMELINE``: the same entry points and results, plus the
+  per-workgroup timeline of ``include/mpgemm_timeline.h`` (diagnostics);
 * with ``candidates=True`` also ``libmpgemm_candidates.so``: the product
   library plus the alternative tile shapes of tile sweeps
   (``-DMPGEMM_CANDIDATES``), which the factory never picks.
@@ -33,6 +36,7 @@ DEPS = [SRC, os.path.join(CSRC, "kernels.hpp"), os.path.join(ROOT, "include", "m
 LIB = os.path.join(HERE, "libmpgemm.so")
 PROBES_LIB = os.path.join(HERE, "libmpgemm_probes.so")
 CANDIDATES_LIB = os.path.join(HERE, "libmpgemm_candidates.so")
+TIMELINE_LIB = os.path.join(HERE, "libmpgemm_timeline.so")
 ARCH = "gfx950"
 
 
@@ -70,11 +74,12 @@ def _finish(job):
 def build(extra=(), out: str = LIB, verbose: bool = False, probes: bool = True,
           candidates: bool = False) -> str:
     """Compile the product library to ``out`` (default: in-tree
-    ``libmpgemm.so``), the diagnostics library, and optionally the
-    candidates library, in parallel.  Returns ``out``."""
+    ``libmpgemm.so``), the diagnostics libraries (probes, timeline), and
+    optionally the candidates library, in parallel.  Returns ``out``."""
     jobs = [_start(SRC, out, extra, verbose)]
     if probes:
         jobs.append(_start(PROBES_SRC, PROBES_LIB, extra, verbose))
+        jobs.append(_start(SRC, TIMELINE_LIB, (*extra, "-DMPGEMM_TIMELINE"), verbose))
     if candidates:
         jobs.append(_start(SRC, CANDIDATES_LIB, (*extra, "-DMPGEMM_CANDIDATES"), verbose))
     errors = []

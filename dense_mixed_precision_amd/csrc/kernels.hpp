@@ -55,6 +55,21 @@ constexpr int32_t kStoreNT = 2;
 // each with a private L2.
 constexpr int kNumXcd = 8;
 
+#ifdef MPGEMM_TIMELINE
+// Timeline build only (libmpgemm_timeline.so, a diagnostics library; the
+// product library compiles none of this).  The pipelined kernel records, for
+// each of the first kTimelineWgs workgroups of a launch, when it started,
+// when each of its first kTimelineTiles K tiles was published, and when its
+// K loop and its epilogue ended (slot layout in mpgemm_timeline.h).  Thread 0
+// keeps the stamps in LDS while the kernel runs -- LDS writes do not count
+// against the vector memory counter the ring's waits rely on -- and copies
+// them to g_timeline after its last store.
+constexpr int kTimelineSlots = 48;
+constexpr int kTimelineWgs = 4096;
+constexpr int kTimelineTiles = 41;
+__device__ uint64_t g_timeline[kTimelineWgs * kTimelineSlots];
+#endif
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
@@ -580,6 +595,24 @@ gemm_pipe(GemmArgs args_in)
     const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
     const int tid = threadIdx.x;
+#ifdef MPGEMM_TIMELINE
+    __shared__ uint64_t timeline[kTimelineSlots];
+    if (tid == 0) {
+        timeline[0] = __builtin_amdgcn_s_memrealtime();
+        timeline[1] = __builtin_amdgcn_s_memtime();
+        for (int i = 2; i < kTimelineSlots; ++i)
+            timeline[i] = 0;
+    }
+#endif
+    // timeline build: shader-clock stamp of tile t's publish (no code otherwise)
+    auto stamp_tile = [&](int64_t t) __attribute__((always_inline)) {
+#ifdef MPGEMM_TIMELINE
+        if (tid == 0 && t < kTimelineTiles)
+            timeline[2 + t] = __builtin_amdgcn_s_memtime();
+#else
+        (void)t;
+#endif
+    };
     const int lane = tid & 63;
     // wave index, made explicitly wave-uniform so everything derived from it
     // (copy offsets, M0) stays in scalar registers
@@ -837,6 +870,7 @@ gemm_pipe(GemmArgs args_in)
                 copy_one(c);
         }
         publish(0, 0, (int)(num_k - 1 < S - 1 ? num_k - 1 : S - 1));
+        stamp_tile(0);
 #pragma unroll
         for (int grp = 0; grp < FM; ++grp)
             read_group(0, ks0, 0, grp);
@@ -855,6 +889,7 @@ gemm_pipe(GemmArgs args_in)
                 // tiles kt+2 .. kt+S-1 may still be in flight
                 const int64_t newer = num_k - 2 - kt;
                 publish(kt + 1, nbuf, (int)(newer < S - 2 ? newer : S - 2));
+                stamp_tile(kt + 1);
             }
             if (last)
                 begin_copies(kt + S, buf);
@@ -944,6 +979,11 @@ gemm_pipe(GemmArgs args_in)
                     acc[i][j] = mfma16<Cfg::IN>(ta[i], tb[j], acc[i][j]);
             }
     }
+
+#ifdef MPGEMM_TIMELINE
+    if (tid == 0)
+        timeline[44] = __builtin_amdgcn_s_memtime();
+#endif
 
     // ---- epilogue: C = alpha*acc + beta*C through buffer stores whose
     // out-of-range offsets the hardware drops (and loads read as zero).
@@ -1082,6 +1122,20 @@ gemm_pipe(GemmArgs args_in)
         }
         }
     }
+#ifdef MPGEMM_TIMELINE
+    if (tid == 0) {
+        timeline[45] = __builtin_amdgcn_s_memtime();
+        timeline[46] = __builtin_amdgcn_s_memrealtime();
+        uint32_t hw_id, xcc_id;
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw_id));
+        asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc_id));
+        timeline[47] = ((uint64_t)xcc_id << 32) | hw_id;
+        timeline[43] = (uint64_t)num_k;
+        if (blockIdx.x < kTimelineWgs)
+            for (int i = 0; i < kTimelineSlots; ++i)
+                g_timeline[(int64_t)blockIdx.x * kTimelineSlots + i] = timeline[i];
+    }
+#endif
 }
 
 // ---------------------------------------------------------------------------

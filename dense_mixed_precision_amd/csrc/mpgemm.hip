@@ -9,6 +9,9 @@
 // fills the 256 compute units, with the 64-bit direct kernel for whatever
 // the tiled kernels' 32-bit buffer offsets cannot address.
 #include "mpgemm.h"
+#ifdef MPGEMM_TIMELINE
+#include "mpgemm_timeline.h"
+#endif
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -920,5 +923,35 @@ const char *mpgemm_strerror(int code)
 }
 
 const char *mpgemm_version(void) { return "mpgemm 0.7.0 gfx950"; }
+
+#ifdef MPGEMM_TIMELINE
+// Timeline build only: host access to the per-workgroup stamps the
+// pipelined kernel leaves in mpg::g_timeline.
+int64_t mpgemm_timeline_entries(void) { return (int64_t)mpg::kTimelineWgs * mpg::kTimelineSlots; }
+
+int mpgemm_timeline_read(uint64_t *out, int64_t entries)
+{
+    if (out == nullptr)
+        return MPGEMM_ENULL;
+    if (entries < 0 || entries > mpgemm_timeline_entries())
+        return MPGEMM_EDIM;
+    if (entries == 0)
+        return MPGEMM_OK;
+    if (hipDeviceSynchronize() != hipSuccess)
+        return MPGEMM_ELAUNCH;
+    return hipMemcpyFromSymbol(out, HIP_SYMBOL(mpg::g_timeline), (size_t)entries * sizeof(uint64_t), 0,
+                               hipMemcpyDeviceToHost) == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
+}
+
+int mpgemm_timeline_clear(void)
+{
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(mpg::g_timeline)) != hipSuccess || p == nullptr)
+        return MPGEMM_ELAUNCH;
+    if (hipMemset(p, 0, (size_t)mpgemm_timeline_entries() * sizeof(uint64_t)) != hipSuccess)
+        return MPGEMM_ELAUNCH;
+    return hipDeviceSynchronize() == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
+}
+#endif
 
 }  // extern "C"

@@ -15,6 +15,7 @@ from dense_mixed_precision_amd.workloads import WORKLOADS
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mpgemm.h")
 PROBES_HEADER = os.path.join(ROOT, "include", "mpgemm_probes.h")
+TIMELINE_HEADER = os.path.join(ROOT, "include", "mpgemm_timeline.h")
 
 FAKE_A = 0x7F0000000000   # 256-byte aligned fake device addresses
 FAKE_B = 0x7F1000000000
@@ -47,6 +48,22 @@ def test_probes_library_exports_its_header_and_the_product_none_of_it():
     assert not [n for n in probes if not hasattr(lib, n)]
     product = ctypes.CDLL(mp.lib_path())
     assert not [n for n in probes if hasattr(product, n)]
+
+
+def test_timeline_build_exports_its_header_and_the_product_none_of_it():
+    names = declared_functions(TIMELINE_HEADER)
+    assert names == ["mpgemm_timeline_clear", "mpgemm_timeline_entries", "mpgemm_timeline_read"]
+    lib = mp.load_timeline()
+    assert not [n for n in names + declared_functions() if not hasattr(lib, n)]
+    product = ctypes.CDLL(mp.lib_path())
+    assert not [n for n in names if hasattr(product, n)]
+    assert lib.mpgemm_timeline_entries() == 4096 * mp.TIMELINE_SLOTS
+    # argument checks come before any HIP call
+    assert lib.mpgemm_timeline_read(None, 1) == mp.MPGEMM_ENULL
+    out = (ctypes.c_uint64 * 4)()
+    assert lib.mpgemm_timeline_read(out, -1) == mp.MPGEMM_EDIM
+    assert lib.mpgemm_timeline_read(out, 4096 * mp.TIMELINE_SLOTS + 1) == mp.MPGEMM_EDIM
+    assert lib.mpgemm_timeline_read(out, 0) == mp.MPGEMM_OK
 
 
 def test_version_and_strerror():

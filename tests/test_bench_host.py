@@ -58,3 +58,34 @@ def test_spread_reports_median_and_cv():
 
 def test_cpu_model_is_reported():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_timeline_summary_reads_the_record_layout():
+    """Synthetic records with a 2 GHz shader clock: 2 us to the first tile,
+    1.2 us between tiles, 0.5 us to the loop end, 0.3 us of epilogue."""
+    import numpy as np
+
+    nwg, ntiles, ghz = 16, 5, 2.0
+    rec = np.zeros((nwg, 48), dtype=np.uint64)
+    for b in range(nwg):
+        rt0, mt0 = 1000 + b, 5_000_000 + 37 * b
+        cyc = [mt0, mt0 + 4000]                       # start, tile 0 after 2 us
+        for _ in range(1, ntiles):
+            cyc.append(cyc[-1] + 2400)                # 1.2 us per tile
+        loop_end = cyc[-1] + 1000
+        epi_end = loop_end + 600
+        rec[b, 0], rec[b, 1] = rt0, mt0
+        for t in range(ntiles):
+            rec[b, 2 + t] = cyc[1 + t]
+        rec[b, 43], rec[b, 44], rec[b, 45] = ntiles, loop_end, epi_end
+        rec[b, 46] = rt0 + round((epi_end - mt0) / ghz / 10)   # 100 MHz ticks
+        rec[b, 47] = ((b % 8) << 32) | 0x123
+    s = bench.timeline_summary(rec, nwg)
+    assert s["k_tiles"] == ntiles and s["workgroups"] == nwg
+    assert abs(s["shader_clock_GHz"] - ghz) < 0.01
+    assert abs(s["first_tile_us"] - 2.0) < 0.01
+    assert s["tile_interval_us"] == [1.2] * (ntiles - 1)
+    assert abs(s["last_recorded_tile_to_loop_end_us"] - 0.5) < 0.01
+    assert abs(s["epilogue_us"] - 0.3) < 0.01
+    assert s["start_skew_us"]["max"] == 0.15
+    assert sorted(s["xcd_end_us"]) == list(range(8))
