@@ -413,13 +413,15 @@ def fill_rate(torch, mp):
     buf = torch.ones(48 * MiB // 4, dtype=torch.float32, device=dev)
     wgs = 256
     sink = torch.empty(wgs * 512, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(wgs * 4, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
     names = {mp.MPGEMM_FILL_LDS16: "lds16", mp.MPGEMM_FILL_REG16: "reg16", mp.MPGEMM_FILL_REG4: "reg4"}
+    ghz = {}
 
-    def measure(mode, depth, footprint, shared=0, replicas=1, workgroups=wgs):
+    def measure(mode, depth, footprint, shared=0, replicas=1, workgroups=wgs, key=None):
         passes = max(4, int(64 * 6 * MiB // footprint)) if workgroups == wgs else 16
         args = (mode, depth, buf.data_ptr(), buf.numel() * 4, footprint, shared, replicas, passes, workgroups,
-                sink.data_ptr(), sink.numel(), stream.cuda_stream)
+                sink.data_ptr(), sink.numel(), clocks.data_ptr(), clocks.numel(), stream.cuda_stream)
         rc = mp.mpgemm_probe_fill(*args)
         if rc != mp.MPGEMM_OK:
             raise mp.MpgemmError(rc, "mpgemm_probe_fill")
@@ -432,6 +434,9 @@ def fill_rate(torch, mp):
             e1.record(stream)
             torch.cuda.synchronize()
             best = min(best, e0.elapsed_time(e1) * 1e-3)
+        if key is not None:
+            c = clocks[:4 * workgroups].view(workgroups, 4).cpu().double()
+            ghz[key] = round(float(((c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 100e6)).median()) / 1e9, 3)
         return round(footprint * passes / best / 1e9, 1)
 
     out = {"per_xcd_GBps": {}, "unit": "GB/s per XCD (unique bytes)"}
@@ -445,11 +450,36 @@ def fill_rate(torch, mp):
     # one workgroup per XCD: what a single compute unit's copy path moves
     out["per_cu_GBps"] = {}
     for depth in (1, 2, 4, 8, 16):
-        out["per_cu_GBps"][f"hit_2MiB_lds16_d{depth}_1cu"] = measure(mp.MPGEMM_FILL_LDS16, depth, 2 * MiB,
-                                                                      workgroups=8)
+        key = f"hit_2MiB_lds16_d{depth}_1cu"
+        out["per_cu_GBps"][key] = measure(mp.MPGEMM_FILL_LDS16, depth, 2 * MiB, workgroups=8, key=key)
     for depth in (2, 8):
-        out["per_cu_GBps"][f"hit_2MiB_lds16_d{depth}_32cu"] = round(
-            out["per_xcd_GBps"][f"hit_2MiB_lds16_d{depth}"] / 32, 1)
+        key = f"hit_2MiB_lds16_d{depth}_32cu"
+        out["per_cu_GBps"][key] = round(measure(mp.MPGEMM_FILL_LDS16, depth, 2 * MiB, key=key) / 32, 1)
+    # a stream from HBM: 128 MiB per XCD (1 GiB in all, four times the
+    # memory-side cache), each byte once per pass
+    big = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    out["stream_GBps"] = {}
+    for mode, depth in ((mp.MPGEMM_FILL_LDS16, 4), (mp.MPGEMM_FILL_LDS16, 8), (mp.MPGEMM_FILL_LDS16, 16),
+                        (mp.MPGEMM_FILL_REG16, 8)):
+        args = (mode, depth, big.data_ptr(), big.numel() * 4, 128 * MiB, 0, 1, 2, wgs, sink.data_ptr(),
+                sink.numel(), 0, 0, stream.cuda_stream)
+        rc = mp.mpgemm_probe_fill(*args)
+        if rc != mp.MPGEMM_OK:
+            raise mp.MpgemmError(rc, "mpgemm_probe_fill")
+        best = float("inf")
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            mp.mpgemm_probe_fill(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e-3)
+        out["stream_GBps"][f"stream_1GiB_{names[mode]}_d{depth}"] = round((1 << 30) * 2 / best / 1e9, 1)
+    del big
+    # the same in bytes per shader clock (each case's median workgroup clock)
+    out["shader_clock_GHz"] = ghz
+    out["per_cu_bytes_per_clk"] = {k: round(v / ghz[k], 1) for k, v in out["per_cu_GBps"].items()}
     vals = out["per_xcd_GBps"]
     out["best_fill_GBps"] = max(v for k, v in vals.items() if k.startswith("fill_6MiB_") and "_x8cu" not in k)
     out["best_hit_GBps"] = max(v for k, v in vals.items() if k.startswith("hit_"))

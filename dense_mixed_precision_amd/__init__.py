@@ -26,7 +26,7 @@ Diagnostics (libmpgemm_probes.so):
     mpgemm_probe_mfma_layout(shape, out, stream)
     mpgemm_probe_mfma_rate(in_type, shape, ops, ops_len, iters, workgroups, out, out_len, stream)
     mpgemm_probe_fill(mode, depth, buf, buf_bytes, footprint, shared, replicas, passes, workgroups,
-                      sink, sink_len, stream)
+                      sink, sink_len, clocks, clocks_len, stream)
 
 Timeline build (libmpgemm_timeline.so, include/mpgemm_timeline.h), loaded
 beside the product by ``load_timeline()``: mpgemm_f16f32 plus

@@ -146,7 +146,7 @@ def load_probes():
     lib.mpgemm_probe_mfma_layout.restype = i32
     lib.mpgemm_probe_mfma_rate.argtypes = [i32, i32, vp, i64, i64, i32, vp, i64, vp]
     lib.mpgemm_probe_mfma_rate.restype = i32
-    lib.mpgemm_probe_fill.argtypes = [i32, i32, vp, i64, i64, i32, i32, i64, i32, vp, i64, vp]
+    lib.mpgemm_probe_fill.argtypes = [i32, i32, vp, i64, i64, i32, i32, i64, i32, vp, i64, vp, i64, vp]
     lib.mpgemm_probe_fill.restype = i32
     _probes = lib
     return lib
@@ -313,9 +313,10 @@ def mpgemm_probe_mfma_rate(in_type: int, shape: int, ops: int, ops_len: int, ite
 
 
 def mpgemm_probe_fill(mode: int, depth: int, buf: int, buf_bytes: int, footprint: int, shared: int,
-                      replicas: int, passes: int, workgroups: int, sink: int, sink_len: int, stream=0) -> int:
+                      replicas: int, passes: int, workgroups: int, sink: int, sink_len: int, clocks: int = 0,
+                      clocks_len: int = 0, stream=0) -> int:
     return int(load_probes().mpgemm_probe_fill(mode, depth, buf, buf_bytes, footprint, shared, replicas,
-                                               passes, workgroups, sink, sink_len, stream))
+                                               passes, workgroups, sink, sink_len, clocks, clocks_len, stream))
 
 
 def mpgemm_strerror(code: int) -> str:

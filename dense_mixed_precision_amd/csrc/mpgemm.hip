@@ -226,6 +226,11 @@ const Entry kTable[] = {
     pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 8>>(60),
     pipe_entry<PipeCfg<32, 64, 128, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16, 64>>(61),
     pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 32, 4>>(62),
+    // deeper rings of 64-deep K tiles: more of a streamed A in flight
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 4>>(63),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 5>>(64),
+    pipe_entry<PipeCfg<64, 128, 64, 1, 4, 3>>(65),
+    pipe_entry<PipeCfg<64, 128, 64, 1, 4, 4>>(66),
 #endif
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);

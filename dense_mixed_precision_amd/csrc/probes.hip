@@ -103,8 +103,10 @@ probe_mfma_rate(const uint16_t *ops, int64_t iters, float *out)
 // forms XOR what they load into one value per thread and store it.
 template <int MODE, int DEPTH>
 __global__ void __launch_bounds__(512)
-probe_fill(const uint8_t *buf, uint32_t footprint, int shared, int replicas, int64_t passes, float *sink)
+probe_fill(const uint8_t *buf, uint32_t footprint, int shared, int replicas, int64_t passes, float *sink,
+           uint64_t *clocks)
 {
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
     __shared__ __attribute__((aligned(1024))) uint8_t lds_sink[8 * 1024];
     constexpr uint32_t REQ = MODE == 2 ? 4 : 16;     // bytes per lane
     constexpr uint32_t BLK = 64 * REQ;               // bytes per wave instruction
@@ -162,6 +164,15 @@ probe_fill(const uint8_t *buf, uint32_t footprint, int shared, int replicas, int
         }
     }
     sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = __builtin_bit_cast(float, acc);
+    // the workgroup's shader-clock and 100 MHz-clock spans (thread 0's view)
+    if (clocks != nullptr && threadIdx.x == 0) {
+        const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+        uint64_t *c = clocks + 4 * (int64_t)blockIdx.x;
+        c[0] = t0;
+        c[1] = t1;
+        c[2] = r0;
+        c[3] = r1;
+    }
 }
 
 }  // namespace mpg
@@ -170,28 +181,28 @@ namespace {
 
 template <int MODE>
 hipError_t launch_fill(int depth, dim3 grid, hipStream_t s, const uint8_t *buf, uint32_t footprint,
-                       int shared, int replicas, int64_t passes, float *sink)
+                       int shared, int replicas, int64_t passes, float *sink, uint64_t *clocks)
 {
     switch (depth) {
     case 1:
         hipLaunchKernelGGL((mpg::probe_fill<MODE, 1>), grid, dim3(512), 0, s, buf, footprint, shared, replicas,
-                           passes, sink);
+                           passes, sink, clocks);
         break;
     case 2:
         hipLaunchKernelGGL((mpg::probe_fill<MODE, 2>), grid, dim3(512), 0, s, buf, footprint, shared, replicas,
-                           passes, sink);
+                           passes, sink, clocks);
         break;
     case 4:
         hipLaunchKernelGGL((mpg::probe_fill<MODE, 4>), grid, dim3(512), 0, s, buf, footprint, shared, replicas,
-                           passes, sink);
+                           passes, sink, clocks);
         break;
     case 8:
         hipLaunchKernelGGL((mpg::probe_fill<MODE, 8>), grid, dim3(512), 0, s, buf, footprint, shared, replicas,
-                           passes, sink);
+                           passes, sink, clocks);
         break;
     default:
         hipLaunchKernelGGL((mpg::probe_fill<MODE, 16>), grid, dim3(512), 0, s, buf, footprint, shared, replicas,
-                           passes, sink);
+                           passes, sink, clocks);
         break;
     }
     return hipGetLastError();
@@ -242,7 +253,7 @@ int mpgemm_probe_mfma_rate(int in_type, int shape, const uint16_t *ops, int64_t 
 
 int mpgemm_probe_fill(int mode, int depth, const void *buf, int64_t buf_bytes, int64_t footprint,
                       int shared, int replicas, int64_t passes, int workgroups, float *sink,
-                      int64_t sink_len, void *stream)
+                      int64_t sink_len, uint64_t *clocks, int64_t clocks_len, void *stream)
 {
     if (mode != MPGEMM_FILL_LDS16 && mode != MPGEMM_FILL_REG16 && mode != MPGEMM_FILL_REG4)
         return MPGEMM_ECONFIG;
@@ -260,6 +271,8 @@ int mpgemm_probe_fill(int mode, int depth, const void *buf, int64_t buf_bytes, i
         return MPGEMM_EDIM;
     if (passes < 1 || passes > ((int64_t)1 << 20) || sink_len < (int64_t)workgroups * 512)
         return MPGEMM_EDIM;
+    if (clocks != nullptr && clocks_len < (int64_t)workgroups * 4)
+        return MPGEMM_EDIM;
     (void)hipGetLastError();
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)workgroups);
@@ -267,11 +280,11 @@ int mpgemm_probe_fill(int mode, int depth, const void *buf, int64_t buf_bytes, i
     const uint32_t fp = (uint32_t)footprint;
     hipError_t err;
     if (mode == MPGEMM_FILL_LDS16)
-        err = launch_fill<0>(depth, grid, s, b, fp, shared, replicas, passes, sink);
+        err = launch_fill<0>(depth, grid, s, b, fp, shared, replicas, passes, sink, clocks);
     else if (mode == MPGEMM_FILL_REG16)
-        err = launch_fill<1>(depth, grid, s, b, fp, shared, replicas, passes, sink);
+        err = launch_fill<1>(depth, grid, s, b, fp, shared, replicas, passes, sink, clocks);
     else
-        err = launch_fill<2>(depth, grid, s, b, fp, shared, replicas, passes, sink);
+        err = launch_fill<2>(depth, grid, s, b, fp, shared, replicas, passes, sink, clocks);
     return err == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
 }
 

@@ -86,15 +86,20 @@ int mpgemm_probe_mfma_rate(int in_type, int shape, const uint16_t *ops, int64_t 
  * call = footprint * passes * replicas (requested) and footprint * passes
  * (unique).  Register forms write each thread's XOR of what it loaded to
  * sink[thread id] (sink_len >= workgroups*512 floats; the LDS form writes
- * zeros there), so no load is dead.
+ * zeros there), so no load is dead.  `clocks` is NULL or device memory for
+ * clocks_len >= 4 * workgroups uint64 values: workgroup b writes its shader
+ * clock (s_memtime) at its start and end to clocks[4b], clocks[4b + 1] and
+ * the constant 100 MHz clock (s_memrealtime) at its start and end to
+ * clocks[4b + 2], clocks[4b + 3], so a caller can state a rate in bytes per
+ * shader clock.
  * footprint: a positive multiple of 64 KiB with footprint * (shared ? 1 : 8)
  * <= buf_bytes < 2^31.  MPGEMM_ECONFIG for an unknown mode or depth,
- * MPGEMM_EDIM for any other size out of range, MPGEMM_ENULL for NULL,
- * MPGEMM_EALIGN for a buffer that is not 16-byte aligned.
+ * MPGEMM_EDIM for any other size out of range, MPGEMM_ENULL for NULL buf or
+ * sink, MPGEMM_EALIGN for a buffer that is not 16-byte aligned.
  */
 int mpgemm_probe_fill(int mode, int depth, const void *buf, int64_t buf_bytes, int64_t footprint,
                       int shared, int replicas, int64_t passes, int workgroups, float *sink,
-                      int64_t sink_len, void *stream);
+                      int64_t sink_len, uint64_t *clocks, int64_t clocks_len, void *stream);
 
 #ifdef __cplusplus
 }

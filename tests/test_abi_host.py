@@ -441,9 +441,9 @@ def test_mfma_rate_probe_rejects_bad_arguments_before_launch():
 
 def test_fill_probe_rejects_bad_arguments_before_launch():
     names = ("mode", "depth", "buf", "buf_bytes", "footprint", "shared", "replicas", "passes", "workgroups",
-             "sink", "sink_len", "stream")
+             "sink", "sink_len", "clocks", "clocks_len", "stream")
     ok = dict(zip(names, (mp.MPGEMM_FILL_LDS16, 8, FAKE_A, 8 << 20, 1 << 20, 0, 1, 4, 256, FAKE_C,
-                          256 * 512, 0)))
+                          256 * 512, FAKE_C, 4 * 256, 0)))
 
     def call(**kw):
         args = dict(ok)
@@ -462,6 +462,7 @@ def test_fill_probe_rejects_bad_arguments_before_launch():
     assert call(buf_bytes=1 << 31, footprint=1 << 20) == mp.MPGEMM_EDIM
     assert call(passes=0) == mp.MPGEMM_EDIM
     assert call(sink_len=256 * 512 - 1) == mp.MPGEMM_EDIM
+    assert call(clocks_len=4 * 256 - 1) == mp.MPGEMM_EDIM   # too short for the clock spans
 
 
 def test_factory_gives_narrow_products_the_narrow_kernel():
