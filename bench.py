@@ -75,15 +75,20 @@ def parse():
     return p.parse_args()
 
 
+#: the sources the product library is compiled from
+PRODUCT_SOURCES = ("dense_mixed_precision_amd/csrc/kernels.hpp", "dense_mixed_precision_amd/csrc/mpgemm.hip",
+                   "include/mpgemm.h")
+
+
 def kernel_source_digest() -> str:
-    """Digest of the HIP sources; counter readings are only reused while it matches."""
+    """Digest of the sources the product library is built from (not the
+    diagnostics'); counter readings are only reused while it matches."""
     import hashlib
 
     h = hashlib.sha256()
-    base = os.path.join(ROOT, "dense_mixed_precision_amd", "csrc")
-    for name in sorted(os.listdir(base)):
-        with open(os.path.join(base, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+    for rel in PRODUCT_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

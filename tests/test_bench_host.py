@@ -89,3 +89,16 @@ def test_timeline_summary_reads_the_record_layout():
     assert abs(s["epilogue_us"] - 0.3) < 0.01
     assert s["start_skew_us"]["max"] == 0.15
     assert sorted(s["xcd_end_us"]) == list(range(8))
+
+
+def test_kernel_source_digest_covers_exactly_the_product_sources():
+    """The digest changes with the product library's sources and with
+    nothing else under csrc/ (the diagnostics' probes.hip)."""
+    import os
+
+    assert set(bench.PRODUCT_SOURCES) == {"dense_mixed_precision_amd/csrc/kernels.hpp",
+                                          "dense_mixed_precision_amd/csrc/mpgemm.hip", "include/mpgemm.h"}
+    from dense_mixed_precision_amd import build
+
+    built_from = {os.path.relpath(p, bench.ROOT) for p in build.DEPS}
+    assert built_from == set(bench.PRODUCT_SOURCES)
