@@ -103,7 +103,10 @@ typedef struct mpgemm_config {
     int64_t grid;        /* workgroups for the queried shape (0 in the table)     */
     int32_t layout_a;    /* storage order of A the entry reads (MPGEMM_*_MAJOR)   */
     int32_t layout_b;    /* storage order of B; the direct and scale kernels take
-                            any order and report the one they were asked for     */
+                            any order and report the one they were asked for.
+                            A one-column row-major B with ldb == 1 (K
+                            consecutive values) is read, and reported, as
+                            column-major: the same bytes                        */
     int32_t in_type;     /* input format the entry reads (MPGEMM_IN_*)            */
     int32_t k_groups;    /* wave groups sharing each LDS tile, each taking its own
                             k-steps over the whole block; threads =

@@ -181,6 +181,25 @@ def test_factory_choices_for_the_workloads():
     assert (c["bm"], c["bn"], c["bk"], c["stages"], c["k_order"]) == (128, 128, 128, 2, 2)
 
 
+def test_one_column_row_major_b_is_read_as_column_major():
+    """A (K x 1) row-major B with ldb 1 is K consecutive values: when the
+    narrow kernel takes the product, the factory reads the column-major form
+    of the same bytes (K-contiguous loads); a strided column, a wider B, or
+    a product another kernel takes keeps the order it was given."""
+    c = q(4096, 1, 4096, ldb=1)
+    assert c["kind_name"] == "narrow" and c["layout_b"] == mp.MPGEMM_COL_MAJOR
+    c = q(4096, 1, 4096, ldb=8)
+    assert c["kind_name"] == "narrow" and c["layout_b"] == mp.MPGEMM_ROW_MAJOR
+    assert q(4096, 2, 4096)["layout_b"] == mp.MPGEMM_ROW_MAJOR
+    # only the narrow kernel takes the other form: a column-major A keeps B as given
+    c = ql(mp.MPGEMM_COL_MAJOR, mp.MPGEMM_ROW_MAJOR, 2048, 1, 2048, ldb=1)
+    assert c["kind_name"] == "pipe" and c["layout_b"] == mp.MPGEMM_ROW_MAJOR
+    # the caller's arguments are validated as given: ldb 0 is still refused
+    assert code(4096, 1, 4096, ldb=0) == mp.MPGEMM_ELD
+    plan = mp.mpgemm_splitk_plan(mp.MPGEMM_IN_F16, 0, 0, 4096, 1, 4096, FAKE_A, 4096, FAKE_B, 1, 0)
+    assert mp.mpgemm_config_info(plan["config_id"])["layout_b"] == mp.MPGEMM_COL_MAJOR
+
+
 def test_factory_alignment_and_degenerate_cases():
     # any 2-byte aligned operand takes the 16-byte copy path
     assert q(512, 512, 512, A=FAKE_A + 2)["vec_a"] == 8
@@ -474,11 +493,13 @@ def test_factory_gives_narrow_products_the_narrow_kernel():
             if lb and N == 1:
                 continue
             c = ql(0, lb, 1000, N, 617)
-            assert c["kind_name"] == "narrow" and c["layout_b"] == lb and c["grid"] == -(-1000 // 16), (N, lb, c)
+            # a packed one-column row-major B is read in its column-major form
+            want = 1 if N == 1 else lb
+            assert c["kind_name"] == "narrow" and c["layout_b"] == want and c["grid"] == -(-1000 // 16), (N, lb, c)
             assert c["in_type"] == mp.MPGEMM_IN_F16
             c = mp.mpgemm_bf16f32_layout_query(0, lb, 1000, N, 617, FAKE_A, 617, FAKE_B, 617 if lb else N,
                                                FAKE_C, N, 1.0, 0.0)
-            assert c["kind_name"] == "narrow" and c["in_type"] == mp.MPGEMM_IN_BF16 and c["layout_b"] == lb
+            assert c["kind_name"] == "narrow" and c["in_type"] == mp.MPGEMM_IN_BF16 and c["layout_b"] == want
     assert ql(0, 0, 1000, 17, 617)["kind_name"] == "pipe"
     assert ql(1, 0, 1000, 16, 617)["kind_name"] != "narrow"
     assert ql(0, 0, 1000, 16, 617, lda=1 << 27)["kind_name"] == "direct"
