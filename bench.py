@@ -64,6 +64,8 @@ def parse():
                    help="skip the L2 fill-rate probe")
     p.add_argument("--no-timeline", dest="timeline", action="store_false",
                    help="skip the per-workgroup timeline of the headline workload (timeline build)")
+    p.add_argument("--no-breakdown", dest="breakdown", action="store_false",
+                   help="skip the ragged workload's time breakdown")
     p.add_argument("--no-others", action="store_true", help="time only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -818,7 +820,7 @@ def main():
     if args.timeline and args.config is None:
         print("# per-workgroup timeline (timeline build)", file=sys.stderr, flush=True)
         line["timeline"] = timeline(head, torch, mp, warm=max(5, min(200, int(2e13 / head.flop))))
-    if (head.name == "ragged1000x800x617" or not args.no_others) and args.config is None:
+    if args.breakdown and (head.name == "ragged1000x800x617" or not args.no_others) and args.config is None:
         print("# ragged breakdown", file=sys.stderr, flush=True)
         line["ragged_breakdown"] = ragged_breakdown(torch, mp)
     if args.fill and head.name == "square2048" and args.config is None:
