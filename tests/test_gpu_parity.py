@@ -68,6 +68,49 @@ def test_mfma_rate_probe_does_the_work_it_counts(shape, fmt):
     assert torch.all(out == per_lane)
 
 
+@pytest.mark.parametrize("mode", [mp.MPGEMM_FILL_REG16, mp.MPGEMM_FILL_REG4, mp.MPGEMM_FILL_LDS16])
+def test_fill_probe_reads_every_byte_and_reports_clock_spans(mode):
+    """The register forms XOR every 32-bit word a thread loads: with each
+    word of the buffer equal to its own index, a thread's XOR is known from
+    the blocks it reads, so a skipped or misplaced load changes it.  The
+    clock spans are ordered, and the shader clock they imply is plausible."""
+    MiB = 1 << 20
+    words = 8 * MiB // 4
+    buf = torch.arange(words, dtype=torch.int32, device=device())
+    wgs, depth, footprint = 16, 4, 1 * MiB
+    sink = torch.zeros(wgs * 512, dtype=torch.float32, device=device())
+    clocks = torch.zeros(wgs * 4, dtype=torch.int64, device=device())
+    rc = mp.mpgemm_probe_fill(mode, depth, buf.data_ptr(), words * 4, footprint, 0, 1, 1, wgs, sink.data_ptr(),
+                              sink.numel(), clocks.data_ptr(), clocks.numel(), 0)
+    assert rc == mp.MPGEMM_OK
+    torch.cuda.synchronize()
+    c = clocks.view(wgs, 4).cpu().numpy()
+    assert (c[:, 1] > c[:, 0]).all() and (c[:, 3] > c[:, 2]).all()
+    ghz = (c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 100e6) / 1e9
+    assert ((ghz > 0.3) & (ghz < 3.0)).all(), ghz
+    if mode == mp.MPGEMM_FILL_LDS16:
+        assert torch.all(sink == 0)       # the LDS form writes zeros
+        return
+    # expected XOR per thread: workgroup b on XCD x = b % 8, member j = b // 8;
+    # wave u = 8 j + w takes blocks u, u + 8 m, ... (m members per XCD)
+    req = 16 if mode == mp.MPGEMM_FILL_REG16 else 4
+    blk = 64 * req
+    members = wgs // 8
+    nblk = footprint // blk
+    got = sink.view(torch.int32).cpu().numpy().reshape(wgs, 512)
+    for b in (0, 5, wgs - 1):
+        x, j = b % 8, b // 8
+        for t in (0, 63, 64, 511):
+            w, lane = t // 64, t % 64
+            u = j * 8 + w
+            acc = 0
+            for blk_i in range(u, nblk, 8 * members):
+                base = (x * footprint + blk_i * blk + lane * req) // 4
+                for k in range(req // 4):
+                    acc ^= base + k
+            assert got[b, t] == np.int32(np.uint32(acc).view(np.int32)), (b, t)
+
+
 # ----------------------------------------------------------------------------
 # The six workloads
 # ----------------------------------------------------------------------------
