@@ -3,12 +3,15 @@ sizes and in its launch configuration (the factory's choice): the 2048^3 and
 8192^3 workloads with B column-major, A and B column-major, BF16 inputs
 (row-major and B column-major), and a per-column bias.
 
-Each checks sampled entries against the oracle (one in every 128x128 block,
-the last row and column, the corners) within |C - C_ref| <= 1e-3 * S + 1e-5,
-and the whole output with Freivalds' check: for a random +-1 vector x, row i
-of C@x - (alpha*A@(B@x) + bias*sum(x)) is a signed sum of the row's element
-errors, so it is bounded by 1e-3*(|A|@(|B|@|x|))_i + 1e-5*N when every
-element is within tolerance.
+At 2048^3 every element is compared with the oracle; at 8192^3 every
+element of whole 256x256 output tiles (the four corner tiles and one tile at
+each of four XCD slots, one per round of 256 resident workgroups, chosen with
+the kernel's tile order) and of the first and last rows and columns, all
+within |C - C_ref| <= 1e-3 * S + 1e-5 and the accumulation diagnostic.  Both
+also get Freivalds' check over the whole output: for a random +-1 vector x,
+row i of C@x - (alpha*A@(B@x) + bias*sum(x)) is a signed sum of the row's
+element errors, so it is bounded by 1e-3*(|A|@(|B|@|x|))_i + 1e-5*N when
+every element is within tolerance.
 """
 import numpy as np
 import pytest
@@ -17,7 +20,8 @@ import torch
 import dense_mixed_precision_amd as mp
 import oracle
 from dense_mixed_precision_amd.workloads import WORKLOADS, bits, workload_inputs
-from tests.gpu_util import assert_close, run_layout, stored, tile_samples
+from tests.gpu_util import assert_close, run_layout, stored
+from tests.test_gpu_fullsize import kernel_tile
 
 pytestmark = pytest.mark.gpu
 
@@ -41,9 +45,18 @@ def freivalds(got, A, B, alpha, bias, seed):
     return bool(np.all(err <= bound)), float(np.max(err / bound))
 
 
+def query(w, la, lb, fmt):
+    """The factory's choice for the workload in this operand form (no launch;
+    stand-in pointers, which the query only checks for alignment)."""
+    fn = mp.mpgemm_bf16f32_layout_query if fmt == "bf16" else mp.mpgemm_f16f32_layout_query
+    lda = w.M if la else w.K
+    ldb = w.K if lb else w.N
+    return fn(la, lb, w.M, w.N, w.K, 1 << 20, lda, 1 << 21, ldb, 1 << 22, w.N, w.alpha, w.beta)
+
+
 @pytest.mark.parametrize("la,lb,fmt,with_bias", VARIANTS)
 @pytest.mark.parametrize("name", ["square2048", "square8192"])
-def test_bench_variant_sampled_and_freivalds(name, la, lb, fmt, with_bias):
+def test_bench_variant_parity(name, la, lb, fmt, with_bias):
     w = WORKLOADS[name]
     dtype = torch.bfloat16 if fmt == "bf16" else torch.float16
     label = f"{name} A{'col' if la else 'row'} B{'col' if lb else 'row'} {fmt}{' bias' if with_bias else ''}"
@@ -56,10 +69,36 @@ def test_bench_variant_sampled_and_freivalds(name, la, lb, fmt, with_bias):
     got, gC = run_layout(A, B, None, w.alpha, w.beta, la, lb, bias=bias)
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"
     assert gC.untouched_outside_window()
-    rows, cols = tile_samples(w.M, w.N, tile=128, per_tile=1, seed=w.seed + la + 2 * lb)
-    ref, absdot = oracle.gemm_entries(bits(stored(A, la)), bits(stored(B, lb)), None, w.alpha, w.beta, rows,
-                                      cols, layout_a=la, layout_b=lb, in_type=fmt, bias=bias)
-    assert_close(label, got[rows, cols], ref, absdot, rows, cols, K=w.K, alpha=w.alpha)
+    As, Bs = bits(stored(A, la)), bits(stored(B, lb))
+    opts = dict(layout_a=la, layout_b=lb, in_type=fmt, bias=bias)
+    if name == "square2048":
+        print(f"[{label}] oracle over all {w.M * w.N} entries", flush=True)
+        ref, absdot = oracle.gemm(As, Bs, None, w.alpha, w.beta, **opts)
+        assert_close(label, got, ref, absdot, K=w.K, alpha=w.alpha)
+    else:
+        cfg = query(w, la, lb, fmt)
+        T = cfg["bm"]
+        assert (cfg["bm"], cfg["bn"], cfg["grid"]) == (256, 256, 1024)
+        tm_, tn_ = w.M // T, w.N // T
+        rng = np.random.default_rng(w.seed + la + 2 * lb)
+        tiles = {(0, 0), (0, tn_ - 1), (tm_ - 1, 0), (tm_ - 1, tn_ - 1)}
+        for rnd in range(4):
+            x = int(rng.integers(0, 8))
+            tiles.add(kernel_tile(256 * rnd + x + 8 * int(rng.integers(0, 32)), tm_ * tn_, tm_, tn_))
+        print(f"[{label}] {len(tiles)} whole tiles: {sorted(tiles)}", flush=True)
+        for tm, tn in sorted(tiles):
+            rr, cc = np.meshgrid(np.arange(tm * T, tm * T + T), np.arange(tn * T, tn * T + T), indexing="ij")
+            rows, cols = rr.ravel(), cc.ravel()
+            ref, absdot = oracle.gemm_entries(As, Bs, None, w.alpha, w.beta, rows, cols, **opts)
+            assert_close(f"{label} tile ({tm},{tn})", got[rows, cols], ref, absdot, rows, cols, K=w.K,
+                         alpha=w.alpha)
+        rows = np.concatenate([np.zeros(w.N), np.full(w.N, w.M - 1), np.arange(w.M),
+                               np.arange(w.M)]).astype(np.int64)
+        cols = np.concatenate([np.arange(w.N), np.arange(w.N), np.zeros(w.M),
+                               np.full(w.M, w.N - 1)]).astype(np.int64)
+        ref, absdot = oracle.gemm_entries(As, Bs, None, w.alpha, w.beta, rows, cols, **opts)
+        assert_close(f"{label} edge rows/columns", got[rows, cols], ref, absdot, rows, cols, K=w.K,
+                     alpha=w.alpha)
     ok, ratio = freivalds(got, A, B, w.alpha, bias, seed=w.seed)
-    print(f"[{label}] {rows.size} sampled entries ok; Freivalds worst ratio {ratio:.3g}", flush=True)
+    print(f"[{label}] Freivalds worst ratio {ratio:.3g}", flush=True)
     assert ok, f"{label}: Freivalds check failed (worst err/bound {ratio:.3g})"
