@@ -13,7 +13,7 @@ import torch
 import dense_mixed_precision_amd as mp
 import oracle
 from dense_mixed_precision_amd.workloads import bits, make_inputs
-from tests.gpu_util import assert_close, freivalds_ok, run_layout, stored, tile_samples
+from tests.gpu_util import assert_close, freivalds_ok, run_layout, stored
 
 pytestmark = pytest.mark.gpu
 
@@ -86,13 +86,12 @@ def test_wide_exponent_range():
     full_check("bf16 scaled", A, B, None, 1.0, 0.0, 0, 0)
 
 
-def test_2048_sampled_and_freivalds():
+def test_2048_every_element_and_freivalds():
     M = N = K = 2048
     A, B, _ = make_inputs(M, N, K, "uniform", seed=1101, dtype=BF16)
     got, _ = run_layout(A, B, None, 1.0, 0.0, 0, 0)
     assert np.all(np.isfinite(got))
-    rows, cols = tile_samples(M, N, tile=128, per_tile=1, seed=9)
-    ref, absdot = oracle.gemm_entries(bits(A), bits(B), None, 1.0, 0.0, rows, cols, in_type="bf16")
-    assert_close("2048 bf16", got[rows, cols], ref, absdot, rows, cols, K=K, alpha=1.0)
+    ref, absdot = oracle.gemm(bits(A), bits(B), None, 1.0, 0.0, in_type="bf16")
+    assert_close("2048 bf16", got, ref, absdot, K=K, alpha=1.0)
     ok, ratio = freivalds_ok(got, A.float(), B.float(), None, 1.0, 0.0, seed=9)
     assert ok, f"Freivalds failed (worst {ratio:.3g})"

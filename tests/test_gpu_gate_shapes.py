@@ -4,8 +4,9 @@
 normal inputs, 256^3 with adversarial FP16 edge values (+-65504, subnormals,
 the smallest normal, zeros, mixed signs; no FP32 overflow possible), and the
 4096^3 timing shape.  Every element against the oracle where the oracle
-finishes in seconds; sampled entries (one in every 128x128 block, the last
-row and column, the corners) plus Freivalds' whole-output check at 4096^3.
+finishes in seconds; at 4096^3 every element of eight whole 256x256 output
+tiles (the corners and four more) and of the first and last rows and
+columns, plus Freivalds' whole-output check.
 Each shape runs with beta = 0 on a NaN-poisoned C and with alpha = 1.5,
 beta = 0.5 on a prefilled C.
 """
@@ -14,7 +15,7 @@ import pytest
 
 import oracle
 from dense_mixed_precision_amd.workloads import bits, make_inputs
-from tests.gpu_util import assert_close, freivalds_ok, run, tile_samples
+from tests.gpu_util import assert_close, freivalds_ok, run
 
 pytestmark = pytest.mark.gpu
 
@@ -33,15 +34,30 @@ def test_gate_shape_every_element(name, M, N, K, dist):
         assert gC.untouched_outside_window()
 
 
-def test_gate_shape_4096_sampled_and_freivalds():
+def test_gate_shape_4096_tiles_edges_and_freivalds():
     M = N = K = 4096
+    T = 256
     A, B, C = make_inputs(M, N, K, "uniform", seed=4096, c_init="uniform")
-    rows, cols = tile_samples(M, N, tile=128, per_tile=1, seed=4096)
+    Ab, Bb = bits(A), bits(B)
+    rng = np.random.default_rng(4096)
+    tiles = {(0, 0), (0, N // T - 1), (M // T - 1, 0), (M // T - 1, N // T - 1)}
+    while len(tiles) < 8:
+        tiles.add((int(rng.integers(0, M // T)), int(rng.integers(0, N // T))))
+    edge_rows = np.concatenate([np.zeros(N), np.full(N, M - 1), np.arange(M), np.arange(M)]).astype(np.int64)
+    edge_cols = np.concatenate([np.arange(N), np.arange(N), np.zeros(M), np.full(M, N - 1)]).astype(np.int64)
     for alpha, beta, c0 in ((1.0, 0.0, None), (1.5, 0.5, C)):
         got, _ = run(A, B, c0, alpha, beta)
         assert np.all(np.isfinite(got))
-        ref, absdot = oracle.gemm_entries(bits(A), bits(B), None if c0 is None else c0.numpy(), alpha, beta,
-                                          rows, cols)
-        assert_close(f"4096 beta={beta}", got[rows, cols], ref, absdot, rows, cols, K=K, alpha=alpha)
+        cn = None if c0 is None else c0.numpy()
+        for tm, tn in sorted(tiles):
+            r0, c0_ = tm * T, tn * T
+            ref, absdot = oracle.gemm(Ab[r0:r0 + T], Bb[:, c0_:c0_ + T],
+                                      None if cn is None else np.ascontiguousarray(cn[r0:r0 + T, c0_:c0_ + T]),
+                                      alpha, beta)
+            assert_close(f"4096 beta={beta} tile ({tm},{tn})", got[r0:r0 + T, c0_:c0_ + T], ref, absdot,
+                         K=K, alpha=alpha)
+        ref, absdot = oracle.gemm_entries(Ab, Bb, cn, alpha, beta, edge_rows, edge_cols)
+        assert_close(f"4096 beta={beta} edge rows/columns", got[edge_rows, edge_cols], ref, absdot, edge_rows,
+                     edge_cols, K=K, alpha=alpha)
         ok, ratio = freivalds_ok(got, A, B, c0, alpha, beta, seed=4096)
         assert ok, f"4096 beta={beta}: Freivalds failed (worst {ratio:.3g})"
