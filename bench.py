@@ -667,6 +667,28 @@ def timeline(w, torch, mp, warm=200, launches=3):
     return out
 
 
+def copy_bound(w, cfg, tl, fill, kernel_ms):
+    """The launch time this tiling allows when every compute unit's copies
+    into LDS run at the best rate the fill probe measured for all compute
+    units copying at once (bytes per shader clock), at the shader clock the
+    timeline measured under this load: each workgroup copies (BM + BN) * K * 2
+    bytes, plus the first-tile wait and the epilogue the timeline measured
+    (they do not overlap the loop).  A bound for this decomposition, not for
+    the product: another tiling moves other bytes."""
+    per_cu = fill["per_cu_bytes_per_clk"]
+    rate = max(v for k, v in per_cu.items() if k.endswith("_32cu"))
+    ghz = tl["shader_clock_GHz"]
+    copy_bytes = (cfg["bm"] + cfg["bn"]) * w.K * 2
+    loop_us = copy_bytes / rate / (ghz * 1e3)
+    # the first tile's copies are part of the first-tile wait
+    loop_us *= (tl["k_tiles"] - 1) / tl["k_tiles"]
+    bound_us = loop_us + tl["first_tile_us"] + tl["epilogue_us"]
+    return {"copy_bytes_per_workgroup": copy_bytes, "copy_bytes_per_clk": rate, "shader_clock_GHz": ghz,
+            "loop_us": round(loop_us, 3), "first_tile_us": tl["first_tile_us"], "epilogue_us": tl["epilogue_us"],
+            "bound_us": round(bound_us, 3), "bound_tflops": round(w.flop / (bound_us * 1e-6) / 1e12, 1),
+            "kernel_us": round(kernel_ms * 1e3, 3), "frac_of_bound": round(bound_us / (kernel_ms * 1e3), 3)}
+
+
 def roofline_entry(w, kernel_ms):
     """MFMA bound for the compute-heavy shapes, HBM bound where the
     arithmetic intensity (FLOP per algorithmic byte) is below the ridge."""
@@ -826,6 +848,9 @@ def main():
     if args.fill and head.name == "square2048" and args.config is None:
         print("# L2 fill-rate probe", file=sys.stderr, flush=True)
         line["fill_rate"] = fill_rate(torch, mp)
+        if line.get("timeline"):
+            line["copy_bound"] = copy_bound(head, res["cfg"], line["timeline"], line["fill_rate"],
+                                            res["kernel_ms"])
     others = {}
     if not args.no_others:
         for name, w in WORKLOADS.items():

@@ -102,3 +102,18 @@ def test_kernel_source_digest_covers_exactly_the_product_sources():
 
     built_from = {os.path.relpath(p, bench.ROOT) for p in build.DEPS}
     assert built_from == set(bench.PRODUCT_SOURCES)
+
+
+def test_copy_bound_adds_the_loop_at_the_copy_rate_to_the_measured_phases():
+    w = WORKLOADS["square2048"]
+    cfg = {"bm": 128, "bn": 128}
+    tl = {"shader_clock_GHz": 2.0, "k_tiles": 16, "first_tile_us": 2.5, "epilogue_us": 1.5}
+    fill = {"per_cu_bytes_per_clk": {"hit_2MiB_lds16_d2_1cu": 40.0, "hit_2MiB_lds16_d2_32cu": 32.0,
+                                     "hit_2MiB_lds16_d8_32cu": 25.0}}
+    b = bench.copy_bound(w, cfg, tl, fill, 0.025)
+    copy = (128 + 128) * 2048 * 2
+    assert b["copy_bytes_per_workgroup"] == copy and b["copy_bytes_per_clk"] == 32.0
+    loop = copy / 32.0 / 2000.0 * 15 / 16            # us: bytes / (B/clk) / (clk per us), less the first tile
+    assert abs(b["loop_us"] - loop) < 1e-3
+    assert abs(b["bound_us"] - (loop + 4.0)) < 1e-3
+    assert abs(b["frac_of_bound"] - (loop + 4.0) / 25.0) < 1e-3
