@@ -109,6 +109,24 @@ def test_exact_integers_and_determinism():
     assert np.array_equal(g1, g2)
 
 
+@pytest.mark.parametrize("splits", [2, 3])
+def test_forced_splits_on_the_staggered_k_order_entry(splits):
+    """Forced pieces on a shape the 128x128x128 entry takes: its workgroups
+    walk their piece's K tiles in a rotated order (k_order 2), so every
+    piece's K range must still be covered once.  Exact small integers make
+    every order give the same bits; uniform inputs go to the oracle."""
+    M, N, K = 1024, 2048, 1024 + 640
+    A, B, _ = make_inputs(M, N, K, "smallint", seed=98)
+    got, _, plan = run_split(A, B, None, 1.0, 0.0, splits=splits)
+    c = mp.mpgemm_config_info(plan["config_id"])
+    assert plan["splits"] == splits and (c["bm"], c["bn"], c["bk"], c["k_order"]) == (128, 128, 128, 2), plan
+    # small integers: every product and sum is exact in float64 as in FP32
+    exact = A.numpy().astype(np.float64) @ B.numpy().astype(np.float64)
+    assert np.array_equal(got, exact.astype(np.float32))
+    A, B, C = make_inputs(M, N, K, "uniform", seed=99, c_init="uniform")
+    check(f"staggered splits={splits}", A, B, C, 1.5, 0.5, splits=splits)
+
+
 def test_single_piece_is_the_ordinary_path():
     """A full grid plans one piece and needs no workspace: bit for bit the
     ordinary call."""
