@@ -1073,53 +1073,55 @@ gemm_pipe(GemmArgs args_in)
                 }
             }
         } else {
-        // the bias of each of this lane's FN columns (0 past the last column)
-        float bv[FN];
+            // the bias of each of this lane's FN columns (0 past the last column)
+            float bv[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-            bv[j] = 0.0f;
-        if (args.bias) {
-            const __amdgpu_buffer_rsrc_t rsBias = make_rsrc(args.bias + wcol0);
+            for (int j = 0; j < FN; ++j)
+                bv[j] = 0.0f;
+            if (args.bias) {
+                const __amdgpu_buffer_rsrc_t rsBias = make_rsrc(args.bias + wcol0);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int c = MI * j + cl;
-                bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                      rsBias, c < wcols ? (uint32_t)(c * 4) : kOOB, 0, 0));
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int c = MI * j + cl;
-                const bool c_ok = c < wcols;
-                uint32_t off[AV];
-#pragma unroll
-                for (int v = 0; v < AV; ++v) {
-                    const int r = MI * i + rl + (MI == 32 ? 8 * (v >> 2) + (v & 3) : v);
-                    off[v] = (c_ok && r < wrows) ? (uint32_t)((r * ldc + c) * 4) : kOOB;
-                }
-                // With beta != 0 all of the tile's C loads go out before its
-                // first store: the loads and stores share a buffer, so the
-                // compiler keeps them in program order, and loading each
-                // element just before its store would serialize the loads.
-                float cin[AV];
-                if (beta != 0.0f) {
-#pragma unroll
-                    for (int v = 0; v < AV; ++v)
-                        cin[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsC, off[v], 0, 0));
-                }
-#pragma unroll
-                for (int v = 0; v < AV; ++v) {
-                    float val = alpha * acc[i][j][v];
-                    if (beta != 0.0f)
-                        val = __builtin_fmaf(beta, cin[v], val);
-                    if (args.bias)
-                        val += bv[j];
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off[v], 0, kStoreNT);
+                for (int j = 0; j < FN; ++j) {
+                    const int c = MI * j + cl;
+                    bv[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                          rsBias, c < wcols ? (uint32_t)(c * 4) : kOOB, 0, 0));
                 }
             }
-        }
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int c = MI * j + cl;
+                    const bool c_ok = c < wcols;
+                    uint32_t off[AV];
+#pragma unroll
+                    for (int v = 0; v < AV; ++v) {
+                        const int r = MI * i + rl + (MI == 32 ? 8 * (v >> 2) + (v & 3) : v);
+                        off[v] = (c_ok && r < wrows) ? (uint32_t)((r * ldc + c) * 4) : kOOB;
+                    }
+                    // With beta != 0 all of the tile's C loads go out before its
+                    // first store: the loads and stores share a buffer, so the
+                    // compiler keeps them in program order, and loading each
+                    // element just before its store would serialize the loads.
+                    float cin[AV];
+                    if (beta != 0.0f) {
+#pragma unroll
+                        for (int v = 0; v < AV; ++v)
+                            cin[v] = __builtin_bit_cast(
+                                float, __builtin_amdgcn_raw_buffer_load_b32(rsC, off[v], 0, 0));
+                    }
+#pragma unroll
+                    for (int v = 0; v < AV; ++v) {
+                        float val = alpha * acc[i][j][v];
+                        if (beta != 0.0f)
+                            val = __builtin_fmaf(beta, cin[v], val);
+                        if (args.bias)
+                            val += bv[j];
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off[v], 0,
+                                                              kStoreNT);
+                    }
+                }
+            }
         }
     }
 #ifdef MPGEMM_TIMELINE
