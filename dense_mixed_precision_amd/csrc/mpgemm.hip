@@ -200,37 +200,43 @@ const Entry kTable[] = {
     narrow_entry<kInF16, kColMajor, 4>(38),
     narrow_entry<kInBF16, kRowMajor, 4>(39),
     narrow_entry<kInBF16, kColMajor, 4>(40),
+    // small row-major FP16 products whose 64x64 tiles would leave most of the
+    // chip idle and whose B rows hold whole 16-byte vectors: 16x64 tiles on
+    // 4 waves, twice the workgroups of 32x64 and fewer bytes copied by each
+    pipe_entry<PipeCfg<16, 64, 128, 1, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16>>(41),
 #ifdef MPGEMM_CANDIDATES
     // Alternatives the factory does not choose, compiled only into the
     // candidates build for tile sweeps (FP16, A and B row-major).
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2>>(41),                   // 32x32x16 on the big tile
-    pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4>>(42),                   // 4 waves of 128x128
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 2>>(43),
-    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, kRowMajor, kRowMajor, kInF16, 2, 32, 2>>(44),  // 2 k-groups
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2>>(45),                  // ascending K order
-    pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3>>(46),                   // 4 waves
-    pipe_entry<PipeCfg<256, 128, 64, 4, 2, 3>>(47),
-    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 32, 2>>(48),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 2>>(49),
-    pipe_entry<PipeCfg<64, 64, 128, 2, 2, 3>>(50),                    // 4 waves of 32x32x16
-    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(51),
-    pipe_entry<PipeCfg<32, 64, 128, 2, 2, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(52),
-    narrow_entry<kInF16, kRowMajor, 8>(53),                           // 8 k-steps in flight
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2>>(42),                   // 32x32x16 on the big tile
+    pipe_entry<PipeCfg<256, 256, 32, 2, 2, 4>>(43),                   // 4 waves of 128x128
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 2>>(44),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 2, 2, kRowMajor, kRowMajor, kInF16, 2, 32, 2>>(45),  // 2 k-groups
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2>>(46),                  // ascending K order
+    pipe_entry<PipeCfg<128, 128, 64, 2, 2, 3>>(47),                   // 4 waves
+    pipe_entry<PipeCfg<256, 128, 64, 4, 2, 3>>(48),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 32, 2>>(49),
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 2>>(50),
+    pipe_entry<PipeCfg<64, 64, 128, 2, 2, 3>>(51),                    // 4 waves of 32x32x16
+    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(52),
+    pipe_entry<PipeCfg<32, 64, 128, 2, 2, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(53),
+    narrow_entry<kInF16, kRowMajor, 8>(54),                           // 8 k-steps in flight
     // K orders with more start offsets
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 32, 4>>(54),
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 32, 8>>(55),
-    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 32, 16>>(56),
-    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 64>>(57),
-    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 2>>(58),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 4>>(59),
-    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 8>>(60),
-    pipe_entry<PipeCfg<32, 64, 128, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16, 64>>(61),
-    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 32, 4>>(62),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 32, 4>>(55),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 32, 8>>(56),
+    pipe_entry<PipeCfg<128, 128, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 32, 16>>(57),
+    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 64>>(58),
+    pipe_entry<PipeCfg<64, 64, 128, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 2>>(59),
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 4>>(60),
+    pipe_entry<PipeCfg<256, 256, 64, 2, 4, 2, kRowMajor, kRowMajor, kInF16, 1, 16, 8>>(61),
+    pipe_entry<PipeCfg<32, 64, 128, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16, 64>>(62),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 32, 4>>(63),
     // deeper rings of 64-deep K tiles: more of a streamed A in flight
-    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 4>>(63),
-    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 5>>(64),
-    pipe_entry<PipeCfg<64, 128, 64, 1, 4, 3>>(65),
-    pipe_entry<PipeCfg<64, 128, 64, 1, 4, 4>>(66),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 4>>(64),
+    pipe_entry<PipeCfg<128, 128, 64, 2, 4, 5>>(65),
+    pipe_entry<PipeCfg<64, 128, 64, 1, 4, 3>>(66),
+    pipe_entry<PipeCfg<64, 128, 64, 1, 4, 4>>(67),
+    // 16x64 tiles with a 3-deep ring
+    pipe_entry<PipeCfg<16, 64, 128, 1, 4, 3, kRowMajor, kRowMajor, kInF16, 1, 16>>(68),
 #endif
 };
 constexpr int kNumEntries = sizeof(kTable) / sizeof(kTable[0]);
@@ -241,6 +247,7 @@ constexpr int family(int in, int la, int lb) { return 3 + 16 * in + 4 * (la + 2 
 // small row-major FP16 products, K tiles of 128: 64x64 and 32x64
 constexpr int kSmallDeepKId = 35;
 constexpr int kTinyDeepKId = 36;
+constexpr int kTiny16Id = 41;
 // narrow kernel (N <= 16, A row-major) per input format and storage order of B
 constexpr int kNarrowIds[2][2] = {{37, 38}, {39, 40}};
 // below this many 16-row workgroups the narrow kernel leaves most compute
@@ -417,12 +424,19 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
     } else if (small_deep_k && p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR &&
                p.lb == MPGEMM_ROW_MAJOR && p.K > 64) {
         // Small row-major FP16 products with more than one 64-deep K tile
-        // take K tiles of 128 (half as many barriers per K) on 8 waves:
-        // 32x64 tiles when 64x64 ones would fill less than half the chip
-        // (256^3: 3.6 against 4.1 us per call), else 64x64 (ragged
-        // 1000x800x617: 7.1 against 7.3 us).
-        if (mul_sat(cdiv(p.M, 64), cdiv(p.N, 64)) < kNumCu / 2)
+        // take K tiles of 128 (half as many barriers per K) and the
+        // 16x16x32 instruction.  When 64x64 tiles would fill less than half
+        // the chip: 16x64 tiles on 4 waves (256^3: 3.36 against 3.68 us for
+        // 32x64 and 4.4 for 64x64), unless N is not a multiple of 8 -- then
+        // the last column of tiles fills partial B vectors through registers
+        // on every K tile, which 8 waves share better: 32x64 on 8 waves
+        // (200x300x400: 6.7 against 8.1 us).  Otherwise 64x64 on 8 waves
+        // (ragged 1000x800x617: 7.1 against 7.3 us for 4 waves).
+        if (mul_sat(cdiv(p.M, 64), cdiv(p.N, 64)) < kNumCu / 2) {
+            if (p.N % 8 == 0)
+                order[n++] = kTiny16Id;
             order[n++] = kTinyDeepKId;
+        }
         order[n++] = kSmallDeepKId;
     }
     order[n++] = fam + kSmall;
@@ -557,7 +571,7 @@ SplitPlan plan_split(const Problem &p, int requested)
     if (narrow && requested == 0 && cdiv(p.M, 16) >= kNarrowMinGroups)
         return sp;
     int id = narrow ? select(p, true, false) : sp.id;
-    if (id == kSmallDeepKId || id == kTinyDeepKId)
+    if (id == kSmallDeepKId || id == kTinyDeepKId || id == kTiny16Id)
         id = select(p, false, false);
     const mpgemm_config &c = kTable[id].cfg;
     if (c.kind != MPGEMM_KIND_PIPE)

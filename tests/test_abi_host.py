@@ -171,8 +171,11 @@ def test_factory_choices_for_the_workloads():
     # 208 tiles of 64x64 fill more than half the chip: 64x64, 8 waves, 2 stages
     assert (c["bm"], c["bn"], c["bk"], c["stages"], c["threads"], c["mfma_m"]) == (64, 64, 128, 2, 512, 16)
     c = _pick(WORKLOADS["square256"])
-    # 16 tiles of 64x64 would leave most of the chip idle: 32x64 tiles
-    assert c["kind_name"] == "pipe" and c["grid"] == 32
+    # 16 tiles of 64x64 would leave most of the chip idle: 16x64 tiles on 4 waves
+    assert c["kind_name"] == "pipe" and c["grid"] == 64
+    assert (c["bm"], c["bn"], c["bk"], c["stages"], c["threads"], c["mfma_m"]) == (16, 64, 128, 2, 256, 16)
+    # ... unless N is not a multiple of 8 (partial B vectors on every K tile): 32x64 on 8 waves
+    c = q(200, 300, 400)
     assert (c["bm"], c["bn"], c["bk"], c["stages"], c["threads"]) == (32, 64, 128, 3, 512)
     # one K tile of 64 or less keeps the 64-deep tile
     assert q(256, 256, 64)["bk"] == 64
@@ -518,7 +521,7 @@ def test_product_table_holds_what_the_factory_can_choose():
             for lb in (0, 1):
                 f = mp.mpgemm_bf16f32_layout_query if in_type else mp.mpgemm_f16f32_layout_query
                 for M, N, K in [(8192, 8192, 8192), (2048, 2048, 2048), (32768, 128, 4096), (256, 256, 256), (1000, 800, 617),
-                                (256, 256, 64), (1000, 16, 617), (300, 300, 64)]:
+                                (256, 256, 64), (1000, 16, 617), (300, 300, 64), (200, 300, 400)]:
                     lda = M if la else K
                     ldb = K if lb else N
                     chosen.add(f(la, lb, M, N, K, FAKE_A, lda, FAKE_B, ldb, FAKE_C, N, 1.0, 0.0)["id"])
