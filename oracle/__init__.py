@@ -245,6 +245,54 @@ def gemm_entries(A, B, C, alpha: float, beta: float, rows, cols,
     return ref, absdot
 
 
+def gemm_matmul(A, B, C=None, alpha: float = 1.0, beta: float = 0.0,
+                layout_a: int = ROW_MAJOR, layout_b: int = ROW_MAJOR, in_type: str = "f16", bias=None):
+    """The same full product as :func:`gemm`, with the K-sums taken by a
+    library FP64 matrix product (numpy's ``@``) instead of the C loop, for
+    sizes the loop cannot finish in a test's time (8192^3: about half an hour
+    on 8 cores for the loop, seconds for the library product).  Returns ``(ref,
+    absdot)`` like :func:`gemm`, with the same conventions (operands,
+    layouts, bias, alpha and beta rounded to float32, C not read when
+    ``beta == 0``, A and B not read when ``alpha == 0`` or ``K == 0``).
+
+    It is still the plain definition ("Capstone 4: a tensor-core GEMM",
+    Compare like with like: every element against the double-precision
+    result): the inputs are widened exactly by the oracle's own decoders,
+    every product of two widened inputs is exact in FP64, and only the order
+    in which the library adds them differs from the loop's ascending k, so
+    each sum is within K * 2^-53 * S of the exact one on both paths
+    (S = sum_k |a_ik b_kj|) and the two agree to 2 * K * 2^-53 * S, eight
+    orders of magnitude inside the acceptance tolerance at K = 8192.  The
+    library product does not promise the loop's handling of Inf and NaN, so
+    operands that are read must be finite (``ValueError`` otherwise; use
+    :func:`gemm` for non-finite inputs)."""
+    _bf16_flag(in_type)
+    A, _, B, _, M, N, K = _operands(A, B, layout_a, layout_b)
+    bias = _as_bias(bias, N)
+    alpha = float(np.float32(alpha))
+    beta = float(np.float32(beta))
+    C, _ = _as_c(C, M, N, beta)
+    ref = np.zeros((M, N), dtype=np.float64)
+    absdot = np.zeros((M, N), dtype=np.float64)
+    if alpha != 0.0 and K > 0 and M > 0 and N > 0:
+        decode = bf16_to_f64 if in_type == "bf16" else f16_to_f64
+        a = decode(A)
+        b = decode(B)
+        if not (np.all(np.isfinite(a)) and np.all(np.isfinite(b))):
+            raise ValueError("gemm_matmul needs finite A and B; use gemm for Inf or NaN inputs")
+        if layout_a == COL_MAJOR:
+            a = a.T
+        if layout_b == COL_MAJOR:
+            b = b.T
+        ref = alpha * (a @ b)
+        absdot = np.abs(a) @ np.abs(b)
+    if beta != 0.0:
+        ref = ref + beta * C.astype(np.float64)
+    if bias is not None:
+        ref = ref + bias.astype(np.float64)[None, :]
+    return ref, absdot
+
+
 def tolerance_ok(got, ref, absdot):
     """Elementwise acceptance: ``|got - ref| <= 1e-3*absdot + 1e-5``.
 

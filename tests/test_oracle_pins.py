@@ -12,6 +12,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from dense_mixed_precision_amd.workloads import WORKLOADS, bits, make_inputs, workload_inputs
@@ -667,3 +668,83 @@ def test_accumulation_bound_terms():
     got[1] = np.nan
     assert oracle.accumulation_ratio(got, ref, absdot, 100, 1.0) == np.inf
     assert oracle.accumulation_ratio(np.zeros(2), np.zeros(2), np.zeros(2), 0, 1.0) == 0.0
+
+
+# ----------------------------------------------------------------------------
+# The library-matmul form of the full product (for the 8192^3 comparisons)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (17, 15, 33), (33, 31, 65)])
+@pytest.mark.parametrize("in_type", ["f16", "bf16"])
+def test_matmul_form_against_exact_rationals(M, N, K, in_type):
+    """Every layout pair (rows wider than the extents, NaN in the padding),
+    with beta and a bias, against exact rational arithmetic (within the FP64
+    sum's own rounding bound)."""
+    dtype = torch.bfloat16 if in_type == "bf16" else torch.float16
+    A, B, C = make_inputs(M, N, K, "uniform", seed=3 * M + K, c_init="uniform", dtype=dtype)
+    Ab, Bb, C_np = bits(A), bits(B), C.numpy()
+    bias = np.linspace(-1.0, 1.0, N).astype(np.float32)
+    eref, eabs, _ = exact_gemm(Ab, Bb, C_np, -0.75, 1.5, in_type=in_type, bias=bias)
+    bound = fp64_sum_bound(K, -0.75, 1.5, eabs, C_np, bias)
+    for la in (oracle.ROW_MAJOR, oracle.COL_MAJOR):
+        for lb in (oracle.ROW_MAJOR, oracle.COL_MAJOR):
+            ref, absdot = oracle.gemm_matmul(_stored(Ab, la, pad=3), _stored(Bb, lb, pad=5), C_np, -0.75, 1.5,
+                                             layout_a=la, layout_b=lb, in_type=in_type, bias=bias)
+            assert np.all(np.abs(ref - eref) <= bound), (la, lb)
+            assert np.allclose(absdot, eabs, rtol=(K + 1) * 2.0 ** -52, atol=0), (la, lb)
+
+
+@pytest.mark.parametrize("name", ["square256", "ragged1000x800x617"])
+def test_matmul_form_against_the_loop(name):
+    """The two forms of the full product differ only in the order of the
+    FP64 additions: within twice the FP64 sum bound of each other."""
+    w = WORKLOADS[name]
+    A, B, C = workload_inputs(w)
+    C_np = None if C is None else C.numpy()
+    ref, absdot = oracle.gemm(bits(A), bits(B), C_np, w.alpha, w.beta)
+    ref2, absdot2 = oracle.gemm_matmul(bits(A), bits(B), C_np, w.alpha, w.beta)
+    bound = 2 * fp64_sum_bound(w.K, w.alpha, w.beta, absdot, C_np)
+    assert np.all(np.abs(ref - ref2) <= bound)
+    assert np.allclose(absdot, absdot2, rtol=2 * w.K * 2.0 ** -53, atol=0)
+
+
+def test_matmul_form_exact_integers():
+    """Small integers on a ragged shape: every sum is exact, so the result
+    equals int64 matmul bit for bit."""
+    A, B, _ = make_inputs(123, 77, 617, "smallint", seed=11)
+    ref, absdot = oracle.gemm_matmul(bits(A), bits(B))
+    ints = A.numpy().astype(np.int64) @ B.numpy().astype(np.int64)
+    assert np.array_equal(ref, ints.astype(np.float64))
+    assert np.array_equal(absdot, np.abs(A.numpy().astype(np.int64)) @ np.abs(B.numpy().astype(np.int64)))
+
+
+def test_matmul_form_special_cases():
+    """alpha = 0 and K = 0 read neither A nor B (non-finite operands allowed,
+    the result is beta*C plus the bias and the sum of |a*b| is 0); beta = 0
+    does not read C; otherwise non-finite operands are refused."""
+    M, N, K = 6, 9, 31
+    A, B, C = make_inputs(M, N, K, "uniform", seed=5, c_init="uniform")
+    Ab, Bb, C_np = bits(A).copy(), bits(B), C.numpy()
+    Ab[2, 3] = 0x7E00                          # FP16 NaN
+    bias = np.arange(N, dtype=np.float32)
+    ref, absdot = oracle.gemm_matmul(Ab, Bb, C_np, 0.0, 0.5, bias=bias)
+    assert np.array_equal(ref, 0.5 * C_np.astype(np.float64) + bias.astype(np.float64))
+    assert np.all(absdot == 0)
+    ref0, _ = oracle.gemm(Ab, Bb, C_np, 0.0, 0.5, bias=bias)
+    assert np.array_equal(ref, ref0)
+    refk, _ = oracle.gemm_matmul(np.zeros((M, 0), np.uint16), np.zeros((0, N), np.uint16), C_np, 1.0, 2.0)
+    assert np.array_equal(refk, 2.0 * C_np.astype(np.float64))
+    with pytest.raises(ValueError, match="finite"):
+        oracle.gemm_matmul(Ab, Bb, C_np, 1.0, 0.5)
+    nan_c = np.full((M, N), np.nan, dtype=np.float32)
+    r1, _ = oracle.gemm_matmul(bits(A), Bb, nan_c, 1.0, 0.0)
+    assert np.all(np.isfinite(r1))
+
+
+def test_matmul_form_catches_a_transposed_operand():
+    """A square B passed in the wrong storage order gives a different
+    product, which the comparison with the loop detects."""
+    A, B, _ = make_inputs(16, 16, 16, "uniform", seed=9)
+    ref, absdot = oracle.gemm(bits(A), bits(B))
+    wrong, _ = oracle.gemm_matmul(bits(A), bits(B), layout_b=oracle.COL_MAJOR)
+    assert not np.all(np.abs(ref - wrong) <= 2 * fp64_sum_bound(16, 1.0, 0.0, absdot))
