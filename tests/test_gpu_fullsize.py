@@ -6,11 +6,13 @@ like" and "Results").
 
 * 2048^3 (the headline) and the tall-skinny 32768x128x4096 workload: every
   element.
-* 8192^3: every element of whole 256x256 output tiles -- one tile at each of
-  the 8 XCD slots in each of the 4 rounds of 256 workgroups the 1024-tile
-  grid runs in, and the four corner tiles -- plus the whole first and last
-  rows and columns (an entry of every edge tile), and Freivalds' check over
-  the whole output.
+* 8192^3: every element, against the oracle's library-matmul form of the
+  product (the C loop would take about half an hour here); and, against the
+  loop form itself, every element of whole 256x256 output tiles -- one tile
+  at each of the 8 XCD slots in each of the 4 rounds of 256 workgroups the
+  1024-tile grid runs in, and the four corner tiles -- plus the whole first
+  and last rows and columns (an entry of every edge tile), and Freivalds'
+  check over the whole output.
 
 Each comparison also applies the accumulation diagnostic (the error against
 the worst case of an FP32 running sum of K products).
@@ -36,6 +38,16 @@ def test_workload_every_element(name):
     print(f"[{name}] oracle over all {w.M * w.N} entries ({oracle.num_threads()} threads)", flush=True)
     ref, absdot = oracle.gemm(bits(A), bits(B), None if C is None else C.numpy(), w.alpha, w.beta)
     assert_close(name, got, ref, absdot, K=w.K, alpha=w.alpha)
+
+
+def test_square8192_every_element():
+    w = WORKLOADS["square8192"]
+    A, B, C = workload_inputs(w)
+    got, gC = run(A, B, C, w.alpha, w.beta)
+    assert gC.untouched_outside_window()
+    print(f"[square8192] oracle (library-matmul form) over all {w.M * w.N} entries", flush=True)
+    ref, absdot = oracle.gemm_matmul(bits(A), bits(B), None if C is None else C.numpy(), w.alpha, w.beta)
+    assert_close("square8192", got, ref, absdot, K=w.K, alpha=w.alpha)
 
 
 def kernel_tile(bid, nb, tiles_m, tiles_n, group_m=8, xcds=8):
