@@ -3,10 +3,10 @@
 128^3, the odd 611x613x617 case, the skinny 4096x16x4096 case, 1024^3 with
 normal inputs, 256^3 with adversarial FP16 edge values (+-65504, subnormals,
 the smallest normal, zeros, mixed signs; no FP32 overflow possible), and the
-4096^3 timing shape.  Every element against the oracle where the oracle
-finishes in seconds; at 4096^3 every element of eight whole 256x256 output
-tiles (the corners and four more) and of the first and last rows and
-columns, plus Freivalds' whole-output check.
+4096^3 timing shape.  Every element against the oracle; at 4096^3 against
+its library-matmul form, and, against the C loop itself, every element of
+eight whole 256x256 output tiles (the corners and four more) and of the
+first and last rows and columns, plus Freivalds' whole-output check.
 Each shape runs with beta = 0 on a NaN-poisoned C and with alpha = 1.5,
 beta = 0.5 on a prefilled C.
 """
@@ -49,6 +49,8 @@ def test_gate_shape_4096_tiles_edges_and_freivalds():
         got, _ = run(A, B, c0, alpha, beta)
         assert np.all(np.isfinite(got))
         cn = None if c0 is None else c0.numpy()
+        ref, absdot = oracle.gemm_matmul(Ab, Bb, cn, alpha, beta)
+        assert_close(f"4096 beta={beta} every element", got, ref, absdot, K=K, alpha=alpha)
         for tm, tn in sorted(tiles):
             r0, c0_ = tm * T, tn * T
             ref, absdot = oracle.gemm(Ab[r0:r0 + T], Bb[:, c0_:c0_ + T],
