@@ -761,8 +761,9 @@ def cpu_baseline(w, res, seconds):
         out["gpu_rows_worst_err_over_tol"] = float(err.max())
         # the error against the worst case of an FP32 running sum (at most 1
         # for FP32 accumulation; an FP16 running sum exceeds it)
+        epi = oracle.epilogue_abs(w.beta, None if Cn is None else Cn[r0:r0 + rows])
         out["gpu_rows_accumulation_ratio"] = oracle.accumulation_ratio(got[r0:r0 + rows], ref, absdot, w.K,
-                                                                       w.alpha)
+                                                                       w.alpha, epilogue_abs=epi)
     return out
 
 

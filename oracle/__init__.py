@@ -310,19 +310,23 @@ U_FP32 = 2.0 ** -24
 TINY_FP32 = 2.0 ** -126
 
 
-def accumulation_bound(ref, absdot, K: int, alpha: float, extra_adds: int = 64):
+def accumulation_bound(ref, absdot, K: int, alpha: float, extra_adds: int = 64, epilogue_abs=0.0):
     """Worst-case error of an FP32 running sum of exact products (recursive
     summation, gamma_n = n*u/(1 - n*u) with u = 2^-24) plus the epilogue's
     own roundings:
 
-        gamma_n * |alpha| * S + 2u * |ref| + K * 2^-126 + 2^-149,   n = K + extra_adds
+        gamma_n * |alpha| * S + 3u * E + 2u * |ref| + K * 2^-126 + 2^-149,   n = K + extra_adds
 
-    S = sum_k |a_ik b_kj| (the oracle's ``absdot``).  ``extra_adds`` covers
-    the additions a kernel makes beyond the K of the product (partial sums
-    of split pieces or of K slices, the alpha scaling, the beta and bias
-    terms); the last term allows for FP32 partial sums below the normal
-    range being flushed (2^-149, the smallest FP32 value, keeps the bound
-    positive).  This is a diagnostic, not the acceptance rule:
+    S = sum_k |a_ik b_kj| (the oracle's ``absdot``); E = |beta*c| + |bias|
+    (``epilogue_abs``, from :func:`epilogue_abs`; 0 without C and bias).
+    ``extra_adds`` covers the additions a kernel makes beyond the K of the
+    product (partial sums of split pieces or of K slices, the alpha
+    scaling); the E term covers the rounding of beta*c and of the two
+    additions that bring in beta*c and the bias, whose operands can be far
+    larger than the result when they cancel; the last terms allow for FP32
+    partial sums below the normal range being flushed (2^-149, the smallest
+    FP32 value, keeps the bound positive).  This is a diagnostic, not the
+    acceptance rule:
     an FP32-accumulating kernel stays below it on any data, while an FP16
     (or BF16) running sum exceeds it by orders of magnitude on ordinary
     data, although the acceptance rule can still pass it ("Capstone 4: a
@@ -332,11 +336,27 @@ def accumulation_bound(ref, absdot, K: int, alpha: float, extra_adds: int = 64):
     n = K + extra_adds
     gamma = n * U_FP32 / (1.0 - n * U_FP32)
     alpha = abs(float(np.float32(alpha)))
-    return (gamma * alpha * np.asarray(absdot) + 2 * U_FP32 * np.abs(ref) + K * TINY_FP32
-            + 2.0 ** -149)
+    return (gamma * alpha * np.asarray(absdot) + 3 * U_FP32 * np.asarray(epilogue_abs)
+            + 2 * U_FP32 * np.abs(ref) + K * TINY_FP32 + 2.0 ** -149)
 
 
-def accumulation_ratio(got, ref, absdot, K: int, alpha: float, extra_adds: int = 64) -> float:
+def epilogue_abs(beta: float, C=None, bias=None, rows=None, cols=None):
+    """E = |beta*c_ij| + |bias_j| for :func:`accumulation_bound`: over the
+    whole (M, N) C, or at entries (rows[t], cols[t]) when those are given;
+    0.0 when there is neither a C term (beta == 0 or no C) nor a bias."""
+    beta = float(np.float32(beta))
+    e = 0.0
+    if beta != 0.0 and C is not None:
+        c = np.asarray(C, dtype=np.float64)
+        e = np.abs(beta * (c[rows, cols] if rows is not None else c))
+    if bias is not None:
+        b = np.abs(np.asarray(bias, dtype=np.float64))
+        e = e + (b[cols] if rows is not None else b[None, :])
+    return e
+
+
+def accumulation_ratio(got, ref, absdot, K: int, alpha: float, extra_adds: int = 64,
+                       epilogue_abs=0.0) -> float:
     """max |got - ref| / accumulation_bound(...) over the finite entries of
     ``ref`` (NaN/Inf in ``got`` there count as infinitely far); 0 for no
     entries.  At most 1 for an FP32-accumulating kernel."""
@@ -347,7 +367,8 @@ def accumulation_ratio(got, ref, absdot, K: int, alpha: float, extra_adds: int =
         return 0.0
     err = np.abs(got[fin] - ref[fin])
     err = np.where(np.isfinite(err), err, np.inf)
-    bound = accumulation_bound(ref[fin], np.asarray(absdot)[fin], K, alpha, extra_adds)
+    epi = np.broadcast_to(np.asarray(epilogue_abs, dtype=np.float64), ref.shape)[fin]
+    bound = accumulation_bound(ref[fin], np.asarray(absdot)[fin], K, alpha, extra_adds, epi)
     return float(np.max(err / bound))
 
 

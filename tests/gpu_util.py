@@ -96,16 +96,20 @@ def describe_failure(label, got, ref, absdot, rows=None, cols=None):
             f"err {w['err']:.3g} > tol {w['tol']:.3g}")
 
 
-def assert_close(label, got, ref, absdot, rows=None, cols=None, *, K, alpha):
+def assert_close(label, got, ref, absdot, rows=None, cols=None, *, K, alpha, beta=0.0, C0=None, bias=None):
     """The acceptance rule |got - ref| <= 1e-3*S + 1e-5 on every element, and
     the accumulation diagnostic: the worst error over the bound an FP32
     running sum of K products obeys (oracle.accumulation_bound) must be at
     most 1, which an FP16 or BF16 running sum would exceed although it can
-    pass the acceptance rule.  Prints the diagnostic ratio."""
+    pass the acceptance rule.  beta, C0 (the whole C before the call) and
+    bias give the bound its epilogue term.  Prints the diagnostic ratio."""
     ok = oracle.tolerance_ok(got, ref, absdot)
     if not ok.all():
         raise AssertionError(describe_failure(label, got, ref, absdot, rows, cols))
-    ratio = oracle.accumulation_ratio(got, ref, absdot, K, alpha)
+    if isinstance(C0, torch.Tensor):
+        C0 = C0.numpy()
+    epi = oracle.epilogue_abs(beta, C0, bias, rows, cols)
+    ratio = oracle.accumulation_ratio(got, ref, absdot, K, alpha, epilogue_abs=epi)
     print(f"[{label}] accumulation ratio {ratio:.3g}", flush=True)
     assert ratio <= 1.0, (f"{label}: error {ratio:.3g} times the FP32 running-sum bound "
                           f"(K = {K}): the sum is not carried in FP32")

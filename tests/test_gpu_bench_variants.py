@@ -73,13 +73,13 @@ def test_bench_variant_parity(name, la, lb, fmt, with_bias):
     if name == "square2048":
         print(f"[{label}] oracle over all {w.M * w.N} entries", flush=True)
         ref, absdot = oracle.gemm(As, Bs, None, w.alpha, w.beta, **opts)
-        assert_close(label, got, ref, absdot, K=w.K, alpha=w.alpha)
+        assert_close(label, got, ref, absdot, K=w.K, alpha=w.alpha, bias=bias)
     else:
         cfg = query(w, la, lb, fmt)
         assert (cfg["bm"], cfg["bn"], cfg["grid"]) == (256, 256, 1024)
         print(f"[{label}] oracle (library-matmul form) over all {w.M * w.N} entries", flush=True)
         ref, absdot = oracle.gemm_matmul(As, Bs, None, w.alpha, w.beta, **opts)
-        assert_close(label, got, ref, absdot, K=w.K, alpha=w.alpha)
+        assert_close(label, got, ref, absdot, K=w.K, alpha=w.alpha, bias=bias)
         del ref, absdot
         rows = np.concatenate([np.zeros(w.N), np.full(w.N, w.M - 1), np.arange(w.M),
                                np.arange(w.M)]).astype(np.int64)
@@ -87,7 +87,7 @@ def test_bench_variant_parity(name, la, lb, fmt, with_bias):
                                np.full(w.M, w.N - 1)]).astype(np.int64)
         ref, absdot = oracle.gemm_entries(As, Bs, None, w.alpha, w.beta, rows, cols, **opts)
         assert_close(f"{label} edge rows/columns", got[rows, cols], ref, absdot, rows, cols, K=w.K,
-                     alpha=w.alpha)
+                     alpha=w.alpha, bias=bias)
     ok, ratio = freivalds(got, A, B, w.alpha, bias, seed=w.seed)
     print(f"[{label}] Freivalds worst ratio {ratio:.3g}", flush=True)
     assert ok, f"{label}: Freivalds check failed (worst err/bound {ratio:.3g})"

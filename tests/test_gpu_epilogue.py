@@ -32,7 +32,7 @@ def check(label, A, B, C0, alpha, beta, la, lb, bias, **kw):
     ref, absdot = oracle.gemm(bits(stored(A, la)), bits(stored(B, lb)),
                               None if C0 is None else C0.numpy(), alpha, beta,
                               layout_a=la, layout_b=lb, in_type=in_type, bias=bias)
-    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha)
+    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha, beta=beta, C0=C0, bias=bias)
     assert gC.untouched_outside_window(), f"{label}: wrote outside the M x N window"
 
 

@@ -37,7 +37,7 @@ def test_workload_every_element(name):
     assert gC.untouched_outside_window()
     print(f"[{name}] oracle over all {w.M * w.N} entries ({oracle.num_threads()} threads)", flush=True)
     ref, absdot = oracle.gemm(bits(A), bits(B), None if C is None else C.numpy(), w.alpha, w.beta)
-    assert_close(name, got, ref, absdot, K=w.K, alpha=w.alpha)
+    assert_close(name, got, ref, absdot, K=w.K, alpha=w.alpha, beta=w.beta, C0=C)
 
 
 def test_square8192_every_element():
@@ -47,7 +47,7 @@ def test_square8192_every_element():
     assert gC.untouched_outside_window()
     print(f"[square8192] oracle (library-matmul form) over all {w.M * w.N} entries", flush=True)
     ref, absdot = oracle.gemm_matmul(bits(A), bits(B), None if C is None else C.numpy(), w.alpha, w.beta)
-    assert_close("square8192", got, ref, absdot, K=w.K, alpha=w.alpha)
+    assert_close("square8192", got, ref, absdot, K=w.K, alpha=w.alpha, beta=w.beta, C0=C)
 
 
 def kernel_tile(bid, nb, tiles_m, tiles_n, group_m=8, xcds=8):

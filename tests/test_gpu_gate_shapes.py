@@ -30,7 +30,7 @@ def test_gate_shape_every_element(name, M, N, K, dist):
     for alpha, beta, c0 in ((1.0, 0.0, None), (1.5, 0.5, C)):
         got, gC = run(A, B, c0, alpha, beta)
         ref, absdot = oracle.gemm(bits(A), bits(B), None if c0 is None else c0.numpy(), alpha, beta)
-        assert_close(f"{name} alpha={alpha} beta={beta}", got, ref, absdot, K=K, alpha=alpha)
+        assert_close(f"{name} alpha={alpha} beta={beta}", got, ref, absdot, K=K, alpha=alpha, beta=beta, C0=c0)
         assert gC.untouched_outside_window()
 
 
@@ -50,16 +50,16 @@ def test_gate_shape_4096_tiles_edges_and_freivalds():
         assert np.all(np.isfinite(got))
         cn = None if c0 is None else c0.numpy()
         ref, absdot = oracle.gemm_matmul(Ab, Bb, cn, alpha, beta)
-        assert_close(f"4096 beta={beta} every element", got, ref, absdot, K=K, alpha=alpha)
+        assert_close(f"4096 beta={beta} every element", got, ref, absdot, K=K, alpha=alpha, beta=beta, C0=cn)
         for tm, tn in sorted(tiles):
             r0, c0_ = tm * T, tn * T
             ref, absdot = oracle.gemm(Ab[r0:r0 + T], Bb[:, c0_:c0_ + T],
                                       None if cn is None else np.ascontiguousarray(cn[r0:r0 + T, c0_:c0_ + T]),
                                       alpha, beta)
             assert_close(f"4096 beta={beta} tile ({tm},{tn})", got[r0:r0 + T, c0_:c0_ + T], ref, absdot,
-                         K=K, alpha=alpha)
+                         K=K, alpha=alpha, beta=beta, C0=None if cn is None else cn[r0:r0 + T, c0_:c0_ + T])
         ref, absdot = oracle.gemm_entries(Ab, Bb, cn, alpha, beta, edge_rows, edge_cols)
         assert_close(f"4096 beta={beta} edge rows/columns", got[edge_rows, edge_cols], ref, absdot, edge_rows,
-                     edge_cols, K=K, alpha=alpha)
+                     edge_cols, K=K, alpha=alpha, beta=beta, C0=cn)
         ok, ratio = freivalds_ok(got, A, B, c0, alpha, beta, seed=4096)
         assert ok, f"4096 beta={beta}: Freivalds failed (worst {ratio:.3g})"

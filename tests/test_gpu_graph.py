@@ -66,7 +66,7 @@ def test_graph_replay_split_k_and_bias():
     torch.cuda.synchronize()
     eager = C.clone()
     ref, absdot = oracle.gemm(bits(A), bits(B), None, 1.0, 0.0, bias=bias.cpu().numpy())
-    assert_close("graph split-K", eager.cpu().numpy(), ref, absdot, K=K, alpha=1.0)
+    assert_close("graph split-K", eager.cpu().numpy(), ref, absdot, K=K, alpha=1.0, bias=bias.cpu().numpy())
     print(f"[graph] split-K {plan['splits']} pieces", flush=True)
     _replays_match(lambda: mp.gemm_splitk(Ad, Bd, C, 1.0, 0.0, bias=bias, workspace=ws, splits=8), C, eager)
     assert np.isfinite(C.cpu().numpy()).all()

@@ -55,5 +55,5 @@ def test_k_tail_every_pipe_config(cfg, K):
     A, B, C = make_inputs(M, N, K, "uniform", seed=cfg * 37 + K, c_init="uniform", dtype=dtype)
     got, gC = run_layout(A, B, C, 1.5, 0.5, la, lb, config=cfg, lda=lda, ldb=ldb, ldc=N + 2)
     ref, absdot = _ref(A, B, C, 1.5, 0.5, la, lb, in_type)
-    assert_close(f"config {cfg} K={K} beta=.5", got, ref, absdot, K=K, alpha=1.5)
+    assert_close(f"config {cfg} K={K} beta=.5", got, ref, absdot, K=K, alpha=1.5, beta=0.5, C0=C)
     assert gC.untouched_outside_window()

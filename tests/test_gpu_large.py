@@ -64,7 +64,8 @@ def test_output_past_2_31_elements():
     mp.gemm(Ad, Bd, C, 1.5, 0.5)
     torch.cuda.synchronize()
     got = C[ri, ci].cpu().numpy()
-    assert_close("large C beta=.5", got, ref + 0.125, absdot, rows, cols, K=K, alpha=1.5)
+    assert_close("large C beta=.5", got, ref + 0.125, absdot, rows, cols, K=K, alpha=1.5, beta=0.5,
+                 C0=np.broadcast_to(np.float32(0.25), (M, N)))
     del flat, C
     torch.cuda.empty_cache()
 

@@ -28,7 +28,7 @@ def oracle_layout(A, B, C0, alpha, beta, la, lb):
 def full_check(label, A, B, C0, alpha, beta, la, lb, **kw):
     got, gC = run_layout(A, B, C0, alpha, beta, la, lb, **kw)
     ref, absdot = oracle_layout(A, B, C0, alpha, beta, la, lb)
-    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha)
+    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha, beta=beta, C0=C0)
     assert gC.untouched_outside_window(), f"{label}: wrote outside the M x N window"
     return got
 

@@ -80,7 +80,7 @@ def test_narrow_config(cfg, M, N, K):
     A, B, C = make_inputs(M, N, K, "uniform", seed=cfg * 17 + M + N + K, c_init="uniform", dtype=dtype)
     got, gC = runner(A, B, C, 1.5, 0.5, 0, lb, config=cfg, lda=lda, ldb=ldb, ldc=N + 2)
     ref, absdot = _ref(A, B, C, 1.5, 0.5, lb, fmt)
-    assert_close(f"config {cfg} {M}x{N}x{K} beta=.5", got, ref, absdot, K=K, alpha=1.5)
+    assert_close(f"config {cfg} {M}x{N}x{K} beta=.5", got, ref, absdot, K=K, alpha=1.5, beta=0.5, C0=C)
     assert gC.untouched_outside_window()
 
 
@@ -113,7 +113,7 @@ def test_narrow_bias_and_scale(cfg):
     bias = np.linspace(-1.0, 1.0, N).astype(np.float32)
     got, _ = run_layout(A, B, C, 0.75, -1.25, 0, lb, config=cfg, bias=bias)
     ref, absdot = _ref(A, B, C, 0.75, -1.25, lb, fmt, bias=bias)
-    assert_close(f"config {cfg} bias", got, ref, absdot, K=K, alpha=0.75)
+    assert_close(f"config {cfg} bias", got, ref, absdot, K=K, alpha=0.75, beta=-1.25, C0=C, bias=bias)
 
 
 def test_narrow_entries_refuse_what_they_cannot_run():

@@ -27,7 +27,7 @@ def _c_np(C):
 def full_check(label, A, B, C0, alpha, beta, **kw):
     got, gC = run(A, B, C0, alpha, beta, **kw)
     ref, absdot = oracle.gemm(bits(A), bits(B), _c_np(C0), alpha, beta)
-    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha)
+    assert_close(label, got, ref, absdot, K=A.shape[1], alpha=alpha, beta=beta, C0=C0)
     assert gC.untouched_outside_window(), f"{label}: wrote outside the M x N window"
     return got, ref
 
@@ -133,7 +133,7 @@ def test_workload_sampled_and_freivalds(name):
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
     rows, cols = tile_samples(w.M, w.N, tile=128, per_tile=1, seed=w.seed)
     ref, absdot = oracle.gemm_entries(bits(A), bits(B), _c_np(C), w.alpha, w.beta, rows, cols)
-    assert_close(name, got[rows, cols], ref, absdot, rows, cols, K=w.K, alpha=w.alpha)
+    assert_close(name, got[rows, cols], ref, absdot, rows, cols, K=w.K, alpha=w.alpha, beta=w.beta, C0=C)
     ok, ratio = freivalds_ok(got, A, B, C, w.alpha, w.beta, seed=w.seed)
     print(f"[{name}] {rows.size} sampled entries ok; Freivalds worst ratio {ratio:.3g}", flush=True)
     assert ok, f"{name}: Freivalds check failed (worst err/bound {ratio:.3g})"

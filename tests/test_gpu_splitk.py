@@ -46,7 +46,8 @@ def check(label, A, B, C0, alpha, beta, la=0, lb=0, splits=0, bias=None, ldc=Non
     ref, absdot = oracle.gemm(bits(stored(A, la)), bits(stored(B, lb)),
                               None if C0 is None else C0.numpy(), alpha, beta,
                               layout_a=la, layout_b=lb, in_type=in_type, bias=bias)
-    assert_close(f"{label} ({plan['splits']} pieces)", got, ref, absdot, K=A.shape[1], alpha=alpha)
+    assert_close(f"{label} ({plan['splits']} pieces)", got, ref, absdot, K=A.shape[1], alpha=alpha, beta=beta,
+                 C0=C0, bias=bias)
     assert gC.untouched_outside_window(), f"{label}: wrote outside the M x N window"
     return got, plan
 

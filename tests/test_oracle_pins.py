@@ -748,3 +748,37 @@ def test_matmul_form_catches_a_transposed_operand():
     ref, absdot = oracle.gemm(bits(A), bits(B))
     wrong, _ = oracle.gemm_matmul(bits(A), bits(B), layout_b=oracle.COL_MAJOR)
     assert not np.all(np.abs(ref - wrong) <= 2 * fp64_sum_bound(16, 1.0, 0.0, absdot))
+
+
+def test_accumulation_bound_epilogue_term():
+    """beta*c and the bias enter through FP32 roundings whose operands can be
+    far larger than the result: with c and the bias cancelling, an exact
+    FP32 epilogue (each operation rounded once) stays within the bound only
+    with the E = |beta*c| + |bias| term, which covers it."""
+    a, b = np.float16(0.0123), np.float16(0.0047)
+    s = float(a) * float(b)                        # exact product, K = 1
+    c = np.float32(0.7)
+    bias = np.float32(-0.7000001)
+    ref = s + float(c) + float(bias)               # FP64: exact here
+    t = np.float32(np.float32(s) + np.float32(1.0) * c)   # alpha*s + beta*c in FP32
+    got = float(np.float32(t + bias))
+    absdot = np.array([abs(s)])
+    e = oracle.epilogue_abs(1.0, np.array([[c]]), np.array([bias]))
+    assert e.shape == (1, 1) and e[0, 0] == abs(float(c)) + abs(float(bias))
+    assert oracle.accumulation_ratio(np.array([got]), np.array([ref]), absdot, 1, 1.0) > 1.0
+    assert oracle.accumulation_ratio(np.array([got]), np.array([ref]), absdot, 1, 1.0,
+                                     epilogue_abs=e.ravel()) <= 1.0
+
+
+def test_epilogue_abs_forms():
+    """Whole-matrix and sampled-entry forms agree; beta = 0 ignores C; no C
+    and no bias give 0."""
+    rng = np.random.default_rng(3)
+    C = rng.uniform(-2, 2, (5, 7)).astype(np.float32)
+    bias = rng.uniform(-1, 1, 7).astype(np.float32)
+    whole = oracle.epilogue_abs(-0.25, C, bias)
+    assert np.array_equal(whole, np.abs(-0.25 * C.astype(np.float64)) + np.abs(bias.astype(np.float64)))
+    rows, cols = np.array([0, 4, 2]), np.array([6, 0, 3])
+    assert np.array_equal(oracle.epilogue_abs(-0.25, C, bias, rows, cols), whole[rows, cols])
+    assert np.array_equal(oracle.epilogue_abs(0.0, C, bias), np.broadcast_to(np.abs(bias.astype(np.float64)), (1, 7)))
+    assert oracle.epilogue_abs(0.5, None, None) == 0.0

@@ -55,7 +55,7 @@ def test_static_scratch_equals_the_workspace_entry_point_on_two_calls():
     assert plan["splits"] > 1 and plan["workspace_bytes"] <= mp.MPGEMM_STATIC_SCRATCH_BYTES
     assert np.array_equal(st, ws), "static scratch differs from the workspace entry point"
     ref, absdot = oracle.gemm(bits(A), bits(B), C.numpy(), 1.5, 0.5)
-    assert_close("static scratch, first call", st, ref, absdot, K=65536, alpha=1.5)
+    assert_close("static scratch, first call", st, ref, absdot, K=65536, alpha=1.5, beta=0.5, C0=C)
     # second call, smaller, with a bias and beta == 0 (C NaN-poisoned)
     A, B, _ = make_inputs(100, 48, 8192, "uniform", seed=302)
     bias = np.linspace(-1, 1, 48).astype(np.float32)
@@ -64,7 +64,7 @@ def test_static_scratch_equals_the_workspace_entry_point_on_two_calls():
     assert plan["splits"] == 6
     assert np.array_equal(st, ws), "static scratch differs from the workspace entry point"
     ref, absdot = oracle.gemm(bits(A), bits(B), None, 1.0, 0.0, bias=bias)
-    assert_close("static scratch, second call", st, ref, absdot, K=8192, alpha=1.0)
+    assert_close("static scratch, second call", st, ref, absdot, K=8192, alpha=1.0, bias=bias)
 
 
 def test_static_scratch_refuses_a_plan_larger_than_itself():
