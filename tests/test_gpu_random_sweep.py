@@ -13,6 +13,10 @@ Each case draws, from its own seed:
 * a per-column bias or none;
 * the entry point: the factory (through the tensor binding) or split-K with
   the library's plan or a requested number of pieces.
+A second sweep forces a random entry of the product table on each case (in
+its input format and storage orders; N <= 16 for the narrow kernel, alpha
+= 0 for the scale-only kernel), so every kernel variant meets shapes the
+factory would not give it.
 Every element must meet the acceptance rule and the accumulation diagnostic,
 and nothing outside C's window (guards, the ldc gap) may change.  Each case
 prints its draw before it runs.
@@ -28,7 +32,7 @@ from tests.gpu_util import Guarded, assert_close, device, stored
 
 pytestmark = pytest.mark.gpu
 
-CASES = 300
+CASES = 600
 BASE_SEED = 7300
 MAX_MNK = 20_000_000
 
@@ -63,10 +67,46 @@ def draw(idx):
     )
 
 
+def forced_draw(idx):
+    """A case for a random table entry: the entry's input format and storage
+    orders; M, N, K >= 2 so the binding reads the storage order from the
+    strides; N <= 16 for the narrow kernel; alpha = 0 for the scale kernel."""
+    d = draw(FORCED_SEED_OFFSET + idx)
+    rng = np.random.default_rng(BASE_SEED + FORCED_SEED_OFFSET + idx)
+    cfg = int(rng.integers(0, mp.mpgemm_num_configs()))
+    c = mp.mpgemm_config_info(cfg)
+    d.update(config=cfg, splitk=False, M=max(d["M"], 2), N=max(d["N"], 2), K=max(d["K"], 2))
+    d["fmt"] = "bf16" if c["in_type"] == mp.MPGEMM_IN_BF16 else "f16"
+    if c["kind_name"] in ("pipe", "narrow"):
+        d["la"], d["lb"] = c["layout_a"], c["layout_b"]
+    if c["kind_name"] == "narrow":
+        d["N"] = int(rng.integers(2, 17))
+    if c["kind_name"] == "scale":
+        d["alpha"] = 0.0
+    while d["M"] * d["N"] * d["K"] > MAX_MNK:
+        d["K"] = max(2, d["K"] // 2)
+    return d
+
+
+FORCED_CASES = 400
+FORCED_SEED_OFFSET = 100_000
+
+
 @pytest.mark.parametrize("idx", range(CASES), ids=lambda i: f"case{i:03d}")
 def test_random_case(idx):
     d = draw(idx)
     print(f"[sweep {idx}] {d}", flush=True)
+    check(idx, d)
+
+
+@pytest.mark.parametrize("idx", range(FORCED_CASES), ids=lambda i: f"forced{i:03d}")
+def test_random_forced_config(idx):
+    d = forced_draw(idx)
+    print(f"[forced {idx}] {d}", flush=True)
+    check(f"forced {idx}", d)
+
+
+def check(idx, d):
     M, N, K = d["M"], d["N"], d["K"]
     dtype = torch.bfloat16 if d["fmt"] == "bf16" else torch.float16
     A, B, C = make_inputs(M, N, K, "uniform", seed=d["seed"], c_init="uniform" if d["beta"] != 0 else None,
@@ -90,7 +130,7 @@ def test_random_case(idx):
     if d["splitk"]:
         mp.gemm_splitk(a_view, b_view, gC.view(), d["alpha"], d["beta"], bias=bias_d, splits=d["splits"])
     else:
-        mp.gemm(a_view, b_view, gC.view(), d["alpha"], d["beta"], bias=bias_d)
+        mp.gemm(a_view, b_view, gC.view(), d["alpha"], d["beta"], bias=bias_d, config=d.get("config"))
     torch.cuda.synchronize()
     got = gC.result()
     assert gC.untouched_outside_window(), f"case {idx}: a write outside C's window"
