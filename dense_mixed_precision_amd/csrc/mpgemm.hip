@@ -244,7 +244,7 @@ constexpr int kDirectIds[2] = {0, 1};  // per input format
 constexpr int kScaleId = 2;
 // first entry of the family of input format `in` and storage orders (la, lb)
 constexpr int family(int in, int la, int lb) { return 3 + 16 * in + 4 * (la + 2 * lb); }
-// small row-major FP16 products, K tiles of 128: 64x64 and 32x64
+// small row-major FP16 products, K tiles of 128: 64x64, 32x64 and 16x64
 constexpr int kSmallDeepKId = 35;
 constexpr int kTinyDeepKId = 36;
 constexpr int kTiny16Id = 41;

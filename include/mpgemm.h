@@ -289,11 +289,14 @@ int mpgemm_gemm_ex_with_config(int config_id, int in_type, int layout_a, int lay
  * mpgemm_splitk_plan reports, without any HIP call, how many pieces a call
  * would use (`splits_requested` 0: automatic, split only when the grid
  * fills less than half the chip, into enough pieces for about two
- * workgroups per compute unit, at most 32, each at least 4 K tiles long;
- * a product the factory gives the narrow kernel stays whole when it has at
- * least 64 groups of 16 rows; n > 0: n pieces of a tile kernel, at most one
- * per K tile), the workspace bytes that needs (splits*M*N*4; 0 when
- * splits == 1) and the kernel's table entry.  Output pointers may be
+ * workgroups per compute unit, at most 32 and at most a quarter of the K
+ * tiles; a product the factory gives the narrow kernel stays whole when it
+ * has at least 64 groups of 16 rows; n > 0: a tile kernel's K tiles dealt
+ * into n pieces, at most one per K tile.  Every piece but the last holds
+ * ceil(K tiles / pieces asked) K tiles, so the count can come out below the
+ * one asked for, e.g. 2 pieces of 2 tiles for 3 asked of 4 tiles), the
+ * workspace bytes that needs (splits*M*N*4; 0 when splits == 1) and the
+ * kernel's table entry.  Output pointers may be
  * NULL.  Arguments as for mpgemm_gemm_ex; C, alpha and beta are not needed
  * to plan.
  *
