@@ -276,6 +276,41 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
     return out
 
 
+def cold_timing(w, torch, mp, reps=20, scrub_mib=512):
+    """Per-launch kernel time with cold caches: before each launch a
+    `scrub_mib` MiB write (twice the 256 MB memory-side cache) evicts the
+    operands from the L2s and the memory-side cache; HIP events on the
+    launch stream bracket the launch alone.  Median over `reps` launches
+    (the timed steps run warm, as the pages time)."""
+    import statistics
+
+    from dense_mixed_precision_amd.workloads import workload_inputs
+
+    dev = torch.device("cuda:0")
+    A, B, C = workload_inputs(w)
+    Ad, Bd = A.to(dev), B.to(dev)
+    Cd = C.to(dev) if C is not None else torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    scrub = torch.empty(scrub_mib * (1 << 18), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    mp.gemm(Ad, Bd, Cd, w.alpha, w.beta)
+    us = []
+    for i in range(reps):
+        scrub.fill_(float(i))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        mp.gemm(Ad, Bd, Cd, w.alpha, w.beta)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3)
+    med = statistics.median(us)
+    del scrub
+    return {"median_us": round(med, 3), "min_us": round(min(us), 3), "max_us": round(max(us), 3),
+            "tflops": round(w.flop / (med * 1e-6) / 1e12, 2), "reps": reps, "scrub_mib": scrub_mib,
+            "note": "not the value: each launch after a 512 MiB write that evicts the L2s and the "
+                    "memory-side cache (the timed steps run with warm caches)"}
+
+
 def warmup_for(w, warmup):
     """Warm-up steps for a secondary workload: about 40 ms of GPU time (the
     clocks settle within ~25 ms of sustained load), at most `warmup`, at
@@ -840,6 +875,9 @@ def main():
                               "back-to-back launches after the timed steps: median of the runs' means, CV "
                               "across runs (the pages' medians of 5 x 20)"}
     line["graph_us"] = round(res["graph_us"], 3)
+    if args.config is None:
+        print("# cold-cache launches", file=sys.stderr, flush=True)
+        line["cold"] = cold_timing(head, torch, mp)
     if args.timeline and args.config is None:
         print("# per-workgroup timeline (timeline build)", file=sys.stderr, flush=True)
         line["timeline"] = timeline(head, torch, mp, warm=max(5, min(200, int(2e13 / head.flop))))
