@@ -278,10 +278,13 @@ def time_workload(w, steps, warmup, torch, mp, layout_a=0, layout_b=0, dtype=Non
 
 def cold_timing(w, torch, mp, reps=20, scrub_mib=512):
     """Per-launch kernel time with cold caches: before each launch a
-    `scrub_mib` MiB write (twice the 256 MB memory-side cache) evicts the
+    `scrub_mib` MiB pass (twice the 256 MB memory-side cache) evicts the
     operands from the L2s and the memory-side cache; HIP events on the
-    launch stream bracket the launch alone.  Median over `reps` launches
-    (the timed steps run warm, as the pages time)."""
+    launch stream bracket the launch alone.  Two forms: the pass reads the
+    buffer (the evicted lines are clean), or writes it (the product's reads
+    then also push the pass's dirty lines out to HBM).  Medians over `reps`
+    launches each (the timed steps run with warm caches, as the pages
+    time)."""
     import statistics
 
     from dense_mixed_precision_amd.workloads import workload_inputs
@@ -290,25 +293,32 @@ def cold_timing(w, torch, mp, reps=20, scrub_mib=512):
     A, B, C = workload_inputs(w)
     Ad, Bd = A.to(dev), B.to(dev)
     Cd = C.to(dev) if C is not None else torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
-    scrub = torch.empty(scrub_mib * (1 << 18), dtype=torch.float32, device=dev)
+    scrub = torch.ones(scrub_mib * (1 << 18), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    mp.gemm(Ad, Bd, Cd, w.alpha, w.beta)
-    us = []
-    for i in range(reps):
-        scrub.fill_(float(i))
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+    out = {"reps": reps, "scrub_mib": scrub_mib,
+           "note": "not the value: each launch after a pass over a 512 MiB buffer that evicts the L2s "
+                   "and the memory-side cache; read: the pass reads it, write: the pass writes it"}
+    for mode in ("read", "write", "read"):
         mp.gemm(Ad, Bd, Cd, w.alpha, w.beta)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us.append(e0.elapsed_time(e1) * 1e3)
-    med = statistics.median(us)
+        us = []
+        for i in range(reps):
+            if mode == "read":
+                scrub.sum()
+            else:
+                scrub.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            mp.gemm(Ad, Bd, Cd, w.alpha, w.beta)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3)
+        med = statistics.median(us)
+        # the first read pass follows the buffer's initial write: keep the last
+        out[mode] = {"median_us": round(med, 3), "min_us": round(min(us), 3), "max_us": round(max(us), 3),
+                     "tflops": round(w.flop / (med * 1e-6) / 1e12, 2)}
     del scrub
-    return {"median_us": round(med, 3), "min_us": round(min(us), 3), "max_us": round(max(us), 3),
-            "tflops": round(w.flop / (med * 1e-6) / 1e12, 2), "reps": reps, "scrub_mib": scrub_mib,
-            "note": "not the value: each launch after a 512 MiB write that evicts the L2s and the "
-                    "memory-side cache (the timed steps run with warm caches)"}
+    return out
 
 
 def warmup_for(w, warmup):
