@@ -408,12 +408,22 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
     // Else 128x128 if that makes at least half a wave of workgroups.
     // Else 64x64.
     const int fam = family(p.in_type, p.la, p.lb);
+    // Small row-major FP16 products with more than one 64-deep K tile have
+    // K tiles of 128 and the 16x16x32 instruction (half as many barriers
+    // per K).
+    const bool deep_k = small_deep_k && p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR &&
+                        p.lb == MPGEMM_ROW_MAJOR && p.K > 64;
+    const int64_t tiles64 = mul_sat(cdiv(p.M, 64), cdiv(p.N, 64));
     int order[4];
     int n = 0;
     if (mul_sat(cdiv(p.M, 256), cdiv(p.N, 256)) >= kNumCu) {
         order[n++] = fam + kBig;
         order[n++] = fam + kMid;
-    } else if (mul_sat(cdiv(p.M, 128), cdiv(p.N, 128)) >= kNumCu / 2) {
+    } else if (mul_sat(cdiv(p.M, 128), cdiv(p.N, 128)) >= kNumCu / 2 &&
+               !(deep_k && tiles64 <= 2 * kNumCu)) {
+        // (Half a wave of 128x128 tiles whose 64x64 tiles come to at most
+        // two per compute unit runs faster as 64x64 tiles on every unit:
+        // 1024x2048x2048 17.7 against 22.0 us, graph-replayed.)
         // 128x128 tiles with both panels reused across tiles (B panels by at
         // least four column tiles) take K steps of 128: half as many
         // barriers.  A tall-skinny product streams A once and keeps the
@@ -421,21 +431,29 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
         if (cdiv(p.N, 128) >= 4 && cdiv(p.M, 128) >= 4)
             order[n++] = fam + kWide;
         order[n++] = fam + kMid;
-    } else if (small_deep_k && p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR &&
-               p.lb == MPGEMM_ROW_MAJOR && p.K > 64) {
-        // Small row-major FP16 products with more than one 64-deep K tile
-        // take K tiles of 128 (half as many barriers per K) and the
-        // 16x16x32 instruction.  When 64x64 tiles would fill less than half
-        // the chip: 16x64 tiles on 4 waves (256^3: 3.36 against 3.68 us for
-        // 32x64 and 4.4 for 64x64), unless N is not a multiple of 8 -- then
-        // the last column of tiles fills partial B vectors through registers
-        // on every K tile, which 8 waves share better: 32x64 on 8 waves
-        // (200x300x400: 6.7 against 8.1 us).  Otherwise 64x64 on 8 waves
-        // (ragged 1000x800x617: 7.1 against 7.3 us for 4 waves).
-        if (mul_sat(cdiv(p.M, 64), cdiv(p.N, 64)) < kNumCu / 2) {
-            if (p.N % 8 == 0)
+    } else if (deep_k) {
+        // Fewer 64x64 tiles than compute units (times graph-replayed):
+        // * 16x64 tiles on 4 waves while they come to at most one per unit
+        //   and K is moderate (256^3: 3.34 against 3.66 us for 32x64 and
+        //   3.94 for 64x64; 512x512x2048 9.98 against 10.56 and 11.32), and
+        //   N a multiple of 8 -- otherwise the last column of tiles fills
+        //   partial B vectors through registers on every K tile, which 8
+        //   waves share better (200x300x400: 6.7 against 8.1 us for 32x64);
+        // * else 32x64 tiles on 8 waves with a 3-deep ring while they come
+        //   to at most one per unit (512x768x1024 6.85 against 7.22 for
+        //   16x64 and 7.29 for 64x64) or K is long (the deeper ring keeps
+        //   pace where the 2-deep ones fall behind: 512x512x8192 33.9
+        //   against 43.5 for 16x64 and 46.7 for 64x64; 768x768x8192 45.3
+        //   against 47.7 for 64x64);
+        // * else 64x64 on 8 waves (ragged 1000x800x617: 7.1 against 7.3 us
+        //   for 4 waves).
+        if (tiles64 < kNumCu) {
+            const int64_t tiles16 = mul_sat(cdiv(p.M, 16), cdiv(p.N, 64));
+            const int64_t tiles32 = mul_sat(cdiv(p.M, 32), cdiv(p.N, 64));
+            if (p.N % 8 == 0 && ((tiles16 <= kNumCu && p.K <= 2048) || (tiles16 <= kNumCu / 2 && p.K <= 4096)))
                 order[n++] = kTiny16Id;
-            order[n++] = kTinyDeepKId;
+            if (tiles32 <= kNumCu || p.K >= 4096)
+                order[n++] = kTinyDeepKId;
         }
         order[n++] = kSmallDeepKId;
     }

@@ -184,6 +184,28 @@ def test_factory_choices_for_the_workloads():
     assert (c["bm"], c["bn"], c["bk"], c["stages"], c["k_order"]) == (128, 128, 128, 2, 2)
 
 
+@pytest.mark.parametrize("M,N,K,shape", [
+    # half a wave of 128x128 tiles whose 64x64 tiles come to two per unit: 64x64
+    (1024, 2048, 2048, (64, 64, 128, 2)), (2048, 1024, 512, (64, 64, 128, 2)),
+    # more than half a wave otherwise: 128x128
+    (1536, 1536, 2048, (128, 128, 128, 2)), (1280, 2048, 8192, (128, 128, 128, 2)),
+    # fewer 64x64 tiles than units: 16x64 on 4 waves while at most one per
+    # unit and K moderate
+    (512, 512, 2048, (16, 64, 128, 2)), (384, 384, 2048, (16, 64, 128, 2)), (256, 256, 4096, (16, 64, 128, 2)),
+    # ... else 32x64 with 3 stages while at most one per unit or K long
+    (512, 512, 8192, (32, 64, 128, 3)), (384, 384, 4096, (32, 64, 128, 3)), (512, 768, 1024, (32, 64, 128, 3)),
+    (512, 1024, 512, (32, 64, 128, 3)), (768, 768, 4096, (32, 64, 128, 3)),
+    # ... else 64x64
+    (768, 768, 1024, (64, 64, 128, 2)), (768, 1024, 2048, (64, 64, 128, 2)),
+])
+def test_factory_small_and_mid_shapes(M, N, K, shape):
+    """The measured choices for small and mid-size row-major FP16 products
+    (graph-replayed sweeps over the three small entries and the 128x128
+    one)."""
+    c = q(M, N, K)
+    assert (c["bm"], c["bn"], c["bk"], c["stages"]) == shape, (M, N, K, c["id"])
+
+
 def test_one_column_row_major_b_is_read_as_column_major():
     """A (K x 1) row-major B with ldb 1 is K consecutive values: when the
     narrow kernel takes the product, the factory reads the column-major form
