@@ -66,6 +66,8 @@ def parse():
                    help="skip the per-workgroup timeline of the headline workload (timeline build)")
     p.add_argument("--no-breakdown", dest="breakdown", action="store_false",
                    help="skip the ragged workload's time breakdown")
+    p.add_argument("--no-cold", dest="cold", action="store_false",
+                   help="skip the cold-cache launches of the headline workload")
     p.add_argument("--no-others", action="store_true", help="time only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -885,7 +887,7 @@ def main():
                               "back-to-back launches after the timed steps: median of the runs' means, CV "
                               "across runs (the pages' medians of 5 x 20)"}
     line["graph_us"] = round(res["graph_us"], 3)
-    if args.config is None:
+    if args.cold and args.config is None:
         print("# cold-cache launches", file=sys.stderr, flush=True)
         line["cold"] = cold_timing(head, torch, mp)
     if args.timeline and args.config is None:
