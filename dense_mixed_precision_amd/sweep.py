@@ -1,0 +1,84 @@
+"""Graph-replayed timing of table entries on given shapes (factory tuning).
+
+    python -m dense_mixed_precision_amd.sweep --shapes 512x512,1024x2048 --ks 256,2048,8192 \\
+        --configs 35,36,41 [--candidates] [--rounds 5]
+
+For every M x N x K it captures, per forced table entry, a HIP graph of
+back-to-back launches of that entry (row-major FP16 operands, uniform
+inputs, alpha 1, beta 0), replays the graphs in alternating rounds and
+prints one line per shape: the median per-launch time of each entry, the
+factory's own choice and the fastest entry.  Launch overhead on the host is
+outside the graphs, so microsecond-scale kernels are timed as the GPU runs
+them back to back.
+"""
+from __future__ import annotations
+
+import argparse
+import itertools
+import json
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--shapes", required=True, help="comma-separated MxN pairs")
+    p.add_argument("--ks", required=True, help="comma-separated K values")
+    p.add_argument("--configs", required=True, help="comma-separated table entries to force")
+    p.add_argument("--candidates", action="store_true", help="load the candidates build")
+    p.add_argument("--rounds", type=int, default=5)
+    p.add_argument("--seed", type=int, default=7)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    import torch
+
+    import dense_mixed_precision_amd as mp
+    from dense_mixed_precision_amd.workloads import make_inputs
+
+    mp.load(mp.CANDIDATES_PATH if args.candidates else None)
+    dev = torch.device("cuda:0")
+    shapes = [tuple(int(x) for x in s.split("x")) for s in args.shapes.split(",")]
+    ks = [int(k) for k in args.ks.split(",")]
+    cfgs = [int(c) for c in args.configs.split(",")]
+    for (M, N), K in itertools.product(shapes, ks):
+        A, B, _ = make_inputs(M, N, K, "uniform", seed=args.seed)
+        A, B = A.to(dev), B.to(dev)
+        C = torch.empty(M, N, device=dev)
+        factory = mp.query_for(A, B, C)["id"]
+        # about 0.4 ms of work per graph at 1 PFLOP/s, 4..40 launches
+        per = max(4, min(40, int(4e5 / (2 * M * N * K / 1e6 + 1))))
+        side = torch.cuda.Stream()
+        graphs = {}
+        for c in cfgs:
+            with torch.cuda.stream(side):
+                for _ in range(2):
+                    mp.gemm(A, B, C, 1.0, 0.0, config=c)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(per):
+                    mp.gemm(A, B, C, 1.0, 0.0, config=c)
+            graphs[c] = g
+        torch.cuda.synchronize()
+        times = {c: [] for c in cfgs}
+        for _ in range(args.rounds):
+            for c in cfgs:
+                graphs[c].replay()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                graphs[c].replay()
+                e1.record()
+                torch.cuda.synchronize()
+                times[c].append(e0.elapsed_time(e1) * 1e3 / per)
+        med = {c: sorted(v)[len(v) // 2] for c, v in times.items()}
+        best = min(med, key=med.get)
+        print(json.dumps({"M": M, "N": N, "K": K, "factory": factory, "best": best,
+                          "factory_over_best": round(med[factory] / med[best], 3) if factory in med else None,
+                          "us": {str(c): round(v, 3) for c, v in med.items()}}), flush=True)
+        del graphs, A, B, C
+
+
+if __name__ == "__main__":
+    main()

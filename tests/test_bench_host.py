@@ -117,3 +117,15 @@ def test_copy_bound_adds_the_loop_at_the_copy_rate_to_the_measured_phases():
     assert abs(b["loop_us"] - loop) < 1e-3
     assert abs(b["bound_us"] - (loop + 4.0)) < 1e-3
     assert abs(b["frac_of_bound"] - (loop + 4.0) / 25.0) < 1e-3
+
+
+def test_sweep_tool_parses_its_arguments(monkeypatch):
+    """The factory sweep's command line (the GPU part runs on the device only)."""
+    import sys
+
+    from dense_mixed_precision_amd import sweep
+    monkeypatch.setattr(sys, "argv", ["sweep", "--shapes", "256x512,1024x2048", "--ks", "256,8192",
+                                      "--configs", "35,36,41"])
+    a = sweep.parse()
+    assert (a.shapes, a.ks, a.configs, a.rounds, a.candidates) == ("256x512,1024x2048", "256,8192", "35,36,41",
+                                                                    5, False)
