@@ -416,7 +416,14 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
     const int64_t tiles64 = mul_sat(cdiv(p.M, 64), cdiv(p.N, 64));
     int order[4];
     int n = 0;
-    if (mul_sat(cdiv(p.M, 256), cdiv(p.N, 256)) >= kNumCu) {
+    // Row-major FP16 with one 128-row or 128-column tile band: a 256x256
+    // tile would be at least half empty, and the 128x128 class is faster
+    // (65536x128x4096 130.2 against 159.7 us, 128x65536x4096 122.1 against
+    // 139.3; with 192 columns the big tile leads, 185.2 against 212.0).
+    const bool rr16 = p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR && p.lb == MPGEMM_ROW_MAJOR;
+    const int64_t tm128 = cdiv(p.M, 128), tn128 = cdiv(p.N, 128);
+    const bool one_band = tm128 == 1 || tn128 == 1;
+    if (mul_sat(cdiv(p.M, 256), cdiv(p.N, 256)) >= kNumCu && !(rr16 && one_band)) {
         order[n++] = fam + kBig;
         order[n++] = fam + kMid;
     } else if (mul_sat(cdiv(p.M, 128), cdiv(p.N, 128)) >= kNumCu / 2 &&
@@ -424,11 +431,24 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
         // (Half a wave of 128x128 tiles whose 64x64 tiles come to at most
         // two per compute unit runs faster as 64x64 tiles on every unit:
         // 1024x2048x2048 17.7 against 22.0 us, graph-replayed.)
-        // 128x128 tiles with both panels reused across tiles (B panels by at
-        // least four column tiles) take K steps of 128: half as many
-        // barriers.  A tall-skinny product streams A once and keeps the
-        // deeper 64-wide ring.
-        if (cdiv(p.N, 128) >= 4 && cdiv(p.M, 128) >= 4)
+        // 128x128 tiles take K steps of 128 (half as many barriers) when
+        // both panels are reused across tiles.  Row-major FP16, by
+        // graph-replayed sweeps of the two shapes: at least two tile rows
+        // and two tile columns (16384x256x4096 49.3 against 55.4 us,
+        // 8192x384x1024 13.0 against 14.7, 256x16384x4096 48.6 against
+        // 55.5); one tile column, where A is streamed once, only up to
+        // K = 1024 (32768x128x1024 16.9 against 17.6; x4096 62.7 against
+        // 58.5 for the deeper 64-wide ring); one tile row, where B is
+        // streamed once, up to K = 2048 (128x32768x2048 28.3 against 29.7;
+        // 128x65536x4096 143.3 against 122.1); two tile columns keep the
+        // 64-deep ring from K = 8192 (32768x256x8192 196.5 against 225.4,
+        // 16384x192x8192 92.7 against 98.1).  Other storage orders and
+        // BF16: both panels reused by at least four tiles.
+        bool wide = tm128 >= 4 && tn128 >= 4;
+        if (rr16)
+            wide = (tm128 >= 2 && tn128 >= 2 && !(tn128 == 2 && p.K >= 8192)) || (tn128 == 1 && p.K <= 1024) ||
+                   (tm128 == 1 && p.K <= 2048);
+        if (wide)
             order[n++] = fam + kWide;
         order[n++] = fam + kMid;
     } else if (deep_k) {
@@ -461,6 +481,14 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
     for (int i = 0; i < n; ++i)
         if (entry_fits(kTable[order[i]], p))
             return order[i];
+    // Leading dimensions so large that the preferred tiles' stages overflow
+    // 32-bit offsets: any other tiled entry whose stages fit (the smallest
+    // tiles first) before the 64-bit direct kernel.
+    const int rest[] = {rr16 ? kTiny16Id : -1, rr16 ? kTinyDeepKId : -1, rr16 ? kSmallDeepKId : -1,
+                        fam + kMid, fam + kWide, fam + kBig};
+    for (int id : rest)
+        if (id >= 0 && entry_fits(kTable[id], p))
+            return id;
     return kDirectIds[p.in_type];
 }
 

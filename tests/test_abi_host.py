@@ -189,6 +189,19 @@ def test_factory_choices_for_the_workloads():
     (1024, 2048, 2048, (64, 64, 128, 2)), (2048, 1024, 512, (64, 64, 128, 2)),
     # more than half a wave otherwise: 128x128
     (1536, 1536, 2048, (128, 128, 128, 2)), (1280, 2048, 8192, (128, 128, 128, 2)),
+    # 128-deep K tiles with at least two tile rows and columns; with one tile
+    # column (A streamed once) only up to K 1024, with one tile row (B
+    # streamed once) up to K 4096; else the 3-deep ring of 64-deep tiles
+    (16384, 256, 4096, (128, 128, 128, 2)), (8192, 384, 1024, (128, 128, 128, 2)),
+    (32768, 256, 8192, (128, 128, 64, 3)), (16384, 384, 8192, (128, 128, 128, 2)),
+    (16384, 192, 4096, (128, 128, 128, 2)), (256, 16384, 4096, (128, 128, 128, 2)),
+    (32768, 128, 1024, (128, 128, 128, 2)), (32768, 128, 4096, (128, 128, 64, 3)),
+    (32768, 128, 8192, (128, 128, 64, 3)), (128, 32768, 2048, (128, 128, 128, 2)),
+    (128, 32768, 4096, (128, 128, 64, 3)), (128, 32768, 8192, (128, 128, 64, 3)),
+    # one 128-row or 128-column band takes 128x128 tiles even where enough
+    # 256x256 tiles would fill the chip (they would be half empty)
+    (65536, 128, 1024, (128, 128, 128, 2)), (65536, 128, 4096, (128, 128, 64, 3)),
+    (128, 65536, 4096, (128, 128, 64, 3)), (65536, 192, 4096, (256, 256, 64, 2)),
     # fewer 64x64 tiles than units: 16x64 on 4 waves while at most one per
     # unit and K moderate
     (512, 512, 2048, (16, 64, 128, 2)), (384, 384, 2048, (16, 64, 128, 2)), (256, 256, 4096, (16, 64, 128, 2)),
@@ -332,6 +345,9 @@ def test_layout_factory_choices(la, lb):
     assert (c["layout_a"], c["layout_b"]) == (la, lb) and c["grid"] == 1024
     c = ql(la, lb, 2048, 2048, 2048)
     assert (c["bm"], c["bn"], c["bk"]) == (128, 128, 128) and c["grid"] == 256
+    # other storage orders keep 64-deep tiles unless both panels are reused
+    # by at least four tiles
+    assert ql(la, lb, 16384, 256, 4096)["bk"] == 64
     c = ql(la, lb, 1000, 800, 617, lda=(1001 if la else 617), ldb=(617 if lb else 800))
     assert c["kind_name"] == "pipe" and (c["vec_a"], c["vec_b"]) == (8, 8)
     # a stored stage beyond 32-bit offsets leaves only the 64-bit direct kernel

@@ -9,9 +9,10 @@ a tensor-core GEMM", section "Capability").
   the oracle, every element finite, and the columns between N and ldc
   untouched.
 * Leading dimensions so large that one LDS stage of A or of B spans more
-  than 32-bit buffer offsets: the factory falls back to the 64-bit direct
-  kernel, which must give the oracle's product; the gaps between the rows
-  hold NaN, so a read outside the rows shows up.
+  than 32-bit buffer offsets: the factory falls back to a tiled entry whose
+  stages still fit (16-row tiles), or else to the 64-bit direct kernel;
+  either must give the oracle's product; the gaps between the rows hold
+  NaN, so a read outside the rows shows up.
 * K = 2^31 + 9 through split-K, exact.
 
 The large buffers are made on the device and freed after each test; only
@@ -80,12 +81,19 @@ def _strided_on_device(X, ld, fill):
     return buf, view
 
 
-@pytest.mark.parametrize("which", ["A", "B"])
-def test_stage_span_past_32_bit_offsets_takes_the_direct_kernel(which):
+@pytest.mark.parametrize("which,big,kind", [
+    ("A", (1 << 24) + 5, "pipe"),    # 64 rows of this stride span 2^31 bytes, 16 rows do not
+    ("A", (1 << 26) + 5, "direct"),  # 16 rows of this stride already span 2^31 bytes
+    ("B", (1 << 24) + 5, "direct"),  # 64 k rows of this stride span 2^31 bytes
+])
+def test_stage_span_past_32_bit_offsets_takes_a_kernel_that_fits(which, big, kind):
+    """Leading dimensions so large that a tile's stage overflows 32-bit
+    buffer offsets: the factory takes a tiled entry whose stages still fit
+    (the 16-row tiles), else the 64-bit direct kernel."""
     M, N, K = 70, 50, 40
     A, B, C = make_inputs(M, N, K, "uniform", seed=3131, c_init="uniform")
-    big = (1 << 24) + 5            # 64 rows of this stride already span 2^31 bytes
     nan = float("nan")
+    print(f"[huge ld{which.lower()} {big}] {M}x{N}x{K}", flush=True)
     if which == "A":
         bufA, Ad = _strided_on_device(A, big, nan)
         Bd = B.to(device())
@@ -94,7 +102,9 @@ def test_stage_span_past_32_bit_offsets_takes_the_direct_kernel(which):
         bufB, Bd = _strided_on_device(B, big, nan)
     Cd = C.to(device())
     cfg = mp.query_for(Ad, Bd, Cd, 1.5, 0.5)
-    assert cfg["kind_name"] == "direct", cfg
+    assert cfg["kind_name"] == kind, cfg
+    if kind == "pipe":
+        assert (cfg["bm"] * big + cfg["bk"]) * 2 < 0x7FFFFFF0, cfg
     mp.gemm(Ad, Bd, Cd, 1.5, 0.5)
     torch.cuda.synchronize()
     ref, absdot = oracle.gemm(bits(A), bits(B), C.numpy(), 1.5, 0.5)
