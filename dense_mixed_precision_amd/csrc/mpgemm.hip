@@ -159,10 +159,10 @@ constexpr Entry scale_entry(int id)
 
 // The tile shapes the factory chooses from, for one input format and
 // storage-order pair (entries base .. base+3):
-//   big   256x256x64, 2 stages, 8 waves of 128x64 on 16x16x32: products with
-//         enough 256x256 tiles for every compute unit (under the board's
-//         power limit this instruction does 3-8% more work per joule than
-//         32x32x16);
+//   big   256x256x64, 2 stages, 8 waves of 128x64 on 16x16x32: products
+//         whose 256x256 tiles take at most a third of the 128x128 tiles'
+//         rounds over the compute units (under the board's power limit this
+//         instruction does 3-8% more work per joule than 32x32x16);
 //   mid   128x128x64, 3 stages, 8 waves: the 128x128 class when a panel is
 //         streamed once (tall-skinny), where the deeper ring streams A better;
 //   wide  128x128x128, 2 stages, 8 waves: the 128x128 class with reused
@@ -387,8 +387,9 @@ int64_t grid_for(const mpgemm_config &c, const Problem &p)
     }
 }
 
-// The factory.  Largest tile whose grid still fills the chip; smaller tiles
-// when the product is small.  Returns a table id, or -1 for "nothing to do".
+// The factory.  The tile by rounds of workgroups over the compute units;
+// smaller tiles when the product is small.  Returns a table id, or -1 for
+// "nothing to do".
 // `small_deep_k` = false keeps 64-deep K tiles for small products (split-K
 // counts its pieces in K tiles).
 int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
@@ -404,7 +405,7 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
         if (entry_fits(kTable[nid], p))
             return nid;
     }
-    // Enough 256x256 tiles for every CU: large products.
+    // 256x256 for large products (by rounds, below).
     // Else 128x128 if that makes at least half a wave of workgroups.
     // Else 64x64.
     const int fam = family(p.in_type, p.la, p.lb);
@@ -416,14 +417,22 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
     const int64_t tiles64 = mul_sat(cdiv(p.M, 64), cdiv(p.N, 64));
     int order[4];
     int n = 0;
-    // Row-major FP16 with one 128-row or 128-column tile band: a 256x256
-    // tile would be at least half empty, and the 128x128 class is faster
-    // (65536x128x4096 130.2 against 159.7 us, 128x65536x4096 122.1 against
-    // 139.3; with 192 columns the big tile leads, 185.2 against 212.0).
+    // 256x256 or 128x128 tiles, by the rounds of workgroups each puts on
+    // the compute units (one workgroup per unit): a 256x256 tile takes about
+    // three times as long as a 128x128 one (4096^3: 133.8 us for one round
+    // of 256 against 44.3 per round of 128x128 tiles), and a round that
+    // leaves units idle takes about as long as a full one.  So the big tile
+    // wins when 3 * its rounds <= the 128x128 rounds (3072x2816x4096: 106.4
+    // against 123.4 us with 132 big tiles; 4352x4096x4096: 230.6 against
+    // 209.1 with 272, two rounds, for 5 rounds of 128x128; the same for
+    // both input formats and every storage order).  A product with one
+    // 128-row or 128-column band never takes it: its 256x256 tiles would be
+    // at least half empty (65536x128x4096 159.7 against 130.2 us).
     const bool rr16 = p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR && p.lb == MPGEMM_ROW_MAJOR;
     const int64_t tm128 = cdiv(p.M, 128), tn128 = cdiv(p.N, 128);
-    const bool one_band = tm128 == 1 || tn128 == 1;
-    if (mul_sat(cdiv(p.M, 256), cdiv(p.N, 256)) >= kNumCu && !(rr16 && one_band)) {
+    const int64_t rounds256 = cdiv(mul_sat(cdiv(p.M, 256), cdiv(p.N, 256)), kNumCu);
+    const int64_t rounds128 = cdiv(mul_sat(tm128, tn128), kNumCu);
+    if (mul_sat(3, rounds256) <= rounds128) {
         order[n++] = fam + kBig;
         order[n++] = fam + kMid;
     } else if (mul_sat(cdiv(p.M, 128), cdiv(p.N, 128)) >= kNumCu / 2 &&
@@ -432,22 +441,19 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
         // two per compute unit runs faster as 64x64 tiles on every unit:
         // 1024x2048x2048 17.7 against 22.0 us, graph-replayed.)
         // 128x128 tiles take K steps of 128 (half as many barriers) when
-        // both panels are reused across tiles.  Row-major FP16, by
-        // graph-replayed sweeps of the two shapes: at least two tile rows
-        // and two tile columns (16384x256x4096 49.3 against 55.4 us,
-        // 8192x384x1024 13.0 against 14.7, 256x16384x4096 48.6 against
-        // 55.5); one tile column, where A is streamed once, only up to
-        // K = 1024 (32768x128x1024 16.9 against 17.6; x4096 62.7 against
-        // 58.5 for the deeper 64-wide ring); one tile row, where B is
-        // streamed once, up to K = 2048 (128x32768x2048 28.3 against 29.7;
-        // 128x65536x4096 143.3 against 122.1); two tile columns keep the
-        // 64-deep ring from K = 8192 (32768x256x8192 196.5 against 225.4,
-        // 16384x192x8192 92.7 against 98.1).  Other storage orders and
-        // BF16: both panels reused by at least four tiles.
-        bool wide = tm128 >= 4 && tn128 >= 4;
-        if (rr16)
-            wide = (tm128 >= 2 && tn128 >= 2 && !(tn128 == 2 && p.K >= 8192)) || (tn128 == 1 && p.K <= 1024) ||
-                   (tm128 == 1 && p.K <= 2048);
+        // both panels are reused across tiles, by graph-replayed sweeps of
+        // the two shapes (row-major FP16; the BF16 and column-major forms
+        // follow the same pattern): at least two tile rows and two tile
+        // columns (16384x256x4096 49.3 against 55.4 us, 8192x384x1024 13.0
+        // against 14.7, 256x16384x4096 48.6 against 55.5), except two tile
+        // columns from K = 8192 (32768x256x8192 196.5 against 225.4); one
+        // tile column, where A is streamed once, only up to K = 1024
+        // (32768x128x1024 16.9 against 17.6; x4096 62.7 against 58.5 for
+        // the deeper 64-wide ring); one tile row, where B is streamed once,
+        // up to K = 2048 (128x32768x2048 28.3 against 29.7; 128x65536x4096
+        // 143.3 against 122.1).
+        const bool wide = (tm128 >= 2 && tn128 >= 2 && !(tn128 == 2 && p.K >= 8192)) ||
+                          (tn128 == 1 && p.K <= 1024) || (tm128 == 1 && p.K <= 2048);
         if (wide)
             order[n++] = fam + kWide;
         order[n++] = fam + kMid;

@@ -1,11 +1,12 @@
 """Graph-replayed timing of table entries on given shapes (factory tuning).
 
     python -m dense_mixed_precision_amd.sweep --shapes 512x512,1024x2048 --ks 256,2048,8192 \\
-        --configs 35,36,41 [--candidates] [--rounds 5]
+        --configs 35,36,41 [--candidates] [--rounds 5] [--in f16|bf16] [--layout rr|cr|rc|cc]
 
 For every M x N x K it captures, per forced table entry, a HIP graph of
-back-to-back launches of that entry (row-major FP16 operands, uniform
-inputs, alpha 1, beta 0), replays the graphs in alternating rounds and
+back-to-back launches of that entry (FP16 or BF16 operands, each row- or
+column-major, uniform inputs, alpha 1, beta 0), replays the graphs in
+alternating rounds and
 prints one line per shape: the median per-launch time of each entry, the
 factory's own choice and the fastest entry.  Launch overhead on the host is
 outside the graphs, so microsecond-scale kernels are timed as the GPU runs
@@ -26,6 +27,9 @@ def parse():
     p.add_argument("--candidates", action="store_true", help="load the candidates build")
     p.add_argument("--rounds", type=int, default=5)
     p.add_argument("--seed", type=int, default=7)
+    p.add_argument("--in", dest="in_type", choices=("f16", "bf16"), default="f16", help="input format")
+    p.add_argument("--layout", choices=("rr", "cr", "rc", "cc"), default="rr",
+                   help="storage orders of A and B (r: row-major, c: column-major)")
     return p.parse_args()
 
 
@@ -42,8 +46,11 @@ def main():
     ks = [int(k) for k in args.ks.split(",")]
     cfgs = [int(c) for c in args.configs.split(",")]
     for (M, N), K in itertools.product(shapes, ks):
-        A, B, _ = make_inputs(M, N, K, "uniform", seed=args.seed)
-        A, B = A.to(dev), B.to(dev)
+        dtype = torch.bfloat16 if args.in_type == "bf16" else torch.float16
+        A, B, _ = make_inputs(M, N, K, "uniform", seed=args.seed, dtype=dtype)
+        # a column-major operand is stored transposed and passed as the transposed view
+        A = A.t().contiguous().to(dev).t() if args.layout[0] == "c" else A.to(dev)
+        B = B.t().contiguous().to(dev).t() if args.layout[1] == "c" else B.to(dev)
         C = torch.empty(M, N, device=dev)
         factory = mp.query_for(A, B, C)["id"]
         # about 0.4 ms of work per graph at 1 PFLOP/s, 4..40 launches

@@ -189,6 +189,12 @@ def test_factory_choices_for_the_workloads():
     (1024, 2048, 2048, (64, 64, 128, 2)), (2048, 1024, 512, (64, 64, 128, 2)),
     # more than half a wave otherwise: 128x128
     (1536, 1536, 2048, (128, 128, 128, 2)), (1280, 2048, 8192, (128, 128, 128, 2)),
+    # 256x256 tiles where 3 x their rounds over the compute units <= the
+    # 128x128 tiles' rounds, even with fewer big tiles than units
+    (3072, 2816, 4096, (256, 256, 64, 2)), (4096, 2304, 1024, (256, 256, 64, 2)),
+    (3328, 3328, 4096, (256, 256, 64, 2)), (2816, 2816, 4096, (128, 128, 128, 2)),
+    (4096, 2048, 4096, (128, 128, 128, 2)), (4352, 4096, 4096, (128, 128, 128, 2)),
+    (5376, 5376, 4096, (256, 256, 64, 2)),
     # 128-deep K tiles with at least two tile rows and columns; with one tile
     # column (A streamed once) only up to K 1024, with one tile row (B
     # streamed once) up to K 4096; else the 3-deep ring of 64-deep tiles
@@ -345,9 +351,13 @@ def test_layout_factory_choices(la, lb):
     assert (c["layout_a"], c["layout_b"]) == (la, lb) and c["grid"] == 1024
     c = ql(la, lb, 2048, 2048, 2048)
     assert (c["bm"], c["bn"], c["bk"]) == (128, 128, 128) and c["grid"] == 256
-    # other storage orders keep 64-deep tiles unless both panels are reused
-    # by at least four tiles
-    assert ql(la, lb, 16384, 256, 4096)["bk"] == 64
+    # every storage order: 128-deep tiles with two or more tile rows and
+    # columns, the 64-deep ring for one tile column at long K, 256x256 tiles
+    # by rounds over the compute units
+    assert ql(la, lb, 16384, 256, 4096)["bk"] == 128
+    assert ql(la, lb, 32768, 128, 4096)["bk"] == 64
+    assert ql(la, lb, 3072, 2816, 4096)["bm"] == 256
+    assert ql(la, lb, 4096, 2048, 4096)["bm"] == 128
     c = ql(la, lb, 1000, 800, 617, lda=(1001 if la else 617), ldb=(617 if lb else 800))
     assert c["kind_name"] == "pipe" and (c["vec_a"], c["vec_b"]) == (8, 8)
     # a stored stage beyond 32-bit offsets leaves only the 64-bit direct kernel

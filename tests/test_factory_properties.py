@@ -12,8 +12,9 @@ header and table state:
   read as column-major by the narrow kernel), whose 32-bit per-stage buffer
   offsets hold, with the grid its tile size gives; the narrow kernel only
   for N <= 16 with A row-major; the 64-bit direct kernel only when no tiled
-  entry of the family fits; the largest tile only when its grid fills the
-  chip;
+  entry of the family fits; the largest tile only when three times its
+  rounds of workgroups over the compute units come to at most the 128x128
+  tiles' rounds;
 * split-K: at least one piece, the workspace exactly pieces * M * N * 4
   bytes (none for one piece), pieces only of a tiled kernel, each but the
   last holding ceil(K tiles / pieces asked) K tiles (so a requested count
@@ -113,7 +114,9 @@ def test_factory_choice_obeys_the_table_rules(p):
     assert (c["layout_a"], c["layout_b"]) == (p["la"], p["lb"])
     assert spans_fit(c, p["la"], p["lb"], lda, ldb, ldc, M, N)
     if c["bm"] == 256:
-        assert cdiv(M, 256) * cdiv(N, 256) >= NUM_CU
+        # the big tile only where its rounds of workgroups over the compute
+        # units come to at most a third of the 128x128 tiles' rounds
+        assert 3 * cdiv(cdiv(M, 256) * cdiv(N, 256), NUM_CU) <= cdiv(cdiv(M, 128) * cdiv(N, 128), NUM_CU)
 
 
 @SETTINGS
@@ -149,9 +152,14 @@ def test_strategies_reach_every_kind():
     assert kinds == {"scale", "narrow", "pipe", "direct", "none"}
 
 
-@pytest.mark.parametrize("M,N", [(16 * 256, 16 * 256), (256 * 16, 256 * 15)])
-def test_largest_tile_needs_a_full_grid(M, N):
+@pytest.mark.parametrize("M,N", [(16 * 256, 16 * 256), (256 * 16, 256 * 15), (256 * 16, 256 * 8),
+                                 (256 * 12, 256 * 11), (256 * 11, 256 * 11), (256 * 17, 256 * 16)])
+def test_largest_tile_by_rounds_over_the_compute_units(M, N):
+    """256x256 tiles exactly when three times their rounds of workgroups over
+    the compute units come to at most the 128x128 tiles' rounds (4096 x 3840:
+    240 big tiles, one round, against 960 tiles in four; 4096 x 2048: 128
+    big tiles against two rounds; 4352 x 4096: two rounds against five)."""
     base = dict(in_type=0, la=0, lb=0, pad_a=0, pad_b=0, pad_c=0, alpha=1.0, off_a=0, off_b=0, K=512)
     c = query(dict(base, M=M, N=N))
-    full = cdiv(M, 256) * cdiv(N, 256) >= NUM_CU
-    assert (c["bm"] == 256) == full
+    big = 3 * cdiv(cdiv(M, 256) * cdiv(N, 256), NUM_CU) <= cdiv(cdiv(M, 128) * cdiv(N, 128), NUM_CU)
+    assert (c["bm"] == 256) == big
