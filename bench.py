@@ -84,21 +84,48 @@ def parse():
     return p.parse_args()
 
 
-#: the sources the product library is compiled from
-PRODUCT_SOURCES = ("dense_mixed_precision_amd/csrc/kernels.hpp", "dense_mixed_precision_amd/csrc/mpgemm.hip",
-                   "include/mpgemm.h")
+#: the product library as built in-tree
+PRODUCT_LIB = os.path.join("dense_mixed_precision_amd", "libmpgemm.so")
 
 
-def kernel_source_digest() -> str:
-    """Digest of the sources the product library is built from (not the
-    diagnostics'); counter readings are only reused while it matches."""
+def _elf_section(data: bytes, name: bytes):
+    """(offset, size) of the named section of a 64-bit little-endian ELF file."""
+    import struct
+
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+
+    def header(i):
+        return struct.unpack_from("<IIQQQQ", data, shoff + i * shentsize)
+
+    strtab = header(shstrndx)[4]
+    for i in range(shnum):
+        name_off, _, _, _, off, size = header(i)
+        end = data.index(b"\0", strtab + name_off)
+        if data[strtab + name_off:end] == name:
+            return off, size
+    return None
+
+
+def kernel_code_digest(lib: str | None = None):
+    """Digest of the device code the product library carries (the code
+    objects of every kernel in its .hip_fatbin section), or None if it is
+    not built.  Counter readings are only reused while it matches: a change
+    to host code alone (which table entry the factory picks) leaves it as it
+    is, any change to a kernel or to the table's template arguments does
+    not."""
     import hashlib
 
-    h = hashlib.sha256()
-    for rel in PRODUCT_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(rel.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
+    path = lib or os.path.join(ROOT, PRODUCT_LIB)
+    if not os.path.exists(path):
+        return None
+    with open(path, "rb") as f:
+        data = f.read()
+    sec = _elf_section(data, b".hip_fatbin")
+    if sec is None:
+        return None
+    off, size = sec
+    return hashlib.sha256(data[off:off + size]).hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel_ms: float):
@@ -115,7 +142,8 @@ def measured_traffic(workload: str, kernel_ms: float):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_digest") != kernel_source_digest():
+    digest = kernel_code_digest()
+    if digest is None or vals.get("kernel_code_digest") != digest:
         return None
     try:
         read_b = float(vals["l2_miss_read_bytes_per_launch"])

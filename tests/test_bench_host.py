@@ -1,4 +1,6 @@
 """CPU: the benchmark's host-side helpers (no GPU needed)."""
+import pytest
+
 import bench
 from dense_mixed_precision_amd.workloads import WORKLOADS
 
@@ -28,17 +30,17 @@ def test_secondary_warmup_is_about_40ms_of_gpu_time():
     assert bench.warmup_for(WORKLOADS["square8192"], 2) == 3          # at least 3
 
 
-def test_measured_traffic_follows_the_kernel_source_digest(tmp_path, monkeypatch):
+def test_measured_traffic_follows_the_kernel_code_digest(tmp_path, monkeypatch):
     """L2-miss bytes come from a committed counter summary only while the
-    kernel sources it was taken on are unchanged."""
-    digest = bench.kernel_source_digest()
+    device code it was taken on is unchanged."""
+    digest = "0123456789abcdef"
     prof = tmp_path / "profiles"
     prof.mkdir()
-    text = ("# L2-miss bytes\nkernel_source_digest: {d}\nl2_miss_read_bytes_per_launch: 3000\n"
+    text = ("# L2-miss bytes\nkernel_code_digest: {d}\nl2_miss_read_bytes_per_launch: 3000\n"
             "l2_miss_write_bytes_per_launch: 1000\n")
     (prof / "l2_miss_bytes_square2048.txt").write_text(text.format(d=digest))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "kernel_source_digest", lambda: digest)
+    monkeypatch.setattr(bench, "kernel_code_digest", lambda lib=None: digest)
     t = bench.measured_traffic("square2048", 0.001)
     assert t["bytes_per_launch"] == 4000 and t["GBps"] == 4.0
     roof = bench.with_traffic(bench.roofline_entry(WORKLOADS["square2048"], 0.025), t)
@@ -47,6 +49,10 @@ def test_measured_traffic_follows_the_kernel_source_digest(tmp_path, monkeypatch
     assert bench.measured_traffic("square2048", 0.001) is None
     assert bench.measured_traffic("square8192", 0.001) is None
     assert bench.with_traffic({"bound": "mfma"}, None)["traffic"] is None
+    # no library built: no digest, no reuse
+    monkeypatch.setattr(bench, "kernel_code_digest", lambda lib=None: None)
+    (prof / "l2_miss_bytes_square2048.txt").write_text(text.format(d=digest))
+    assert bench.measured_traffic("square2048", 0.001) is None
 
 
 def test_spread_reports_median_and_cv():
@@ -91,17 +97,33 @@ def test_timeline_summary_reads_the_record_layout():
     assert sorted(s["xcd_end_us"]) == list(range(8))
 
 
-def test_kernel_source_digest_covers_exactly_the_product_sources():
-    """The digest changes with the product library's sources and with
-    nothing else under csrc/ (the diagnostics' probes.hip)."""
+def test_kernel_code_digest_covers_the_device_code_only(tmp_path):
+    """The digest is that of the library's .hip_fatbin section (the kernels'
+    code objects): a byte changed inside the section changes it, a byte
+    changed elsewhere (host code) does not."""
+    import hashlib
     import os
 
-    assert set(bench.PRODUCT_SOURCES) == {"dense_mixed_precision_amd/csrc/kernels.hpp",
-                                          "dense_mixed_precision_amd/csrc/mpgemm.hip", "include/mpgemm.h"}
-    from dense_mixed_precision_amd import build
-
-    built_from = {os.path.relpath(p, bench.ROOT) for p in build.DEPS}
-    assert built_from == set(bench.PRODUCT_SOURCES)
+    lib = os.path.join(bench.ROOT, bench.PRODUCT_LIB)
+    if not os.path.exists(lib):
+        pytest.skip("product library not built")
+    data = bytearray(open(lib, "rb").read())
+    off, size = bench._elf_section(bytes(data), b".hip_fatbin")
+    assert size > 0
+    d0 = bench.kernel_code_digest(lib)
+    assert d0 == hashlib.sha256(bytes(data[off:off + size])).hexdigest()[:16]
+    host = tmp_path / "host.so"
+    data_h = bytearray(data)
+    data_h[off - 1] ^= 0xFF
+    data_h[off + size] ^= 0xFF
+    host.write_bytes(bytes(data_h))
+    assert bench.kernel_code_digest(str(host)) == d0
+    dev = tmp_path / "dev.so"
+    data_d = bytearray(data)
+    data_d[off + size // 2] ^= 0xFF
+    dev.write_bytes(bytes(data_d))
+    assert bench.kernel_code_digest(str(dev)) != d0
+    assert bench.kernel_code_digest(str(tmp_path / "missing.so")) is None
 
 
 def test_copy_bound_adds_the_loop_at_the_copy_rate_to_the_measured_phases():
