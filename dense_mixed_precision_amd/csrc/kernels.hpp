@@ -578,7 +578,7 @@ struct OpReader {
     }
 };
 
-template <class Cfg>
+template <class Cfg, bool NT_STORES = true>
 __global__ void __launch_bounds__(Cfg::NT)
 gemm_pipe(GemmArgs args_in)
 {
@@ -987,9 +987,12 @@ gemm_pipe(GemmArgs args_in)
 
     // ---- epilogue: C = alpha*acc + beta*C through buffer stores whose
     // out-of-range offsets the hardware drops (and loads read as zero).
-    // The stores are non-temporal: C is written once and should not evict
-    // the A and B panels other workgroups are still streaming through the
-    // caches (about 5% at 8192^3).
+    // The stores' cache policy is the kernel's NT_STORES: non-temporal, so
+    // C does not evict the A and B panels other workgroups are still
+    // streaming through the caches, or plain, so that a large burst of C (or
+    // rows that start mid-line) is absorbed by the caches; the host picks
+    // the variant per call.
+    constexpr int32_t kPolicy = NT_STORES ? kStoreNT : 0;
     const int64_t wrow0 = m0 + wm * Cfg::WTM;
     const int64_t wcol0 = n0 + wn * Cfg::WTN;
     const int64_t wrows = args.M - wrow0;
@@ -1067,7 +1070,7 @@ gemm_pipe(GemmArgs args_in)
                             if (args.bias)
                                 val += bp[p];
                             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC,
-                                                                  off[h][v], 0, kStoreNT);
+                                                                  off[h][v], 0, kPolicy);
                         }
                     }
                 }
@@ -1118,7 +1121,7 @@ gemm_pipe(GemmArgs args_in)
                         if (args.bias)
                             val += bv[j];
                         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), rsC, off[v], 0,
-                                                              kStoreNT);
+                                                              kPolicy);
                     }
                 }
             }

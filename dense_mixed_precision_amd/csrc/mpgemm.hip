@@ -36,15 +36,18 @@ constexpr int kNumCu = 256;
 // ---------------------------------------------------------------------------
 using launch_fn = hipError_t (*)(const GemmArgs &, dim3, hipStream_t);
 
+// `launch` runs the entry with non-temporal C stores, `launch_plain` with
+// plain ones (the same launch where the entry has one variant only).
 struct Entry {
     mpgemm_config cfg;
     launch_fn launch;
+    launch_fn launch_plain;
 };
 
-template <class Cfg>
+template <class Cfg, bool NT_STORES>
 hipError_t launch_pipe(const GemmArgs &a, dim3 grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(mpg::gemm_pipe<Cfg>, grid, dim3(Cfg::NT), 0, s, a);
+    hipLaunchKernelGGL((mpg::gemm_pipe<Cfg, NT_STORES>), grid, dim3(Cfg::NT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -89,7 +92,11 @@ constexpr Entry pipe_entry(int id)
     c.in_type = Cfg::IN;
     c.k_groups = Cfg::KGROUPS;
     c.k_order = Cfg::STAGGER;
-    return Entry{c, &launch_pipe<Cfg>};
+    // 256x256 tiles also come with plain C stores (see nt_stores)
+    launch_fn plain = &launch_pipe<Cfg, true>;
+    if constexpr (Cfg::BM == 256)
+        plain = &launch_pipe<Cfg, false>;
+    return Entry{c, &launch_pipe<Cfg, true>, plain};
 }
 
 // N <= 16 with A row-major: 16 rows of C per workgroup, 8 waves over K.
@@ -118,7 +125,7 @@ constexpr Entry narrow_entry(int id)
     c.layout_b = LB;
     c.in_type = IN;
     c.k_groups = 8;     // waves splitting K
-    return Entry{c, &launch_narrow<IN, LB, DEPTH>};
+    return Entry{c, &launch_narrow<IN, LB, DEPTH>, &launch_narrow<IN, LB, DEPTH>};
 }
 
 template <int IN>
@@ -144,7 +151,7 @@ constexpr Entry direct_entry(int id)
     c.lds_bytes = 0;
     c.in_type = IN;
     c.k_groups = 1;
-    return Entry{c, &launch_direct<IN>};
+    return Entry{c, &launch_direct<IN>, &launch_direct<IN>};
 }
 
 constexpr Entry scale_entry(int id)
@@ -154,7 +161,7 @@ constexpr Entry scale_entry(int id)
     c.kind = MPGEMM_KIND_SCALE;
     c.threads = 256;
     c.k_groups = 1;
-    return Entry{c, nullptr};
+    return Entry{c, nullptr, nullptr};
 }
 
 // The tile shapes the factory chooses from, for one input format and
@@ -538,6 +545,29 @@ int fill_config(int id, const Problem &p, mpgemm_config *out)
     return MPGEMM_OK;
 }
 
+// Cache policy of the pipelined kernel's C stores, by graph-replayed A/B of
+// the two policies.  Non-temporal stores keep C from evicting the operand
+// panels and win for 128x128 and smaller tiles, which have that variant
+// only (2048^3 24.5 against 25.7 us, 32768x128x4096 52.9 against 57.7,
+// 16384x256x1024 14.2 against 15.8; rows that start mid-line make no
+// difference there: 2049^2 x 2048 59.0 against 58.9).  256x256 tiles write
+// up to 64 MiB of C per round at once, which plain stores let the caches
+// absorb (8192x8192x512 100.8 against 116.4 us, 4096^3 113.0 against
+// 117.1, 1456x10608x512 24.2 against 27.7); non-temporal stores win for
+// them only with at most 160 tiles (3072x2816x1024 29.7 against 31.2) or
+// several rounds at long K (8192^3 855 against 881, 8192x8192x2048 259.8
+// against 263.6), and never when rows start mid-line (ldc not a multiple
+// of 32 floats, or C not 128-byte aligned), where non-temporal partial
+// lines cost up to 2.5x (1457x10609x128: 16.8 against 42.1 us).
+bool nt_stores(const mpgemm_config &c, const Problem &p)
+{
+    if (c.kind != MPGEMM_KIND_PIPE || c.bm < 256)
+        return true;
+    const bool aligned = p.ldc % 32 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 127) == 0;
+    const int64_t tiles = mul_sat(cdiv(p.M, c.bm), cdiv(p.N, c.bn));
+    return aligned && (tiles <= 160 || (tiles > kNumCu && p.K >= 2048));
+}
+
 int run(int id, const Problem &p, void *stream)
 {
     if (id < 0)
@@ -591,7 +621,8 @@ int run(int id, const Problem &p, void *stream)
     // A launch error from an earlier, unrelated call must not be reported
     // as this call's failure.
     (void)hipGetLastError();
-    const hipError_t err = e.launch(a, dim3((unsigned)grid), s);
+    const launch_fn launch = nt_stores(e.cfg, p) ? e.launch : e.launch_plain;
+    const hipError_t err = launch(a, dim3((unsigned)grid), s);
     return err == hipSuccess ? MPGEMM_OK : MPGEMM_ELAUNCH;
 }
 
@@ -682,6 +713,7 @@ int run_split(const SplitPlan &sp, const Problem &p, float *ws, void *stream)
     a.splits = sp.splits;
     a.k_split = sp.k_split;
     a.ws = ws;
+
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * sp.splits;
     (void)hipGetLastError();
     hipError_t err = e.launch(a, dim3((unsigned)grid), s);
