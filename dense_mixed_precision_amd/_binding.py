@@ -43,7 +43,8 @@ class MpgemmConfig(ctypes.Structure):
         "id", "kind", "bm", "bn", "bk", "waves_m", "waves_n", "wave_m", "wave_n",
         "mfma_m", "mfma_n", "mfma_k", "vec_a", "vec_b", "stages", "threads", "lds_bytes")] + [
         ("grid", ctypes.c_int64), ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32),
-        ("in_type", ctypes.c_int32), ("k_groups", ctypes.c_int32), ("k_order", ctypes.c_int32)]
+        ("in_type", ctypes.c_int32), ("k_groups", ctypes.c_int32), ("k_order", ctypes.c_int32),
+        ("c_stores", ctypes.c_int32)]
 
 
 config_fields = [f[0] for f in MpgemmConfig._fields_]

@@ -92,6 +92,7 @@ constexpr Entry pipe_entry(int id)
     c.in_type = Cfg::IN;
     c.k_groups = Cfg::KGROUPS;
     c.k_order = Cfg::STAGGER;
+    c.c_stores = Cfg::BM == 256 ? 2 : 1;
     // 256x256 tiles also come with plain C stores (see nt_stores)
     launch_fn plain = &launch_pipe<Cfg, true>;
     if constexpr (Cfg::BM == 256)
@@ -125,6 +126,7 @@ constexpr Entry narrow_entry(int id)
     c.layout_b = LB;
     c.in_type = IN;
     c.k_groups = 8;     // waves splitting K
+    c.c_stores = 1;
     return Entry{c, &launch_narrow<IN, LB, DEPTH>, &launch_narrow<IN, LB, DEPTH>};
 }
 
@@ -422,7 +424,7 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
     const bool deep_k = small_deep_k && p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR &&
                         p.lb == MPGEMM_ROW_MAJOR && p.K > 64;
     const int64_t tiles64 = mul_sat(cdiv(p.M, 64), cdiv(p.N, 64));
-    int order[4];
+    int order[6];
     int n = 0;
     // 256x256 or 128x128 tiles, by the rounds of workgroups each puts on
     // the compute units (one workgroup per unit): a 256x256 tile takes about
@@ -437,9 +439,28 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
     // at least half empty (65536x128x4096 159.7 against 130.2 us).
     const bool rr16 = p.in_type == MPGEMM_IN_F16 && p.la == MPGEMM_ROW_MAJOR && p.lb == MPGEMM_ROW_MAJOR;
     const int64_t tm128 = cdiv(p.M, 128), tn128 = cdiv(p.N, 128);
-    const int64_t rounds256 = cdiv(mul_sat(cdiv(p.M, 256), cdiv(p.N, 256)), kNumCu);
+    const int64_t tiles256 = mul_sat(cdiv(p.M, 256), cdiv(p.N, 256));
+    const int64_t rounds256 = cdiv(tiles256, kNumCu);
     const int64_t rounds128 = cdiv(mul_sat(tm128, tn128), kNumCu);
-    if (mul_sat(3, rounds256) <= rounds128) {
+    const bool big_by_rounds = mul_sat(3, rounds256) <= rounds128;
+    // Short K (at most 256) over at least two 64x64 tiles per compute unit:
+    // writing C is much of the work, and the 64x64x64 tiles on 4 waves,
+    // several workgroups per unit, overlap one tile's stores with another's
+    // loads.  They win unless the 256x256 tiles come to nearly a full round
+    // (at least 240 of them: 4096^2 x 64 14.6 against 16.6 us, 1456x10608x128
+    // 16.8 against 18.5) or the 128x128 class has whole 128-deep K tiles
+    // (2048^2 x 128 6.48 against 6.59): 3328^2 x 128 12.8 against 14.4 us
+    // for 169 big tiles, 6144x2048x192 16.2 against 16.5, 2048^2 x 192 7.0
+    // against 7.9, 2048x1024x192 5.3 against 6.2, 5907x1622x137 18.9
+    // against 26.3.
+    if (p.K <= 256 && tiles64 >= 2 * kNumCu) {
+        if (big_by_rounds && tiles256 >= 240)
+            order[n++] = fam + kBig;
+        else if (!big_by_rounds && p.K % 128 == 0)
+            order[n++] = fam + kWide;
+        order[n++] = fam + kSmall;
+        order[n++] = fam + kMid;
+    } else if (big_by_rounds) {
         order[n++] = fam + kBig;
         order[n++] = fam + kMid;
     } else if (mul_sat(cdiv(p.M, 128), cdiv(p.N, 128)) >= kNumCu / 2 &&
@@ -524,6 +545,31 @@ Problem canonical(Problem p)
     return id >= 0 && kTable[id].cfg.kind == MPGEMM_KIND_NARROW ? q : p;
 }
 
+// Cache policy of the pipelined kernel's C stores, by graph-replayed A/B of
+// the two policies.  Non-temporal stores keep C from evicting the operand
+// panels and win for 128x128 and smaller tiles, which have that variant
+// only (2048^3 24.5 against 25.7 us, 32768x128x4096 52.9 against 57.7,
+// 16384x256x1024 14.2 against 15.8; rows that start mid-line make no
+// difference there: 2049^2 x 2048 59.0 against 58.9).  256x256 tiles write
+// up to 64 MiB of C per round at once, which plain stores let the caches
+// absorb from about 190 tiles on (6144x2048x1024, 192 tiles, 32.8 against
+// 33.5 us; 3584x4096x1024, 224, 35.2 against 36.3; 8192x8192x512 103.9
+// against 117.5; 4096^3 113.0 against 116.1); with fewer tiles (up to 169
+// measured: 3328^2 x 512 21.1 against 21.4, 2560^2 x 512 18.5 against
+// 20.6) or more than one round at long K (8192^3 855 against 881,
+// 8192x8192x2048 262.0 against 265.0) non-temporal stores win.  Rows that
+// start mid-line (ldc not a multiple of 32 floats, or C not 128-byte
+// aligned) take plain stores: there non-temporal partial lines cost up to
+// 2.5x (1457x10609x128: 16.8 against 42.1 us).
+bool nt_stores(const mpgemm_config &c, const Problem &p)
+{
+    if (c.kind != MPGEMM_KIND_PIPE || c.bm < 256)
+        return true;
+    const bool aligned = p.ldc % 32 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 127) == 0;
+    const int64_t tiles = mul_sat(cdiv(p.M, c.bm), cdiv(p.N, c.bn));
+    return aligned && (tiles <= 176 || (tiles > kNumCu && p.K >= 2048));
+}
+
 int fill_config(int id, const Problem &p, mpgemm_config *out)
 {
     if (id < 0) {
@@ -539,34 +585,14 @@ int fill_config(int id, const Problem &p, mpgemm_config *out)
     }
     *out = kTable[id].cfg;
     out->grid = grid_for(out[0], p);
+    if (out->kind == MPGEMM_KIND_PIPE)
+        out->c_stores = nt_stores(*out, p) ? 1 : 0;
     out->layout_a = p.la;
     out->layout_b = p.lb;
     out->in_type = p.in_type;
     return MPGEMM_OK;
 }
 
-// Cache policy of the pipelined kernel's C stores, by graph-replayed A/B of
-// the two policies.  Non-temporal stores keep C from evicting the operand
-// panels and win for 128x128 and smaller tiles, which have that variant
-// only (2048^3 24.5 against 25.7 us, 32768x128x4096 52.9 against 57.7,
-// 16384x256x1024 14.2 against 15.8; rows that start mid-line make no
-// difference there: 2049^2 x 2048 59.0 against 58.9).  256x256 tiles write
-// up to 64 MiB of C per round at once, which plain stores let the caches
-// absorb (8192x8192x512 100.8 against 116.4 us, 4096^3 113.0 against
-// 117.1, 1456x10608x512 24.2 against 27.7); non-temporal stores win for
-// them only with at most 160 tiles (3072x2816x1024 29.7 against 31.2) or
-// several rounds at long K (8192^3 855 against 881, 8192x8192x2048 259.8
-// against 263.6), and never when rows start mid-line (ldc not a multiple
-// of 32 floats, or C not 128-byte aligned), where non-temporal partial
-// lines cost up to 2.5x (1457x10609x128: 16.8 against 42.1 us).
-bool nt_stores(const mpgemm_config &c, const Problem &p)
-{
-    if (c.kind != MPGEMM_KIND_PIPE || c.bm < 256)
-        return true;
-    const bool aligned = p.ldc % 32 == 0 && (reinterpret_cast<uintptr_t>(p.C) & 127) == 0;
-    const int64_t tiles = mul_sat(cdiv(p.M, c.bm), cdiv(p.N, c.bn));
-    return aligned && (tiles <= 160 || (tiles > kNumCu && p.K >= 2048));
-}
 
 int run(int id, const Problem &p, void *stream)
 {
@@ -1050,7 +1076,7 @@ const char *mpgemm_strerror(int code)
     }
 }
 
-const char *mpgemm_version(void) { return "mpgemm 0.7.0 gfx950"; }
+const char *mpgemm_version(void) { return "mpgemm 0.8.0 gfx950"; }
 
 #ifdef MPGEMM_TIMELINE
 // Timeline build only: host access to the per-workgroup stamps the

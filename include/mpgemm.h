@@ -117,6 +117,12 @@ typedef struct mpgemm_config {
                             and wraps round (its sum over K is taken in another
                             order, so its rounding differs from the ascending
                             entry's)                                            */
+    int32_t c_stores;    /* cache policy of the stores of C: for a queried call
+                            1 non-temporal, 0 plain; in the table 1 or 0 for
+                            an entry built with that policy only, 2 for one
+                            built with both (256x256 tiles: plain when more
+                            than 176 of them write their C in one round at
+                            K < 2048, or when the rows of C start mid-line)  */
 } mpgemm_config;
 
 /*
@@ -363,7 +369,7 @@ int mpgemm_config_info(int config_id, mpgemm_config *out);
 /* Static text for an error code (never NULL). */
 const char *mpgemm_strerror(int code);
 
-/* Library version string, e.g. "mpgemm 0.7.0 gfx950". */
+/* Library version string, e.g. "mpgemm 0.8.0 gfx950". */
 const char *mpgemm_version(void);
 
 #ifdef __cplusplus

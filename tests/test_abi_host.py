@@ -189,6 +189,14 @@ def test_factory_choices_for_the_workloads():
     (1024, 2048, 2048, (64, 64, 128, 2)), (2048, 1024, 512, (64, 64, 128, 2)),
     # more than half a wave otherwise: 128x128
     (1536, 1536, 2048, (128, 128, 128, 2)), (1280, 2048, 8192, (128, 128, 128, 2)),
+    # short K over at least two 64x64 tiles per unit: 64x64x64 tiles, unless
+    # the big tiles come to nearly a full round or the 128x128 class has
+    # whole 128-deep K tiles
+    (3072, 3072, 128, (64, 64, 64, 2)), (2048, 2048, 192, (64, 64, 64, 2)), (2048, 1024, 64, (64, 64, 64, 2)),
+    (5907, 1622, 137, (64, 64, 64, 2)), (3328, 3328, 256, (64, 64, 64, 2)),
+    (4096, 4096, 64, (256, 256, 64, 2)), (1457, 10609, 128, (256, 256, 64, 2)),
+    (2048, 2048, 128, (128, 128, 128, 2)), (2048, 2048, 256, (128, 128, 128, 2)),
+    (3072, 3072, 384, (256, 256, 64, 2)), (1024, 1024, 128, (64, 64, 128, 2)),
     # 256x256 tiles where 3 x their rounds over the compute units <= the
     # 128x128 tiles' rounds, even with fewer big tiles than units
     (3072, 2816, 4096, (256, 256, 64, 2)), (4096, 2304, 1024, (256, 256, 64, 2)),
@@ -242,6 +250,31 @@ def test_one_column_row_major_b_is_read_as_column_major():
     assert code(4096, 1, 4096, ldb=0) == mp.MPGEMM_ELD
     plan = mp.mpgemm_splitk_plan(mp.MPGEMM_IN_F16, 0, 0, 4096, 1, 4096, FAKE_A, 4096, FAKE_B, 1, 0)
     assert mp.mpgemm_config_info(plan["config_id"])["layout_b"] == mp.MPGEMM_COL_MAJOR
+
+
+@pytest.mark.parametrize("M,N,K,ldc,c_off,stores", [
+    # 128x128 and smaller tiles: non-temporal stores only
+    (2048, 2048, 2048, None, 0, 1), (32768, 128, 4096, None, 0, 1), (1000, 800, 617, None, 0, 1),
+    (2049, 2049, 2048, None, 0, 1),
+    # 256x256: non-temporal over several rounds at K >= 2048 or with at most 176 tiles
+    (8192, 8192, 8192, None, 0, 1), (8192, 8192, 2048, None, 0, 1), (3072, 2816, 1024, None, 0, 1),
+    (3328, 3328, 512, None, 0, 1), (3584, 4096, 384, None, 0, 0),
+    # ... plain for a full round at shorter K
+    (8192, 8192, 512, None, 0, 0), (4096, 4096, 4096, None, 0, 0), (4096, 4096, 1024, None, 0, 0),
+    (1456, 10608, 512, None, 0, 0),
+    # ... and whenever the rows of C start mid-line
+    (8192, 8192, 8192, 8200, 0, 0), (8192, 8192, 8192, None, 4, 0), (1457, 10609, 128, None, 0, 0),
+])
+def test_factory_c_store_policy(M, N, K, ldc, c_off, stores):
+    """The cache policy of the C stores the query reports (1 non-temporal,
+    0 plain), by the measured rule; the table marks the entries built with
+    both (the 256x256 tiles) with 2."""
+    c = q(M, N, K, ldc=ldc, C=FAKE_C + c_off)
+    assert c["c_stores"] == stores, (M, N, K, ldc, c_off, c["bm"])
+    kinds = {mp.mpgemm_config_info(i)["bm"]: mp.mpgemm_config_info(i)["c_stores"]
+             for i in range(mp.mpgemm_num_configs()) if mp.mpgemm_config_info(i)["kind_name"] == "pipe"}
+    assert kinds[256] == 2 and all(v == 1 for bm, v in kinds.items() if bm != 256)
+    assert mp.mpgemm_config_info(0)["c_stores"] == 0      # the direct kernel's plain stores
 
 
 def test_factory_alignment_and_degenerate_cases():
