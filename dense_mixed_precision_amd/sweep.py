@@ -2,6 +2,7 @@
 
     python -m dense_mixed_precision_amd.sweep --shapes 512x512,1024x2048 --ks 256,2048,8192 \\
         --configs 35,36,41 [--candidates] [--rounds 5] [--in f16|bf16] [--layout rr|cr|rc|cc]
+    python -m dense_mixed_precision_amd.sweep --triples 5907x1622x137,652x11198x66 --configs 3,5,6
 
 For every M x N x K it captures, per forced table entry, a HIP graph of
 back-to-back launches of that entry (FP16 or BF16 operands, each row- or
@@ -21,8 +22,9 @@ import json
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    p.add_argument("--shapes", required=True, help="comma-separated MxN pairs")
-    p.add_argument("--ks", required=True, help="comma-separated K values")
+    p.add_argument("--shapes", help="comma-separated MxN pairs (with --ks)")
+    p.add_argument("--ks", help="comma-separated K values (with --shapes)")
+    p.add_argument("--triples", help="comma-separated MxNxK products (instead of --shapes and --ks)")
     p.add_argument("--configs", required=True, help="comma-separated table entries to force")
     p.add_argument("--candidates", action="store_true", help="load the candidates build")
     p.add_argument("--rounds", type=int, default=5)
@@ -42,10 +44,16 @@ def main():
 
     mp.load(mp.CANDIDATES_PATH if args.candidates else None)
     dev = torch.device("cuda:0")
-    shapes = [tuple(int(x) for x in s.split("x")) for s in args.shapes.split(",")]
-    ks = [int(k) for k in args.ks.split(",")]
+    if args.triples:
+        products = [tuple(int(x) for x in t.split("x")) for t in args.triples.split(",")]
+    elif args.shapes and args.ks:
+        shapes = [tuple(int(x) for x in s.split("x")) for s in args.shapes.split(",")]
+        ks = [int(k) for k in args.ks.split(",")]
+        products = [(M, N, K) for (M, N), K in itertools.product(shapes, ks)]
+    else:
+        raise SystemExit("give --triples, or --shapes and --ks")
     cfgs = [int(c) for c in args.configs.split(",")]
-    for (M, N), K in itertools.product(shapes, ks):
+    for M, N, K in products:
         dtype = torch.bfloat16 if args.in_type == "bf16" else torch.float16
         A, B, _ = make_inputs(M, N, K, "uniform", seed=args.seed, dtype=dtype)
         # a column-major operand is stored transposed and passed as the transposed view
