@@ -482,6 +482,16 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
         // 143.3 against 122.1).
         const bool wide = (tm128 >= 2 && tn128 >= 2 && !(tn128 == 2 && p.K >= 8192)) ||
                           (tn128 == 1 && p.K <= 1024) || (tm128 == 1 && p.K <= 2048);
+        // Row-major FP16 whose B rows are not 16-byte aligned, with a second
+        // round of at most 64 128x128 tiles: the 64x64x128 tiles (two
+        // workgroups per unit) balance the tail better (2049^2 x 2048 57.0
+        // against 60.6 us, 2048x2049x2048 57.3 against 64.5, 2100^2 x 2048
+        // 57.9 against 64.3, 1744x2439x2048 59.4 against 63.8; with aligned
+        // B rows the 128x128 tiles keep the lead: 2049x2048x2048 42.4
+        // against 44.2).
+        const int64_t tail128 = mul_sat(tm128, tn128) - kNumCu;
+        if (rr16 && p.ldb % 8 != 0 && rounds128 == 2 && tail128 <= 64)
+            order[n++] = kSmallDeepKId;
         if (wide)
             order[n++] = fam + kWide;
         order[n++] = fam + kMid;

@@ -197,6 +197,11 @@ def test_factory_choices_for_the_workloads():
     (4096, 4096, 64, (256, 256, 64, 2)), (1457, 10609, 128, (256, 256, 64, 2)),
     (2048, 2048, 128, (128, 128, 128, 2)), (2048, 2048, 256, (128, 128, 128, 2)),
     (3072, 3072, 384, (256, 256, 64, 2)), (1024, 1024, 128, (64, 64, 128, 2)),
+    # B rows not 16-byte aligned with a second round of at most 64 128x128
+    # tiles: 64x64x128 tiles; aligned B rows or a fuller second round keep
+    # the 128x128 tiles
+    (2049, 2049, 2048, (64, 64, 128, 2)), (2100, 2100, 2048, (64, 64, 128, 2)),
+    (2049, 2048, 2048, (128, 128, 128, 2)), (2304, 2305, 2048, (128, 128, 128, 2)),
     # 256x256 tiles where 3 x their rounds over the compute units <= the
     # 128x128 tiles' rounds, even with fewer big tiles than units
     (3072, 2816, 4096, (256, 256, 64, 2)), (4096, 2304, 1024, (256, 256, 64, 2)),
