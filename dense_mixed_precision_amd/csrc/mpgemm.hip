@@ -442,7 +442,14 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
     const int64_t tiles256 = mul_sat(cdiv(p.M, 256), cdiv(p.N, 256));
     const int64_t rounds256 = cdiv(tiles256, kNumCu);
     const int64_t rounds128 = cdiv(mul_sat(tm128, tn128), kNumCu);
-    const bool big_by_rounds = mul_sat(3, rounds256) <= rounds128;
+    // With A row-major and B column-major (both K-contiguous, every operand
+    // read by ds_read_b128) the big tile is relatively cheaper: it wins at
+    // 2.5 times its rounds (1504x12052x2229, two rounds against five: 150.3
+    // against 171.5 us; 7198x2381x2219 148.5 against 168.4; 1018x16708x510
+    // 49.5 against 53.2; 4352x4096x4096 201.0 against 197.7 the one loss).
+    const bool big_by_rounds = (p.la == MPGEMM_ROW_MAJOR && p.lb == MPGEMM_COL_MAJOR)
+                                   ? mul_sat(5, rounds256) <= mul_sat(2, rounds128)
+                                   : mul_sat(3, rounds256) <= rounds128;
     // Short K (at most 256) over at least two 64x64 tiles per compute unit:
     // writing C is much of the work, and the 64x64x64 tiles on 4 waves,
     // several workgroups per unit, overlap one tile's stores with another's

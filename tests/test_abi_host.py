@@ -396,6 +396,9 @@ def test_layout_factory_choices(la, lb):
     assert ql(la, lb, 32768, 128, 4096)["bk"] == 64
     assert ql(la, lb, 3072, 2816, 4096)["bm"] == 256
     assert ql(la, lb, 4096, 2048, 4096)["bm"] == 128
+    # two rounds of 256x256 tiles against five of 128x128: the big tile for
+    # A row-major with B column-major only
+    assert ql(la, lb, 1504, 12052, 2229)["bm"] == (256 if (la, lb) == (0, 1) else 128)
     c = ql(la, lb, 1000, 800, 617, lda=(1001 if la else 617), ldb=(617 if lb else 800))
     assert c["kind_name"] == "pipe" and (c["vec_a"], c["vec_b"]) == (8, 8)
     # a stored stage beyond 32-bit offsets leaves only the 64-bit direct kernel
