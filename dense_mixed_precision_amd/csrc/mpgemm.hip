@@ -497,7 +497,7 @@ int select(const Problem &p, bool small_deep_k = true, bool allow_narrow = true)
         // B rows the 128x128 tiles keep the lead: 2049x2048x2048 42.4
         // against 44.2).
         const int64_t tail128 = mul_sat(tm128, tn128) - kNumCu;
-        if (rr16 && p.ldb % 8 != 0 && rounds128 == 2 && tail128 <= 64)
+        if (small_deep_k && rr16 && p.ldb % 8 != 0 && rounds128 == 2 && tail128 <= 64)
             order[n++] = kSmallDeepKId;
         if (wide)
             order[n++] = fam + kWide;
