@@ -679,9 +679,10 @@ struct SplitPlan {
     int64_t ws_bytes; // workspace the partial products need
 };
 
-// `requested` 0: automatic (split only when the tile grid fills less than
-// half the chip, up to 16 ranges of at least 4 K tiles each); otherwise that
-// many ranges, at most one per K tile.  Empty ranges are never planned.
+// `requested` 0: automatic (split only a grid under one wave of resident
+// workgroups with K >= 4096, into ranges of about 1024 K, at most about 4
+// workgroups per compute unit and at most 32 ranges); otherwise that many
+// ranges, at most one per K tile.  Empty ranges are never planned.
 SplitPlan plan_split(const Problem &p, int requested)
 {
     // an unsplit plan keeps the factory's own choice
@@ -706,15 +707,27 @@ SplitPlan plan_split(const Problem &p, int requested)
     const int64_t ktiles = cdiv(p.K, c.bk);
     int64_t s;
     if (requested == 0) {
-        // About two workgroups per compute unit: the pieces are short, so a
-        // second resident workgroup keeps more copies in flight (measured
-        // best among 1x/2x/4x the unit count on 4096x16x4096,
-        // 512x512x16384 and 256x256x65536).  Pieces of at least 4 K tiles.
-        s = tiles >= kNumCu / 2 ? 1 : cdiv(2 * kNumCu, tiles);
-        if (s > 32)
-            s = 32;
-        if (s > ktiles / 4)
-            s = ktiles / 4;
+        // Only grids under one wave of resident workgroups (the config's
+        // LDS allows `occ` per compute unit), only K of at least 4096, and
+        // pieces of about 1024 K, at most about 4 workgroups per unit and at
+        // most 32 pieces.  By graph-replayed sweeps of forced piece counts:
+        // 256x256x8192 8 pieces 16.0 us (32 pieces 22.7, unsplit 33.5),
+        // 256x256x65536 32 pieces 45.2, 2048x256x8192 8 pieces 26.8
+        // (unsplit 36.1), 1024x1024x8192 4 pieces 41.5 (unsplit 48.0);
+        // shorter K stays whole (512x512x2048 unsplit 10.3 against 13.5 for
+        // 2 pieces and 14.1 for 8).
+        const int64_t occ = c.lds_bytes > 0 ? (160 * 1024) / c.lds_bytes : 1;
+        const int64_t resident = kNumCu * (occ < 1 ? 1 : occ > 4 ? 4 : occ);
+        if (tiles >= resident || p.K < 4096)
+            s = 1;
+        else {
+            s = p.K / 1024;
+            const int64_t cap = cdiv(4 * kNumCu, tiles);
+            if (s > cap)
+                s = cap;
+            if (s > 32)
+                s = 32;
+        }
     } else {
         s = requested < ktiles ? requested : ktiles;
     }
@@ -1037,7 +1050,13 @@ int mpgemm_gemm_splitk_static(int in_type, int layout_a, int layout_b, int64_t M
     if (rc != MPGEMM_OK)
         return rc;
     const Problem p = canonical(given);
-    const SplitPlan sp = plan_split(p, splits_requested);
+    SplitPlan sp = plan_split(p, splits_requested);
+    if (splits_requested == 0 && sp.splits > 1 && sp.ws_bytes > kScratchBytes) {
+        // an automatic plan larger than the scratch: as many pieces as fit
+        // (the unsplit product when fewer than two do)
+        const int64_t fit = kScratchBytes / mul_sat(mul_sat(p.M, p.N), 4);
+        sp = fit >= 2 ? plan_split(p, (int)(fit < 32 ? fit : 32)) : SplitPlan{select(p), 1, 0, 0};
+    }
     if (sp.splits <= 1)
         return run(sp.id, p, stream);
     if (sp.ws_bytes > kScratchBytes)

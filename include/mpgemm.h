@@ -293,10 +293,11 @@ int mpgemm_gemm_ex_with_config(int config_id, int in_type, int layout_a, int lay
  *     C[i][j] <- alpha * sum_s P_s[i][j] + beta * C[i][j] + bias[j]
  *
  * mpgemm_splitk_plan reports, without any HIP call, how many pieces a call
- * would use (`splits_requested` 0: automatic, split only when the grid
- * fills less than half the chip, into enough pieces for about two
- * workgroups per compute unit, at most 32 and at most a quarter of the K
- * tiles; a product the factory gives the narrow kernel stays whole when it
+ * would use (`splits_requested` 0: automatic, split only when K >= 4096
+ * and the grid is under one wave of the workgroups the compute units hold
+ * at once, into pieces of about 1024 K, at most about 4 workgroups per
+ * compute unit and at most 32 pieces; a product the factory gives the
+ * narrow kernel stays whole when it
  * has at least 64 groups of 16 rows; n > 0: a tile kernel's K tiles dealt
  * into n pieces, at most one per K tile.  Every piece but the last holds
  * ceil(K tiles / pieces asked) K tiles, so the count can come out below the
@@ -336,10 +337,13 @@ int mpgemm_gemm_splitk(int in_type, int layout_a, int layout_b,
  * allocation): mpgemm_gemm_splitk with the partial products in a static
  * array of MPGEMM_STATIC_SCRATCH_BYTES bytes that the library's code object
  * holds on each device it is loaded on, until the process ends, instead of
- * a caller workspace.  The plan is the one mpgemm_splitk_plan reports; a
- * plan of one piece runs the ordinary path and touches no scratch.  A plan
- * whose workspace exceeds MPGEMM_STATIC_SCRATCH_BYTES returns
- * MPGEMM_ESCRATCH before any HIP call; other errors as mpgemm_gemm_splitk.
+ * a caller workspace.  The plan is the one mpgemm_splitk_plan reports,
+ * except that an automatic plan (`splits_requested` 0) whose workspace
+ * exceeds the scratch takes as many pieces as fit (the unsplit product
+ * when fewer than two do); a plan of one piece runs the ordinary path and
+ * touches no scratch.  A requested plan whose workspace exceeds
+ * MPGEMM_STATIC_SCRATCH_BYTES returns MPGEMM_ESCRATCH before any HIP call;
+ * other errors as mpgemm_gemm_splitk.
  * The scratch is the current device's, so `stream` must belong to the
  * current device.  Every call on a device shares that device's scratch and
  * leaves its partial products there (each call writes every partial it then

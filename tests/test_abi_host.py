@@ -472,16 +472,28 @@ def test_splitk_plan_skinny_case_fills_the_chip():
     assert mp.mpgemm_config_info(p["config_id"])["kind_name"] == "narrow"
     assert (p["splits"], p["workspace_bytes"]) == (1, 0)
     # 256 x 16 x 65536: 16 narrow workgroups would leave the chip idle, so
-    # the plan splits a tile kernel into enough pieces for ~2 workgroups per
-    # compute unit, at most 32
+    # the plan splits a tile kernel into pieces of about 1024 K, at most ~4
+    # workgroups per compute unit and at most 32
     p = plan(256, 16, 65536)
     c = mp.mpgemm_config_info(p["config_id"])
     tiles = -(-256 // c["bm"])
-    assert c["kind_name"] == "pipe" and p["splits"] == min(32, -(-2 * 256 // tiles))
+    assert c["kind_name"] == "pipe" and p["splits"] == min(32, 65536 // 1024, -(-4 * 256 // tiles))
     assert p["workspace_bytes"] == p["splits"] * 256 * 16 * 4
     # a requested piece count splits a tile kernel whatever the shape
     p = plan(4096, 16, 4096, splits=4)
     assert p["splits"] == 4 and mp.mpgemm_config_info(p["config_id"])["kind_name"] == "pipe"
+
+
+@pytest.mark.parametrize("M,N,K,pieces", [
+    (512, 512, 2048, 1), (512, 512, 1024, 1),          # K < 4096 stays whole
+    (256, 256, 8192, 8), (256, 256, 16384, 16),        # pieces of 1024 K
+    (256, 256, 65536, 32),                             # at most 32
+    (1024, 1024, 8192, 4), (2048, 256, 8192, 8),       # at most ~4 workgroups per unit
+    (2048, 2048, 8192, 1),                             # a full wave of 128x128 tiles
+])
+def test_splitk_automatic_plan(M, N, K, pieces):
+    """The automatic plan, by graph-replayed sweeps of forced piece counts."""
+    assert plan(M, N, K)["splits"] == pieces
 
 
 def test_splitk_plan_keeps_full_grids_whole():

@@ -19,8 +19,8 @@ header and table state:
   bytes (none for one piece), pieces only of a tiled kernel, each but the
   last holding ceil(K tiles / pieces asked) K tiles (so a requested count
   n gives ceil(K tiles / ceil(K tiles / n)) pieces, at most n and at most
-  one per K tile), and an automatic split into at most 32 pieces and at
-  most a quarter of the K tiles.
+  one per K tile), and an automatic split only for K >= 4096, into at most
+  32 pieces of at least 1024 K.
 """
 import pytest
 from hypothesis import HealthCheck, given, settings
@@ -140,7 +140,8 @@ def test_splitk_plan_obeys_its_contract(p, requested):
         n = min(requested, k_tiles)
         assert s == cdiv(k_tiles, cdiv(k_tiles, n)) and s <= n
     else:
-        assert s <= 32 and s * 4 <= k_tiles
+        # K of at least 4096, pieces of at least 1024 K, at most 32
+        assert s <= 32 and K >= 4096 and s <= K // 1024
 
 
 def test_strategies_reach_every_kind():

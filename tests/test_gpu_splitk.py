@@ -87,7 +87,8 @@ def test_more_pieces_than_k_tiles_is_capped():
 
 @pytest.mark.parametrize("la,lb", [(0, 1), (1, 0), (1, 1)])
 def test_layouts(la, lb):
-    A, B, C = make_inputs(256, 96, 3000, "uniform", seed=90 + la + 2 * lb, c_init="uniform")
+    """A ragged K past 4096 with two tiles of C: the automatic plan splits it."""
+    A, B, C = make_inputs(256, 96, 5000, "uniform", seed=90 + la + 2 * lb, c_init="uniform")
     check(f"layout {la}{lb}", A, B, C, 0.75, -1.0, la, lb)
 
 
