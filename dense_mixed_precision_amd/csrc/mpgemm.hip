@@ -715,13 +715,18 @@ SplitPlan plan_split(const Problem &p, int requested)
         // 256x256x65536 32 pieces 45.2, 2048x256x8192 8 pieces 26.8
         // (unsplit 36.1), 1024x1024x8192 4 pieces 41.5 (unsplit 48.0);
         // shorter K stays whole (512x512x2048 unsplit 10.3 against 13.5 for
-        // 2 pieces and 14.1 for 8).
+        // 2 pieces and 14.1 for 8).  A grid of at most 64 tiles takes at
+        // least 8 pieces (pieces of 512 K and more): 256x96x5000 12.5 us in
+        // 8 against 15.0 in 4, 256x256x4096 12.4 against 13.5, 512x48x4096
+        // 11.8 against 13.3.
         const int64_t occ = c.lds_bytes > 0 ? (160 * 1024) / c.lds_bytes : 1;
         const int64_t resident = kNumCu * (occ < 1 ? 1 : occ > 4 ? 4 : occ);
         if (tiles >= resident || p.K < 4096)
             s = 1;
         else {
             s = p.K / 1024;
+            if (tiles <= 64 && s < 8)
+                s = 8;
             const int64_t cap = cdiv(4 * kNumCu, tiles);
             if (s > cap)
                 s = cap;

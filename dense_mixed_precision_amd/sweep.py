@@ -3,13 +3,16 @@
     python -m dense_mixed_precision_amd.sweep --shapes 512x512,1024x2048 --ks 256,2048,8192 \\
         --configs 35,36,41 [--candidates] [--rounds 5] [--in f16|bf16] [--layout rr|cr|rc|cc]
     python -m dense_mixed_precision_amd.sweep --triples 5907x1622x137,652x11198x66 --configs 3,5,6
+    python -m dense_mixed_precision_amd.sweep --triples 256x256x8192 --splits 0,1,4,8,16,32
 
 For every M x N x K it captures, per forced table entry, a HIP graph of
 back-to-back launches of that entry (FP16 or BF16 operands, each row- or
 column-major, uniform inputs, alpha 1, beta 0), replays the graphs in
 alternating rounds and
 prints one line per shape: the median per-launch time of each entry, the
-factory's own choice and the fastest entry.  Launch overhead on the host is
+factory's own choice and the fastest entry.  With ``--splits`` the variants
+are split-K piece counts instead (0: the automatic plan, 1: one piece),
+each launched through the split-K entry with a workspace of its plan's size.  Launch overhead on the host is
 outside the graphs, so microsecond-scale kernels are timed as the GPU runs
 them back to back.
 """
@@ -25,7 +28,8 @@ def parse():
     p.add_argument("--shapes", help="comma-separated MxN pairs (with --ks)")
     p.add_argument("--ks", help="comma-separated K values (with --shapes)")
     p.add_argument("--triples", help="comma-separated MxNxK products (instead of --shapes and --ks)")
-    p.add_argument("--configs", required=True, help="comma-separated table entries to force")
+    p.add_argument("--configs", help="comma-separated table entries to force")
+    p.add_argument("--splits", help="comma-separated split-K piece counts to force (instead of --configs)")
     p.add_argument("--candidates", action="store_true", help="load the candidates build")
     p.add_argument("--rounds", type=int, default=5)
     p.add_argument("--seed", type=int, default=7)
@@ -52,7 +56,9 @@ def main():
         products = [(M, N, K) for (M, N), K in itertools.product(shapes, ks)]
     else:
         raise SystemExit("give --triples, or --shapes and --ks")
-    cfgs = [int(c) for c in args.configs.split(",")]
+    if bool(args.configs) == bool(args.splits):
+        raise SystemExit("give one of --configs and --splits")
+    cfgs = [int(c) for c in (args.configs or args.splits).split(",")]
     for M, N, K in products:
         dtype = torch.bfloat16 if args.in_type == "bf16" else torch.float16
         A, B, _ = make_inputs(M, N, K, "uniform", seed=args.seed, dtype=dtype)
@@ -60,7 +66,18 @@ def main():
         A = A.t().contiguous().to(dev).t() if args.layout[0] == "c" else A.to(dev)
         B = B.t().contiguous().to(dev).t() if args.layout[1] == "c" else B.to(dev)
         C = torch.empty(M, N, device=dev)
-        factory = mp.query_for(A, B, C)["id"]
+        if args.splits:
+            factory = 0
+            plans = {c: mp.splitk_plan_for(A, B, C, c) for c in cfgs}
+            ws = {c: torch.empty(max(plans[c]["workspace_bytes"] // 4, 1), device=dev) for c in cfgs}
+
+            def launch(c):
+                mp.gemm_splitk(A, B, C, 1.0, 0.0, splits=c, workspace=ws[c])
+        else:
+            factory = mp.query_for(A, B, C)["id"]
+
+            def launch(c):
+                mp.gemm(A, B, C, 1.0, 0.0, config=c)
         # about 0.4 ms of work per graph at 1 PFLOP/s, 4..40 launches
         per = max(4, min(40, int(4e5 / (2 * M * N * K / 1e6 + 1))))
         side = torch.cuda.Stream()
@@ -68,12 +85,12 @@ def main():
         for c in cfgs:
             with torch.cuda.stream(side):
                 for _ in range(2):
-                    mp.gemm(A, B, C, 1.0, 0.0, config=c)
+                    launch(c)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=side):
                 for _ in range(per):
-                    mp.gemm(A, B, C, 1.0, 0.0, config=c)
+                    launch(c)
             graphs[c] = g
         torch.cuda.synchronize()
         times = {c: [] for c in cfgs}
@@ -89,9 +106,14 @@ def main():
                 times[c].append(e0.elapsed_time(e1) * 1e3 / per)
         med = {c: sorted(v)[len(v) // 2] for c, v in times.items()}
         best = min(med, key=med.get)
-        print(json.dumps({"M": M, "N": N, "K": K, "factory": factory, "best": best,
-                          "factory_over_best": round(med[factory] / med[best], 3) if factory in med else None,
-                          "us": {str(c): round(v, 3) for c, v in med.items()}}), flush=True)
+        line = {"M": M, "N": N, "K": K, "factory": factory, "best": best,
+                "factory_over_best": round(med[factory] / med[best], 3) if factory in med else None,
+                "us": {str(c): round(v, 3) for c, v in med.items()}}
+        if args.splits:
+            line["pieces"] = {str(c): plans[c]["splits"] for c in cfgs}
+            line["config"] = {str(c): plans[c]["config_id"] for c in cfgs}
+            del ws
+        print(json.dumps(line), flush=True)
         del graphs, A, B, C
 
 

@@ -151,3 +151,6 @@ def test_sweep_tool_parses_its_arguments(monkeypatch):
     a = sweep.parse()
     assert (a.shapes, a.ks, a.configs, a.rounds, a.candidates) == ("256x512,1024x2048", "256,8192", "35,36,41",
                                                                     5, False)
+    monkeypatch.setattr(sys, "argv", ["sweep", "--triples", "256x96x5000", "--splits", "0,1,8"])
+    a = sweep.parse()
+    assert (a.triples, a.splits, a.configs) == ("256x96x5000", "0,1,8", None)
