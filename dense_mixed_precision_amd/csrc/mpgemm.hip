@@ -718,15 +718,19 @@ SplitPlan plan_split(const Problem &p, int requested)
         // 2 pieces and 14.1 for 8).  A grid of at most 64 tiles takes at
         // least 8 pieces (pieces of 512 K and more): 256x96x5000 12.5 us in
         // 8 against 15.0 in 4, 256x256x4096 12.4 against 13.5, 512x48x4096
-        // 11.8 against 13.3.
+        // 11.8 against 13.3.  A larger one takes at least 6 while that keeps
+        // it within 4 workgroups per unit: 640x640x4096 17.4 in 6 against
+        // 19.2 in 4, 1536x256x4096 17.5 against 19.3 (1024x1024x4096, 256
+        // tiles, keeps 4: 26.9 against 31.1 in 6).
         const int64_t occ = c.lds_bytes > 0 ? (160 * 1024) / c.lds_bytes : 1;
         const int64_t resident = kNumCu * (occ < 1 ? 1 : occ > 4 ? 4 : occ);
         if (tiles >= resident || p.K < 4096)
             s = 1;
         else {
             s = p.K / 1024;
-            if (tiles <= 64 && s < 8)
-                s = 8;
+            const int64_t floor_s = tiles <= 64 ? 8 : 6;
+            if (s < floor_s && tiles * floor_s <= 4 * kNumCu)
+                s = floor_s;
             const int64_t cap = cdiv(4 * kNumCu, tiles);
             if (s > cap)
                 s = cap;

@@ -296,8 +296,9 @@ int mpgemm_gemm_ex_with_config(int config_id, int in_type, int layout_a, int lay
  * would use (`splits_requested` 0: automatic, split only when K >= 4096
  * and the grid is under one wave of the workgroups the compute units hold
  * at once, into pieces of about 1024 K (at least 8 pieces for a grid of
- * at most 64 tiles), at most about 4 workgroups per compute unit and at
- * most 32 pieces; a product the factory gives the
+ * at most 64 tiles, at least 6 for a larger one while it stays within 4
+ * workgroups per compute unit), at most about 4 workgroups per compute
+ * unit and at most 32 pieces; a product the factory gives the
  * narrow kernel stays whole when it
  * has at least 64 groups of 16 rows; n > 0: a tile kernel's K tiles dealt
  * into n pieces, at most one per K tile.  Every piece but the last holds

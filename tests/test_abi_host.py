@@ -492,7 +492,9 @@ def test_splitk_plan_skinny_case_fills_the_chip():
     (2048, 2048, 8192, 1),                             # a full wave of 128x128 tiles
     (256, 256, 4096, 8), (256, 96, 5000, 8),           # at least 8 on grids of <= 64 tiles
     (512, 48, 4096, 8),
-    (768, 768, 6144, 6), (1024, 512, 4096, 4),         # larger grids keep 1024 K pieces
+    (768, 768, 6144, 6), (1024, 512, 4096, 6),         # at least 6 on larger grids ...
+    (640, 640, 4096, 6), (1280, 512, 4096, 6),
+    (1024, 1024, 4096, 4),                             # ... within 4 workgroups per unit
 ])
 def test_splitk_automatic_plan(M, N, K, pieces):
     """The automatic plan, by graph-replayed sweeps of forced piece counts."""

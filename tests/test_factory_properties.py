@@ -20,7 +20,7 @@ header and table state:
   last holding ceil(K tiles / pieces asked) K tiles (so a requested count
   n gives ceil(K tiles / ceil(K tiles / n)) pieces, at most n and at most
   one per K tile), and an automatic split only for K >= 4096, into at most
-  32 pieces of at least 1024 K (of at least 512 K when that makes 8).
+  32 pieces of at least 1024 K (of at least 512 K when that makes 6 or 8).
 """
 import pytest
 from hypothesis import HealthCheck, given, settings
@@ -140,8 +140,8 @@ def test_splitk_plan_obeys_its_contract(p, requested):
         n = min(requested, k_tiles)
         assert s == cdiv(k_tiles, cdiv(k_tiles, n)) and s <= n
     else:
-        # K of at least 4096, pieces of at least 1024 K (512 K for the floor
-        # of 8 pieces on small grids), at most 32
+        # K of at least 4096, pieces of at least 1024 K (512 K for the floors
+        # of 6 and 8 pieces), at most 32
         assert s <= 32 and K >= 4096 and s <= max(K // 1024, 8) and s <= K // 512
 
 
