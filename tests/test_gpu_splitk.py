@@ -92,6 +92,15 @@ def test_layouts(la, lb):
     check(f"layout {la}{lb}", A, B, C, 0.75, -1.0, la, lb)
 
 
+def test_floor_of_six_pieces_on_a_larger_grid():
+    """512 x 768 x 4096 (96 tiles of 64 x 64): the automatic plan takes 6
+    pieces of about 683 K rather than 4 of 1024 K."""
+    A, B, C = make_inputs(512, 768, 4096, "uniform", seed=93, c_init="uniform")
+    print("[splitk] floor of six", flush=True)
+    _, plan = check("floor of six", A, B, C, 1.0, 1.0)
+    assert plan["splits"] == 6
+
+
 def test_bf16_with_bias():
     A, B, C = make_inputs(512, 48, 4096, "uniform", seed=95, c_init="uniform", dtype=torch.bfloat16)
     bias = np.linspace(-1, 1, 48).astype(np.float32)
